@@ -1,0 +1,69 @@
+"""The five workload shapes of the routed-MoE expert path.
+
+Shapes follow the model geometry the Strata pages describe: hidden 2560,
+512 routed experts per layer, top-10, 48 layers (lcz.me/topic/2153,
+section 三 "Strata 的源码绑死了什么"; blog.5616760.com/0039.html, section 五
+"MoE 的本质"), the 1+3-token MTP verify window (devotd.net "Strata memory
+tiers", section "用草拟 token 提高生成速度的 MTP"), the 8192-token prefill
+chunk (same page, section "读取提示与写出回答时"; blog.5616760.com/0039.html
+section 七) and the DeepSeek-V4-Flash layer with 256 routed experts plus one
+shared expert (lcz.me/topic/2153, section 一).  Expert widths, block formats
+and value distributions are the workload definitions the pages leave open.
+
+Only storage parameters live here (bits per code, bytes per block); the
+dequantisation offsets belong to the arithmetic and are defined separately
+by each implementation.
+"""
+
+from dataclasses import dataclass
+from typing import Dict
+
+# fmt -> (bits per code, code bytes per 32-weight block)
+FORMATS: Dict[int, tuple] = {2: (2, 8), 3: (3, 12), 4: (4, 16)}
+BLOCK = 32          # weights per quantised block
+SCALE_BYTES = 2     # one fp16 scale per block, stored after the codes
+
+
+def canonical_block_bytes(fmt: int) -> int:
+    """Bytes of one canonical block: codes followed by the fp16 scale."""
+    return FORMATS[fmt][1] + SCALE_BYTES
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    hidden: int          # H
+    inter: int           # I, expert intermediate width
+    n_experts: int       # E routed experts per layer
+    top_k: int           # k
+    fmt: int             # 2 / 3 / 4 bit codes
+    tokens: int          # T per call
+    biased: bool         # log-Zipf router bias present
+    n_shared: int = 0    # always-on shared experts (0 or 1)
+    n_layers: int = 1    # layers in the stack
+    steps: int = 1       # decode steps in the stream (stack workload)
+    zipf_s: float = 1.1
+
+    def expert_bytes(self) -> int:
+        blk = canonical_block_bytes(self.fmt)
+        return 3 * self.inter * (self.hidden // BLOCK) * blk
+
+    def router_bytes(self) -> int:
+        return 4 * self.n_experts * self.hidden
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # single layer, one token, Q2, unbiased router
+    "decode_t1_q2": Workload("decode_t1_q2", 2560, 512, 512, 10, 2, 1, False),
+    # same layer, 1+3-token MTP verify batch, Zipf-skewed router
+    "mtp_verify_t4_q2": Workload("mtp_verify_t4_q2", 2560, 512, 512, 10, 2, 4, True),
+    # 48-layer Q3 stack, single-token decode stream of 256 steps
+    "stack48_q3_decode": Workload("stack48_q3_decode", 2560, 512, 512, 10, 3, 1, True,
+                                  n_layers=48, steps=256),
+    # 8192-token prefill chunk through one Q2 layer, Zipf-skewed router
+    "prefill_t8192_q2": Workload("prefill_t8192_q2", 2560, 512, 512, 10, 2, 8192, True),
+    # DeepSeek-V4-Flash-shaped layer, Q4, 256 routed + 1 shared, top-6
+    "deepseek_q4_t1": Workload("deepseek_q4_t1", 4096, 2048, 256, 6, 4, 1, True, n_shared=1),
+    "deepseek_q4_t2048": Workload("deepseek_q4_t2048", 4096, 2048, 256, 6, 4, 2048, True,
+                                  n_shared=1),
+}
