@@ -1,0 +1,172 @@
+/*
+ * strata_moe.h - C ABI of the MI355X (gfx950) routed mixture-of-experts FFN
+ * layer over low-bit block-quantised experts.
+ *
+ * The operation (blog.5616760.com/0039.html, section 五 "MoE 的本质": the
+ * router scores every expert of the layer, the top-k are selected and their
+ * outputs merged with softmax weights; ai-coding.wiselychen.com "Strata two
+ * weeks", section 成功思路一: the GPU computes the selected experts and sums
+ * their results; lcz.me/topic/2153, section 一: 256 routed experts plus one
+ * always-on shared expert in the DeepSeek-shaped layer), per token t:
+ *
+ *   l[t,e]  = sum_h x[t,h] Wr[e,h] + b[e]                  router logits
+ *   S_t     = the k largest l[t,.]                          top-k
+ *   w[t,j]  = softmax of l[t,.] over S_t                    renormalised weights
+ *   y_e(x)  = Wd_e (silu(Wg_e x) * (Wu_e x))                SwiGLU expert
+ *   out[t]  = sum_{e in S_t} w[t,e] y_e(x_t) [+ y_shared(x_t)] [+ x_t | + out_t]
+ *
+ * Expert weights are 32-weight blocks: b-bit codes q then an fp16 scale d,
+ * w = d (q - c): Q2 (8 code bytes, c = 1.5), Q3 (12 bytes, c = 3.5),
+ * Q4 (16 bytes, c = 8).  Code j of a block occupies bits [b*j, b*j+b) of
+ * the code bytes read as one little-endian bit string.
+ *
+ * Canonical expert record (the input of strata_moe_create): gate
+ * [I rows][H/32 blocks], up [I][H/32], down [H rows][I/32 blocks], each
+ * block = code bytes followed by the little-endian fp16 scale, no padding.
+ * Routed experts are stored back to back in expert-id order.
+ *
+ * Conventions
+ *  - Every pointer named "device" is HIP device memory owned by the caller.
+ *    The library never allocates or frees device memory and never
+ *    synchronises inside route/forward.
+ *  - Streams are hipStream_t passed as void* (NULL = the null stream).
+ *  - Every function returning int returns STRATA_OK or a negative status;
+ *    argument checks run on the host before anything is enqueued, and the
+ *    reason is available from strata_moe_last_error() (thread-local).
+ *    Nothing aborts and no C++ exception crosses the ABI.
+ *  - One handle's workspace serves one call at a time: calls on one handle
+ *    must be ordered on one stream.  Distinct handles (with distinct
+ *    workspaces) are independent.
+ */
+#ifndef STRATA_MOE_H
+#define STRATA_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define STRATA_API __attribute__((visibility("default")))
+#else
+#define STRATA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    STRATA_OK = 0,
+    STRATA_E_INVALID = -1,      /* bad argument (shape, pointer, size, flag) */
+    STRATA_E_UNSUPPORTED = -2,  /* valid but outside what the kernels cover  */
+    STRATA_E_HIP = -3           /* a HIP runtime call or launch failed       */
+};
+
+enum { STRATA_Q2 = 2, STRATA_Q3 = 3, STRATA_Q4 = 4 };      /* expert block format */
+enum { STRATA_BF16 = 0, STRATA_FP32 = 1 };                 /* activation dtype    */
+
+/* forward flags */
+enum {
+    STRATA_ACCUMULATE = 1u,     /* out[t] += moe(x)[t]                          */
+    STRATA_ADD_INPUT = 2u,      /* out[t]  = x[t] + moe(x)[t] (residual)        */
+    STRATA_FORCE_DECODE = 4u,   /* use the GEMV path (T <= STRATA_DECODE_MAX_T) */
+    STRATA_FORCE_PREFILL = 8u   /* use the grouped-GEMM path at any T           */
+};
+
+/* Calls with T <= STRATA_DECODE_MAX_T take the decode (GEMV) path unless
+ * STRATA_FORCE_PREFILL is given; larger T take the grouped-GEMM path. */
+#define STRATA_DECODE_MAX_T 8
+
+typedef struct {
+    int32_t hidden;      /* H: multiple of 256                                */
+    int32_t inter;       /* I: expert intermediate width, multiple of 256     */
+    int32_t n_experts;   /* E: routed experts, 1..4096                        */
+    int32_t top_k;       /* k: 1..min(E, 64)                                  */
+    int32_t n_shared;    /* 0 or 1 always-on shared expert (weight 1)         */
+    int32_t qfmt;        /* STRATA_Q2 / STRATA_Q3 / STRATA_Q4                 */
+    int32_t max_tokens;  /* largest T any call on the handle will pass, >= 1  */
+} strata_moe_config;
+
+typedef struct strata_moe strata_moe;   /* opaque; one per MoE layer */
+
+/* Bytes of one canonical expert record, 3 * I * (H/32) * (code bytes + 2).
+ * Returns 0 for an invalid config. */
+STRATA_API size_t strata_moe_expert_bytes(const strata_moe_config* cfg);
+
+/* Bytes of the device buffer `packed` that strata_moe_create fills: the
+ * experts (routed, then shared) repacked into the kernels' layout (the same
+ * byte count as the canonical records) plus a bf16 hi/lo split of the
+ * router rows.  Returns 0 for an invalid config. */
+STRATA_API size_t strata_moe_packed_bytes(const strata_moe_config* cfg);
+
+/* Bytes of the device buffer `workspace` (router logits, top-k, counts,
+ * offsets, permutation, per-pair activations and outputs, ticket counters),
+ * sized for cfg->max_tokens.  Returns 0 for an invalid config. */
+STRATA_API size_t strata_moe_workspace_bytes(const strata_moe_config* cfg);
+
+/*
+ * Build a layer handle.
+ *   router_w       device, fp32 [E][H] row-major; borrowed for the handle's life
+ *   router_bias    device, fp32 [E], or NULL for no bias; borrowed
+ *   experts_canon  device, E canonical records back to back; read during the
+ *                  call only (may be freed once it returns)
+ *   shared_canon   device, one canonical record if n_shared = 1, else NULL;
+ *                  read during the call only
+ *   packed         device, strata_moe_packed_bytes(cfg) bytes, 256-B aligned;
+ *                  filled here and borrowed for the handle's life
+ *   workspace      device, strata_moe_workspace_bytes(cfg) bytes, 256-B aligned;
+ *                  borrowed for the handle's life (its counters are zeroed here)
+ *   stream         the repack runs on it; the call synchronises it before
+ *                  returning
+ *   out            receives the handle (host memory, freed by _destroy)
+ */
+STRATA_API int strata_moe_create(const strata_moe_config* cfg, const float* router_w,
+                      const float* router_bias, const void* experts_canon,
+                      const void* shared_canon, void* packed, void* workspace,
+                      void* stream, strata_moe** out);
+
+/*
+ * Routing only (router logits, top-k, renormalised weights, stable
+ * token->expert permutation).  All outputs are device buffers:
+ *   x          device, [T][H] of x_dtype (STRATA_BF16 or STRATA_FP32)
+ *   topk_idx   int32 [T][k], expert ids of S_t in ascending order
+ *   topk_w     fp32  [T][k], weights matching topk_idx
+ *   perm       int32 [T*k], sorted slot -> pair p = t*k + j, pairs ordered
+ *              by (expert, p)
+ *   offsets    int32 [E+1], first slot of each expert; offsets[E] = T*k
+ * T must be in [1, max_tokens].  Uses the same kernels as strata_moe_forward
+ * for the same T and flags (STRATA_FORCE_DECODE / STRATA_FORCE_PREFILL).
+ */
+STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
+                     int32_t* topk_idx, float* topk_w, int32_t* perm,
+                     int32_t* offsets, uint32_t flags, void* stream);
+
+/*
+ * The full layer: out[T][H] fp32 (device) = moe(x), or with
+ * STRATA_ACCUMULATE out += moe(x), or with STRATA_ADD_INPUT out = x + moe(x).
+ * x and out must not overlap.  Stream-ordered and asynchronous.
+ */
+STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
+                       float* out, uint32_t flags, void* stream);
+
+/*
+ * A stack of MoE layers with residual adds (48 layers x 512 experts is the
+ * Qwen3.8-Flash-Next expert set of the pages: ai-coding.wiselychen.com
+ * "Strata two weeks", Table 1):  h_0 = x,  h_{l+1} = h_l + moe_l(h_l),
+ * computed in fp32.  The final h is written to `out` (device fp32 [T][H]);
+ * `tmp` (device fp32 [T][H]) is scratch for the ping-pong.  Layers must share
+ * H and run their calls on this stream; x must not overlap out or tmp.
+ */
+STRATA_API int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers,
+                             const void* x, int32_t x_dtype, int32_t T,
+                             float* out, float* tmp, void* stream);
+
+/* Free the host-side handle.  NULL-safe.  Device buffers stay the caller's. */
+STRATA_API void strata_moe_destroy(strata_moe* h);
+
+/* Message for the last failing call on this thread ("" if none). */
+STRATA_API const char* strata_moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* STRATA_MOE_H */

@@ -19,6 +19,9 @@ consumes): gate [I rows][H/32 blocks], up [I][H/32], down [H][I/32]; each
 block is its code bytes followed by the little-endian fp16 scale.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .workloads import FORMATS, BLOCK, canonical_block_bytes
@@ -84,8 +87,13 @@ def layer_canonical(seed: int, layer: int, hidden: int, inter: int, n_experts: i
     """All routed experts of a layer, [E, record_bytes] uint8, expert-id order."""
     rec = _expert_blocks(hidden, inter) * canonical_block_bytes(fmt)
     out = np.empty((n_experts, rec), dtype=np.uint8)
-    for e in range(n_experts):
+
+    def fill(e):
         out[e] = expert_canonical(seed, layer, e, hidden, inter, fmt)
+
+    # each expert has its own generator, so the draws are independent of the thread count
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, range(n_experts)))
     return out
 
 

@@ -50,13 +50,13 @@ def block_bytes(fmt):
 def unpack_codes(code_bytes, bits):
     """Codes of a little-endian bit string: code j = bits [bits*j, bits*j+bits).
 
-    code_bytes: uint8 [..., nbytes]  ->  int64 [..., nbytes*8 // bits]
+    code_bytes: uint8 [..., nbytes]  ->  int16 [..., nbytes*8 // bits]
     """
     stream = np.unpackbits(np.asarray(code_bytes, dtype=np.uint8), axis=-1, bitorder="little")
     n = stream.shape[-1] // bits
-    stream = stream[..., : n * bits].reshape(*stream.shape[:-1], n, bits).astype(np.int64)
-    place = np.int64(1) << np.arange(bits, dtype=np.int64)
-    return (stream * place).sum(axis=-1)
+    stream = stream[..., : n * bits].reshape(*stream.shape[:-1], n, bits)
+    place = (np.uint8(1) << np.arange(bits, dtype=np.uint8))     # bit i of a code weighs 2^i
+    return (stream * place).sum(axis=-1, dtype=np.int16)
 
 
 def dequant_blocks(blocks, fmt):

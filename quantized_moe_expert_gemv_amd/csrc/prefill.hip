@@ -1,0 +1,520 @@
+// Prefill path (T > 8): the batched regime of the pages, where one prepared
+// expert weight serves many tokens of a prefill chunk of up to 8192 tokens
+// (devotd.net "Strata memory tiers", section 读取提示与写出回答时;
+// blog.5616760.com/0039.html, section 七).  Here every expert is resident in
+// HBM, so the chunk is a grouped, genuinely dense contraction and runs on
+// the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//
+//   k_router_gemm    logits = x Wr^T + b, fp32-accurate from bf16 MFMA by
+//                    splitting Wr (and an fp32 x) into bf16 high + low parts
+//   k_topk_chunks    top-k + renormalised softmax per token (one wave per
+//                    token) and, per chunk of 32 tokens, the expert
+//                    histogram and every pair's rank inside the chunk
+//   k_scan           per-expert chunk bases, counts, offsets and the flat
+//                    list of (expert, 128-row tile) GEMM work items
+//   k_scatter        the stable permutation: slot of pair p =
+//                    offset[e] + base[e][chunk] + rank  (no atomics, so the
+//                    order is (expert, p) on every run)
+//   k_gemm_gateup    per work item: gathered token rows x rows of dequantised
+//                    gate|up weights staged as bf16 in LDS -> SwiGLU -> bf16
+//   k_gemm_down      per work item: SwiGLU rows x dequantised down weights ->
+//                    per-pair fp32 output rows
+//   k_combine        out[t] = sum_j w[t, j] y[slot(t, j)] (+ shared, residual)
+//
+// Dequantised weights d (q - c) are rounded to bf16 (8-bit mantissa) before
+// the MFMA; activations are bf16 (exact for bf16 inputs).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace strata {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int BM = PREFILL_BM;      // 128 token rows
+constexpr int BN = 128;             // output columns per tile
+constexpr int BK = 64;              // reduction step (two quantised blocks)
+constexpr int LDK = BK + 8;         // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
+constexpr int CT = PREFILL_CHUNK_T;
+
+__device__ inline float ld_coherent_f(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline bf16x8 lds_frag(const uint16_t* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ inline uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
+
+// 8 fp32 -> 8 bf16 (RNE) as a 16-B vector; optionally the bf16 of the remainder
+__device__ inline uint4 to_bf16x8(const float* f, uint4* rem) {
+  uint16_t h[8], r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = f32_to_bf16_rne(f[i]);
+    if (rem) r[i] = f32_to_bf16_rne(f[i] - bf16_to_f32(h[i]));
+  }
+  if (rem) *rem = make_uint4(pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7]));
+  return make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+}
+
+// One wave's 64x64 sub-tile: 2 x 2 MFMA 32x32 tiles over one BK step.
+__device__ inline void mma_step(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[2][2],
+                                int wm, int wn, int lane) {
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ++ks) {
+    const int kof = ks * 16 + 8 * (lane >> 5);
+    bf16x8 af[2], bfr[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) af[mt] = lds_frag(As + (64 * wm + 32 * mt + (lane & 31)) * LDK + kof);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) bfr[nt] = lds_frag(Bs + (64 * wn + 32 * nt + (lane & 31)) * LDK + kof);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+  }
+}
+
+// row of element v of a 32x32 accumulator held by `lane`
+__device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// Dequantise one 32-weight block (codes + scale in the packed layout) of one
+// weight row into 32 bf16 at dst (LDS, 16-B aligned).
+template <int FMT>
+__device__ inline void dequant_block_to_lds(const uint8_t* rowsb /* row's superblock base */,
+                                            int bb, uint16_t* dst) {
+  constexpr int NCV = Fmt<FMT>::ncv;
+  constexpr float C = Fmt<FMT>::c;
+  const uint16_t draw = *reinterpret_cast<const uint16_t*>(rowsb + NCV * 1024 + bb * 2);
+  const float d = half_bits_to_f32(draw);
+  float w[32];
+  if constexpr (FMT == 2) {
+    const uint2 c = *reinterpret_cast<const uint2*>(rowsb + (bb >> 1) * 1024 + (bb & 1) * 8);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t W = (j < 16) ? c.x : c.y;
+      w[j] = d * ((float)((W >> (2 * (j & 15))) & 3u) - C);
+    }
+  } else if constexpr (FMT == 4) {
+    const uint4 c = *reinterpret_cast<const uint4*>(rowsb + bb * 1024);
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) w[j] = d * ((float)((cw[j >> 3] >> (4 * (j & 7))) & 15u) - C);
+  } else {
+    const uint2 c = *reinterpret_cast<const uint2*>(rowsb + (bb >> 1) * 1024 + (bb & 1) * 8);
+    const uint32_t hw = *reinterpret_cast<const uint32_t*>(rowsb + (4 + (bb >> 2)) * 1024 + (bb & 3) * 4);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t W = (j < 16) ? c.x : c.y;
+      const int ww = j >> 4, i = (j & 15) >> 2, s = j & 3;
+      const uint32_t q = ((W >> (2 * (j & 15))) & 3u) | (((hw >> (8 * i + 4 * ww + s)) & 1u) << 2);
+      w[j] = d * ((float)q - C);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<uint4*>(dst + 8 * q) = to_bf16x8(w + 8 * q, nullptr);
+}
+
+// ------------------------------------------------------------------ router GEMM
+struct RouterArgs {
+  const void* x;
+  int x_f32, T, H, E;
+  const uint16_t* whi;
+  const uint16_t* wlo;
+  const float* bias;
+  float* logits;
+};
+
+template <bool XF32>
+__global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ahi[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Alo[XF32 ? BM * LDK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t Bhi[BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Blo[BN * LDK];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+  const int t0 = blockIdx.y * BM, e0 = blockIdx.x * BN;
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < a.H; k0 += BK) {
+    // A: 128 rows x 64 bf16 (8 chunks of 16 B per row)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+      const int t = t0 + r;
+      uint4 hv = make_uint4(0, 0, 0, 0), lv = make_uint4(0, 0, 0, 0);
+      if (t < a.T) {
+        if constexpr (XF32) {
+          const float* src = reinterpret_cast<const float*>(a.x) + (size_t)t * a.H + k0 + kc * 8;
+          float f[8];
+          *reinterpret_cast<float4*>(f) = *reinterpret_cast<const float4*>(src);
+          *reinterpret_cast<float4*>(f + 4) = *reinterpret_cast<const float4*>(src + 4);
+          hv = to_bf16x8(f, &lv);
+        } else {
+          hv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H + k0 + kc * 8);
+        }
+      }
+      *reinterpret_cast<uint4*>(Ahi + r * LDK + kc * 8) = hv;
+      if constexpr (XF32) *reinterpret_cast<uint4*>(Alo + r * LDK + kc * 8) = lv;
+      // B: router rows e0 + r, hi and lo planes
+      const int e = e0 + r;
+      uint4 bh = make_uint4(0, 0, 0, 0), bl = make_uint4(0, 0, 0, 0);
+      if (e < a.E) {
+        bh = *reinterpret_cast<const uint4*>(a.whi + (size_t)e * a.H + k0 + kc * 8);
+        bl = *reinterpret_cast<const uint4*>(a.wlo + (size_t)e * a.H + k0 + kc * 8);
+      }
+      *reinterpret_cast<uint4*>(Bhi + r * LDK + kc * 8) = bh;
+      *reinterpret_cast<uint4*>(Blo + r * LDK + kc * 8) = bl;
+    }
+    __syncthreads();
+    mma_step(Ahi, Bhi, acc, wm, wn, lane);
+    mma_step(Ahi, Blo, acc, wm, wn, lane);
+    if constexpr (XF32) mma_step(Alo, Bhi, acc, wm, wn, lane);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = t0 + 64 * wm + 32 * mt + acc_row(v, lane);
+        const int e = e0 + 64 * wn + 32 * nt + (lane & 31);
+        if (t < a.T && e < a.E) a.logits[(size_t)t * a.E + e] = acc[mt][nt][v] + (a.bias ? a.bias[e] : 0.f);
+      }
+}
+
+// ------------------------------------------------------------------ routing
+struct TopkArgs {
+  int T, E, k, nchunks;
+  Work w;
+};
+
+__global__ __launch_bounds__(256) void k_topk_chunks(TopkArgs a) {
+  extern __shared__ int lds_i[];
+  int* sel = lds_i;                 // [CT][k]
+  int* hist = sel + CT * a.k;       // [E]
+  __shared__ int s_sel[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int chunk = blockIdx.x, tb = chunk * CT;
+  const int k = a.k, E = a.E;
+  for (int tl = wv; tl < CT; tl += 4) {
+    const int t = tb + tl;
+    if (t < a.T) {
+      wave_topk(a.w.logits + (size_t)t * E, E, k, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int nt = min(CT, a.T - tb);
+  for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
+    const int e = sel[i];
+    a.w.topk_idx[(size_t)tb * k + i] = e;
+    atomicAdd(&hist[e], 1);
+    // rank among this chunk's earlier tokens that chose e (each token's ids are sorted)
+    const int tl = i / k;
+    int rank = 0;
+    for (int t2 = 0; t2 < tl; ++t2) {
+      const int* s2 = sel + t2 * k;
+      int lo = 0, hi = k;
+      while (lo < hi) { const int mid = (lo + hi) >> 1; if (s2[mid] < e) lo = mid + 1; else hi = mid; }
+      rank += (lo < k && s2[lo] == e);
+    }
+    a.w.pair_rank[(size_t)tb * k + i] = rank;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)e * a.nchunks + chunk] = hist[e];
+}
+
+struct ScanArgs {
+  int T, E, k, n_shared, nchunks;
+  Work w;
+};
+
+__global__ __launch_bounds__(1024) void k_scan(ScanArgs a) {
+  __shared__ int2 tmp[16];
+  const int E = a.E, P = a.T * a.k, nch = a.nchunks;
+  // per expert: running sum over chunks (in place -> chunk bases) and the count
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int* row = a.w.chunk_base + (size_t)e * nch;
+    int run = 0;
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nch) ? row[c0 + i] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < nch) row[c0 + i] = run;
+        run += v[i];
+      }
+    }
+    a.w.counts[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan over experts (the shared expert is entry E) of (count, tiles)
+  const int n_ent = E + (a.n_shared ? 1 : 0);
+  const int per = (n_ent + blockDim.x - 1) / blockDim.x;
+  const int e0 = threadIdx.x * per;
+  auto cnt_of = [&](int e) { return e < E ? a.w.counts[e] : a.T; };
+  int2 loc = make_int2(0, 0);
+  for (int e = e0; e < min(n_ent, e0 + per); ++e) {
+    const int c = cnt_of(e);
+    loc.x += (e < E) ? c : 0;
+    loc.y += (c + BM - 1) / BM;
+  }
+  int2 total;
+  int2 base = block_exclusive_scan(loc, tmp, &total);
+  for (int e = e0; e < min(n_ent, e0 + per); ++e) {
+    const int c = cnt_of(e);
+    const int first = (e < E) ? base.x : P;
+    if (e < E) a.w.offsets[e] = base.x;
+    const int nt = (c + BM - 1) / BM;
+    for (int q = 0; q < nt; ++q)
+      a.w.tiles[base.y + q] = make_int4(e, first + q * BM, min(BM, c - q * BM), 0);
+    if (e < E) base.x += c;
+    base.y += nt;
+  }
+  if (threadIdx.x == 0) {
+    a.w.offsets[E] = P;
+    a.w.meta[1] = total.y;
+  }
+}
+
+__global__ void k_scatter(TopkArgs a) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  const int P = a.T * a.k;
+  if (p >= P) return;
+  const int e = a.w.topk_idx[p];
+  const int chunk = (p / a.k) / CT;
+  const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)e * a.nchunks + chunk] + a.w.pair_rank[p];
+  a.w.perm[slot] = p;
+  a.w.inv[p] = slot;
+}
+
+// ------------------------------------------------------------------ grouped GEMMs
+struct GemmArgs {
+  const uint8_t* packed;
+  size_t stride;
+  int H, I, E, k, T, P;
+  const void* x;
+  int x_f32;
+  Work w;
+};
+
+template <int FMT, bool XF32>
+__global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  __shared__ const void* rowsrc[BM];
+  const int j = blockIdx.y;
+  if (j >= a.w.meta[1]) return;
+  const int4 tl = a.w.tiles[j];
+  const int e = tl.x, slot0 = tl.y, rows = tl.z;
+  const int itile = blockIdx.x;                       // 64 intermediate rows: gate + up = 128 columns
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+  constexpr int NV = Fmt<FMT>::ncv + 1;
+  const int nsbH = a.H / SB_WEIGHTS;
+  if (tid < BM) {
+    const void* p = nullptr;
+    if (tid < rows) {
+      const int slot = slot0 + tid;
+      const int t = slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
+      p = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + (size_t)t * a.H)
+               : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H);
+    }
+    rowsrc[tid] = p;
+  }
+  // B column n of this tile: matrix (n % 64) / 32 (0 gate, 1 up), row (n / 64) * 32 + n % 32
+  const int bn = tid >> 1, bhalf = tid & 1;
+  const int bmat = (bn & 63) >> 5, brow = (bn >> 6) * 32 + (bn & 31);
+  const uint8_t* bsrc = a.packed + (size_t)e * a.stride + gu_off(NV, nsbH, itile, 0, bmat, 0) + brow * 16;
+  __syncthreads();
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < a.H; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+      uint4 hv = make_uint4(0, 0, 0, 0);
+      const void* src = rowsrc[r];
+      if (src) {
+        if constexpr (XF32) {
+          const float* f = reinterpret_cast<const float*>(src) + k0 + kc * 8;
+          float v[8];
+          *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(f);
+          *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(f + 4);
+          hv = to_bf16x8(v, nullptr);
+        } else {
+          hv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + k0 + kc * 8);
+        }
+      }
+      *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
+    }
+    const int sb = k0 / SB_WEIGHTS, bb = (k0 % SB_WEIGHTS) / BLOCK_W + bhalf;
+    dequant_block_to_lds<FMT>(bsrc + (size_t)sb * 2 * NV * 1024, bb, Bs + bn * LDK + bhalf * 32);
+    __syncthreads();
+    mma_step(As, Bs, acc, wm, wn, lane);
+    __syncthreads();
+  }
+  // SwiGLU epilogue: nt = 0 holds gate, nt = 1 up, for the same 32 rows i
+  uint16_t* act = reinterpret_cast<uint16_t*>(a.w.act);
+  const int i = itile * 64 + wn * 32 + (lane & 31);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 64 * wm + 32 * mt + acc_row(v, lane);
+      if (m < rows) {
+        const float g = acc[mt][0][v], u = acc[mt][1][v];
+        act[(size_t)(slot0 + m) * a.I + i] = f32_to_bf16_rne(silu_f(g) * u);
+      }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  const int j = blockIdx.y;
+  if (j >= a.w.meta[1]) return;
+  const int4 tl = a.w.tiles[j];
+  const int e = tl.x, slot0 = tl.y, rows = tl.z;
+  const int h0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+  constexpr int NV = Fmt<FMT>::ncv + 1;
+  const int nsbI = a.I / SB_WEIGHTS;
+  const int bn = tid >> 1, bhalf = tid & 1;
+  const int hrow = h0 + bn;
+  const uint8_t* bsrc = a.packed + (size_t)e * a.stride + gu_bytes(FMT, a.H, a.I) +
+                        dn_off(NV, nsbI, hrow / 64, 0, 0) + (hrow % 64) * 16;
+  const uint16_t* act = reinterpret_cast<const uint16_t*>(a.w.act);
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < a.I; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+      uint4 hv = make_uint4(0, 0, 0, 0);
+      if (r < rows) hv = *reinterpret_cast<const uint4*>(act + (size_t)(slot0 + r) * a.I + k0 + kc * 8);
+      *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
+    }
+    const int sb = k0 / SB_WEIGHTS, bb = (k0 % SB_WEIGHTS) / BLOCK_W + bhalf;
+    dequant_block_to_lds<FMT>(bsrc + (size_t)sb * NV * 1024, bb, Bs + bn * LDK + bhalf * 32);
+    __syncthreads();
+    mma_step(As, Bs, acc, wm, wn, lane);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = 64 * wm + 32 * mt + acc_row(v, lane);
+        if (m < rows) a.w.y[(size_t)(slot0 + m) * a.H + h0 + 64 * wn + 32 * nt + (lane & 31)] = acc[mt][nt][v];
+      }
+}
+
+struct CombineArgs {
+  int T, H, k, P, n_shared;
+  const void* x;
+  int x_f32;
+  uint32_t flags;
+  float* out;
+  Work w;
+};
+
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  const int t = blockIdx.x;
+  const int k = a.k;
+  __shared__ int s_slot[64];
+  __shared__ float s_w[64];
+  if (threadIdx.x < k) {
+    s_slot[threadIdx.x] = a.w.inv[t * k + threadIdx.x];
+    s_w[threadIdx.x] = a.w.topk_w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int h = threadIdx.x * 4; h < a.H; h += blockDim.x * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 y = *reinterpret_cast<const float4*>(a.w.y + (size_t)s_slot[j] * a.H + h);
+      const float wj = s_w[j];
+      acc.x = fmaf(wj, y.x, acc.x); acc.y = fmaf(wj, y.y, acc.y);
+      acc.z = fmaf(wj, y.z, acc.z); acc.w = fmaf(wj, y.w, acc.w);
+    }
+    if (a.n_shared) {
+      const float4 y = *reinterpret_cast<const float4*>(a.w.y + (size_t)(a.P + t) * a.H + h);
+      acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
+    }
+    const size_t o = (size_t)t * a.H + h;
+    if (a.flags & 2u) {
+      if (a.x_f32) {
+        const float4 xv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + o);
+        acc.x += xv.x; acc.y += xv.y; acc.z += xv.z; acc.w += xv.w;
+      } else {
+        const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + o);
+        acc.x += __uint_as_float(r.x << 16); acc.y += __uint_as_float(r.x & 0xffff0000u);
+        acc.z += __uint_as_float(r.y << 16); acc.w += __uint_as_float(r.y & 0xffff0000u);
+      }
+    }
+    if (a.flags & 1u) {
+      const float4 ov = *reinterpret_cast<const float4*>(a.out + o);
+      acc.x += ov.x; acc.y += ov.y; acc.z += ov.z; acc.w += ov.w;
+    }
+    *reinterpret_cast<float4*>(a.out + o) = acc;
+  }
+}
+
+template <int FMT>
+hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+  GemmArgs g;
+  g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
+  g.T = c.T; g.P = c.T * L.k; g.x = c.x; g.x_f32 = c.x_f32; g.w = W;
+  const int max_tiles = W.max_tiles;
+  if (c.x_f32)
+    hipLaunchKernelGGL((k_gemm_gateup<FMT, true>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL((k_gemm_gateup<FMT, false>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_down<FMT>), dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+  RouterArgs r;
+  r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
+  r.whi = L.router_hi; r.wlo = L.router_lo; r.bias = L.router_b; r.logits = W.logits;
+  dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM);
+  if (c.x_f32) hipLaunchKernelGGL(k_router_gemm<true>, grid, dim3(256), 0, s, r);
+  else hipLaunchKernelGGL(k_router_gemm<false>, grid, dim3(256), 0, s, r);
+  TopkArgs t;
+  t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
+  const size_t lds = ((size_t)CT * L.k + L.E) * 4;
+  hipLaunchKernelGGL(k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
+  ScanArgs sa;
+  sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, sa);
+  const int P = c.T * L.k;
+  hipLaunchKernelGGL(k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+  hipError_t err;
+  switch (L.fmt) {
+    case 2: err = launch_gemms_fmt<2>(L, W, c, s); break;
+    case 3: err = launch_gemms_fmt<3>(L, W, c, s); break;
+    default: err = launch_gemms_fmt<4>(L, W, c, s); break;
+  }
+  if (err != hipSuccess) return err;
+  CombineArgs cb;
+  cb.T = c.T; cb.H = L.H; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
+  cb.x = c.x; cb.x_f32 = c.x_f32; cb.flags = c.flags; cb.out = c.out; cb.w = W;
+  hipLaunchKernelGGL(k_combine, dim3(c.T), dim3(256), 0, s, cb);
+  return hipGetLastError();
+}
+
+}  // namespace strata

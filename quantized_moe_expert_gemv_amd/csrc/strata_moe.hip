@@ -1,0 +1,340 @@
+// C ABI of the strata_moe library: argument checks, buffer layouts and the
+// per-call kernel sequence.  The operation each entry point performs is
+// specified in include/strata_moe.h.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+#include <string>
+#include <new>
+
+#include "strata_moe.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace strata;
+
+namespace strata {
+hipError_t prepare_decode_kernels(const Layer& L, int max_tokens);
+}
+
+struct strata_moe {
+  strata_moe_config cfg;
+  Layer L;
+  Work W;          // regions sized for cfg.max_tokens (max_tiles set per call)
+  uint8_t* ws;
+  size_t ws_bytes;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return STRATA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_config(const strata_moe_config* c) {
+  if (!c) return fail(STRATA_E_INVALID, "config is NULL");
+  if (c->qfmt != STRATA_Q2 && c->qfmt != STRATA_Q3 && c->qfmt != STRATA_Q4)
+    return fail(STRATA_E_INVALID, "qfmt %d is not 2, 3 or 4", c->qfmt);
+  if (c->hidden <= 0 || c->inter <= 0) return fail(STRATA_E_INVALID, "hidden and inter must be positive");
+  if (c->hidden % 256 || c->inter % 256)
+    return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 256",
+                c->hidden, c->inter);
+  if (c->n_experts < 1 || c->n_experts > 4096)
+    return fail(STRATA_E_INVALID, "n_experts %d outside [1, 4096]", c->n_experts);
+  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 64)
+    return fail(STRATA_E_INVALID, "top_k %d outside [1, min(n_experts, 64)]", c->top_k);
+  if (c->n_shared != 0 && c->n_shared != 1) return fail(STRATA_E_INVALID, "n_shared must be 0 or 1");
+  if (c->max_tokens < 1) return fail(STRATA_E_INVALID, "max_tokens must be >= 1");
+  if ((long long)c->max_tokens * c->top_k > (1LL << 30) / 4)
+    return fail(STRATA_E_UNSUPPORTED, "max_tokens * top_k too large");
+  return STRATA_OK;
+}
+
+struct WsPlan {
+  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, uexp, uoff, meta, tickets,
+      chunk_base, pair_rank, tiles, act, y, total;
+  int nchunks, max_tiles;
+};
+
+int max_tiles_for(const strata_moe_config& c, int T) {
+  const long long P = (long long)T * c.top_k;
+  const long long t = (P + PREFILL_BM - 1) / PREFILL_BM + (P < c.n_experts ? P : c.n_experts) +
+                      (long long)c.n_shared * ((T + PREFILL_BM - 1) / PREFILL_BM);
+  return (int)t;
+}
+
+WsPlan plan_workspace(const strata_moe_config& c) {
+  WsPlan p;
+  const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  const size_t P = T * k, slots = P + (size_t)c.n_shared * T;
+  p.nchunks = (int)((T + PREFILL_CHUNK_T - 1) / PREFILL_CHUNK_T);
+  p.max_tiles = max_tiles_for(c, (int)T);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+  p.logits = take(T * E * 4);
+  p.topk_idx = take(P * 4);
+  p.topk_w = take(P * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.perm = take(P * 4);
+  p.inv = take(P * 4);
+  p.uexp = take((E + 1) * 4);
+  p.uoff = take((E + 2) * 4);
+  p.meta = take(16 * 4);
+  p.tickets = take((H / 64 + 1) * 4);
+  p.chunk_base = take(E * (size_t)p.nchunks * 4);
+  p.pair_rank = take(P * 4);
+  p.tiles = take((size_t)p.max_tiles * 16);
+  p.act = take(slots * I * 4);
+  p.y = take(slots * H * 4);
+  p.total = o;
+  return p;
+}
+
+size_t packed_experts_bytes(const strata_moe_config& c) {
+  return align256((size_t)(c.n_experts + c.n_shared) * expert_bytes(c.qfmt, c.hidden, c.inter));
+}
+
+size_t packed_total(const strata_moe_config& c) {
+  return packed_experts_bytes(c) + 2 * align256((size_t)c.n_experts * c.hidden * 2);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(STRATA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_call(strata_moe* h, const void* x, int32_t x_dtype, int32_t T) {
+  if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
+  if (!x) return fail(STRATA_E_INVALID, "x is NULL");
+  if (x_dtype != STRATA_BF16 && x_dtype != STRATA_FP32)
+    return fail(STRATA_E_INVALID, "x_dtype %d is not STRATA_BF16 or STRATA_FP32", x_dtype);
+  if (T < 1 || T > h->cfg.max_tokens)
+    return fail(STRATA_E_INVALID, "T = %d outside [1, max_tokens = %d]", T, h->cfg.max_tokens);
+  if (!aligned(x, 16)) return fail(STRATA_E_INVALID, "x must be 16-byte aligned");
+  return STRATA_OK;
+}
+
+bool use_decode(int T, uint32_t flags) {
+  if (flags & STRATA_FORCE_PREFILL) return false;
+  return T <= STRATA_DECODE_MAX_T;
+}
+
+int check_flags(int T, uint32_t flags) {
+  const uint32_t known = STRATA_ACCUMULATE | STRATA_ADD_INPUT | STRATA_FORCE_DECODE | STRATA_FORCE_PREFILL;
+  if (flags & ~known) return fail(STRATA_E_INVALID, "unknown flag bits 0x%x", flags & ~known);
+  if ((flags & STRATA_FORCE_DECODE) && (flags & STRATA_FORCE_PREFILL))
+    return fail(STRATA_E_INVALID, "FORCE_DECODE and FORCE_PREFILL are exclusive");
+  if ((flags & STRATA_FORCE_DECODE) && T > STRATA_DECODE_MAX_T)
+    return fail(STRATA_E_UNSUPPORTED, "the decode path takes at most %d tokens", STRATA_DECODE_MAX_T);
+  if ((flags & STRATA_ACCUMULATE) && (flags & STRATA_ADD_INPUT))
+    return fail(STRATA_E_INVALID, "ACCUMULATE and ADD_INPUT are exclusive");
+  return STRATA_OK;
+}
+
+Call make_call(const void* x, int32_t x_dtype, int32_t T, float* out, uint32_t flags) {
+  Call c;
+  c.x = x;
+  c.x_f32 = (x_dtype == STRATA_FP32);
+  c.T = T;
+  c.out = out;
+  c.flags = flags;
+  return c;
+}
+
+int run_route(strata_moe* h, const Call& c, bool decode, hipStream_t s) {
+  Work W = h->W;
+  W.max_tiles = max_tiles_for(h->cfg, c.T);
+  hipError_t e = decode ? launch_decode_route(h->L, W, c, s) : launch_prefill_route(h->L, W, c, s);
+  if (e != hipSuccess) return hip_fail(e, "route launch");
+  return STRATA_OK;
+}
+
+int run_forward(strata_moe* h, const Call& c, bool decode, hipStream_t s) {
+  int rc = run_route(h, c, decode, s);
+  if (rc) return rc;
+  Work W = h->W;
+  W.max_tiles = max_tiles_for(h->cfg, c.T);
+  hipError_t e = decode ? launch_decode_experts(h->L, W, c, s) : launch_prefill_experts(h->L, W, c, s);
+  if (e != hipSuccess) return hip_fail(e, "expert launch");
+  return STRATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t strata_moe_expert_bytes(const strata_moe_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
+}
+
+size_t strata_moe_packed_bytes(const strata_moe_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return packed_total(*cfg);
+}
+
+size_t strata_moe_workspace_bytes(const strata_moe_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return plan_workspace(*cfg).total;
+}
+
+int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const float* router_bias,
+                      const void* experts_canon, const void* shared_canon, void* packed,
+                      void* workspace, void* stream, strata_moe** out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(STRATA_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!router_w || !experts_canon || !packed || !workspace)
+    return fail(STRATA_E_INVALID, "router_w, experts_canon, packed and workspace must be non-NULL");
+  if (cfg->n_shared == 1 && !shared_canon) return fail(STRATA_E_INVALID, "n_shared = 1 needs shared_canon");
+  if (cfg->n_shared == 0 && shared_canon) return fail(STRATA_E_INVALID, "shared_canon given but n_shared = 0");
+  if (!aligned(packed, 256) || !aligned(workspace, 256))
+    return fail(STRATA_E_INVALID, "packed and workspace must be 256-byte aligned");
+  if (!aligned(router_w, 16)) return fail(STRATA_E_INVALID, "router_w must be 16-byte aligned");
+  if (router_bias && !aligned(router_bias, 4)) return fail(STRATA_E_INVALID, "router_bias must be 4-byte aligned");
+
+  strata_moe* h = new (std::nothrow) strata_moe();
+  if (!h) return fail(STRATA_E_INVALID, "out of host memory");
+  h->cfg = *cfg;
+  const WsPlan p = plan_workspace(*cfg);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  h->ws = ws;
+  h->ws_bytes = p.total;
+  Layer& L = h->L;
+  L.H = cfg->hidden; L.I = cfg->inter; L.E = cfg->n_experts; L.k = cfg->top_k;
+  L.n_shared = cfg->n_shared; L.fmt = cfg->qfmt;
+  L.router_w = router_w; L.router_b = router_bias;
+  L.packed = static_cast<const uint8_t*>(packed);
+  L.expert_stride = expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
+  const size_t rh = packed_experts_bytes(*cfg);
+  L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
+  L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + align256((size_t)cfg->n_experts * cfg->hidden * 2));
+  Work& W = h->W;
+  W.logits = reinterpret_cast<float*>(ws + p.logits);
+  W.topk_idx = reinterpret_cast<int*>(ws + p.topk_idx);
+  W.topk_w = reinterpret_cast<float*>(ws + p.topk_w);
+  W.counts = reinterpret_cast<int*>(ws + p.counts);
+  W.offsets = reinterpret_cast<int*>(ws + p.offsets);
+  W.perm = reinterpret_cast<int*>(ws + p.perm);
+  W.inv = reinterpret_cast<int*>(ws + p.inv);
+  W.uexp = reinterpret_cast<int*>(ws + p.uexp);
+  W.uoff = reinterpret_cast<int*>(ws + p.uoff);
+  W.meta = reinterpret_cast<int*>(ws + p.meta);
+  W.tickets = reinterpret_cast<int*>(ws + p.tickets);
+  W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
+  W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
+  W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
+  W.act = ws + p.act;
+  W.y = reinterpret_cast<float*>(ws + p.y);
+  W.nchunks = p.nchunks;
+  W.max_tiles = p.max_tiles;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemsetAsync(ws + p.meta, 0, p.chunk_base - p.meta, s);   // meta + tickets
+  if (e == hipSuccess) e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
+  if (e == hipSuccess && cfg->n_shared)
+    e = launch_repack(L, static_cast<const uint8_t*>(shared_canon), 1, cfg->n_experts, s);
+  if (e == hipSuccess) e = launch_router_split(L, s);
+  if (e == hipSuccess) e = prepare_decode_kernels(L, cfg->max_tokens);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "create");
+  }
+  *out = h;
+  return ok();
+}
+
+int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, int32_t* topk_idx,
+                     float* topk_w, int32_t* perm, int32_t* offsets, uint32_t flags, void* stream) {
+  int rc = check_call(h, x, x_dtype, T);
+  if (rc) return rc;
+  if ((rc = check_flags(T, flags))) return rc;
+  if (!topk_idx || !topk_w || !perm || !offsets)
+    return fail(STRATA_E_INVALID, "route outputs must be non-NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Call c = make_call(x, x_dtype, T, nullptr, flags);
+  if ((rc = run_route(h, c, use_decode(T, flags), s))) return rc;
+  const size_t P = (size_t)T * h->cfg.top_k;
+  hipError_t e = hipMemcpyAsync(topk_idx, h->W.topk_idx, P * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(topk_w, h->W.topk_w, P * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(perm, h->W.perm, P * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(offsets, h->W.offsets, (size_t)(h->cfg.n_experts + 1) * 4, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "route copy");
+  return ok();
+}
+
+int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, float* out,
+                       uint32_t flags, void* stream) {
+  int rc = check_call(h, x, x_dtype, T);
+  if (rc) return rc;
+  if ((rc = check_flags(T, flags))) return rc;
+  if (!out) return fail(STRATA_E_INVALID, "out is NULL");
+  if (!aligned(out, 16)) return fail(STRATA_E_INVALID, "out must be 16-byte aligned");
+  const size_t xb = (size_t)T * h->cfg.hidden * (x_dtype == STRATA_FP32 ? 4 : 2);
+  const size_t ob = (size_t)T * h->cfg.hidden * 4;
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (xa < oa + ob && oa < xa + xb) return fail(STRATA_E_INVALID, "x and out overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(T, flags), s))) return rc;
+  return ok();
+}
+
+int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const void* x,
+                             int32_t x_dtype, int32_t T, float* out, float* tmp, void* stream) {
+  if (!layers || n_layers < 1) return fail(STRATA_E_INVALID, "need at least one layer");
+  if (!out || !tmp) return fail(STRATA_E_INVALID, "out and tmp must be non-NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l]) return fail(STRATA_E_INVALID, "layer %d is NULL", l);
+    if (layers[l]->cfg.hidden != layers[0]->cfg.hidden)
+      return fail(STRATA_E_INVALID, "layer %d hidden differs from layer 0", l);
+    int rc = check_call(layers[l], x, x_dtype, T);
+    if (rc) return rc;
+  }
+  if (!aligned(out, 16) || !aligned(tmp, 16)) return fail(STRATA_E_INVALID, "out and tmp must be 16-byte aligned");
+  const size_t ob = (size_t)T * layers[0]->cfg.hidden * 4;
+  const size_t xb = (size_t)T * layers[0]->cfg.hidden * (x_dtype == STRATA_FP32 ? 4 : 2);
+  auto overlap = [](uintptr_t a, size_t na, uintptr_t b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap((uintptr_t)out, ob, (uintptr_t)tmp, ob) || overlap((uintptr_t)x, xb, (uintptr_t)out, ob) ||
+      overlap((uintptr_t)x, xb, (uintptr_t)tmp, ob))
+    return fail(STRATA_E_INVALID, "x, out and tmp must not overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* cur = x;
+  int cur_dtype = x_dtype;
+  for (int l = 0; l < n_layers; ++l) {
+    // the last layer writes `out`; earlier layers alternate so that happens
+    float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
+    const Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
+    int rc = run_forward(layers[l], c, use_decode(T, 0), s);
+    if (rc) return rc;
+    cur = dst;
+    cur_dtype = STRATA_FP32;
+  }
+  return ok();
+}
+
+void strata_moe_destroy(strata_moe* h) { delete h; }
+
+const char* strata_moe_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

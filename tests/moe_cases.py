@@ -1,0 +1,88 @@
+"""Shared helpers of the GPU parity tests: seeded layers and tokens, the
+oracle reference on the same inputs, and the HIP layer through the C ABI."""
+
+import numpy as np
+import torch
+
+import oracle as O
+from moe_synth import generate as G
+
+DECODE_TOL = 1e-5      # rel-L2, fp32 decode path vs fp64 oracle
+PREFILL_TOL = 2e-2     # rel-L2, bf16-MFMA prefill path vs fp64 oracle
+MIN_GAP = 1e-2         # logit gap at rank k required of every generated token
+
+
+class HostLayer:
+    """One layer's seeded inputs on the host (canonical records, router)."""
+
+    def __init__(self, seed, layer, H, I, E, k, fmt, biased, n_shared=0, materialise=True):
+        self.seed, self.layer = seed, layer
+        self.H, self.I, self.E, self.k, self.fmt, self.n_shared = H, I, E, k, fmt, n_shared
+        self.wr = G.router_weights(seed, layer, H, E)
+        self.b = G.router_bias(seed, layer, E) if biased else None
+        self.canon = G.layer_canonical(seed, layer, H, I, E, fmt) if materialise else None
+        self.shared = G.shared_canonical(seed, layer, H, I, fmt) if n_shared else None
+
+    def record(self, e):
+        if self.canon is not None:
+            return self.canon[e]
+        return G.expert_canonical(self.seed, self.layer, e, self.H, self.I, self.fmt)
+
+    def oracle(self, x, residual=False):
+        return O.moe_layer(np.asarray(x, np.float64), self.wr, self.b, self.record, self.H, self.I,
+                           self.k, self.fmt, shared_record=self.shared, residual=residual)
+
+    def logits(self, x):
+        return O.router_logits(np.asarray(x, np.float64), self.wr, self.b)
+
+
+def tokens(hl, stream, T, min_gap=MIN_GAP, max_attempts=200):
+    """Gap-filtered bf16 tokens for layer hl: returns (bits uint16 [T,H], fp64 values)."""
+    H = hl.H
+    x = np.stack([G.token_candidates(hl.seed, stream, t, H, 0) for t in range(T)])
+    attempt = np.zeros(T, dtype=np.int64)
+    for _ in range(max_attempts):
+        xf = G.bf16_bits_to_f32(x).astype(np.float64)
+        _, gap = O.select_topk(hl.logits(xf), hl.k)
+        bad = np.nonzero(gap < min_gap)[0]
+        if bad.size == 0:
+            return x, xf
+        for t in bad:
+            attempt[t] += 1
+            x[t] = G.token_candidates(hl.seed, stream, int(t), H, int(attempt[t]))
+    raise RuntimeError("could not draw tokens with the required logit gap")
+
+
+def to_device_bf16(bits, dev):
+    return torch.from_numpy(bits.astype(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def device_layer(hl, max_tokens, dev):
+    from quantized_moe_expert_gemv_amd import binding as B
+    cfg = B.make_config(hl.H, hl.I, hl.E, hl.k, hl.n_shared, hl.fmt, max_tokens)
+    wr = torch.from_numpy(hl.wr).to(dev)
+    b = None if hl.b is None else torch.from_numpy(hl.b).to(dev)
+    canon = torch.from_numpy(np.ascontiguousarray(hl.canon).reshape(-1)).to(dev)
+    sh = None if hl.shared is None else torch.from_numpy(hl.shared).to(dev)
+    layer = B.StrataMoE(cfg, wr, b, canon, sh)
+    del canon, sh
+    return layer
+
+
+def rel_l2(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+
+
+def check_route(layer, hl, x_dev, x_f64, flags=0, w_atol=2e-6):
+    """Route outputs vs the oracle: ids, permutation and offsets bit-exact."""
+    idx, w, perm, offs = layer.route(x_dev, flags=flags)
+    torch.cuda.synchronize()
+    _, oidx, ow, _ = O.route(x_f64, hl.wr, hl.b, hl.k)
+    counts, ooffs, operm, _ = O.permute(oidx, hl.E)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oidx)
+    np.testing.assert_array_equal(perm.cpu().numpy(), operm)
+    np.testing.assert_array_equal(offs.cpu().numpy(), ooffs)
+    np.testing.assert_allclose(w.cpu().numpy(), ow, rtol=0, atol=w_atol)
+    return oidx

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, sizes its buffers as documented, and
+rejects bad arguments before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "strata_moe.h")
+LIB = os.path.join(ROOT, "quantized_moe_expert_gemv_amd", "libstrata_moe.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"STRATA_API\s+[\w\s\*]+?\b(strata_moe_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def B():
+    from quantized_moe_expert_gemv_amd import binding
+    return binding
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == {"strata_moe_expert_bytes", "strata_moe_packed_bytes",
+                          "strata_moe_workspace_bytes", "strata_moe_create", "strata_moe_route",
+                          "strata_moe_forward", "strata_moe_stack_forward", "strata_moe_destroy",
+                          "strata_moe_last_error"}
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTS) == set(declared_functions())
+
+
+def _cfg(B, **kw):
+    base = dict(hidden=2560, inter=512, n_experts=512, top_k=10, n_shared=0, qfmt=2, max_tokens=8)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def test_expert_bytes_match_the_block_format(B):
+    # 3 matrices * I * H/32 blocks * (code bytes + 2 scale bytes)
+    assert B.strata_moe_expert_bytes(_cfg(B)) == 1228800
+    assert B.strata_moe_expert_bytes(_cfg(B, qfmt=3)) == 1720320
+    assert B.strata_moe_expert_bytes(_cfg(B, hidden=4096, inter=2048, n_experts=256, top_k=6, qfmt=4)) == 14155776
+
+
+def test_packed_bytes_cover_experts_and_router_split(B):
+    c = _cfg(B, n_shared=1)
+    per = B.strata_moe_expert_bytes(c)
+    assert B.strata_moe_packed_bytes(c) >= 513 * per + 2 * 512 * 2560 * 2
+
+
+def test_workspace_grows_with_max_tokens(B):
+    small = B.strata_moe_workspace_bytes(_cfg(B, max_tokens=1))
+    big = B.strata_moe_workspace_bytes(_cfg(B, max_tokens=8192))
+    # per-pair fp32 expert outputs dominate: 8192 * 10 * 2560 * 4 bytes
+    assert small > 0 and big > 8192 * 10 * 2560 * 4 > small
+
+
+@pytest.mark.parametrize("bad", [dict(qfmt=5), dict(hidden=2500), dict(inter=100), dict(top_k=0),
+                                 dict(top_k=513), dict(top_k=65, n_experts=100), dict(n_experts=0),
+                                 dict(n_experts=5000), dict(n_shared=2), dict(max_tokens=0)])
+def test_invalid_configs_are_rejected(B, bad):
+    c = _cfg(B, **bad)
+    assert B.strata_moe_packed_bytes(c) == 0
+    assert B.strata_moe_workspace_bytes(c) == 0
+    h = ctypes.c_void_p()
+    dummy = ctypes.c_void_p(256)
+    rc = B._lib.strata_moe_create(ctypes.byref(c), dummy, None, dummy, None, dummy, dummy, None,
+                                  ctypes.byref(h))
+    assert rc in (B.STRATA_E_INVALID, B.STRATA_E_UNSUPPORTED)
+    assert h.value is None
+    assert B.strata_moe_last_error() != ""
+
+
+def test_create_rejects_missing_or_misaligned_buffers(B):
+    c = _cfg(B)
+    h = ctypes.c_void_p()
+    p = ctypes.c_void_p(4096)
+    rc = B._lib.strata_moe_create(ctypes.byref(c), None, None, p, None, p, p, None, ctypes.byref(h))
+    assert rc == B.STRATA_E_INVALID and "non-NULL" in B.strata_moe_last_error()
+    rc = B._lib.strata_moe_create(ctypes.byref(c), p, None, p, None, ctypes.c_void_p(4096 + 16), p, None,
+                                  ctypes.byref(h))
+    assert rc == B.STRATA_E_INVALID and "aligned" in B.strata_moe_last_error()
+    rc = B._lib.strata_moe_create(ctypes.byref(c), p, None, p, p, p, p, None, ctypes.byref(h))
+    assert rc == B.STRATA_E_INVALID and "shared" in B.strata_moe_last_error()
+
+
+def test_calls_on_null_handle_fail_cleanly(B):
+    rc = B._lib.strata_moe_forward(None, ctypes.c_void_p(256), 0, 1, ctypes.c_void_p(512), 0, None)
+    assert rc == B.STRATA_E_INVALID and "handle" in B.strata_moe_last_error()
+    rc = B._lib.strata_moe_stack_forward(None, 0, None, 0, 1, None, None, None)
+    assert rc == B.STRATA_E_INVALID
+    B.strata_moe_destroy(None)            # NULL-safe
