@@ -496,17 +496,25 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
   return hipGetLastError();
 }
 
+// Raise a kernel's dynamic-LDS ceiling to what the device allows beside its
+// static LDS.  A refusal is not fatal (the launch reports it if a call really
+// needs more than the default); the runtime's error state is cleared.
+static void raise_lds_limit(const void* k, int device_limit) {
+  hipFuncAttributes fa;
+  if (hipFuncGetAttributes(&fa, k) != hipSuccess) { (void)hipGetLastError(); return; }
+  const int want = device_limit - (int)fa.sharedSizeBytes;
+  if (want > 0 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
+    (void)hipGetLastError();
+}
+
 template <int FMT>
-hipError_t set_lds_limit(int bytes) {
-  hipError_t e = hipSuccess;
+void set_lds_limits(int lim) {
   const void* ks[] = {
       reinterpret_cast<const void*>(&k_decode_gateup<FMT, 1>), reinterpret_cast<const void*>(&k_decode_gateup<FMT, 2>),
       reinterpret_cast<const void*>(&k_decode_gateup<FMT, 4>), reinterpret_cast<const void*>(&k_decode_gateup<FMT, 8>),
       reinterpret_cast<const void*>(&k_decode_down<FMT, 1>), reinterpret_cast<const void*>(&k_decode_down<FMT, 2>),
       reinterpret_cast<const void*>(&k_decode_down<FMT, 4>), reinterpret_cast<const void*>(&k_decode_down<FMT, 8>)};
-  for (const void* k : ks)
-    if (e == hipSuccess) e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  return e;
+  for (const void* k : ks) raise_lds_limit(k, lim);
 }
 
 // Allow the decode kernels the dynamic LDS the widest decode call needs
@@ -516,14 +524,13 @@ hipError_t prepare_decode_kernels(const Layer& L, int) {
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_route),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lim);
-  if (e != hipSuccess) return e;
+  raise_lds_limit(reinterpret_cast<const void*>(&k_decode_route), lim);
   switch (L.fmt) {
-    case 2: return set_lds_limit<2>(lim);
-    case 3: return set_lds_limit<3>(lim);
-    default: return set_lds_limit<4>(lim);
+    case 2: set_lds_limits<2>(lim); break;
+    case 3: set_lds_limits<3>(lim); break;
+    default: set_lds_limits<4>(lim); break;
   }
+  return hipSuccess;
 }
 
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s) {

@@ -249,16 +249,34 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.max_tiles = p.max_tiles;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* step = "zeroing counters";
   hipError_t e = hipMemsetAsync(ws + p.meta, 0, p.chunk_base - p.meta, s);   // meta + tickets
-  if (e == hipSuccess) e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
-  if (e == hipSuccess && cfg->n_shared)
+  if (e == hipSuccess) {
+    step = "expert repack";
+    e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
+  }
+  if (e == hipSuccess && cfg->n_shared) {
+    step = "shared expert repack";
     e = launch_repack(L, static_cast<const uint8_t*>(shared_canon), 1, cfg->n_experts, s);
-  if (e == hipSuccess) e = launch_router_split(L, s);
-  if (e == hipSuccess) e = prepare_decode_kernels(L, cfg->max_tokens);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
+  if (e == hipSuccess) {
+    step = "router split";
+    e = launch_router_split(L, s);
+  }
+  if (e == hipSuccess) {
+    step = "kernel attributes";
+    e = prepare_decode_kernels(L, cfg->max_tokens);
+  }
+  if (e == hipSuccess) {
+    step = "stream synchronize";
+    e = hipStreamSynchronize(s);
+  }
   if (e != hipSuccess) {
+    (void)hipGetLastError();
     delete h;
-    return hip_fail(e, "create");
+    char what[64];
+    snprintf(what, sizeof what, "create (%s)", step);
+    return hip_fail(e, what);
   }
   *out = h;
   return ok();
