@@ -160,6 +160,19 @@ STRATA_API int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_lay
                              const void* x, int32_t x_dtype, int32_t T,
                              float* out, float* tmp, void* stream);
 
+/*
+ * Per-kernel timing of the next route/forward/stack call on this handle
+ * (one-shot).  events are hipEvent_t created by the caller (void*); the call
+ * records events[0] on its stream before its first kernel and events[i]
+ * after its i-th kernel, for i < n_events; extra kernels are not traced.
+ * Kernel order: decode forward = router/top-k/permute, gate/up, down+combine;
+ * prefill forward = router GEMM, top-k, scan, scatter, gate/up GEMM, down
+ * GEMM, combine (route-only calls stop after the routing kernels).
+ * n_events in [0, STRATA_MAX_TRACE_EVENTS]; 0 disarms.
+ */
+#define STRATA_MAX_TRACE_EVENTS 16
+STRATA_API int strata_moe_trace_next_call(strata_moe* h, void* const* events, int32_t n_events);
+
 /* Free the host-side handle.  NULL-safe.  Device buffers stay the caller's. */
 STRATA_API void strata_moe_destroy(strata_moe* h);
 

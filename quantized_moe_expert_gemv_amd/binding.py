@@ -22,7 +22,9 @@ STRATA_DECODE_MAX_T = 8
 
 EXPORTS = ("strata_moe_expert_bytes", "strata_moe_packed_bytes", "strata_moe_workspace_bytes",
            "strata_moe_create", "strata_moe_route", "strata_moe_forward",
-           "strata_moe_stack_forward", "strata_moe_destroy", "strata_moe_last_error")
+           "strata_moe_stack_forward", "strata_moe_trace_next_call", "strata_moe_destroy",
+           "strata_moe_last_error")
+STRATA_MAX_TRACE_EVENTS = 16
 
 
 class strata_moe_config(ctypes.Structure):
@@ -52,6 +54,7 @@ def _load():
         "strata_moe_route": (ctypes.c_int, [P, P, I32, I32, P, P, P, P, U32, P]),
         "strata_moe_forward": (ctypes.c_int, [P, P, I32, I32, P, U32, P]),
         "strata_moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(P), I32, P, I32, I32, P, P, P]),
+        "strata_moe_trace_next_call": (ctypes.c_int, [P, ctypes.POINTER(P), I32]),
         "strata_moe_destroy": (None, [P]),
         "strata_moe_last_error": (ctypes.c_char_p, []),
     }
@@ -125,6 +128,19 @@ def strata_moe_stack_forward(handles, x, T, out, tmp, stream=None):
     arr = (ctypes.c_void_p * len(handles))(*[h.value for h in handles])
     _check(_lib.strata_moe_stack_forward(arr, len(handles), _ptr(x), _dtype_code(x), T, _ptr(out),
                                          _ptr(tmp), _stream(stream)))
+
+
+def strata_moe_trace_next_call(h, events):
+    """Arm per-kernel timing of the next call with torch.cuda.Event objects
+    (enable_timing=True).  Each event is recorded once first so that its HIP
+    event exists."""
+    handles = []
+    for ev in events:
+        if ev.cuda_event == 0:
+            ev.record()
+        handles.append(ev.cuda_event)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _check(_lib.strata_moe_trace_next_call(h, arr, len(handles)))
 
 
 def strata_moe_destroy(h):

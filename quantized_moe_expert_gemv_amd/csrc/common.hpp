@@ -1,28 +1,30 @@
 // Shared definitions of the strata_moe HIP library (gfx950, wave64).
 //
-// Packed expert layout ("packed"), written once by the create-time repack:
+// Packed expert layout ("packed"), written once by the create-time repack.
+// The bytes are the canonical ones (codes + fp16 scales), regrouped so that
+// one 16-B load per lane delivers exactly the operand a lane feeds to a
+// 16x16x32 matrix-core instruction:
 //
-//   A matrix with R rows and reduction length K is cut into 64-row tiles and
-//   256-weight superblocks (8 quantised blocks).  For one tile and one
-//   superblock the bytes are NV vectors of 64 rows x 16 B: vector v, row
-//   (lane) r sits at  v*1024 + r*16.  NV = NCV code vectors + 1 scale vector
-//   (the 8 fp16 scales of the superblock's blocks).  A wavefront reading
-//   vector v of a tile therefore issues one fully contiguous 1 KiB load,
-//   every lane owning one output row.
+//   A matrix of R rows and reduction length K is cut into 16-row groups and
+//   256-weight superblocks (8 quantised blocks).  The bytes of one (group,
+//   superblock) form a slab:
+//     codes   one 16-B vector per lane (Q4: two vectors, Q3: a 2-bit plane
+//             vector plus an 8-B 1-bit plane); lane l holds row l % 16 and,
+//             of every block of the superblock, the 8 codes of the K-slice
+//             8*(l / 16) .. 8*(l / 16) + 7;
+//     scales  16 rows x 8 fp16 (row r at r * 16).
+//   Slabs are stored group-major: slab (g, sb) at (g * K/256 + sb) * SLAB.
+//   Expert = gate [I x H], up [I x H], down [H x I], back to back.
 //
-//   Expert = [gate/up section][down section]:
-//     gate/up: tiles of 64 intermediate rows i; per (tile, superblock) the
-//              gate vectors then the up vectors (2*NV vectors), so one lane
-//              owns gate row i and up row i and SwiGLU stays in-lane;
-//     down:    tiles of 64 hidden rows h, K = I.
-//   The byte count equals the canonical record's (codes + scales only).
-//
-//   Code vectors inside one row-superblock:
-//     Q2: v = 0..3 holds blocks 2v, 2v+1 (8 B each, canonical bit order);
-//     Q4: v = 0..7 holds block v (16 B, canonical nibble order);
-//     Q3: v = 0..3 holds the low two bits of blocks 2v, 2v+1 laid out like
-//         Q2; v = 4..5 holds the third bit of blocks 4(v-4)..4(v-4)+3, one
-//         32-bit word per block, bit (8i + 4w + s) = bit 2 of code 16w+4i+s.
+//   Bit order inside a lane (per block, 8 codes for K-offsets e = 0..7):
+//     Q2: 16 bits per block (dword w holds blocks 2w | 2w+1 << 16); the code
+//         of offset e sits at bit POS2[e] = {0,4,2,6,8,12,10,14}[e], so that
+//         masking the dword with 0x33333333 (and after >> 2) yields FP4 nibbles
+//         whose byte-wise conversion returns the 8 codes in offset order.
+//     Q3: the low two bits as Q2; the third bit of offset e of block 4h + b at
+//         bit 4e + b of hi dword h.
+//     Q4: 32 bits per block (vector h, dword i holds block 4h + i); the code of
+//         offset e sits at nibble NIB4[e] = {0,4,1,5,2,6,3,7}[e].
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,42 +32,41 @@
 namespace strata {
 
 constexpr int WAVE = 64;
-constexpr int ROWS_PER_TILE = 64;
+constexpr int GROUP_ROWS = 16;
 constexpr int SB_WEIGHTS = 256;        // weights per superblock (8 blocks)
 constexpr int BLOCK_W = 32;            // weights per quantised block
 constexpr int DECODE_MAX_T = 8;
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<2> {
-  static constexpr int bits = 2, code_bytes = 8, ncv = 4;
+  static constexpr int bits = 2, code_bytes = 8, slab_codes = 1024;
   static constexpr float c = 1.5f;
 };
 template <> struct Fmt<3> {
-  static constexpr int bits = 3, code_bytes = 12, ncv = 6;
+  static constexpr int bits = 3, code_bytes = 12, slab_codes = 1536;
   static constexpr float c = 3.5f;
 };
 template <> struct Fmt<4> {
-  static constexpr int bits = 4, code_bytes = 16, ncv = 8;
+  static constexpr int bits = 4, code_bytes = 16, slab_codes = 2048;
   static constexpr float c = 8.0f;
 };
 
 __host__ __device__ inline int fmt_code_bytes(int fmt) { return fmt == 2 ? 8 : (fmt == 3 ? 12 : 16); }
-__host__ __device__ inline int fmt_ncv(int fmt) { return fmt == 2 ? 4 : (fmt == 3 ? 6 : 8); }
-__host__ __device__ inline int fmt_nv(int fmt) { return fmt_ncv(fmt) + 1; }
+__host__ __device__ inline int slab_code_bytes(int fmt) { return 16 * 32 * fmt; }   // 16 rows x 256 codes
+__host__ __device__ inline int slab_bytes(int fmt) { return slab_code_bytes(fmt) + 256; }
+__host__ __device__ inline size_t matrix_bytes(int fmt, int R, int K) {
+  return (size_t)(R / GROUP_ROWS) * (K / SB_WEIGHTS) * slab_bytes(fmt);
+}
 __host__ __device__ inline size_t expert_bytes(int fmt, int H, int I) {
   return (size_t)3 * I * (H / BLOCK_W) * (fmt_code_bytes(fmt) + 2);
 }
-// bytes of the gate/up section of one expert
-__host__ __device__ inline size_t gu_bytes(int fmt, int H, int I) {
-  return (size_t)2 * I * (H / BLOCK_W) * (fmt_code_bytes(fmt) + 2);
-}
-// byte offset of (tile, superblock, matrix m in {0 gate, 1 up}, vector v) in the gate/up section
-__host__ __device__ inline size_t gu_off(int nv, int nsbH, int tile, int sb, int m, int v) {
-  return ((((size_t)tile * nsbH + sb) * 2 + m) * nv + v) * 1024;
-}
-// byte offset of (tile, superblock, vector v) in the down section (relative to its start)
-__host__ __device__ inline size_t dn_off(int nv, int nsbI, int tile, int sb, int v) {
-  return (((size_t)tile * nsbI + sb) * nv + v) * 1024;
+// byte offsets of the three matrices inside an expert
+__host__ __device__ inline size_t gate_off(int, int, int) { return 0; }
+__host__ __device__ inline size_t up_off(int fmt, int H, int I) { return matrix_bytes(fmt, I, H); }
+__host__ __device__ inline size_t down_off(int fmt, int H, int I) { return 2 * matrix_bytes(fmt, I, H); }
+// byte offset of slab (g, sb) inside a matrix with nsb superblocks per row
+__host__ __device__ inline size_t slab_off(int fmt, int nsb, int g, int sb) {
+  return ((size_t)g * nsb + sb) * slab_bytes(fmt);
 }
 
 // ------------------------------------------------------------------ device helpers
@@ -83,54 +84,107 @@ __device__ inline float half_bits_to_f32(uint16_t h) {
   return (float)v;
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+// DPP lane permutations (gfx9 encodings): xor-1 and xor-2 inside quads,
+// mirror inside half-rows of 8 and rows of 16.
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
+              DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
 }
 
-// argmax over the wave of (value, index); ties resolved towards the smaller index
+// Sum over the 64 lanes; every lane receives the same (deterministic) result.
+__device__ inline float wave_sum(float v) {
+  v += dpp_f<DPP_QUAD_XOR1>(v);
+  v += dpp_f<DPP_QUAD_XOR2>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);          // each row of 16 now holds its row sum
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+__device__ inline void argmax_merge(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+}
+
+// argmax over the wave of (value, index); ties resolved towards the smaller
+// index; every lane receives the result
 __device__ inline void wave_argmax(float& v, int& i) {
+  argmax_merge(v, i, dpp_f<DPP_QUAD_XOR1>(v), dpp_i<DPP_QUAD_XOR1>(i));
+  argmax_merge(v, i, dpp_f<DPP_QUAD_XOR2>(v), dpp_i<DPP_QUAD_XOR2>(i));
+  argmax_merge(v, i, dpp_f<DPP_ROW_HALF_MIRROR>(v), dpp_i<DPP_ROW_HALF_MIRROR>(i));
+  argmax_merge(v, i, dpp_f<DPP_ROW_MIRROR>(v), dpp_i<DPP_ROW_MIRROR>(i));
+  float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float ov = __shfl_xor(v, o, WAVE);
-    int oi = __shfl_xor(i, o, WAVE);
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
-  }
+  for (int r = 16; r < 64; r += 16)
+    argmax_merge(bv, bi, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), r)),
+                 __builtin_amdgcn_readlane(i, r));
+  v = bv;
+  i = bi;
 }
 
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
-// Top-k of one token's logits row[0..E) (LDS or global), computed by one
-// wave.  Round r selects the best entry ranked after round r-1's winner in
-// the total order (value descending, id ascending), so nothing is written
-// back to the row and equal values resolve to the lower id.  NaN ranks as
-// -inf, so k <= E rounds always yield k distinct valid ids.  Writes the ids
-// in ascending order to idx_out[0..k) and the renormalised softmax weights
-// to w_out[0..k).  k <= 64.  Every lane of the wave must call it.
-__device__ inline void wave_topk(const float* row, int E, int k, int* idx_out, float* w_out,
+// ------------------------------------------------------------------ top-k
+// Selection order: value descending, then expert id ascending; NaN ranks as
+// -inf.  Each entry becomes one 64-bit key (order-preserving integer image of
+// the float, then the complemented id), so "better" is plain unsigned ">"
+// and every comparison below is branch-free.
+__device__ inline uint32_t sortable_bits(float v) {
+  if (v != v) v = -INFINITY;
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ inline float unsortable_bits(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+template <int CTRL, int ROWS>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t l2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+  const uint32_t h2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+  return ((uint64_t)h2 << 32) | l2;
+}
+__device__ inline uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// maximum 64-bit key over the wave; every lane receives it
+__device__ inline uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<DPP_QUAD_XOR1, 0xF>(v));
+  v = umax64(v, dpp_u64<DPP_QUAD_XOR2, 0xF>(v));
+  v = umax64(v, dpp_u64<DPP_ROW_HALF_MIRROR, 0xF>(v));
+  v = umax64(v, dpp_u64<DPP_ROW_MIRROR, 0xF>(v));       // row maxima
+  v = umax64(v, dpp_u64<0x142, 0xA>(v));                 // row_bcast:15 into rows 1, 3
+  v = umax64(v, dpp_u64<0x143, 0xC>(v));                 // row_bcast:31 into rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline uint64_t topk_key(float v, int e) {
+  return ((uint64_t)sortable_bits(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+
+// Finish a selection: lane r < k holds the r-th best key.  Writes the ids in
+// ascending order to idx_out[0..k) and the renormalised softmax weights
+// (max-shifted exp over the k selected, divided by their sum) to w_out.
+__device__ inline void topk_emit(uint64_t my_key, uint64_t top_key, int k, int* idx_out, float* w_out,
                                  int* sel_lds) {
   const int lane = threadIdx.x & (WAVE - 1);
-  float my_val = 0.f, top = 0.f, pv = INFINITY;
-  int my_id = 0, pi = -1;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int e = lane; e < E; e += WAVE) {
-      float v = row[e];
-      v = (v != v) ? -INFINITY : v;
-      bool after = (v < pv) || (v == pv && e > pi);
-      if (after && (v > bv || (v == bv && e < bi))) { bv = v; bi = e; }
-    }
-    wave_argmax(bv, bi);
-    if (r == 0) top = bv;
-    if (lane == r) { my_val = bv; my_id = bi; }
-    pv = bv;
-    pi = bi;
-  }
-  // renormalised softmax over the selected logits
-  float z = (lane < k) ? expf(my_val - top) : 0.f;
-  float s = wave_sum(z);
+  const int my_id = (int)(0xffffffffu - (uint32_t)my_key);
+  const float my_val = unsortable_bits((uint32_t)(my_key >> 32));
+  const float top = unsortable_bits((uint32_t)(top_key >> 32));
+  const float z = (lane < k) ? expf(my_val - top) : 0.f;
+  const float s = wave_sum(z);
   if (lane < k) sel_lds[lane] = my_id;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -143,6 +197,125 @@ __device__ inline void wave_topk(const float* row, int E, int k, int* idx_out, f
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+}
+
+// Top-k of one token's logits row[0..E), E <= 64*MAXV, one wave; the row is
+// read once into registers.  Round r takes the best key below round r-1's.
+template <int MAXV>
+__device__ inline void wave_topk(const float* row, int E, int k, int* idx_out, float* w_out,
+                                 int* sel_lds) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  uint64_t key[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + WAVE * i;
+    const float v = row[e < E ? e : E - 1];
+    key[i] = (e < E) ? topk_key(v, e) : 0ull;
+  }
+  uint64_t prev = ~0ull, mine = 0ull, top = 0ull;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0ull;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+      const uint64_t c = (key[i] < prev) ? key[i] : 0ull;
+      best = umax64(best, c);
+    }
+    best = wave_max_u64(best);
+    if (r == 0) top = best;
+    mine = (lane == r) ? best : mine;
+    prev = best;
+  }
+  topk_emit(mine, top, k, idx_out, w_out, sel_lds);
+}
+
+// Same selection for any E, re-reading the row each round (E > 512).
+__device__ inline void wave_topk_loop(const float* row, int E, int k, int* idx_out, float* w_out,
+                                      int* sel_lds) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  uint64_t prev = ~0ull, mine = 0ull, top = 0ull;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0ull;
+    for (int e = lane; e < E; e += WAVE) {
+      const uint64_t key = topk_key(row[e], e);
+      best = umax64(best, (key < prev) ? key : 0ull);
+    }
+    best = wave_max_u64(best);
+    if (r == 0) top = best;
+    mine = (lane == r) ? best : mine;
+    prev = best;
+  }
+  topk_emit(mine, top, k, idx_out, w_out, sel_lds);
+}
+
+// Radix select over the order-preserving 32-bit images u of the values
+// (E <= 64*MAXV, one wave): tau = the k-th largest u is fixed bit by bit from
+// the top (population counts of ballots), ties at tau are taken lowest id
+// first, and the selected ids come out in ascending order from prefix counts
+// of the selection ballots.  Same selection as the rounds above.
+template <int MAXV>
+__device__ inline void wave_topk_radix(const float* row, int E, int k, int* idx_out, float* w_out) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  uint32_t u[MAXV];
+  float val[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int e = lane + WAVE * i;
+    const float v = row[e < E ? e : E - 1];
+    val[i] = v;
+    u[i] = (e < E) ? sortable_bits(v) : 0u;    // padding ranks below every value
+  }
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) cnt += __popcll(__ballot(u[i] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) gt += __popcll(__ballot(u[i] > tau));
+  const int need = k - gt;                      // ties at tau to take, lowest ids first
+  uint32_t umax = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) umax = u[i] > umax ? u[i] : umax;
+  umax = (uint32_t)wave_max_u64(umax);
+  const float top = unsortable_bits(umax);
+  int ties_before = 0, sel_before = 0;
+  float zsum = 0.f;
+  bool sel[MAXV];
+  float z[MAXV];
+  int pos[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const bool tie = (u[i] == tau) && (lane + WAVE * i < E);
+    const uint64_t tm = __ballot(tie);
+    const int trank = ties_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
+    ties_before += __popcll(tm);
+    sel[i] = (u[i] > tau) || (tie && trank < need);
+    const uint64_t sm = __ballot(sel[i]);
+    pos[i] = sel_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+    sel_before += __popcll(sm);
+    z[i] = sel[i] ? expf(val[i] - top) : 0.f;
+    zsum += z[i];
+  }
+  const float inv = 1.0f / wave_sum(zsum);
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if (sel[i]) {
+      idx_out[pos[i]] = lane + WAVE * i;
+      w_out[pos[i]] = z[i] * inv;
+    }
+  }
+}
+
+__device__ inline void wave_topk_any(const float* row, int E, int k, int* idx_out, float* w_out,
+                                     int* sel_lds) {
+  if (E <= 256) wave_topk_radix<4>(row, E, k, idx_out, w_out);
+  else if (E <= 512) wave_topk_radix<8>(row, E, k, idx_out, w_out);
+  else wave_topk_loop(row, E, k, idx_out, w_out, sel_lds);
 }
 
 // Exclusive scan of an int2 over the workgroup (<= 16 waves); *total gets the sum.

@@ -83,42 +83,43 @@ __device__ inline void mma_step(const uint16_t* As, const uint16_t* Bs, f32x16 (
 // row of element v of a 32x32 accumulator held by `lane`
 __device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-// Dequantise one 32-weight block (codes + scale in the packed layout) of one
-// weight row into 32 bf16 at dst (LDS, 16-B aligned).
+// Dequantise one lane-slot l of a slab for blocks bb0 and bb0 + 1 (bb0 even):
+// row l % 16, K-slice 8*(l/16) of each block, 16 weights d (q - c) rounded
+// to bf16 into the LDS row dst (columns (b - bb0)*32 + 8*(l/16) + e).
 template <int FMT>
-__device__ inline void dequant_block_to_lds(const uint8_t* rowsb /* row's superblock base */,
-                                            int bb, uint16_t* dst) {
-  constexpr int NCV = Fmt<FMT>::ncv;
+__device__ inline void dequant_lane_pair(const uint8_t* slab, int l, int bb0, uint16_t* dst) {
+  constexpr int POS2[8] = {0, 4, 2, 6, 8, 12, 10, 14};
+  constexpr int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
   constexpr float C = Fmt<FMT>::c;
-  const uint16_t draw = *reinterpret_cast<const uint16_t*>(rowsb + NCV * 1024 + bb * 2);
-  const float d = half_bits_to_f32(draw);
-  float w[32];
-  if constexpr (FMT == 2) {
-    const uint2 c = *reinterpret_cast<const uint2*>(rowsb + (bb >> 1) * 1024 + (bb & 1) * 8);
+  const int r = l & 15, q = l >> 4;
+  const uint32_t sc = *reinterpret_cast<const uint32_t*>(slab + Fmt<FMT>::slab_codes + r * 16 + bb0 * 2);
+  const float d[2] = {half_bits_to_f32((uint16_t)(sc & 0xffffu)), half_bits_to_f32((uint16_t)(sc >> 16))};
+  float w[16];
+  if constexpr (FMT == 4) {
+    const uint2 c = *reinterpret_cast<const uint2*>(slab + (bb0 >> 2) * 1024 + l * 16 + (bb0 & 3) * 4);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t W = (j < 16) ? c.x : c.y;
-      w[j] = d * ((float)((W >> (2 * (j & 15))) & 3u) - C);
+    for (int b = 0; b < 2; ++b) {
+      const uint32_t W = b ? c.y : c.x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[8 * b + e] = d[b] * ((float)((W >> (4 * NIB4[e])) & 15u) - C);
     }
-  } else if constexpr (FMT == 4) {
-    const uint4 c = *reinterpret_cast<const uint4*>(rowsb + bb * 1024);
-    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int j = 0; j < 32; ++j) w[j] = d * ((float)((cw[j >> 3] >> (4 * (j & 7))) & 15u) - C);
   } else {
-    const uint2 c = *reinterpret_cast<const uint2*>(rowsb + (bb >> 1) * 1024 + (bb & 1) * 8);
-    const uint32_t hw = *reinterpret_cast<const uint32_t*>(rowsb + (4 + (bb >> 2)) * 1024 + (bb & 3) * 4);
+    const uint32_t W = *reinterpret_cast<const uint32_t*>(slab + l * 16 + (bb0 >> 1) * 4);
+    uint32_t Hd = 0;
+    if constexpr (FMT == 3) Hd = *reinterpret_cast<const uint32_t*>(slab + 1024 + l * 8 + (bb0 >> 2) * 4);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t W = (j < 16) ? c.x : c.y;
-      const int ww = j >> 4, i = (j & 15) >> 2, s = j & 3;
-      const uint32_t q = ((W >> (2 * (j & 15))) & 3u) | (((hw >> (8 * i + 4 * ww + s)) & 1u) << 2);
-      w[j] = d * ((float)q - C);
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t qv = (W >> (16 * b + POS2[e])) & 3u;
+        if constexpr (FMT == 3) qv |= ((Hd >> (4 * e + ((bb0 + b) & 3))) & 1u) << 2;
+        w[8 * b + e] = d[b] * ((float)qv - C);
+      }
     }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<uint4*>(dst + 8 * q) = to_bf16x8(w + 8 * q, nullptr);
+  for (int b = 0; b < 2; ++b)
+    *reinterpret_cast<uint4*>(dst + 32 * b + 8 * q) = to_bf16x8(w + 8 * b, nullptr);
 }
 
 // ------------------------------------------------------------------ router GEMM
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(256) void k_topk_chunks(TopkArgs a) {
   for (int tl = wv; tl < CT; tl += 4) {
     const int t = tb + tl;
     if (t < a.T) {
-      wave_topk(a.w.logits + (size_t)t * E, E, k, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
+      wave_topk_any(a.w.logits + (size_t)t * E, E, k, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
     }
   }
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
@@ -316,7 +317,6 @@ __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
   const int itile = blockIdx.x;                       // 64 intermediate rows: gate + up = 128 columns
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  constexpr int NV = Fmt<FMT>::ncv + 1;
   const int nsbH = a.H / SB_WEIGHTS;
   if (tid < BM) {
     const void* p = nullptr;
@@ -328,10 +328,13 @@ __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
     }
     rowsrc[tid] = p;
   }
-  // B column n of this tile: matrix (n % 64) / 32 (0 gate, 1 up), row (n / 64) * 32 + n % 32
-  const int bn = tid >> 1, bhalf = tid & 1;
-  const int bmat = (bn & 63) >> 5, brow = (bn >> 6) * 32 + (bn & 31);
-  const uint8_t* bsrc = a.packed + (size_t)e * a.stride + gu_off(NV, nsbH, itile, 0, bmat, 0) + brow * 16;
+  // B columns in groups of 16: column group cg = tid / 32 covers columns 16cg..16cg+15,
+  // i.e. matrix (cg % 4) / 2 (0 gate, 1 up) and rows (cg / 4) * 32 + (cg % 2) * 16 of the
+  // 64-row i-tile; each thread dequantises two lane-slots of that slab per K-step.
+  const int cg = tid >> 5, sub = tid & 31;
+  const int bmat = (cg & 3) >> 1;
+  const int bgroup = itile * 4 + (cg >> 2) * 2 + (cg & 1);
+  const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + (bmat ? up_off(FMT, a.H, a.I) : 0);
   __syncthreads();
   f32x16 acc[2][2] = {};
   for (int k0 = 0; k0 < a.H; k0 += BK) {
@@ -353,14 +356,21 @@ __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
       }
       *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
     }
-    const int sb = k0 / SB_WEIGHTS, bb = (k0 % SB_WEIGHTS) / BLOCK_W + bhalf;
-    dequant_block_to_lds<FMT>(bsrc + (size_t)sb * 2 * NV * 1024, bb, Bs + bn * LDK + bhalf * 32);
+    {
+      const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
+      const uint8_t* slab = bmat_base + slab_off(FMT, nsbH, bgroup, sb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int l = sub + 32 * h;
+        dequant_lane_pair<FMT>(slab, l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
+      }
+    }
     __syncthreads();
     mma_step(As, Bs, acc, wm, wn, lane);
     __syncthreads();
   }
   // SwiGLU epilogue: nt = 0 holds gate, nt = 1 up, for the same 32 rows i
-  uint16_t* act = reinterpret_cast<uint16_t*>(a.w.act);
+  uint16_t* act = reinterpret_cast<uint16_t*>(a.w.act);        // bf16 rows
   const int i = itile * 64 + wn * 32 + (lane & 31);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -384,12 +394,10 @@ __global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
   const int h0 = blockIdx.x * BN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  constexpr int NV = Fmt<FMT>::ncv + 1;
   const int nsbI = a.I / SB_WEIGHTS;
-  const int bn = tid >> 1, bhalf = tid & 1;
-  const int hrow = h0 + bn;
-  const uint8_t* bsrc = a.packed + (size_t)e * a.stride + gu_bytes(FMT, a.H, a.I) +
-                        dn_off(NV, nsbI, hrow / 64, 0, 0) + (hrow % 64) * 16;
+  const int cg = tid >> 5, sub = tid & 31;          // column group: H rows h0 + 16cg .. +15
+  const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
+  const int bgroup = h0 / GROUP_ROWS + cg;
   const uint16_t* act = reinterpret_cast<const uint16_t*>(a.w.act);
   f32x16 acc[2][2] = {};
   for (int k0 = 0; k0 < a.I; k0 += BK) {
@@ -400,8 +408,15 @@ __global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
       if (r < rows) hv = *reinterpret_cast<const uint4*>(act + (size_t)(slot0 + r) * a.I + k0 + kc * 8);
       *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
     }
-    const int sb = k0 / SB_WEIGHTS, bb = (k0 % SB_WEIGHTS) / BLOCK_W + bhalf;
-    dequant_block_to_lds<FMT>(bsrc + (size_t)sb * NV * 1024, bb, Bs + bn * LDK + bhalf * 32);
+    {
+      const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
+      const uint8_t* slab = bmat_base + slab_off(FMT, nsbI, bgroup, sb);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int l = sub + 32 * h;
+        dequant_lane_pair<FMT>(slab, l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
+      }
+    }
     __syncthreads();
     mma_step(As, Bs, acc, wm, wn, lane);
     __syncthreads();
@@ -468,7 +483,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 }
 
 template <int FMT>
-hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   GemmArgs g;
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
   g.T = c.T; g.P = c.T * L.k; g.x = c.x; g.x_f32 = c.x_f32; g.w = W;
@@ -477,43 +492,51 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
     hipLaunchKernelGGL((k_gemm_gateup<FMT, true>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
   else
     hipLaunchKernelGGL((k_gemm_gateup<FMT, false>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+  mark(tr, s);
   hipLaunchKernelGGL((k_gemm_down<FMT>), dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
+  mark(tr, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   RouterArgs r;
   r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
   r.whi = L.router_hi; r.wlo = L.router_lo; r.bias = L.router_b; r.logits = W.logits;
   dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM);
+  mark(tr, s);
   if (c.x_f32) hipLaunchKernelGGL(k_router_gemm<true>, grid, dim3(256), 0, s, r);
   else hipLaunchKernelGGL(k_router_gemm<false>, grid, dim3(256), 0, s, r);
+  mark(tr, s);
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   const size_t lds = ((size_t)CT * L.k + L.E) * 4;
   hipLaunchKernelGGL(k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
+  mark(tr, s);
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, sa);
+  mark(tr, s);
   const int P = c.T * L.k;
   hipLaunchKernelGGL(k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
+  mark(tr, s);
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s) {
+hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   hipError_t err;
   switch (L.fmt) {
-    case 2: err = launch_gemms_fmt<2>(L, W, c, s); break;
-    case 3: err = launch_gemms_fmt<3>(L, W, c, s); break;
-    default: err = launch_gemms_fmt<4>(L, W, c, s); break;
+    case 2: err = launch_gemms_fmt<2>(L, W, c, s, tr); break;
+    case 3: err = launch_gemms_fmt<3>(L, W, c, s, tr); break;
+    default: err = launch_gemms_fmt<4>(L, W, c, s, tr); break;
   }
   if (err != hipSuccess) return err;
   CombineArgs cb;
   cb.T = c.T; cb.H = L.H; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
   cb.x = c.x; cb.x_f32 = c.x_f32; cb.flags = c.flags; cb.out = c.out; cb.w = W;
   hipLaunchKernelGGL(k_combine, dim3(c.T), dim3(256), 0, s, cb);
+  mark(tr, s);
   return hipGetLastError();
 }
 

@@ -1,10 +1,11 @@
-// Create-time repack of canonical expert records into the packed layout,
-// and the bf16 hi/lo split of the router rows used by the prefill router.
+// Create-time repack of canonical expert records into the packed slab
+// layout, and the bf16 hi/lo split of the router rows used by the prefill
+// router.
 //
-// The repack only moves bytes (and, for Q3, reorders the bits of each
-// block's codes into a 2-bit plane and a 1-bit plane); the byte count of an
-// expert is unchanged.  It follows the one-time re-layout of the expert set
-// into a compute-friendly copy that the pages describe for the CPU path
+// The repack only moves bits: every code and every fp16 scale of the
+// canonical record lands in exactly one place, so an expert keeps its byte
+// count.  It follows the one-time re-layout of the expert set into a
+// compute-friendly copy that the pages describe for the CPU path
 // (devotd.net "Strata memory tiers", section 小模型包不等于合适的模型: a
 // one-time ~40 GB copy written for AVX-512 Q2_0) and the contiguous
 // per-expert record (lcz.me/topic/2153, section 三 item 4, the per-expert
@@ -16,72 +17,87 @@ namespace strata {
 
 namespace {
 
-__device__ inline uint32_t ld_u32_unaligned(const uint8_t* p) {
-  return (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+__constant__ int POS2[8] = {0, 4, 2, 6, 8, 12, 10, 14};   // Q2/Q3 low-plane bit of offset e
+__constant__ int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};      // Q4 nibble of offset e
+
+// code j (0..31) of a canonical block: bits [b*j, b*j + b) of the code bytes
+// read as one little-endian bit string
+__device__ inline uint32_t canon_code(const uint8_t* blk, int fmt, int j) {
+  const int p = fmt * j;
+  uint32_t v = blk[p >> 3] >> (p & 7);
+  if ((p & 7) + fmt > 8) v |= (uint32_t)blk[(p >> 3) + 1] << (8 - (p & 7));
+  return v & ((1u << fmt) - 1u);
 }
 
-__global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed,
-                         int fmt, int H, int I, size_t stride, long long n_blocks_total,
-                         int first_expert) {
+// One thread per (expert, matrix, row, superblock): 8 canonical blocks in,
+// the row's share of one slab out (4 lanes' code bits and one scale row).
+__global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int fmt,
+                         int H, int I, size_t stride, long long n_items, int first_expert) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= n_blocks_total) return;
-  const int cb = fmt_code_bytes(fmt);
-  const int bq = cb + 2;
-  const int ncv = fmt_ncv(fmt), nv = ncv + 1;
-  const long long nGU = (long long)I * (H / BLOCK_W);
-  const long long nD = (long long)H * (I / BLOCK_W);
-  const long long per = 2 * nGU + nD;
+  if (gid >= n_items) return;
+  const int bq = fmt_code_bytes(fmt) + 2;
+  const long long gu_items = (long long)I * (H / SB_WEIGHTS);     // per gate or up matrix
+  const long long dn_items = (long long)H * (I / SB_WEIGHTS);
+  const long long per = 2 * gu_items + dn_items;
   const int x = (int)(gid / per);
-  const long long local = gid % per;
+  long long local = gid % per;
 
-  const uint8_t* src = canon + (size_t)x * stride + (size_t)local * bq;
-  uint8_t* ebase = packed + (size_t)(first_expert + x) * stride;
-
-  int row, blk;
-  uint8_t* base;
-  if (local < 2 * nGU) {
-    const int m = (int)(local / nGU);
-    const long long l = local % nGU;
-    row = (int)(l / (H / BLOCK_W));
-    blk = (int)(l % (H / BLOCK_W));
-    base = ebase + gu_off(nv, H / SB_WEIGHTS, row / ROWS_PER_TILE, blk / 8, m, 0);
+  int m, K;
+  if (local < 2 * gu_items) {
+    m = (int)(local / gu_items);
+    local %= gu_items;
+    K = H;
   } else {
-    const long long l = local - 2 * nGU;
-    row = (int)(l / (I / BLOCK_W));
-    blk = (int)(l % (I / BLOCK_W));
-    base = ebase + gu_bytes(fmt, H, I) + dn_off(nv, I / SB_WEIGHTS, row / ROWS_PER_TILE, blk / 8, 0);
+    m = 2;
+    local -= 2 * gu_items;
+    K = I;
   }
-  base += (row % ROWS_PER_TILE) * 16;
-  const int bb = blk % 8;
+  const int nsb = K / SB_WEIGHTS;
+  const int row = (int)(local / nsb), sb = (int)(local % nsb);
+  // canonical: gate blocks [I][H/32], up [I][H/32], down [H][I/32]
+  const size_t mat_canon = (m == 0) ? 0 : (m == 1 ? (size_t)I * (H / BLOCK_W) * bq
+                                                   : (size_t)2 * I * (H / BLOCK_W) * bq);
+  const uint8_t* src = canon + (size_t)x * stride + mat_canon + ((size_t)row * (K / BLOCK_W) + sb * 8) * bq;
+  const size_t mat_packed = (m == 0) ? 0 : (m == 1 ? up_off(fmt, H, I) : down_off(fmt, H, I));
+  uint8_t* slab = packed + (size_t)(first_expert + x) * stride + mat_packed +
+                  slab_off(fmt, nsb, row / GROUP_ROWS, sb);
+  const int r = row % GROUP_ROWS;
 
-  if (fmt == 2) {
-    uint8_t* dst = base + (bb / 2) * 1024 + (bb % 2) * 8;
-    for (int i = 0; i < 8; ++i) dst[i] = src[i];
-  } else if (fmt == 4) {
-    uint8_t* dst = base + bb * 1024;
-    for (int i = 0; i < 16; ++i) dst[i] = src[i];
-  } else {
-    // 32 three-bit codes, code j at bits [3j, 3j+3) of a 96-bit little-endian string
-    uint32_t w[4] = {ld_u32_unaligned(src), ld_u32_unaligned(src + 4), ld_u32_unaligned(src + 8), 0u};
-    uint64_t lo = 0;
-    uint32_t hi = 0;
-    for (int j = 0; j < 32; ++j) {
-      const int p = 3 * j, wd = p >> 5, off = p & 31;
-      uint32_t v = w[wd] >> off;
-      if (off > 29) v |= w[wd + 1] << (32 - off);
-      v &= 7u;
-      lo |= (uint64_t)(v & 3u) << (2 * j);
-      const int ww = j >> 4, i = (j & 15) >> 2, s = j & 3;
-      hi |= ((v >> 2) & 1u) << (8 * i + 4 * ww + s);
+  for (int q = 0; q < 4; ++q) {                 // K-slice -> lane q*16 + r
+    const int lane = q * 16 + r;
+    if (fmt == 4) {
+      uint32_t w[8];
+      for (int bb = 0; bb < 8; ++bb) {
+        uint32_t d = 0;
+        for (int e = 0; e < 8; ++e) d |= canon_code(src + bb * bq, 4, 8 * q + e) << (4 * NIB4[e]);
+        w[bb] = d;
+      }
+      uint32_t* v0 = reinterpret_cast<uint32_t*>(slab + lane * 16);
+      uint32_t* v1 = reinterpret_cast<uint32_t*>(slab + 1024 + lane * 16);
+      for (int i = 0; i < 4; ++i) { v0[i] = w[i]; v1[i] = w[4 + i]; }
+    } else {
+      uint32_t lo[4] = {0, 0, 0, 0}, hi[2] = {0, 0};
+      for (int bb = 0; bb < 8; ++bb) {
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t c = canon_code(src + bb * bq, fmt, 8 * q + e);
+          lo[bb >> 1] |= (c & 3u) << (16 * (bb & 1) + POS2[e]);
+          if (fmt == 3) hi[bb >> 2] |= ((c >> 2) & 1u) << (4 * e + (bb & 3));
+        }
+      }
+      uint32_t* v0 = reinterpret_cast<uint32_t*>(slab + lane * 16);
+      for (int i = 0; i < 4; ++i) v0[i] = lo[i];
+      if (fmt == 3) {
+        uint32_t* vh = reinterpret_cast<uint32_t*>(slab + 1024 + lane * 8);
+        vh[0] = hi[0];
+        vh[1] = hi[1];
+      }
     }
-    uint8_t* dlo = base + (bb / 2) * 1024 + (bb % 2) * 8;
-    for (int i = 0; i < 8; ++i) dlo[i] = (uint8_t)(lo >> (8 * i));
-    uint8_t* dhi = base + (4 + bb / 4) * 1024 + (bb % 4) * 4;
-    for (int i = 0; i < 4; ++i) dhi[i] = (uint8_t)(hi >> (8 * i));
   }
-  uint8_t* dsc = base + ncv * 1024 + bb * 2;
-  dsc[0] = src[cb];
-  dsc[1] = src[cb + 1];
+  uint8_t* sc = slab + slab_code_bytes(fmt) + r * 16;
+  for (int bb = 0; bb < 8; ++bb) {
+    sc[2 * bb] = src[bb * bq + bq - 2];
+    sc[2 * bb + 1] = src[bb * bq + bq - 1];
+  }
 }
 
 __global__ void k_router_split(const float* __restrict__ w, uint16_t* __restrict__ hi,
@@ -98,14 +114,12 @@ __global__ void k_router_split(const float* __restrict__ w, uint16_t* __restrict
 
 hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in, int first_expert,
                          hipStream_t s) {
-  const long long per = 2LL * L.I * (L.H / BLOCK_W) + (long long)L.H * (L.I / BLOCK_W);
+  const long long per = 2LL * L.I * (L.H / SB_WEIGHTS) + (long long)L.H * (L.I / SB_WEIGHTS);
   const long long n = per * n_experts_in;
   if (n == 0) return hipSuccess;
   const int bs = 256;
-  const long long grid = (n + bs - 1) / bs;
-  hipLaunchKernelGGL(k_repack, dim3((unsigned)grid), dim3(bs), 0, s, canon,
-                     const_cast<uint8_t*>(L.packed), L.fmt, L.H, L.I, L.expert_stride, n,
-                     first_expert);
+  hipLaunchKernelGGL(k_repack, dim3((unsigned)((n + bs - 1) / bs)), dim3(bs), 0, s, canon,
+                     const_cast<uint8_t*>(L.packed), L.fmt, L.H, L.I, L.expert_stride, n, first_expert);
   return hipGetLastError();
 }
 

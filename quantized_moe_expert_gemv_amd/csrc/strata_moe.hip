@@ -24,6 +24,8 @@ struct strata_moe {
   Work W;          // regions sized for cfg.max_tokens (max_tiles set per call)
   uint8_t* ws;
   size_t ws_bytes;
+  hipEvent_t trace[STRATA_MAX_TRACE_EVENTS];   // armed by strata_moe_trace_next_call
+  int n_trace;
 };
 
 namespace {
@@ -69,8 +71,8 @@ int check_config(const strata_moe_config* c) {
 }
 
 struct WsPlan {
-  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, uexp, uoff, meta, tickets,
-      chunk_base, pair_rank, tiles, act, y, total;
+  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, udesc, wtab, meta, tickets,
+      chunk_base, pair_rank, tiles, act, xparts, y, total;
   int nchunks, max_tiles;
 };
 
@@ -96,14 +98,18 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.offsets = take((E + 1) * 4);
   p.perm = take(P * 4);
   p.inv = take(P * 4);
-  p.uexp = take((E + 1) * 4);
-  p.uoff = take((E + 2) * 4);
+  p.udesc = take((E + 1) * 16 * 4);
+  p.wtab = take((E + 1) * 8 * 4);
   p.meta = take(16 * 4);
   p.tickets = take((H / 64 + 1) * 4);
   p.chunk_base = take(E * (size_t)p.nchunks * 4);
   p.pair_rank = take(P * 4);
   p.tiles = take((size_t)p.max_tiles * 16);
-  p.act = take(slots * I * 4);
+  const size_t Td = T < STRATA_DECODE_MAX_T ? T : STRATA_DECODE_MAX_T;
+  const size_t act_prefill = slots * I * 2;                                   // bf16 rows
+  const size_t act_decode = (Td * k + (size_t)c.n_shared * Td) * 3 * I * 2;   // fp16 parts
+  p.act = take(act_prefill > act_decode ? act_prefill : act_decode);
+  p.xparts = take(Td * 3 * H * 2);
   p.y = take(slots * H * 4);
   p.total = o;
   return p;
@@ -159,20 +165,34 @@ Call make_call(const void* x, int32_t x_dtype, int32_t T, float* out, uint32_t f
   return c;
 }
 
-int run_route(strata_moe* h, const Call& c, bool decode, hipStream_t s) {
+// A call consumes the events armed by strata_moe_trace_next_call (one-shot).
+struct TraceScope {
+  Tracer t;
+  Tracer* ptr = nullptr;
+  explicit TraceScope(strata_moe* h) {
+    if (h->n_trace > 0) {
+      t.ev = h->trace;
+      t.n = h->n_trace;
+      ptr = &t;
+      h->n_trace = 0;
+    }
+  }
+};
+
+int run_route(strata_moe* h, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
   Work W = h->W;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
-  hipError_t e = decode ? launch_decode_route(h->L, W, c, s) : launch_prefill_route(h->L, W, c, s);
+  hipError_t e = decode ? launch_decode_route(h->L, W, c, s, tr) : launch_prefill_route(h->L, W, c, s, tr);
   if (e != hipSuccess) return hip_fail(e, "route launch");
   return STRATA_OK;
 }
 
-int run_forward(strata_moe* h, const Call& c, bool decode, hipStream_t s) {
-  int rc = run_route(h, c, decode, s);
+int run_forward(strata_moe* h, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
+  int rc = run_route(h, c, decode, s, tr);
   if (rc) return rc;
   Work W = h->W;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
-  hipError_t e = decode ? launch_decode_experts(h->L, W, c, s) : launch_prefill_experts(h->L, W, c, s);
+  hipError_t e = decode ? launch_decode_experts(h->L, W, c, s, tr) : launch_prefill_experts(h->L, W, c, s, tr);
   if (e != hipSuccess) return hip_fail(e, "expert launch");
   return STRATA_OK;
 }
@@ -236,14 +256,16 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.offsets = reinterpret_cast<int*>(ws + p.offsets);
   W.perm = reinterpret_cast<int*>(ws + p.perm);
   W.inv = reinterpret_cast<int*>(ws + p.inv);
-  W.uexp = reinterpret_cast<int*>(ws + p.uexp);
-  W.uoff = reinterpret_cast<int*>(ws + p.uoff);
+  W.udesc = reinterpret_cast<int*>(ws + p.udesc);
   W.meta = reinterpret_cast<int*>(ws + p.meta);
   W.tickets = reinterpret_cast<int*>(ws + p.tickets);
   W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
   W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
   W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
-  W.act = ws + p.act;
+  W.act = reinterpret_cast<float*>(ws + p.act);
+  W.actp = reinterpret_cast<_Float16*>(ws + p.act);
+  W.xparts = reinterpret_cast<_Float16*>(ws + p.xparts);
+  W.wtab = reinterpret_cast<float*>(ws + p.wtab);
   W.y = reinterpret_cast<float*>(ws + p.y);
   W.nchunks = p.nchunks;
   W.max_tiles = p.max_tiles;
@@ -291,7 +313,8 @@ int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, i
     return fail(STRATA_E_INVALID, "route outputs must be non-NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Call c = make_call(x, x_dtype, T, nullptr, flags);
-  if ((rc = run_route(h, c, use_decode(T, flags), s))) return rc;
+  TraceScope ts(h);
+  if ((rc = run_route(h, c, use_decode(T, flags), s, ts.ptr))) return rc;
   const size_t P = (size_t)T * h->cfg.top_k;
   hipError_t e = hipMemcpyAsync(topk_idx, h->W.topk_idx, P * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(topk_w, h->W.topk_w, P * 4, hipMemcpyDeviceToDevice, s);
@@ -314,7 +337,8 @@ int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
   const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
   if (xa < oa + ob && oa < xa + xb) return fail(STRATA_E_INVALID, "x and out overlap");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(T, flags), s))) return rc;
+  TraceScope ts(h);
+  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(T, flags), s, ts.ptr))) return rc;
   return ok();
 }
 
@@ -343,11 +367,25 @@ int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const 
     // the last layer writes `out`; earlier layers alternate so that happens
     float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
     const Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
-    int rc = run_forward(layers[l], c, use_decode(T, 0), s);
+    TraceScope ts(layers[l]);
+    int rc = run_forward(layers[l], c, use_decode(T, 0), s, ts.ptr);
     if (rc) return rc;
     cur = dst;
     cur_dtype = STRATA_FP32;
   }
+  return ok();
+}
+
+int strata_moe_trace_next_call(strata_moe* h, void* const* events, int32_t n_events) {
+  if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
+  if (n_events < 0 || n_events > STRATA_MAX_TRACE_EVENTS)
+    return fail(STRATA_E_INVALID, "n_events %d outside [0, %d]", n_events, STRATA_MAX_TRACE_EVENTS);
+  if (n_events > 0 && !events) return fail(STRATA_E_INVALID, "events is NULL");
+  for (int i = 0; i < n_events; ++i) {
+    if (!events[i]) return fail(STRATA_E_INVALID, "event %d is NULL", i);
+    h->trace[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  h->n_trace = n_events;
   return ok();
 }
 

@@ -30,8 +30,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"strata_moe_expert_bytes", "strata_moe_packed_bytes",
                           "strata_moe_workspace_bytes", "strata_moe_create", "strata_moe_route",
-                          "strata_moe_forward", "strata_moe_stack_forward", "strata_moe_destroy",
-                          "strata_moe_last_error"}
+                          "strata_moe_forward", "strata_moe_stack_forward", "strata_moe_trace_next_call",
+                          "strata_moe_destroy", "strata_moe_last_error"}
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -100,5 +100,7 @@ def test_calls_on_null_handle_fail_cleanly(B):
     rc = B._lib.strata_moe_forward(None, ctypes.c_void_p(256), 0, 1, ctypes.c_void_p(512), 0, None)
     assert rc == B.STRATA_E_INVALID and "handle" in B.strata_moe_last_error()
     rc = B._lib.strata_moe_stack_forward(None, 0, None, 0, 1, None, None, None)
+    assert rc == B.STRATA_E_INVALID
+    rc = B._lib.strata_moe_trace_next_call(None, None, 0)
     assert rc == B.STRATA_E_INVALID
     B.strata_moe_destroy(None)            # NULL-safe

@@ -238,3 +238,33 @@ def test_workload_deepseek_q4(B):
     sample = np.random.default_rng(1).choice(2048, 8, replace=False)
     ref, _ = hl.oracle(xf[sample])
     assert rel_l2(out[sample], ref) <= PREFILL_TOL
+
+
+# ------------------------------------------------------------------ HIP graph capture and replay
+@pytest.mark.parametrize("T", [1, 4, 100])
+def test_graph_replay_matches_eager(B, T):
+    hl, layer = tiny(2, n_shared=1)
+    batches = [to_device_bf16(tokens(hl, 200 + 10 * T + i, T)[0], DEV) for i in range(3)]
+    eager = [layer.forward(x).clone() for x in batches]
+    outs = [torch.empty_like(e) for e in eager]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for x, o in zip(batches, outs):
+            layer.forward(x, out=o)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, o in zip(batches, outs):
+            layer.forward(x, out=o)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs from eager"
+        # eager work on the same handle between replays
+        layer.forward(batches[rep % 3])
+        torch.cuda.synchronize()
