@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB 4 times (reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -60,6 +62,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     from moe_synth import WORKLOADS, generate as G, canonical_block_bytes
     from quantized_moe_expert_gemv_amd import binding as B
 
@@ -185,18 +190,16 @@ def main():
         names = ["route_gemv", "topk", "gateup", "down_combine"]
     else:
         names = ["router_gemm", "topk", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
+    # each kernel's own dispatch start/end, bound to a pair of events on the
+    # launch stream (eager launches of the same steps, after the timed replay)
     n_trace = min(steps, 256)
-    ev_sets = []
-    for i in range(n_trace):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        for e in evs:
-            e.record()
-        ev_sets.append(evs)
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+               for _ in range(n_trace)]
     torch.cuda.synchronize()
     for i in range(n_trace):
         step(i, trace_events=ev_sets[i])
     torch.cuda.synchronize()
-    dur = np.array([[ev[j].elapsed_time(ev[j + 1]) for j in range(len(names))] for ev in ev_sets])
+    dur = np.array([[ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(len(names))] for ev in ev_sets])
     kern_us = dur.mean(axis=0) * 1e3
 
     # algorithmic work per launch
@@ -271,6 +274,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: what the HBM read/write counters report for
+    it scales the counters of the layer's kernels to bytes."""
+    import torch
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 4
+    print(json.dumps({"copy_bytes_each_way": n, "copies": 4, "ms_per_copy": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def cpu_baseline(args, w, host0, xs_h, G):

@@ -162,13 +162,17 @@ STRATA_API int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_lay
 
 /*
  * Per-kernel timing of the next route/forward/stack call on this handle
- * (one-shot).  events are hipEvent_t created by the caller (void*); the call
- * records events[0] on its stream before its first kernel and events[i]
- * after its i-th kernel, for i < n_events; extra kernels are not traced.
- * Kernel order: decode forward = router/top-k/permute, gate/up, down+combine;
- * prefill forward = router GEMM, top-k, scan, scatter, gate/up GEMM, down
- * GEMM, combine (route-only calls stop after the routing kernels).
- * n_events in [0, STRATA_MAX_TRACE_EVENTS]; 0 disarms.
+ * (one-shot).  events are hipEvent_t created by the caller (void*), taken in
+ * pairs: kernel i of the call is launched with events[2i] and events[2i+1]
+ * bound to its own dispatch (hipExtLaunchKernelGGL), so the elapsed time of
+ * the pair is that kernel's execution, without launch gaps.  Kernels beyond
+ * n_events / 2 are not traced.  Kernel order: decode forward = router GEMV,
+ * top-k + permutation, gate/up + SwiGLU, down + weighted combine; prefill
+ * forward = router GEMM, top-k, scan, scatter, gate/up GEMM, down GEMM,
+ * combine (route-only calls stop after the routing kernels).  A stack call
+ * traces the handle's layer only.  n_events even, in
+ * [0, STRATA_MAX_TRACE_EVENTS]; 0 disarms.  The events must outlive the
+ * call's completion on its stream.
  */
 #define STRATA_MAX_TRACE_EVENTS 16
 STRATA_API int strata_moe_trace_next_call(strata_moe* h, void* const* events, int32_t n_events);

@@ -6,22 +6,27 @@
 // 用草拟 token 提高生成速度的 MTP) where tokens that pick the same expert share
 // one read of its weights (blog.5616760.com/0039.html, section 十二).
 //
-// Four launches per layer:
-//   k_route_gemv  router GEMV, one wave per expert row (fp32, the row held
-//                 in registers); each workgroup also writes a slice of the
-//                 tokens as three fp16 parts (x = p0 + p1 + p2 exactly);
-//   k_topk        one workgroup: top-k + renormalised softmax per token, the
-//                 stable token->expert permutation, one descriptor per active
-//                 expert (id, first slot, token ids) and a dense table of
-//                 routing weights per (active expert, token);
-//   k_gateup      one workgroup per (active expert, 64 rows of I); waves split
-//                 the H superblocks; gate and up rows of the same i stay in
-//                 one lane; writes silu(g) * u as three fp16 parts per pair;
-//   k_down        one workgroup per 32 rows of H; waves take (active expert,
-//                 superblock) units, scale each expert's rows by its routing
-//                 weights and the workgroup reduces them in a fixed order:
-//                 the weighted combine happens here, with no cross-workgroup
+// Four launches per forward call, each with many short waves (the time of a
+// kernel this small is the longest chain of dependent memory round trips and
+// instructions of one wave, not the bytes):
+//   k_route_gemv  router GEMV, one workgroup per expert row split over its
+//                 waves; each workgroup also writes a slice of the tokens as
+//                 three fp16 parts (x = p0 + p1 + p2 exactly);
+//   k_topk        one workgroup per token: two-level radix selection of the k
+//                 largest logits and the renormalised softmax weights;
+//   k_gateup      one workgroup per (active expert, 32 rows of I): it finds
+//                 its expert from the top-k ids (experts chosen by any token,
+//                 ascending, then the shared one), its waves split the H
+//                 superblocks; writes silu(g) * u as three fp16 parts per
+//                 (active expert, token);
+//   k_down        one workgroup per 16 rows of H; waves take (active expert,
+//                 superblock) units with the next units' loads in flight,
+//                 scale each expert's rows by its routing weights and the
+//                 workgroup reduces them in a fixed order: the weighted
+//                 combine happens here, with no cross-workgroup
 //                 synchronisation.
+// A route() call runs k_route_gemv, k_topk and k_permute (the stable
+// token->expert permutation that the expert kernels do not need).
 //
 // The multiply-accumulate runs on the matrix cores (16x16x32 fp16 MFMA, fp32
 // accumulation) with exact operands: the code q of a weight becomes the fp16
@@ -41,7 +46,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
-constexpr int DESC = 16;   // ints per active-expert descriptor: e, first slot, n, 0, tokens[8], pad
+constexpr int DESC = 2;    // ints per active expert for the down kernel: expert id, token mask
 constexpr int WTAB = 8;    // routing weights per active expert, indexed by token
 constexpr int NPART = 3;   // fp16 parts of an fp32 activation
 
@@ -69,6 +74,10 @@ __device__ inline f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
 
 __device__ inline f16x8 as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8, v); }
 
+__device__ inline uint4 mask_u4(const uint4& v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 __device__ inline f16x8 join(half2_t a, half2_t b, half2_t c, half2_t d) {
   f16x8 r;
   r[0] = a.x; r[1] = a.y; r[2] = b.x; r[3] = b.y;
@@ -83,14 +92,33 @@ template <> struct Codes<2> { uint4 lo; };
 template <> struct Codes<3> { uint4 lo; uint2 hi; };
 template <> struct Codes<4> { uint4 v0, v1; };
 
+// Buffer loads: one descriptor (SGPRs) per expert record or workspace
+// buffer, a per-lane byte offset (one VGPR) and a wave-uniform byte offset
+// (SGPR), so a wave's many slab loads cost no per-slab address registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
+__device__ inline uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Codes of one lane of the slab at byte soff of an expert record.
 template <int FMT>
-__device__ inline void load_codes(const uint8_t* slab, int lane, Codes<FMT>& c) {
+__device__ inline void bload_codes(rsrc_t r, uint32_t soff, int lane, Codes<FMT>& c) {
   if constexpr (FMT == 4) {
-    c.v0 = *reinterpret_cast<const uint4*>(slab + lane * 16);
-    c.v1 = *reinterpret_cast<const uint4*>(slab + 1024 + lane * 16);
+    c.v0 = bload4(r, lane * 16, soff);
+    c.v1 = bload4(r, 1024 + lane * 16, soff);
   } else {
-    c.lo = *reinterpret_cast<const uint4*>(slab + lane * 16);
-    if constexpr (FMT == 3) c.hi = *reinterpret_cast<const uint2*>(slab + 1024 + lane * 8);
+    c.lo = bload4(r, lane * 16, soff);
+    if constexpr (FMT == 3) c.hi = bload2(r, 1024 + lane * 8, soff);
   }
 }
 
@@ -167,12 +195,6 @@ __device__ inline f32x4 block_offset(const f16x8& a) {
   }
 }
 
-// sum over the three part rows of the 16x16 result (lane groups 0..2; group 3 holds zeros)
-__device__ inline float sum_parts(float v) {
-  v += __shfl_xor(v, 16, WAVE);
-  v += __shfl_xor(v, 32, WAVE);
-  return v;
-}
 
 // ------------------------------------------------------------------ router
 struct RouteArgs {
@@ -184,126 +206,211 @@ struct RouteArgs {
   _Float16* xparts;
 };
 
-// T rows of x -> fp32 LDS (natural order): batches of 16 loads per thread,
-// all issued before any is used (indices clamped into the input)
-__device__ inline void stage_x(const void* x, int x_f32, int T, int H, float* xs) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  float4* dst = reinterpret_cast<float4*>(xs);
-  if (x_f32) {
-    const float4* src = reinterpret_cast<const float4*>(x);
-    const int n4 = T * H / 4;
-    for (int b = tid; b < n4; b += 16 * nt) {
-      float4 r[16];
+constexpr int ROUTE_WAVES = 4;
+constexpr int ROUTE_BATCH = 4;   // float4 columns per lane issued together
+
+// token t, columns 4q..4q+3 of x as fp32
+template <bool XF32>
+__device__ inline float4 x_quad(const void* x, int H, int t, int q) {
+  if constexpr (XF32) return reinterpret_cast<const float4*>(x)[((size_t)t * H >> 2) + q];
+  const uint2 v = reinterpret_cast<const uint2*>(x)[((size_t)t * H >> 2) + q];
+  return bf16x4(v.x, v.y);
+}
+
+// One workgroup per expert row; its waves split the row into float4 columns
+// (strided, so every load instruction of a wave reads 1 KiB contiguously) and
+// meet in LDS.  Workgroup e also writes its slice of the tokens as fp16 parts.
+// TT = T and the input type are template constants so that every load is
+// unconditional (clamped into bounds) and all of a batch are in flight
+// together.
+template <int TT, bool XF32>
+__global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
+  __shared__ float part[ROUTE_WAVES][TT];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, E = a.E, e = blockIdx.x;
+  const int nq = H >> 2;
+  const float4* row = reinterpret_cast<const float4*>(a.Wr + (size_t)e * H);
+  float acc[TT];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) r[q] = src[min(b + q * nt, n4 - 1)];
+  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  for (int q0 = tid; q0 < nq; q0 += ROUTE_BATCH * 64 * ROUTE_WAVES) {
+    float4 w[ROUTE_BATCH];
+    float4 xv[ROUTE_BATCH][TT];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) if (b + q * nt < n4) dst[b + q * nt] = r[q];
+    for (int j = 0; j < ROUTE_BATCH; ++j) {
+      const int q = min(q0 + j * 64 * ROUTE_WAVES, nq - 1);
+      w[j] = row[q];
+#pragma unroll
+      for (int t = 0; t < TT; ++t) xv[j][t] = x_quad<XF32>(a.x, H, t, q);
     }
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(x);
-    const int n8 = T * H / 8;
-    for (int b = tid; b < n8; b += 16 * nt) {
-      uint4 r[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) r[q] = src[min(b + q * nt, n8 - 1)];
+    for (int j = 0; j < ROUTE_BATCH; ++j) {
+      const float m = (q0 + j * 64 * ROUTE_WAVES < nq) ? 1.f : 0.f;   // clamped duplicates count 0
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int i = b + q * nt;
-        if (i < n8) {
-          dst[2 * i] = bf16x4(r[q].x, r[q].y);
-          dst[2 * i + 1] = bf16x4(r[q].z, r[q].w);
-        }
+      for (int t = 0; t < TT; ++t) {
+        float d = w[j].x * xv[j][t].x;
+        d = fmaf(w[j].y, xv[j][t].y, d);
+        d = fmaf(w[j].z, xv[j][t].z, d);
+        d = fmaf(w[j].w, xv[j][t].w, d);
+        acc[t] = fmaf(m, d, acc[t]);
       }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void k_route_gemv(RouteArgs a) {
-  extern __shared__ float xs[];                // [T][H] fp32
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.H, E = a.E, T = a.T;
-  const int e = blockIdx.x * 4 + wv;
-  const int nc = H >> 8;                       // float4 per lane
-  const bool have_row = e < E;
-  // all 16 loads issued unconditionally (indices clamped into the row), used only for c < nc
-  float4 wr[16];
-  {
-    const float4* row = reinterpret_cast<const float4*>(a.Wr + (size_t)(have_row ? e : 0) * H);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) wr[c] = row[lane + 64 * (c < nc ? c : nc - 1)];
+  for (int t = 0; t < TT; ++t) {
+    const float s = wave_sum(acc[t]);
+    if (lane == 0) part[wv][t] = s;
   }
-  const float bias = (have_row && a.bias) ? a.bias[e] : 0.f;
-  stage_x(a.x, a.x_f32, T, H, xs);
-  __syncthreads();
   // this workgroup's slice of the token rows as fp16 parts [t][part][H]
-  const int chunk = ((H + gridDim.x - 1) / gridDim.x + 7) & ~7;
-  const int h0 = blockIdx.x * chunk, len = min(H, h0 + chunk) - h0;
-  for (int idx = tid; idx < T * len; idx += blockDim.x) {
-    const int t = idx / len, h = h0 + idx % len;
+  const int n = TT * H, chunk = (n + E - 1) / E;
+  for (int i = e * chunk + tid; i < min(n, (e + 1) * chunk); i += blockDim.x) {
+    const int t = i / H, h = i - t * H;
+    const float v = XF32 ? reinterpret_cast<const float*>(a.x)[i]
+                         : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[i]);
     _Float16 p[NPART];
-    split3(xs[(size_t)t * H + h], p);
+    split3(v, p);
 #pragma unroll
     for (int q = 0; q < NPART; ++q) a.xparts[((size_t)t * NPART + q) * H + h] = p[q];
   }
-  if (have_row) {
-    float acc[DECODE_MAX_T];
+  __syncthreads();
+  if (tid < TT) {
+    float s = 0.f;
 #pragma unroll
-    for (int t = 0; t < DECODE_MAX_T; ++t) acc[t] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      if (c < nc) {
-#pragma unroll
-        for (int t = 0; t < DECODE_MAX_T; ++t) {
-          if (t < T) {
-            const float4 xv = *reinterpret_cast<const float4*>(xs + (size_t)t * H + 4 * (lane + 64 * c));
-            acc[t] = fmaf(wr[c].x, xv.x, acc[t]);
-            acc[t] = fmaf(wr[c].y, xv.y, acc[t]);
-            acc[t] = fmaf(wr[c].z, xv.z, acc[t]);
-            acc[t] = fmaf(wr[c].w, xv.w, acc[t]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < DECODE_MAX_T; ++t) {
-      if (t < T) {
-        const float s = wave_sum(acc[t]);
-        if (lane == 0) a.logits[(size_t)t * E + e] = s + bias;
-      }
-    }
+    for (int w = 0; w < ROUTE_WAVES; ++w) s += part[w][tid];
+    a.logits[(size_t)tid * E + e] = s + (a.bias ? a.bias[e] : 0.f);
   }
 }
 
-// ------------------------------------------------------------------ top-k + permutation
+// ------------------------------------------------------------------ top-k
+// Radix selection over the keys u[i] of entries lane + 64 i (i < V): marks
+// the k largest (equal keys: lower entry first) and gives each marked entry
+// its rank in entry order.  Needs at least k entries (padding keys 0 count).
+template <int V>
+__device__ inline void wave_select(const uint32_t (&u)[V], int k, bool (&sel)[V], int (&pos)[V]) {
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) cnt += __popcll(__ballot(u[i] >= cand));
+    if (cnt >= k) tau = cand;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) gt += __popcll(__ballot(u[i] > tau));
+  const int need = k - gt;
+  int ties_before = 0, sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const bool tie = u[i] == tau;
+    const uint64_t tm = __ballot(tie);
+    const int trank = ties_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(tm >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)tm, 0u));
+    ties_before += __popcll(tm);
+    sel[i] = (u[i] > tau) || (tie && trank < need);
+    const uint64_t sm = __ballot(sel[i]);
+    pos[i] = sel_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(sm >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)sm, 0u));
+    sel_before += __popcll(sm);
+  }
+}
+
 struct TopkArgs {
   int T, E, k, n_shared;
   Work w;
 };
 
-// T tokens, one wave each (512 threads); LDS: T*k + 2E ints.
-__global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
-  extern __shared__ int lds_i[];
-  __shared__ int s_sel[8][64];
-  __shared__ int2 tmp[16];
-  const int tid = threadIdx.x, wv = tid >> 6, nt = blockDim.x;
-  const int E = a.E, k = a.k, T = a.T, P = T * k;
-  int* sel = lds_i;        // [T][k]
-  int* hist = sel + P;     // [E] counts, then offsets
-  int* uidx = hist + E;    // [E] active-expert index
-  if (wv < T)
-    wave_topk_any(a.w.logits + (size_t)wv * E, E, k, sel + wv * k, a.w.topk_w + (size_t)wv * k, s_sel[wv]);
-  for (int e = tid; e < E; e += nt) hist[e] = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += nt) {
-    a.w.topk_idx[p] = sel[p];
-    atomicAdd(&hist[sel[p]], 1);
+constexpr int TOPK_WAVES = 8;
+
+// One workgroup per token.  Each wave keeps the k best of its own contiguous
+// id range; the candidates land in LDS in id order and wave 0 keeps the k
+// best of those (the global k best are among them: same order everywhere).
+// Writes the ids in ascending order and the renormalised softmax weights
+// (max-shifted exp over the k selected, divided by their sum).
+template <int V1, int V2>
+__global__ __launch_bounds__(64 * TOPK_WAVES) void k_topk(TopkArgs a) {
+  __shared__ uint32_t c_key[TOPK_WAVES * 64];
+  __shared__ float c_val[TOPK_WAVES * 64];
+  __shared__ int c_id[TOPK_WAVES * 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int E = a.E, k = a.k, t = blockIdx.x;
+  const float* row = a.w.logits + (size_t)t * E;
+  const int e0 = wv * 64 * V1;
+  uint32_t u[V1];
+  float val[V1];
+#pragma unroll
+  for (int i = 0; i < V1; ++i) {
+    const int e = e0 + lane + 64 * i;
+    val[i] = row[min(e, E - 1)];
+    u[i] = e < E ? sortable_bits(val[i]) : 0u;
+  }
+  bool sel[V1];
+  int pos[V1];
+  wave_select<V1>(u, k, sel, pos);
+#pragma unroll
+  for (int i = 0; i < V1; ++i) {
+    if (sel[i]) {
+      const int c = wv * k + pos[i];
+      c_key[c] = u[i];
+      c_val[c] = val[i];
+      c_id[c] = e0 + lane + 64 * i;
+    }
   }
   __syncthreads();
-  // exclusive scans over experts of (count, non-empty), contiguous chunks per thread
+  if (wv != 0) return;
+  const int nc = TOPK_WAVES * k;
+  uint32_t u2[V2];
+  float v2[V2];
+  int id2[V2];
+#pragma unroll
+  for (int i = 0; i < V2; ++i) {
+    const int c = lane + 64 * i;
+    u2[i] = c < nc ? c_key[c] : 0u;
+    v2[i] = c < nc ? c_val[c] : 0.f;
+    id2[i] = c < nc ? c_id[c] : 0;
+  }
+  bool sel2[V2];
+  int pos2[V2];
+  wave_select<V2>(u2, k, sel2, pos2);
+  uint32_t umax = 0;
+#pragma unroll
+  for (int i = 0; i < V2; ++i) umax = (sel2[i] && u2[i] > umax) ? u2[i] : umax;
+  const float top = unsortable_bits((uint32_t)wave_max_u64(umax));
+  float z[V2], zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < V2; ++i) {
+    z[i] = sel2[i] ? expf(v2[i] - top) : 0.f;
+    zs += z[i];
+  }
+  const float s = wave_sum(zs);
+#pragma unroll
+  for (int i = 0; i < V2; ++i) {
+    if (sel2[i]) {
+      a.w.topk_idx[(size_t)t * k + pos2[i]] = id2[i];
+      a.w.topk_w[(size_t)t * k + pos2[i]] = z[i] / s;
+    }
+  }
+}
+
+// The stable token->expert permutation of the routing (route() only): counts,
+// offsets (exclusive scan over experts), and for every pair p = t * k + j its
+// slot, earlier tokens of the same expert first.  One workgroup.
+__global__ __launch_bounds__(512) void k_permute(TopkArgs a) {
+  extern __shared__ int lds_i[];
+  __shared__ int2 tmp[16];
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int E = a.E, k = a.k, T = a.T, P = T * k;
+  int* sel = lds_i;        // [P]
+  int* hist = sel + P;     // [E] counts, then offsets
+  for (int e = tid; e < E; e += nt) hist[e] = 0;
+  for (int p = tid; p < P; p += nt) sel[p] = a.w.topk_idx[p];
+  __syncthreads();
+  for (int p = tid; p < P; p += nt) atomicAdd(&hist[sel[p]], 1);
+  __syncthreads();
   const int per = (E + nt - 1) / nt;
   const int e0 = tid * per, e1 = min(E, e0 + per);
   int2 loc = make_int2(0, 0);
-  for (int e = e0; e < e1; ++e) { loc.x += hist[e]; loc.y += (hist[e] > 0); }
+  for (int e = e0; e < e1; ++e) loc.x += hist[e];
   int2 total;
   int2 base = block_exclusive_scan(loc, tmp, &total);
   for (int e = e0; e < e1; ++e) {
@@ -311,18 +418,9 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
     a.w.counts[e] = c;
     a.w.offsets[e] = base.x;
     hist[e] = base.x;
-    if (c > 0) {
-      uidx[e] = base.y;
-      *reinterpret_cast<int4*>(a.w.udesc + (size_t)base.y * DESC) = make_int4(e, base.x, c, 0);
-      float4* wt = reinterpret_cast<float4*>(a.w.wtab + (size_t)base.y * WTAB);
-      wt[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      wt[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     base.x += c;
-    base.y += (c > 0);
   }
   __syncthreads();
-  // stable slot of every pair: earlier tokens that chose the same expert go first
   for (int p = tid; p < P; p += nt) {
     const int t = p / k, e = sel[p];
     int rank = 0;
@@ -331,30 +429,16 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
     const int slot = hist[e] + rank;
     a.w.perm[slot] = p;
     a.w.inv[p] = slot;
-    a.w.udesc[(size_t)uidx[e] * DESC + 4 + rank] = t;
-    a.w.wtab[(size_t)uidx[e] * WTAB + t] = a.w.topk_w[p];
   }
-  if (tid == 0) {
-    const int U = total.y;
-    a.w.offsets[E] = P;
-    if (a.n_shared) {
-      *reinterpret_cast<int4*>(a.w.udesc + (size_t)U * DESC) = make_int4(E, P, T, 0);
-      for (int t = 0; t < DECODE_MAX_T; ++t) {
-        a.w.udesc[(size_t)U * DESC + 4 + t] = t;
-        a.w.wtab[(size_t)U * WTAB + t] = (t < T) ? 1.0f : 0.0f;
-      }
-      a.w.meta[0] = U + 1;
-    } else {
-      a.w.meta[0] = U;
-    }
-  }
+  if (tid == 0) a.w.offsets[E] = P;
 }
 
 // ------------------------------------------------------------------ experts
 struct ExpertArgs {
   const uint8_t* packed;
   size_t stride;
-  int H, I, E, k, T, P;
+  int H, I, E, k, T, P, n_shared;
+  uint32_t actp_bytes;       // bytes of the activation rows of this call
   const void* x;
   int x_f32;
   uint32_t flags;
@@ -362,33 +446,162 @@ struct ExpertArgs {
   Work w;
 };
 
-__device__ inline int desc_token(const int4& d1, const int4& d2, int j) {
-  const int4 v = (j < 4) ? d1 : d2;
-  const int q = j & 3;
-  return q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+// Active expert u of this call: the experts chosen by any token in ascending
+// id order, then the shared expert (id E, every token, weight 1).  Every
+// thread of the workgroup returns the same values; false when u is past the
+// last one.  LDS: bits[ceil(E/32)], info[4], wts[DECODE_MAX_T].
+__device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits, int* info, float* wts,
+                                     int& e_out, uint32_t& mask_out, int& n_active) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
+  const int T = a.T, k = a.k, E = a.E, P = T * k, nwords = (E + 31) >> 5;
+  // the pairs: P <= 512 <= ... one per thread when the workgroup has P threads;
+  // loaded unconditionally (clamped) so that the loads are all in flight
+  const int p0 = min(tid, P - 1);
+  const int my_e = a.w.topk_idx[p0];
+  const float my_w = a.w.topk_w[p0];
+  for (int i = tid; i < nwords; i += nt) bits[i] = 0u;
+  if (tid < DECODE_MAX_T) wts[tid] = 0.f;
+  if (tid == 0) info[1] = 0;
+  __syncthreads();
+  if (tid < P) atomicOr(&bits[my_e >> 5], 1u << (my_e & 31));
+  for (int p = tid + nt; p < P; p += nt) {
+    const int e = a.w.topk_idx[p];
+    atomicOr(&bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // words lane and 64 + lane (E <= 4096); inclusive prefix counts in word order
+    const uint32_t w0 = lane < nwords ? bits[lane] : 0u;
+    const uint32_t w1 = lane + 64 < nwords ? bits[lane + 64] : 0u;
+    const int c0 = __popc(w0), c1 = __popc(w1);
+    int s0 = c0, s1 = c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y0 = __shfl_up(s0, o, 64), y1 = __shfl_up(s1, o, 64);
+      if (lane >= o) { s0 += y0; s1 += y1; }
+    }
+    const int tot0 = __shfl(s0, 63, 64);
+    s1 += tot0;
+    int word = -1, r = 0;
+    uint32_t wbits = 0u;
+    if (u < s0 && u >= s0 - c0) { word = lane; r = u - (s0 - c0); wbits = w0; }
+    if (u < s1 && u >= s1 - c1) { word = lane + 64; r = u - (s1 - c1); wbits = w1; }
+    if (word >= 0) {
+      for (int j = 0; j < r; ++j) wbits &= wbits - 1u;    // drop the r lowest set bits
+      info[0] = word * 32 + __builtin_ctz(wbits);
+    }
+    if (lane == 63) info[2] = s1;
+  }
+  __syncthreads();
+  const int U = __builtin_amdgcn_readfirstlane(info[2]);    // the same in every lane: keep it scalar
+  n_active = U + a.n_shared;
+  if (u >= n_active) return false;
+  if (u < U) {
+    const int e = info[0];
+    if (tid < P && my_e == e) {
+      atomicOr(&info[1], 1 << (tid / k));
+      wts[tid / k] = my_w;
+    }
+    for (int p = tid + nt; p < P; p += nt) {
+      if (a.w.topk_idx[p] == e) {
+        const int t = p / k;
+        atomicOr(&info[1], 1 << t);
+        wts[t] = a.w.topk_w[p];
+      }
+    }
+    __syncthreads();
+    e_out = __builtin_amdgcn_readfirstlane(e);
+    mask_out = (uint32_t)__builtin_amdgcn_readfirstlane(info[1]);
+  } else {
+    e_out = E;
+    mask_out = (1u << T) - 1u;
+    __syncthreads();
+    if (tid < T) wts[tid] = 1.f;
+    __syncthreads();
+  }
+  return true;
 }
 
-// gate/up: a workgroup covers 2 row groups (32 rows i) of one active expert;
-// its waves split the H superblocks, each wave 2 gate + 2 up slabs per
-// superblock; partial sums meet in LDS.
-constexpr int GU_GROUPS = 2;
-constexpr int GU_SLABS = 2 * GU_GROUPS;
+// gate/up: a workgroup covers G row groups (16G rows i) of one active
+// expert; its waves split the H superblocks, each wave G gate + G up slabs
+// per superblock (sharing one activation operand); partial sums meet in LDS.
+// The workgroup first finds its expert from the top-k ids.  Output:
+// silu(g) * u as three fp16 parts, rows (active expert, token) of the
+// activation buffer.  G = 4 when many experts are active (fewer, larger
+// workgroups: all of them resident at once), else 2.
 
-template <int FMT, int NTG>
-__global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
-  extern __shared__ float red[];               // [nw][NTG][GU_SLABS][4 tokens][16 rows]
-  const int u = blockIdx.y, gp = blockIdx.x;
-  const int4* dsc = reinterpret_cast<const int4*>(a.w.udesc + (size_t)u * DESC);
-  const int4 d0 = dsc[0], d1 = dsc[1], d2 = dsc[2];
-  if (u >= a.w.meta[0]) return;
-  const int e = d0.x, s0 = d0.y, n = d0.z;
-  const int H = a.H, I = a.I, nsb = H / SB_WEIGHTS;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int r = lane & 15, ks = lane >> 4;          // weight row in the group, K-slice
-  const int part = (lane & 15) >> 2, jj = lane & 3;  // A-operand row of this lane: (part, token)
-  const uint8_t* gate = a.packed + (size_t)e * a.stride;
-  const uint8_t* up = gate + up_off(FMT, H, I);
+// one superblock of a gate/up wave: 2G slabs and the activation operand
+template <int FMT, int G> struct GuStage {
+  Codes<FMT> cd[2 * G];
+  uint4 sc[2 * G];
+  uint4 av[8];
+};
+
+template <int FMT, int G>
+__device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int sb, rsrc_t xr, uint32_t xvoff,
+                               int lane, GuStage<FMT, G>& st) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
+  const int r = lane & 15;
+#pragma unroll
+  for (int s = 0; s < 2 * G; ++s) {
+    const uint32_t soff = (s < G ? 0u : up_base) + (uint32_t)((G * gp + (s % G)) * nsb + sb) * SLAB;
+    bload_codes<FMT>(wr, soff, lane, st.cd[s]);
+    st.sc[s] = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
+  }
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) st.av[bb] = bload4(xr, xvoff + bb * BLOCK_W * 2, (uint32_t)sb * SB_WEIGHTS * 2);
+}
+
+template <int FMT, int G>
+__device__ inline void gu_compute(const GuStage<FMT, G>& st, float (&acc)[2 * G][4]) {
+  constexpr int GU_SLABS = 2 * G;
+#define STRATA_BLOCK(BB)                                                          \
+  {                                                                               \
+    const f16x8 af = as_f16x8(st.av[BB]);                                         \
+    const f32x4 off = block_offset<FMT>(af);                                      \
+    f32x4 d[GU_SLABS];                                                            \
+    _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s)                          \
+      d[s] = block_product<FMT, BB>(af, st.cd[s], off);                           \
+    _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s) {                        \
+      const float ds = block_scale<FMT, BB>(st.sc[s]);                            \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v)                               \
+        acc[s][v] = fmaf(ds, d[s][v], acc[s][v]);                                 \
+    }                                                                             \
+  }
+  STRATA_BLOCK(0) STRATA_BLOCK(1) STRATA_BLOCK(2) STRATA_BLOCK(3)
+  STRATA_BLOCK(4) STRATA_BLOCK(5) STRATA_BLOCK(6) STRATA_BLOCK(7)
+#undef STRATA_BLOCK
+}
+
+template <int FMT, int NTG, int G>
+__global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
+  constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
+  extern __shared__ float4 red4[];             // [nw][GU_SLABS][48 lanes] x 4 tokens
+  float* red = reinterpret_cast<float*>(red4);
+  __shared__ uint32_t s_bits[128];
+  __shared__ int s_info[4];
+  __shared__ float s_wts[DECODE_MAX_T];
+  const int u = blockIdx.y, gp = blockIdx.x;
+  int e, U;
+  uint32_t mask;
+  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U)) return;
+  const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ks = lane >> 4;                          // K-slice
+  const int part = (lane & 15) >> 2, jj = lane & 3;  // A-operand row of this lane: (part, token)
+  if (gp == 0) {
+    // routing of this active expert for the down kernel
+    if (threadIdx.x == 0) {
+      a.w.udesc[(size_t)u * DESC] = e;
+      a.w.udesc[(size_t)u * DESC + 1] = (int)mask;
+      if (u == 0) a.w.meta[0] = U;
+    }
+    if (threadIdx.x < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + threadIdx.x] = s_wts[threadIdx.x];
+  }
+  const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
+  const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(T * NPART * H * 2));
+  const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
 
   for (int tg = 0; tg < NTG; ++tg) {                // token groups of 4
     float acc[GU_SLABS][4];
@@ -396,75 +609,58 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     for (int s = 0; s < GU_SLABS; ++s)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[s][v] = 0.f;
-    const int j = 4 * tg + jj;
-    const bool valid = part < NPART && j < n;
-    const _Float16* xsrc = a.w.xparts + ((size_t)(valid ? desc_token(d1, d2, j) : 0) * NPART +
-                                         (valid ? part : 0)) * H + 8 * ks;
+    // A row (part, token j): rows past T and the unused fourth part read a
+    // real row (same cache lines as other lanes; their results are not used)
+    const int jr = min(4 * tg + jj, T - 1), pr = min(part, NPART - 1);
+    const uint32_t xvoff = (uint32_t)(((jr * NPART + pr) * H + 8 * ks) * 2);
     for (int sb = wv; sb < nsb; sb += nw) {
-      Codes<FMT> cd[GU_SLABS];
-      uint4 sc[GU_SLABS];
-#pragma unroll
-      for (int s = 0; s < GU_SLABS; ++s) {
-        const uint8_t* slab = (s < GU_GROUPS ? gate : up) +
-                              ((size_t)(GU_GROUPS * gp + (s % GU_GROUPS)) * nsb + sb) * SLAB;
-        load_codes<FMT>(slab, lane, cd[s]);
-        sc[s] = *reinterpret_cast<const uint4*>(slab + Fmt<FMT>::slab_codes + r * 16);
-      }
-      uint4 av[8];
-#pragma unroll
-      for (int bb = 0; bb < 8; ++bb)
-        av[bb] = valid ? *reinterpret_cast<const uint4*>(xsrc + sb * SB_WEIGHTS + bb * BLOCK_W)
-                       : make_uint4(0, 0, 0, 0);
-#define STRATA_BLOCK(BB)                                                          \
-      {                                                                           \
-        const f16x8 af = as_f16x8(av[BB]);                                        \
-        const f32x4 off = block_offset<FMT>(af);                                  \
-        f32x4 d[GU_SLABS];                                                        \
-        _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s)                      \
-          d[s] = block_product<FMT, BB>(af, cd[s], off);                          \
-        _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s) {                    \
-          const float ds = block_scale<FMT, BB>(sc[s]);                           \
-          _Pragma("unroll") for (int v = 0; v < 4; ++v)                           \
-            acc[s][v] = fmaf(ds, d[s][v], acc[s][v]);                             \
-        }                                                                         \
-      }
-      STRATA_BLOCK(0) STRATA_BLOCK(1) STRATA_BLOCK(2) STRATA_BLOCK(3)
-      STRATA_BLOCK(4) STRATA_BLOCK(5) STRATA_BLOCK(6) STRATA_BLOCK(7)
-#undef STRATA_BLOCK
+      GuStage<FMT, G> st;
+      gu_load<FMT, G>(wr, up_base, gp, nsb, sb, xr, xvoff, lane, st);
+      __builtin_amdgcn_sched_barrier(0);            // every load of the stage issued before any use
+      gu_compute<FMT, G>(st, acc);
     }
-    // parts -> lanes 0..15 hold (row r, token v) of each slab
+    // raw 16x16 results to LDS: lane l holds (part l/16, token v) of row l%16
+    if (tg > 0) __syncthreads();                     // the previous group's sums are read
+    // (lanes 48..63 hold the unused fourth part and are not kept)
+    float4* dst = reinterpret_cast<float4*>(red) + ((size_t)wv * GU_SLABS) * 48 + lane;
+    if (lane < 48) {
 #pragma unroll
-    for (int s = 0; s < GU_SLABS; ++s)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float t = sum_parts(acc[s][v]);
-        if (lane < 16) red[((((size_t)wv * NTG + tg) * GU_SLABS + s) * 4 + v) * 16 + lane] = t;
-      }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < NTG * 4 * GU_GROUPS * 16; idx += blockDim.x) {
-    const int row = idx & 15, gi = (idx >> 4) % GU_GROUPS, v = (idx / (16 * GU_GROUPS)) & 3;
-    const int tg = idx / (64 * GU_GROUPS);
-    const int j = 4 * tg + v;
-    if (j >= n) continue;
-    float g = 0.f, uu = 0.f;
-    for (int w = 0; w < nw; ++w) {
-      g += red[((((size_t)w * NTG + tg) * GU_SLABS + gi) * 4 + v) * 16 + row];
-      uu += red[((((size_t)w * NTG + tg) * GU_SLABS + GU_GROUPS + gi) * 4 + v) * 16 + row];
+      for (int s = 0; s < GU_SLABS; ++s)
+        dst[s * 48] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
     }
-    const float act = silu_f(g) * uu;
-    _Float16 p[NPART];
-    split3(act, p);
-    const int i = (GU_GROUPS * gp + gi) * 16 + row;
+    __syncthreads();
+    // sums over waves and parts, SwiGLU, fp16 parts of the result
+    for (int idx = threadIdx.x; idx < 4 * GU_GROUPS * 16; idx += blockDim.x) {
+      const int row = idx & 15, gi = (idx >> 4) % GU_GROUPS, v = idx / (16 * GU_GROUPS);
+      const int t = 4 * tg + v;
+      if (t >= T || !((mask >> t) & 1u)) continue;
+      float g = 0.f, uu = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        const float* rg = red + (((size_t)w * GU_SLABS + gi) * 48 + row) * 4 + v;
+        const float* ru = red + (((size_t)w * GU_SLABS + GU_GROUPS + gi) * 48 + row) * 4 + v;
 #pragma unroll
-    for (int q = 0; q < NPART; ++q) a.w.actp[((size_t)(s0 + j) * NPART + q) * I + i] = p[q];
+        for (int q = 0; q < NPART; ++q) {
+          g += rg[q * 64];
+          uu += ru[q * 64];
+        }
+      }
+      const float act = silu_f(g) * uu;
+      _Float16 p[NPART];
+      split3(act, p);
+      const int i = (GU_GROUPS * gp + gi) * 16 + row;
+#pragma unroll
+      for (int q = 0; q < NPART; ++q) a.w.actp[(((size_t)u * T + t) * NPART + q) * I + i] = p[q];
+    }
   }
 }
 
 // down + weighted combine: one 16-row group of H per workgroup, every active
-// expert; waves take (expert, superblock) units, the next unit's loads in
-// flight while the current one computes.  Descriptors and routing weights of
-// all active experts sit in LDS.
+// expert; waves take (expert, superblock) units in turn, with the loads of
+// the next DN_DEPTH - 1 units in flight while one computes.  The routing of
+// all active experts sits in LDS.
+constexpr int DN_WAVES = 8;
+constexpr int DN_DEPTH = 3;
+
 template <int FMT> struct DownUnit {
   Codes<FMT> cd;
   uint4 sc;
@@ -472,33 +668,38 @@ template <int FMT> struct DownUnit {
 };
 
 template <int FMT>
-__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g,
-                                 int tg, DownUnit<FMT>& du) {
+__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, int tg,
+                                 DownUnit<FMT>& du) {
   const int lane = threadIdx.x & 63, r = lane & 15, ks = lane >> 4;
   const int part = (lane & 15) >> 2, jj = lane & 3;
-  const int u = unit / nsb, sb = unit % nsb;
-  const int* d = ldesc + u * DESC;
-  const int e = d[0], s0 = d[1], n = d[2];
-  const uint8_t* slab = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I) +
-                        ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256);
-  load_codes<FMT>(slab, lane, du.cd);
-  du.sc = *reinterpret_cast<const uint4*>(slab + Fmt<FMT>::slab_codes + r * 16);
-  // A row (part, token t = 4tg + jj): the pair slot of (expert u, token t), if routed
+  const int u = unit / nsb, sb = unit - u * nsb;
+  const int e = __builtin_amdgcn_readfirstlane(ldesc[2 * u]);
+  const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[2 * u + 1]);
+  const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
+  const uint32_t soff = (uint32_t)(down_off(FMT, a.H, a.I) + ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256));
+  bload_codes<FMT>(wr, soff, lane, du.cd);
+  du.sc = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
+  // A row (part, token t = 4tg + jj): the activation of (expert u, token t), if routed
+  // (rows of tokens not routed to u, and the unused fourth part, read the
+  // row of u's first token in the same cache lines, and are zeroed)
   const int t = 4 * tg + jj;
-  int slot = -1;
-  for (int j = 0; j < n; ++j)
-    if (d[4 + j] == t) slot = s0 + j;
-  const bool valid = part < NPART && slot >= 0;
-  const _Float16* src = a.w.actp + ((size_t)(valid ? slot : 0) * NPART + (valid ? part : 0)) * a.I +
-                        sb * SB_WEIGHTS + 8 * ks;
+  const bool routed = t < a.T && ((mask >> t) & 1u);
+  const int tr = routed ? t : __builtin_ctz(mask);
+  const rsrc_t ar = make_rsrc(a.w.actp, a.actp_bytes);
+  const uint32_t voff = (uint32_t)(((tr * NPART + min(part, NPART - 1)) * a.I + 8 * ks) * 2);
+  const uint32_t asoff = (uint32_t)(((size_t)u * a.T * NPART * a.I + (size_t)sb * SB_WEIGHTS) * 2);
 #pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
-    du.av[bb] = valid ? *reinterpret_cast<const uint4*>(src + bb * BLOCK_W) : make_uint4(0, 0, 0, 0);
+  for (int bb = 0; bb < 8; ++bb) du.av[bb] = bload4(ar, voff + bb * BLOCK_W * 2, asoff);
+  const uint32_t amask = routed ? ~0u : 0u;
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb) du.av[bb] = mask_u4(du.av[bb], amask);
 }
 
+// acc[v] += routing weight of token 4tg + v * (this unit's 16x16 product)
 template <int FMT>
-__device__ inline void down_compute(const DownUnit<FMT>& du, float* acc /* [4] */) {
+__device__ inline void down_compute(const DownUnit<FMT>& du, const float* wt, float* out) {
   f32x4 dd[2];
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
     const f16x8 af = as_f16x8(du.av[BB]);                                         \
@@ -514,43 +715,45 @@ __device__ inline void down_compute(const DownUnit<FMT>& du, float* acc /* [4] *
 #undef STRATA_BLOCK
   const float ds = block_scale<FMT, 7>(du.sc);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] = fmaf(ds, dd[1][v], acc[v]);
+  for (int v = 0; v < 4; ++v) {
+    acc[v] = fmaf(ds, dd[1][v], acc[v]);
+    out[v] = fmaf(wt[v], acc[v], out[v]);
+  }
 }
 
 template <int FMT, int NTG>
-__global__ __launch_bounds__(512) void k_down(ExpertArgs a) {
-  extern __shared__ float lds_dn[];
+__global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
+  extern __shared__ float4 lds_dn4[];
+  float* lds_dn = reinterpret_cast<float*>(lds_dn4);
   const int U = a.w.meta[0];
   const int H = a.H, I = a.I, nsb = I / SB_WEIGHTS, T = a.T;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
-  int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [U][DESC]
-  float* lwt = reinterpret_cast<float*>(ldesc + U * DESC);      // [U][WTAB]
-  float* red = lwt + U * WTAB;                                  // [nw][NTG][4][16]
-  for (int i = threadIdx.x; i < U * DESC; i += blockDim.x) ldesc[i] = a.w.udesc[i];
+  int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [U][2]: expert, token mask
+  float* lwt = reinterpret_cast<float*>(ldesc + 2 * U);         // [U][WTAB]
+  float* red = lds_dn + ((DESC + WTAB) * U + 3) / 4 * 4;        // [nw][NTG][64 lanes][4 tokens], 16-B aligned
+  for (int i = threadIdx.x; i < DESC * U; i += blockDim.x) ldesc[i] = a.w.udesc[i];
   for (int i = threadIdx.x; i < U * WTAB; i += blockDim.x) lwt[i] = a.w.wtab[i];
   __syncthreads();
 
   const int units = U * nsb;
   for (int tg = 0; tg < NTG; ++tg) {
     float out[4] = {0.f, 0.f, 0.f, 0.f};
-    DownUnit<FMT> cur, nxt;
-    if (wv < units) down_load<FMT>(a, ldesc, wv, nsb, g, tg, cur);
-    for (int unit = wv; unit < units; unit += nw) {
-      if (unit + nw < units) down_load<FMT>(a, ldesc, unit + nw, nsb, g, tg, nxt);
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      down_compute<FMT>(cur, acc);
-      // routing weight of token 4tg + v for this unit's expert (0 when not routed)
-      const float* wt = lwt + (unit / nsb) * WTAB + 4 * tg;
+    DownUnit<FMT> b[DN_DEPTH];
+    // every load unconditional (unit index clamped; a repeated unit is
+    // loaded but not computed), so the loads of a step are all in flight
 #pragma unroll
-      for (int v = 0; v < 4; ++v) out[v] = fmaf(wt[v], acc[v], out[v]);
-      cur = nxt;
-    }
+    for (int q = 0; q < DN_DEPTH; ++q) down_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, tg, b[q]);
+    for (int unit = wv; unit < units; unit += DN_DEPTH * nw) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float t = sum_parts(out[v]);
-      if (lane < 16) red[(((size_t)wv * NTG + tg) * 4 + v) * 16 + lane] = t;
+      for (int q = 0; q < DN_DEPTH; ++q) {
+        const int cu = unit + q * nw;
+        if (cu < units) down_compute<FMT>(b[q], lwt + (cu / nsb) * WTAB + 4 * tg, out);
+        down_load<FMT>(a, ldesc, min(cu + DN_DEPTH * nw, units - 1), nsb, g, tg, b[q]);
+      }
     }
+    reinterpret_cast<float4*>(red)[((size_t)wv * NTG + tg) * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < NTG * 4 * 16; idx += blockDim.x) {
@@ -558,7 +761,11 @@ __global__ __launch_bounds__(512) void k_down(ExpertArgs a) {
     const int t = 4 * tg + v;
     if (t >= T) continue;
     float s = 0.f;
-    for (int w = 0; w < nw; ++w) s += red[(((size_t)w * NTG + tg) * 4 + v) * 16 + row];
+    for (int w = 0; w < nw; ++w) {
+      const float* r = red + (((size_t)w * NTG + tg) * 64 + row) * 4 + v;
+#pragma unroll
+      for (int q = 0; q < NPART; ++q) s += r[q * 64];
+    }
     const int h = g * 16 + row;
     const size_t o = (size_t)t * H + h;
     if (a.flags & 2u) {
@@ -575,22 +782,30 @@ hipError_t launch_experts_t(const Layer& L, const Work& W, const Call& c, hipStr
   ExpertArgs a;
   a.packed = L.packed;
   a.stride = L.expert_stride;
-  a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.T = c.T; a.P = c.T * L.k;
+  a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.T = c.T; a.P = c.T * L.k; a.n_shared = L.n_shared;
   a.x = c.x; a.x_f32 = c.x_f32; a.flags = c.flags; a.out = c.out; a.w = W;
   const int umax = (a.P < L.E ? a.P : L.E) + L.n_shared;
+  a.actp_bytes = (uint32_t)((size_t)umax * c.T * NPART * L.I * 2);
   // gate/up waves: the largest divisor of the superblock count that is <= 10,
-  // so every wave takes the same number of superblocks
+  // so every wave takes the same number of superblocks.  Row groups per
+  // workgroup: 4 when 2 would give more workgroups than CUs (one 10-wave
+  // workgroup fits a CU at this register count); Q3/Q4 keep 2 (4 would spill).
   const int nsbH = L.H / SB_WEIGHTS;
   int nwg = 1;
   for (int d = 1; d <= 10; ++d)
     if (nsbH % d == 0) nwg = d;
-  const int nwd = 8;
-  const size_t lds_gu = (size_t)nwg * NTG * GU_SLABS * 4 * 16 * 4;
-  const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + (size_t)nwd * NTG * 4 * 16 * 4;
-  hipLaunchKernelGGL((k_gateup<FMT, NTG>), dim3(L.I / (16 * GU_GROUPS), umax), dim3(64 * nwg), lds_gu, s, a);
-  mark(tr, s);
-  hipLaunchKernelGGL((k_down<FMT, NTG>), dim3(L.H / 16), dim3(64 * nwd), lds_dn, s, a);
-  mark(tr, s);
+  const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
+  const int G = wide ? 4 : 2;
+  const size_t lds_gu = (size_t)nwg * 2 * G * 48 * 4 * 4;     // <= 60 KiB
+  const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * NTG * 64 * 4 * 4;
+  const dim3 ggu(L.I / (16 * G), umax);
+  if constexpr (FMT == 2) {
+    if (wide) launch(tr, k_gateup<FMT, NTG, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    else launch(tr, k_gateup<FMT, NTG, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+  } else {
+    launch(tr, k_gateup<FMT, NTG, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+  }
+  launch(tr, k_down<FMT, NTG>, dim3(L.H / 16), dim3(64 * DN_WAVES), lds_dn, s, a);
   return hipGetLastError();
 }
 
@@ -599,42 +814,42 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   return c.T <= 4 ? launch_experts_t<FMT, 1>(L, W, c, s, tr) : launch_experts_t<FMT, 2>(L, W, c, s, tr);
 }
 
-// Raise a kernel's dynamic-LDS ceiling to what the device allows beside its
-// static LDS.  A refusal is not fatal (the launch reports it if a call really
-// needs more than the default); the runtime's error state is cleared.
-void raise_lds_limit(const void* k, int device_limit) {
-  hipFuncAttributes fa;
-  if (hipFuncGetAttributes(&fa, k) != hipSuccess) { (void)hipGetLastError(); return; }
-  const int want = device_limit - (int)fa.sharedSizeBytes;
-  if (want > 0 && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
-    (void)hipGetLastError();
+template <int V1>
+hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
+  if (t.k <= 16) launch(tr, k_topk<V1, 2>, dim3(t.T), dim3(64 * TOPK_WAVES), 0, s, t);
+  else launch(tr, k_topk<V1, 8>, dim3(t.T), dim3(64 * TOPK_WAVES), 0, s, t);
+  return hipGetLastError();
 }
 
 }  // namespace
 
-// Allow the decode kernels the dynamic LDS the widest decode call needs
-// (the router stages up to 8 x 4096 fp32 activations: 128 KiB).
-hipError_t prepare_decode_kernels(const Layer& L, int) {
-  int dev = 0, lim = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
-  if (e != hipSuccess) return e;
-  raise_lds_limit(reinterpret_cast<const void*>(&k_route_gemv), lim);
-  raise_lds_limit(reinterpret_cast<const void*>(&k_topk), lim);
-  return hipSuccess;
-}
-
-hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
+hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
+                               bool permutation) {
   RouteArgs a;
   a.Wr = L.router_w; a.bias = L.router_b; a.x = c.x; a.x_f32 = c.x_f32; a.T = c.T;
   a.H = L.H; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts;
-  mark(tr, s);
-  hipLaunchKernelGGL(k_route_gemv, dim3((L.E + 3) / 4), dim3(256), (size_t)c.T * L.H * 4, s, a);
-  mark(tr, s);
+  switch (c.T) {
+#define STRATA_ROUTE(TT)                                                                 \
+    case TT:                                                                               \
+      if (c.x_f32) launch(tr, k_route_gemv<TT, true>, dim3(L.E), dim3(64 * ROUTE_WAVES), 0, s, a); \
+      else launch(tr, k_route_gemv<TT, false>, dim3(L.E), dim3(64 * ROUTE_WAVES), 0, s, a);        \
+      break;
+    STRATA_ROUTE(1) STRATA_ROUTE(2) STRATA_ROUTE(3) STRATA_ROUTE(4)
+    STRATA_ROUTE(5) STRATA_ROUTE(6) STRATA_ROUTE(7) STRATA_ROUTE(8)
+#undef STRATA_ROUTE
+    default: return hipErrorInvalidValue;
+  }
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.n_shared = L.n_shared; t.w = W;
-  hipLaunchKernelGGL(k_topk, dim3(1), dim3(512), ((size_t)c.T * L.k + 2 * (size_t)L.E) * 4, s, t);
-  mark(tr, s);
+  const int per_wave = (L.E + 64 * TOPK_WAVES - 1) / (64 * TOPK_WAVES);
+  hipError_t e;
+  if (per_wave <= 1) e = launch_topk_v1<1>(t, s, tr);
+  else if (per_wave <= 2) e = launch_topk_v1<2>(t, s, tr);
+  else if (per_wave <= 4) e = launch_topk_v1<4>(t, s, tr);
+  else e = launch_topk_v1<8>(t, s, tr);
+  if (e != hipSuccess) return e;
+  if (permutation)
+    launch(tr, k_permute, dim3(1), dim3(512), ((size_t)c.T * L.k + (size_t)L.E) * 4, s, t);
   return hipGetLastError();
 }
 

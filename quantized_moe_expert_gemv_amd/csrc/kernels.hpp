@@ -2,6 +2,7 @@
 // kernel translation units.  Internal to the library.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -16,15 +17,14 @@ struct Work {
   int* offsets;       // [E+1]
   int* perm;          // [Tmax*k]   sorted slot -> pair
   int* inv;           // [Tmax*k]   pair -> sorted slot
-  int* udesc;         // [E+1][16]  decode: per active expert {e, first slot, n, 0, tokens[8]}
+  int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
   float* wtab;        // [E+1][8]   decode: routing weight per (active expert, token), 0 if not routed
   int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill)
-  int* tickets;       // [H/64 + 1] completion counters (last entry: router)
   int* chunk_base;    // [E][nchunks] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
   int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}
   float* act;         // prefill: bf16 SwiGLU rows [slots][I] (same region as actp)
-  _Float16* actp;     // decode: SwiGLU rows as three fp16 parts [slots][3][I]
+  _Float16* actp;     // decode: SwiGLU rows as three fp16 parts [active expert][T][3][I]
   _Float16* xparts;   // decode: token rows as three fp16 parts [8][3][H]
   float* y;           // [slots][H]  prefill: per-pair expert outputs
   int nchunks;
@@ -49,19 +49,24 @@ struct Call {
   uint32_t flags;
 };
 
-// Optional per-kernel timing: mark() records the next caller-supplied event
-// on the stream; called once before a call's first kernel and after each
-// kernel.
+// Optional per-kernel timing: with a tracer armed, each kernel is launched
+// with the next two caller events bound to its own dispatch, so the pair
+// brackets that kernel's execution (start and end of the dispatch), not the
+// gaps between kernels.
 struct Tracer {
   hipEvent_t* ev = nullptr;
   int n = 0, i = 0;
-  void mark(hipStream_t s) {
-    if (i < n) (void)hipEventRecord(ev[i], s);
-    ++i;
-  }
 };
-inline void mark(Tracer* t, hipStream_t s) {
-  if (t) t->mark(s);
+
+template <typename K, typename... Args>
+inline void launch(Tracer* tr, K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+  if (tr && tr->i + 2 <= tr->n) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, tr->ev[tr->i], tr->ev[tr->i + 1], 0u,
+                          args...);
+    tr->i += 2;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  }
 }
 
 // create-time repack (canonical -> packed) and router split
@@ -69,8 +74,10 @@ hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in,
                          hipStream_t s);
 hipError_t launch_router_split(const Layer& L, hipStream_t s);
 
-// decode path: router + top-k + permute (one launch), gate/up, down + combine
-hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);
+// decode path: router GEMV, top-k (+ the permutation when asked for), then
+// gate/up and down + combine
+hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
+                               bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);
 
 // prefill path

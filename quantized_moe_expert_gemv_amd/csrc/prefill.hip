@@ -489,12 +489,10 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
   g.T = c.T; g.P = c.T * L.k; g.x = c.x; g.x_f32 = c.x_f32; g.w = W;
   const int max_tiles = W.max_tiles;
   if (c.x_f32)
-    hipLaunchKernelGGL((k_gemm_gateup<FMT, true>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+    launch(tr, k_gemm_gateup<FMT, true>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL((k_gemm_gateup<FMT, false>), dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
-  mark(tr, s);
-  hipLaunchKernelGGL((k_gemm_down<FMT>), dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
-  mark(tr, s);
+    launch(tr, k_gemm_gateup<FMT, false>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+  launch(tr, k_gemm_down<FMT>, dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
@@ -505,22 +503,17 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
   r.whi = L.router_hi; r.wlo = L.router_lo; r.bias = L.router_b; r.logits = W.logits;
   dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM);
-  mark(tr, s);
-  if (c.x_f32) hipLaunchKernelGGL(k_router_gemm<true>, grid, dim3(256), 0, s, r);
-  else hipLaunchKernelGGL(k_router_gemm<false>, grid, dim3(256), 0, s, r);
-  mark(tr, s);
+  if (c.x_f32) launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
+  else launch(tr, k_router_gemm<false>, grid, dim3(256), 0, s, r);
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   const size_t lds = ((size_t)CT * L.k + L.E) * 4;
-  hipLaunchKernelGGL(k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
-  mark(tr, s);
+  launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, sa);
-  mark(tr, s);
+  launch(tr, k_scan, dim3(1), dim3(1024), 0, s, sa);
   const int P = c.T * L.k;
-  hipLaunchKernelGGL(k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
-  mark(tr, s);
+  launch(tr, k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
   return hipGetLastError();
 }
 
@@ -535,8 +528,7 @@ hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, 
   CombineArgs cb;
   cb.T = c.T; cb.H = L.H; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
   cb.x = c.x; cb.x_f32 = c.x_f32; cb.flags = c.flags; cb.out = c.out; cb.w = W;
-  hipLaunchKernelGGL(k_combine, dim3(c.T), dim3(256), 0, s, cb);
-  mark(tr, s);
+  launch(tr, k_combine, dim3(c.T), dim3(256), 0, s, cb);
   return hipGetLastError();
 }
 

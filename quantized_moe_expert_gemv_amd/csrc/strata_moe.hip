@@ -15,7 +15,6 @@
 using namespace strata;
 
 namespace strata {
-hipError_t prepare_decode_kernels(const Layer& L, int max_tokens);
 }
 
 struct strata_moe {
@@ -71,7 +70,7 @@ int check_config(const strata_moe_config* c) {
 }
 
 struct WsPlan {
-  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, udesc, wtab, meta, tickets,
+  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, udesc, wtab, meta,
       chunk_base, pair_rank, tiles, act, xparts, y, total;
   int nchunks, max_tiles;
 };
@@ -98,16 +97,16 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.offsets = take((E + 1) * 4);
   p.perm = take(P * 4);
   p.inv = take(P * 4);
-  p.udesc = take((E + 1) * 16 * 4);
+  p.udesc = take((E + 1) * 2 * 4);
   p.wtab = take((E + 1) * 8 * 4);
   p.meta = take(16 * 4);
-  p.tickets = take((H / 64 + 1) * 4);
   p.chunk_base = take(E * (size_t)p.nchunks * 4);
   p.pair_rank = take(P * 4);
   p.tiles = take((size_t)p.max_tiles * 16);
   const size_t Td = T < STRATA_DECODE_MAX_T ? T : STRATA_DECODE_MAX_T;
   const size_t act_prefill = slots * I * 2;                                   // bf16 rows
-  const size_t act_decode = (Td * k + (size_t)c.n_shared * Td) * 3 * I * 2;   // fp16 parts
+  const size_t umax = (Td * k < E ? Td * k : E) + (size_t)c.n_shared;
+  const size_t act_decode = umax * Td * 3 * I * 2;                             // fp16 parts
   p.act = take(act_prefill > act_decode ? act_prefill : act_decode);
   p.xparts = take(Td * 3 * H * 2);
   p.y = take(slots * H * 4);
@@ -179,16 +178,19 @@ struct TraceScope {
   }
 };
 
-int run_route(strata_moe* h, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
+// permutation: the decode path computes the token->expert permutation only
+// when the caller asks for it (route()); its expert kernels do without.
+int run_route(strata_moe* h, const Call& c, bool decode, bool permutation, hipStream_t s, Tracer* tr) {
   Work W = h->W;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
-  hipError_t e = decode ? launch_decode_route(h->L, W, c, s, tr) : launch_prefill_route(h->L, W, c, s, tr);
+  hipError_t e = decode ? launch_decode_route(h->L, W, c, s, tr, permutation)
+                        : launch_prefill_route(h->L, W, c, s, tr);
   if (e != hipSuccess) return hip_fail(e, "route launch");
   return STRATA_OK;
 }
 
 int run_forward(strata_moe* h, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
-  int rc = run_route(h, c, decode, s, tr);
+  int rc = run_route(h, c, decode, false, s, tr);
   if (rc) return rc;
   Work W = h->W;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
@@ -258,7 +260,6 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.inv = reinterpret_cast<int*>(ws + p.inv);
   W.udesc = reinterpret_cast<int*>(ws + p.udesc);
   W.meta = reinterpret_cast<int*>(ws + p.meta);
-  W.tickets = reinterpret_cast<int*>(ws + p.tickets);
   W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
   W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
   W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
@@ -272,7 +273,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* step = "zeroing counters";
-  hipError_t e = hipMemsetAsync(ws + p.meta, 0, p.chunk_base - p.meta, s);   // meta + tickets
+  hipError_t e = hipMemsetAsync(ws + p.meta, 0, 16 * 4, s);
   if (e == hipSuccess) {
     step = "expert repack";
     e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
@@ -284,10 +285,6 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   if (e == hipSuccess) {
     step = "router split";
     e = launch_router_split(L, s);
-  }
-  if (e == hipSuccess) {
-    step = "kernel attributes";
-    e = prepare_decode_kernels(L, cfg->max_tokens);
   }
   if (e == hipSuccess) {
     step = "stream synchronize";
@@ -314,7 +311,7 @@ int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Call c = make_call(x, x_dtype, T, nullptr, flags);
   TraceScope ts(h);
-  if ((rc = run_route(h, c, use_decode(T, flags), s, ts.ptr))) return rc;
+  if ((rc = run_route(h, c, use_decode(T, flags), true, s, ts.ptr))) return rc;
   const size_t P = (size_t)T * h->cfg.top_k;
   hipError_t e = hipMemcpyAsync(topk_idx, h->W.topk_idx, P * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(topk_w, h->W.topk_w, P * 4, hipMemcpyDeviceToDevice, s);
@@ -378,8 +375,8 @@ int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const 
 
 int strata_moe_trace_next_call(strata_moe* h, void* const* events, int32_t n_events) {
   if (!h) return fail(STRATA_E_INVALID, "handle is NULL");
-  if (n_events < 0 || n_events > STRATA_MAX_TRACE_EVENTS)
-    return fail(STRATA_E_INVALID, "n_events %d outside [0, %d]", n_events, STRATA_MAX_TRACE_EVENTS);
+  if (n_events < 0 || n_events > STRATA_MAX_TRACE_EVENTS || (n_events & 1))
+    return fail(STRATA_E_INVALID, "n_events %d is not even in [0, %d]", n_events, STRATA_MAX_TRACE_EVENTS);
   if (n_events > 0 && !events) return fail(STRATA_E_INVALID, "events is NULL");
   for (int i = 0; i < n_events; ++i) {
     if (!events[i]) return fail(STRATA_E_INVALID, "event %d is NULL", i);

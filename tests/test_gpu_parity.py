@@ -268,3 +268,21 @@ def test_graph_replay_matches_eager(B, T):
         # eager work on the same handle between replays
         layer.forward(batches[rep % 3])
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T,n_kernels", [(4, 4), (100, 7)])
+def test_trace_events_bracket_each_kernel(B, T, n_kernels):
+    """Traced calls give the same output and a positive duration per kernel;
+    an odd event count is refused."""
+    hl, layer = tiny(3)
+    x = to_device_bf16(tokens(hl, 300 + T, T)[0], DEV)
+    ref = layer.forward(x).clone()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_kernels)]
+    B.strata_moe_trace_next_call(layer.handle, evs)
+    out = layer.forward(x).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    for j in range(n_kernels):
+        assert evs[2 * j].elapsed_time(evs[2 * j + 1]) > 0.0
+    with pytest.raises(B.StrataError):
+        B.strata_moe_trace_next_call(layer.handle, evs[:3])
