@@ -534,12 +534,22 @@ __device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits,
 template <int FMT, int G> struct GuStage {
   Codes<FMT> cd[2 * G];
   uint4 sc[2 * G];
-  uint4 av[8];
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// the activation operand of superblock sb: 8 blocks x 64 lanes x 16 B,
+// copied by the memory unit straight into this wave's LDS region (lane l's
+// 16 bytes of block b land at b * 1 KiB + 16 l), no registers on the way
+__device__ inline void gu_aload_lds(rsrc_t xr, uint32_t xvoff, int sb, uint4* lds_a) {
+#pragma unroll
+  for (int bb = 0; bb < 8; ++bb)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(lds_a + bb * 64), 16, xvoff + bb * BLOCK_W * 2,
+                                             (uint32_t)sb * SB_WEIGHTS * 2, 0, 0);
+}
+
 template <int FMT, int G>
-__device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int sb, rsrc_t xr, uint32_t xvoff,
-                               int lane, GuStage<FMT, G>& st) {
+__device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int sb, int lane, GuStage<FMT, G>& st) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
   const int r = lane & 15;
 #pragma unroll
@@ -548,16 +558,20 @@ __device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int
     bload_codes<FMT>(wr, soff, lane, st.cd[s]);
     st.sc[s] = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
   }
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) st.av[bb] = bload4(xr, xvoff + bb * BLOCK_W * 2, (uint32_t)sb * SB_WEIGHTS * 2);
 }
 
+// One superblock: per block, the activation operand from LDS, the offset
+// MFMA, the 2G product MFMAs, then the 2G x 4 scale FMAs.
 template <int FMT, int G>
-__device__ inline void gu_compute(const GuStage<FMT, G>& st, float (&acc)[2 * G][4]) {
+__device__ inline void gu_compute(const GuStage<FMT, G>& st, const uint4* lds_a, int lane, float (&acc)[2 * G][4]) {
   constexpr int GU_SLABS = 2 * G;
+  // the LDS copies must have landed: the compiler does not track the
+  // buffer->LDS loads against these reads (the memory clobber also keeps
+  // every LDS read below this point)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
-    const f16x8 af = as_f16x8(st.av[BB]);                                         \
+    const f16x8 af = as_f16x8(lds_a[BB * 64 + lane]);                             \
     const f32x4 off = block_offset<FMT>(af);                                      \
     f32x4 d[GU_SLABS];                                                            \
     _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s)                          \
@@ -576,7 +590,9 @@ __device__ inline void gu_compute(const GuStage<FMT, G>& st, float (&acc)[2 * G]
 template <int FMT, int NTG, int G>
 __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
-  extern __shared__ float4 red4[];             // [nw][GU_SLABS][48 lanes] x 4 tokens
+  // per wave 8 KiB of LDS: its superblock's activation operand, then its
+  // partial sums [GU_SLABS][48 lanes] x 4 tokens
+  extern __shared__ float4 red4[];
   float* red = reinterpret_cast<float*>(red4);
   __shared__ uint32_t s_bits[128];
   __shared__ int s_info[4];
@@ -603,7 +619,9 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(T * NPART * H * 2));
   const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
 
+  uint4* lds_a = reinterpret_cast<uint4*>(red4) + wv * 512;
   for (int tg = 0; tg < NTG; ++tg) {                // token groups of 4
+    if (tg > 0) __syncthreads();                     // the previous group's sums are read
     float acc[GU_SLABS][4];
 #pragma unroll
     for (int s = 0; s < GU_SLABS; ++s)
@@ -615,14 +633,14 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     const uint32_t xvoff = (uint32_t)(((jr * NPART + pr) * H + 8 * ks) * 2);
     for (int sb = wv; sb < nsb; sb += nw) {
       GuStage<FMT, G> st;
-      gu_load<FMT, G>(wr, up_base, gp, nsb, sb, xr, xvoff, lane, st);
+      gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
+      gu_aload_lds(xr, xvoff, sb, lds_a);
       __builtin_amdgcn_sched_barrier(0);            // every load of the stage issued before any use
-      gu_compute<FMT, G>(st, acc);
+      gu_compute<FMT, G>(st, lds_a, lane, acc);
     }
-    // raw 16x16 results to LDS: lane l holds (part l/16, token v) of row l%16
-    if (tg > 0) __syncthreads();                     // the previous group's sums are read
-    // (lanes 48..63 hold the unused fourth part and are not kept)
-    float4* dst = reinterpret_cast<float4*>(red) + ((size_t)wv * GU_SLABS) * 48 + lane;
+    // raw 16x16 results to this wave's LDS region: lane l holds (part l/16,
+    // token v) of row l%16 (lanes 48..63 hold the unused fourth part and are not kept)
+    float4* dst = reinterpret_cast<float4*>(red) + (size_t)wv * 512 + lane;
     if (lane < 48) {
 #pragma unroll
       for (int s = 0; s < GU_SLABS; ++s)
@@ -636,8 +654,8 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
       if (t >= T || !((mask >> t) & 1u)) continue;
       float g = 0.f, uu = 0.f;
       for (int w = 0; w < nw; ++w) {
-        const float* rg = red + (((size_t)w * GU_SLABS + gi) * 48 + row) * 4 + v;
-        const float* ru = red + (((size_t)w * GU_SLABS + GU_GROUPS + gi) * 48 + row) * 4 + v;
+        const float* rg = red + (size_t)w * 2048 + ((size_t)gi * 48 + row) * 4 + v;
+        const float* ru = red + (size_t)w * 2048 + ((size_t)(GU_GROUPS + gi) * 48 + row) * 4 + v;
 #pragma unroll
         for (int q = 0; q < NPART; ++q) {
           g += rg[q * 64];
@@ -796,7 +814,7 @@ hipError_t launch_experts_t(const Layer& L, const Work& W, const Call& c, hipStr
     if (nsbH % d == 0) nwg = d;
   const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
-  const size_t lds_gu = (size_t)nwg * 2 * G * 48 * 4 * 4;     // <= 60 KiB
+  const size_t lds_gu = (size_t)nwg * 8192;                     // <= 80 KiB: ceiling raised at create
   const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * NTG * 64 * 4 * 4;
   const dim3 ggu(L.I / (16 * G), umax);
   if constexpr (FMT == 2) {
@@ -814,6 +832,19 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   return c.T <= 4 ? launch_experts_t<FMT, 1>(L, W, c, s, tr) : launch_experts_t<FMT, 2>(L, W, c, s, tr);
 }
 
+template <int FMT, int NTG>
+hipError_t raise_gateup_lds() {
+  const int want = 96 * 1024;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, NTG, 2>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  if constexpr (FMT == 2) {
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, NTG, 4>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  }
+  return e;
+}
+
 template <int V1>
 hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
   if (t.k <= 16) launch(tr, k_topk<V1, 2>, dim3(t.T), dim3(64 * TOPK_WAVES), 0, s, t);
@@ -822,6 +853,17 @@ hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
 }
 
 }  // namespace
+
+// The gate/up kernels keep up to 80 KiB of dynamic LDS (8 KiB per wave).
+hipError_t prepare_decode_kernels() {
+  hipError_t e = raise_gateup_lds<2, 1>();
+  if (e == hipSuccess) e = raise_gateup_lds<2, 2>();
+  if (e == hipSuccess) e = raise_gateup_lds<3, 1>();
+  if (e == hipSuccess) e = raise_gateup_lds<3, 2>();
+  if (e == hipSuccess) e = raise_gateup_lds<4, 1>();
+  if (e == hipSuccess) e = raise_gateup_lds<4, 2>();
+  return e;
+}
 
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation) {

@@ -75,7 +75,9 @@ hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in,
 hipError_t launch_router_split(const Layer& L, hipStream_t s);
 
 // decode path: router GEMV, top-k (+ the permutation when asked for), then
-// gate/up and down + combine
+// gate/up and down + combine; prepare_decode_kernels raises the gate/up
+// kernels' dynamic-LDS ceiling (once per process is enough)
+hipError_t prepare_decode_kernels();
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);

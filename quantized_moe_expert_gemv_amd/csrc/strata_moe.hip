@@ -287,6 +287,10 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
     e = launch_router_split(L, s);
   }
   if (e == hipSuccess) {
+    step = "kernel attributes";
+    e = prepare_decode_kernels();
+  }
+  if (e == hipSuccess) {
     step = "stream synchronize";
     e = hipStreamSynchronize(s);
   }
