@@ -221,8 +221,15 @@ def main():
                           "GBps": round(alg[n] / (kern_us[j] * 1e-6) / 1e9, 1)}
         dom = max(names, key=lambda n: kernels[n]["us"])
         achieved = kernels[dom]["GBps"]
+        # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+        # if it was taken on the current kernel sources
+        from quantized_moe_expert_gemv_amd import prof_summary
+        measured = prof_summary.read_traffic(
+            os.path.join(ROOT, "profiles", f"decode_hbm_traffic_{args.workload}.md"))
         roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": int(measured[dom]) if dom in measured else None,
+                    "alg_bytes": kernels[dom]["alg_bytes"]}
         layer_bytes = router_bytes + ue * (gu_bytes + dn_bytes) + x_bytes + out_bytes
         if stack:                 # every layer of the pass moves the same algorithmic bytes
             layer_bytes *= w.n_layers

@@ -1,0 +1,140 @@
+"""Condense rocprofv3 CSV output into the short text summaries kept with the
+library's measurements.
+
+    python -m quantized_moe_expert_gemv_amd.prof_summary stats OUT.md CMD KERNEL_STATS_CSV
+    python -m quantized_moe_expert_gemv_amd.prof_summary traffic OUT.md CMD_FETCH CMD_WRITE \
+        FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES
+
+`stats` lists every kernel of a `--kernel-trace --stats` run (calls, average
+and total time).  `traffic` takes two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
+runs of a workload and of a plain device copy of COPY_BYTES bytes each way;
+the copy gives the bytes each counter unit stands for, so a kernel's HBM
+bytes per dispatch = mean counter value x that factor.  The summary ends with
+one `traffic:` line per library kernel (and the hash of the kernel sources the
+counters were taken on), which the benchmark reads.
+"""
+
+import csv
+import hashlib
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# library kernel name fragment -> benchmark name
+KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_gateup", "gateup"),
+           ("k_down", "down_combine"), ("k_router_gemm", "router_gemm"), ("k_topk_chunks", "topk"),
+           ("k_scan", "scan"), ("k_scatter", "scatter"), ("k_gemm_gateup", "gateup_gemm"),
+           ("k_gemm_down", "down_gemm"), ("k_combine", "combine")]
+
+
+def source_hash():
+    """sha256 over the kernel sources (csrc/*.hip, *.hpp), in name order."""
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def bench_name(kernel):
+    m = re.search(r"::(k_[A-Za-z0-9_]+)", kernel)
+    if not m:
+        return None
+    return dict(KERNELS).get(m.group(1))
+
+
+def read_stats(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def stats(out, cmd, stats_csv):
+    rows = read_stats(stats_csv)
+    lines = ["# rocprofv3 kernel statistics", "", "Command:", "", "    " + cmd, "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"]
+        short = name if len(name) < 90 else name[:87] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"kernel sources: {source_hash()}", ""]
+    open(out, "w").write("\n".join(lines))
+
+
+def per_kernel_counter(path):
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def traffic(out, cmd_f, cmd_w, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes):
+    copy_bytes = int(copy_bytes)
+    f = per_kernel_counter(fetch_csv)
+    w = per_kernel_counter(write_csv)
+
+    def copy_factor(path):
+        vals = [v for k, vs in per_kernel_counter(path).items() if "copyBuffer" in k or "copy" in k.lower()
+                for v in vs]
+        vals = sorted(vals)[-4:]                  # the timed copies (largest dispatches)
+        return copy_bytes / (sum(vals) / len(vals))
+
+    ff, fw = copy_factor(cfetch_csv), copy_factor(cwrite_csv)
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             "Commands:", "", "    " + cmd_f, "    " + cmd_w, "",
+             f"Calibration: a plain device copy of {copy_bytes} bytes each way reads "
+             f"{copy_bytes / ff:.0f} KiB of FETCH_SIZE and {copy_bytes / fw:.0f} KiB of "
+             f"WRITE_SIZE: bytes per counter KiB = {ff:.4f} (fetch), {fw:.4f} (write).", "",
+             "| kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes / dispatch |", "|---|---:|---:|---:|---:|"]
+    tagged = []
+    for k in sorted(f):
+        name = bench_name(k)
+        fv = f[k]
+        wv = w.get(k, [0.0])
+        fm, wm = sum(fv) / len(fv), sum(wv) / len(wv)
+        b = fm * ff + wm * fw
+        short = k if len(k) < 70 else k[:67] + "..."
+        lines.append(f"| `{short}` | {len(fv)} | {fm:.1f} | {wm:.1f} | {b:.0f} |")
+        if name:
+            tagged.append((name, b, len(fv)))
+    lines += ["", f"kernel sources: {source_hash()}", ""]
+    merged = {}
+    for name, b, n in tagged:               # several instantiations of one kernel: dispatch-weighted mean
+        tb, tn = merged.get(name, (0.0, 0))
+        merged[name] = (tb + b * n, tn + n)
+    for name, (tb, tn) in sorted(merged.items()):
+        lines.append(f"traffic: kernel={name} bytes_per_dispatch={tb / tn:.0f} sources={source_hash()}")
+    lines.append("")
+    open(out, "w").write("\n".join(lines))
+
+
+def read_traffic(path):
+    """{bench kernel name: bytes per dispatch} from a traffic summary, or {}
+    when it is missing or was taken on other kernel sources."""
+    if not os.path.exists(path):
+        return {}
+    cur = source_hash()
+    res = {}
+    for line in open(path):
+        if line.startswith("traffic:"):
+            kv = dict(p.split("=", 1) for p in line.split()[1:])
+            if kv.get("sources") == cur:
+                res[kv["kernel"]] = float(kv["bytes_per_dispatch"])
+    return res
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "stats":
+        stats(*sys.argv[2:5])
+    elif mode == "traffic":
+        traffic(*sys.argv[2:11])
+    elif mode == "hash":
+        print(source_hash())
+    else:
+        sys.exit(f"unknown mode {mode}")
