@@ -91,8 +91,8 @@ def main():
     for l in range(n_inst):
         wr = torch.from_numpy(G.router_weights(args.seed, l, w.hidden, w.n_experts)).to(dev)
         b = torch.from_numpy(G.router_bias(args.seed, l, w.n_experts, w.zipf_s)).to(dev) if w.biased else None
-        canon_h = G.layer_canonical(args.seed, l, w.hidden, w.inter, w.n_experts, w.fmt)
-        sh_h = G.shared_canonical(args.seed, l, w.hidden, w.inter, w.fmt) if w.n_shared else None
+        canon_h = G.layer_canonical(args.seed, l, w.hidden, w.inter, w.n_experts, w.fmt, w.d_sigma)
+        sh_h = G.shared_canonical(args.seed, l, w.hidden, w.inter, w.fmt, w.d_sigma) if w.n_shared else None
         canon = torch.from_numpy(canon_h.reshape(-1)).to(dev)
         sh = torch.from_numpy(sh_h).to(dev) if sh_h is not None else None
         layers.append(B.StrataMoE(cfg, wr, b, canon, sh))

@@ -56,10 +56,10 @@ def router_bias(seed: int, layer: int, n_experts: int, s: float = 1.1) -> np.nda
     return (-s * np.log(ranks.astype(np.float64))).astype(np.float32)
 
 
-def _blocks(g, n_blocks: int, fmt: int) -> np.ndarray:
+def _blocks(g, n_blocks: int, fmt: int, d_sigma: float = 0.02) -> np.ndarray:
     cb = FORMATS[fmt][1]
     codes = g.integers(0, 256, size=(n_blocks, cb), dtype=np.uint8)
-    d = np.abs(0.02 * g.standard_normal(n_blocks)).astype(np.float16)
+    d = np.abs(d_sigma * g.standard_normal(n_blocks)).astype(np.float16)
     out = np.empty((n_blocks, canonical_block_bytes(fmt)), dtype=np.uint8)
     out[:, :cb] = codes
     out[:, cb:] = d.astype("<f2").view(np.uint8).reshape(n_blocks, 2)
@@ -71,25 +71,26 @@ def _expert_blocks(hidden: int, inter: int) -> int:
 
 
 def expert_canonical(seed: int, layer: int, expert: int, hidden: int, inter: int,
-                     fmt: int) -> np.ndarray:
+                     fmt: int, d_sigma: float = 0.02) -> np.ndarray:
     """One routed expert's canonical record as a flat uint8 array."""
     g = _rng(seed, TAG_EXPERT, layer, expert)
-    return _blocks(g, _expert_blocks(hidden, inter), fmt).reshape(-1)
+    return _blocks(g, _expert_blocks(hidden, inter), fmt, d_sigma).reshape(-1)
 
 
-def shared_canonical(seed: int, layer: int, hidden: int, inter: int, fmt: int) -> np.ndarray:
+def shared_canonical(seed: int, layer: int, hidden: int, inter: int, fmt: int,
+                     d_sigma: float = 0.02) -> np.ndarray:
     g = _rng(seed, TAG_SHARED, layer)
-    return _blocks(g, _expert_blocks(hidden, inter), fmt).reshape(-1)
+    return _blocks(g, _expert_blocks(hidden, inter), fmt, d_sigma).reshape(-1)
 
 
 def layer_canonical(seed: int, layer: int, hidden: int, inter: int, n_experts: int,
-                    fmt: int) -> np.ndarray:
+                    fmt: int, d_sigma: float = 0.02) -> np.ndarray:
     """All routed experts of a layer, [E, record_bytes] uint8, expert-id order."""
     rec = _expert_blocks(hidden, inter) * canonical_block_bytes(fmt)
     out = np.empty((n_experts, rec), dtype=np.uint8)
 
     def fill(e):
-        out[e] = expert_canonical(seed, layer, e, hidden, inter, fmt)
+        out[e] = expert_canonical(seed, layer, e, hidden, inter, fmt, d_sigma)
 
     # each expert has its own generator, so the draws are independent of the thread count
     with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:

@@ -43,6 +43,7 @@ class Workload:
     n_layers: int = 1    # layers in the stack
     steps: int = 1       # decode steps in the stream (stack workload)
     zipf_s: float = 1.1
+    d_sigma: float = 0.02  # expert scales d = |N(0, d_sigma^2)|
 
     def expert_bytes(self) -> int:
         blk = canonical_block_bytes(self.fmt)
@@ -58,8 +59,11 @@ WORKLOADS: Dict[str, Workload] = {
     # same layer, 1+3-token MTP verify batch, Zipf-skewed router
     "mtp_verify_t4_q2": Workload("mtp_verify_t4_q2", 2560, 512, 512, 10, 2, 4, True),
     # 48-layer Q3 stack, single-token decode stream of 256 steps
+    # (scales a quarter of the single-layer ones: with d ~ |N(0, 0.02^2)| each
+    # layer's output grows as the square of its input and the residual stream
+    # overflows fp32 by about layer 8; at 0.005 each layer moves h by ~2%)
     "stack48_q3_decode": Workload("stack48_q3_decode", 2560, 512, 512, 10, 3, 1, True,
-                                  n_layers=48, steps=256),
+                                  n_layers=48, steps=256, d_sigma=0.005),
     # 8192-token prefill chunk through one Q2 layer, Zipf-skewed router
     "prefill_t8192_q2": Workload("prefill_t8192_q2", 2560, 512, 512, 10, 2, 8192, True),
     # DeepSeek-V4-Flash-shaped layer, Q4, 256 routed + 1 shared, top-6

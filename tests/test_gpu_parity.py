@@ -3,12 +3,14 @@ seeded inputs.  Routing (ids, permutation, offsets) must be bit-exact; the
 fp32 decode path within rel-L2 1e-5; the bf16-MFMA prefill path within
 rel-L2 2e-2."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from moe_synth import WORKLOADS
+from moe_synth import WORKLOADS, generate as G
 from tests.moe_cases import (HostLayer, tokens, to_device_bf16, device_layer, rel_l2, check_route,
                              DECODE_TOL, PREFILL_TOL)
 
@@ -286,3 +288,35 @@ def test_trace_events_bracket_each_kernel(B, T, n_kernels):
         assert evs[2 * j].elapsed_time(evs[2 * j + 1]) > 0.0
     with pytest.raises(B.StrataError):
         B.strata_moe_trace_next_call(layer.handle, evs[:3])
+
+
+# ------------------------------------------------------------------ 48-layer Q3 stack (full size)
+@pytest.mark.timeout(900)
+def test_workload_stack48_q3(B):
+    """Every layer resident (42.5 GB), tokens and expected h_48 from the
+    oracle (tests/golden/stack48_q3_expected.npz, written by
+    tests/golden/make_stack48_expected.py); gated on h_48 - h_0."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "stack48_q3_expected.npz")
+    ref = np.load(path)
+    w = WORKLOADS["stack48_q3_decode"]
+    seed = int(ref["draw"][0][0])
+    cfg = B.make_config(w.hidden, w.inter, w.n_experts, w.top_k, 0, w.fmt, 1)
+    layers = []
+    for l in range(w.n_layers):
+        wr = torch.from_numpy(G.router_weights(seed, l, w.hidden, w.n_experts)).to(DEV)
+        b = torch.from_numpy(G.router_bias(seed, l, w.n_experts, w.zipf_s)).to(DEV)
+        canon = torch.from_numpy(
+            G.layer_canonical(seed, l, w.hidden, w.inter, w.n_experts, w.fmt, w.d_sigma).reshape(-1)).to(DEV)
+        layers.append(B.StrataMoE(cfg, wr, b, canon))
+        del canon
+    torch.cuda.synchronize()
+    for s in range(ref["x_bits"].shape[0]):
+        bits = ref["x_bits"][s:s + 1]
+        x = to_device_bf16(bits, DEV)
+        h = B.stack_forward(layers, x).cpu().numpy().astype(np.float64)
+        x0 = G.bf16_bits_to_f32(bits).astype(np.float64)
+        err = rel_l2(h - x0, ref["h48"][s:s + 1] - x0)
+        print(f"stack step {s}: rel-L2 of h48 - h0 = {err:.3e}", flush=True)
+        assert err <= DECODE_TOL, err
+    del layers
+    torch.cuda.empty_cache()
