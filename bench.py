@@ -189,7 +189,7 @@ def main():
     if decode:                                              # (stack: layer 0 of each pass)
         names = ["route_gemv", "topk", "gateup", "down_combine"]
     else:
-        names = ["router_gemm", "topk", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
+        names = ["router_gemm", "topk", "colscan", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
     # each kernel's own dispatch start/end, bound to a pair of events on the
     # launch stream (eager launches of the same steps, after the timed replay)
     n_trace = min(steps, 256)

@@ -20,13 +20,13 @@ struct Work {
   int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
   float* wtab;        // [E+1][8]   decode: routing weight per (active expert, token), 0 if not routed
   int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill)
-  int* chunk_base;    // [E][nchunks] prefill: per-chunk counts, then bases
+  int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
   int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}
   float* act;         // prefill: bf16 SwiGLU rows [slots][I] (same region as actp)
   _Float16* actp;     // decode: SwiGLU rows as three fp16 parts [active expert][T][3][I]
   _Float16* xparts;   // decode: token rows as three fp16 parts [8][3][H]
-  float* y;           // [slots][H]  prefill: per-pair expert outputs
+  uint16_t* ybf;      // [slots][H]  prefill: per-pair expert outputs, bf16
   int nchunks;
   int max_tiles;
 };

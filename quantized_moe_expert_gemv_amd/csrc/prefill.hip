@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void k_topk_chunks(TopkArgs a) {
     a.w.pair_rank[(size_t)tb * k + i] = rank;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)e * a.nchunks + chunk] = hist[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = hist[e];
 }
 
 struct ScanArgs {
@@ -236,26 +236,51 @@ struct ScanArgs {
   Work w;
 };
 
+// Column scan of the per-chunk expert histograms (chunk-major [nch][E]): each
+// count becomes the number of that expert's pairs in earlier chunks, and
+// counts[e] the expert's total.  A workgroup takes 64 experts; its 16 waves
+// each sum a range of chunks, then rescan it from the ranges' prefix.  Loads
+// go in unconditional batches (indices clamped).
+constexpr int COLSCAN_GROUPS = 16;
+
+__global__ __launch_bounds__(64 * COLSCAN_GROUPS) void k_colscan(ScanArgs a) {
+  __shared__ int part[COLSCAN_GROUPS][64];
+  const int E = a.E, nch = a.nchunks;
+  const int el = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + el, ec = min(e, E - 1);
+  const int per = (nch + COLSCAN_GROUPS - 1) / COLSCAN_GROUPS;
+  const int c0 = min(nch, g * per), c1 = min(nch, c0 + per);
+  int* cb_col = a.w.chunk_base + ec;
+  int sum = 0;
+  for (int cb = c0; cb < c1; cb += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = cb_col[(size_t)min(cb + i, nch - 1) * E];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += (cb + i < c1) ? v[i] : 0;
+  }
+  part[g][el] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int q = 0; q < g; ++q) run += part[q][el];
+  for (int cb = c0; cb < c1; cb += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = cb_col[(size_t)min(cb + i, nch - 1) * E];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (cb + i < c1 && e < E) cb_col[(size_t)(cb + i) * E] = run;
+      run += (cb + i < c1) ? v[i] : 0;
+    }
+  }
+  if (g == COLSCAN_GROUPS - 1 && e < E) a.w.counts[e] = run;    // the last range ends at the total
+}
+
+// Offsets (exclusive scan of the expert counts) and the flat tile list.
+// One workgroup.
 __global__ __launch_bounds__(1024) void k_scan(ScanArgs a) {
   __shared__ int2 tmp[16];
-  const int E = a.E, P = a.T * a.k, nch = a.nchunks;
-  // per expert: running sum over chunks (in place -> chunk bases) and the count
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int* row = a.w.chunk_base + (size_t)e * nch;
-    int run = 0;
-    for (int c0 = 0; c0 < nch; c0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < nch) ? row[c0 + i] : 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (c0 + i < nch) row[c0 + i] = run;
-        run += v[i];
-      }
-    }
-    a.w.counts[e] = run;
-  }
-  __syncthreads();
+  const int E = a.E, P = a.T * a.k;
   // exclusive scan over experts (the shared expert is entry E) of (count, tiles)
   const int n_ent = E + (a.n_shared ? 1 : 0);
   const int per = (n_ent + blockDim.x - 1) / blockDim.x;
@@ -291,7 +316,7 @@ __global__ void k_scatter(TopkArgs a) {
   if (p >= P) return;
   const int e = a.w.topk_idx[p];
   const int chunk = (p / a.k) / CT;
-  const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)e * a.nchunks + chunk] + a.w.pair_rank[p];
+  const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)chunk * a.E + e] + a.w.pair_rank[p];
   a.w.perm[slot] = p;
   a.w.inv[p] = slot;
 }
@@ -428,7 +453,8 @@ __global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = 64 * wm + 32 * mt + acc_row(v, lane);
-        if (m < rows) a.w.y[(size_t)(slot0 + m) * a.H + h0 + 64 * wn + 32 * nt + (lane & 31)] = acc[mt][nt][v];
+        if (m < rows)
+          a.w.ybf[(size_t)(slot0 + m) * a.H + h0 + 64 * wn + 32 * nt + (lane & 31)] = f32_to_bf16_rne(acc[mt][nt][v]);
       }
 }
 
@@ -441,44 +467,68 @@ struct CombineArgs {
   Work w;
 };
 
+// out[t] = sum_j w[t][j] * y[slot(t, j)] (+ shared expert row) (+ x) (+ out),
+// fixed j order.  One workgroup per token; each thread 8 columns per pass;
+// the bf16 per-pair rows are read in batches of 8 unconditional loads.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int t = blockIdx.x;
   const int k = a.k;
   __shared__ int s_slot[64];
   __shared__ float s_w[64];
-  if (threadIdx.x < k) {
-    s_slot[threadIdx.x] = a.w.inv[t * k + threadIdx.x];
-    s_w[threadIdx.x] = a.w.topk_w[t * k + threadIdx.x];
+  if (threadIdx.x < 64) {
+    const int j = min((int)threadIdx.x, k - 1);
+    s_slot[threadIdx.x] = a.w.inv[t * k + j];
+    s_w[threadIdx.x] = (threadIdx.x < (unsigned)k) ? a.w.topk_w[t * k + j] : 0.f;
   }
   __syncthreads();
-  for (int h = threadIdx.x * 4; h < a.H; h += blockDim.x * 4) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float4 y = *reinterpret_cast<const float4*>(a.w.y + (size_t)s_slot[j] * a.H + h);
-      const float wj = s_w[j];
-      acc.x = fmaf(wj, y.x, acc.x); acc.y = fmaf(wj, y.y, acc.y);
-      acc.z = fmaf(wj, y.z, acc.z); acc.w = fmaf(wj, y.w, acc.w);
-    }
-    if (a.n_shared) {
-      const float4 y = *reinterpret_cast<const float4*>(a.w.y + (size_t)(a.P + t) * a.H + h);
-      acc.x += y.x; acc.y += y.y; acc.z += y.z; acc.w += y.w;
-    }
-    const size_t o = (size_t)t * a.H + h;
-    if (a.flags & 2u) {
-      if (a.x_f32) {
-        const float4 xv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + o);
-        acc.x += xv.x; acc.y += xv.y; acc.z += xv.z; acc.w += xv.w;
-      } else {
-        const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + o);
-        acc.x += __uint_as_float(r.x << 16); acc.y += __uint_as_float(r.x & 0xffff0000u);
-        acc.z += __uint_as_float(r.y << 16); acc.w += __uint_as_float(r.y & 0xffff0000u);
+  for (int h = threadIdx.x * 8; h < a.H; h += blockDim.x * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      uint4 y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        y[j] = *reinterpret_cast<const uint4*>(a.w.ybf + (size_t)s_slot[min(j0 + j, 63)] * a.H + h);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = s_w[min(j0 + j, 63)];                 // 0 past k
+        const uint32_t q[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * c] = fmaf(wj, __uint_as_float(q[c] << 16), acc[2 * c]);
+          acc[2 * c + 1] = fmaf(wj, __uint_as_float(q[c] & 0xffff0000u), acc[2 * c + 1]);
+        }
       }
     }
-    if (a.flags & 1u) {
-      const float4 ov = *reinterpret_cast<const float4*>(a.out + o);
-      acc.x += ov.x; acc.y += ov.y; acc.z += ov.z; acc.w += ov.w;
+    if (a.n_shared) {
+      const uint4 ys = *reinterpret_cast<const uint4*>(a.w.ybf + (size_t)(a.P + t) * a.H + h);
+      const uint32_t q[4] = {ys.x, ys.y, ys.z, ys.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] += __uint_as_float(q[c] << 16);
+        acc[2 * c + 1] += __uint_as_float(q[c] & 0xffff0000u);
+      }
     }
-    *reinterpret_cast<float4*>(a.out + o) = acc;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int hh = h + 4 * half;
+      float4 r = make_float4(acc[4 * half], acc[4 * half + 1], acc[4 * half + 2], acc[4 * half + 3]);
+      const size_t o = (size_t)t * a.H + hh;
+      if (a.flags & 2u) {
+        if (a.x_f32) {
+          const float4 xv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + o);
+          r.x += xv.x; r.y += xv.y; r.z += xv.z; r.w += xv.w;
+        } else {
+          const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.x) + o);
+          r.x += __uint_as_float(b.x << 16); r.y += __uint_as_float(b.x & 0xffff0000u);
+          r.z += __uint_as_float(b.y << 16); r.w += __uint_as_float(b.y & 0xffff0000u);
+        }
+      }
+      if (a.flags & 1u) {
+        const float4 ov = *reinterpret_cast<const float4*>(a.out + o);
+        r.x += ov.x; r.y += ov.y; r.z += ov.z; r.w += ov.w;
+      }
+      *reinterpret_cast<float4*>(a.out + o) = r;
+    }
   }
 }
 
@@ -511,6 +561,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
+  launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);
   launch(tr, k_scan, dim3(1), dim3(1024), 0, s, sa);
   const int P = c.T * L.k;
   launch(tr, k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);

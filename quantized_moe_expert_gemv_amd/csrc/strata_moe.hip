@@ -109,7 +109,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   const size_t act_decode = umax * Td * 3 * I * 2;                             // fp16 parts
   p.act = take(act_prefill > act_decode ? act_prefill : act_decode);
   p.xparts = take(Td * 3 * H * 2);
-  p.y = take(slots * H * 4);
+  p.y = take(slots * H * 2);
   p.total = o;
   return p;
 }
@@ -267,7 +267,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.actp = reinterpret_cast<_Float16*>(ws + p.act);
   W.xparts = reinterpret_cast<_Float16*>(ws + p.xparts);
   W.wtab = reinterpret_cast<float*>(ws + p.wtab);
-  W.y = reinterpret_cast<float*>(ws + p.y);
+  W.ybf = reinterpret_cast<uint16_t*>(ws + p.y);
   W.nchunks = p.nchunks;
   W.max_tiles = p.max_tiles;
 

@@ -63,8 +63,8 @@ def test_packed_bytes_cover_experts_and_router_split(B):
 def test_workspace_grows_with_max_tokens(B):
     small = B.strata_moe_workspace_bytes(_cfg(B, max_tokens=1))
     big = B.strata_moe_workspace_bytes(_cfg(B, max_tokens=8192))
-    # per-pair fp32 expert outputs dominate: 8192 * 10 * 2560 * 4 bytes
-    assert small > 0 and big > 8192 * 10 * 2560 * 4 > small
+    # per-pair bf16 expert outputs dominate: 8192 * 10 * 2560 * 2 bytes
+    assert small > 0 and big > 8192 * 10 * 2560 * 2 > small
 
 
 @pytest.mark.parametrize("bad", [dict(qfmt=5), dict(hidden=2500), dict(inter=100), dict(top_k=0),
