@@ -49,6 +49,19 @@ __device__ inline bf16x8 lds_frag(const uint16_t* p) {
 
 __device__ inline uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// 16-byte chunk as a native vector: copies stay in registers (a struct copy can
+// become a memcpy through private memory)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// two fp32 -> two bf16 (RNE) in one dword, low half first
+__device__ inline uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // 8 fp32 -> 8 bf16 (RNE) as a 16-B vector; optionally the bf16 of the remainder
 __device__ inline uint4 to_bf16x8(const float* f, uint4* rem) {
   uint16_t h[8], r[8];
@@ -83,43 +96,74 @@ __device__ inline void mma_step(const uint16_t* As, const uint16_t* Bs, f32x16 (
 // row of element v of a 32x32 accumulator held by `lane`
 __device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
 
-// Dequantise one lane-slot l of a slab for blocks bb0 and bb0 + 1 (bb0 even):
-// row l % 16, K-slice 8*(l/16) of each block, 16 weights d (q - c) rounded
-// to bf16 into the LDS row dst (columns (b - bb0)*32 + 8*(l/16) + e).
+// One lane-slot l of a slab for blocks bb0 and bb0 + 1 (bb0 even): row l % 16,
+// K-slice 8*(l/16) of each block.  RawB holds its codes and the two scales as
+// loaded; dequant_rawb writes the 16 weights d (q - c), rounded to bf16, to
+// the LDS row dst (columns (b - bb0)*32 + 8*(l/16) + e).  The raw loads are
+// issued a K-step ahead of the conversion.
+template <int FMT> struct RawB;
+template <> struct RawB<2> { uint32_t w, sc; };
+template <> struct RawB<3> { uint32_t w, hi, sc; };
+template <> struct RawB<4> { uint2 w; uint32_t sc; };
+
 template <int FMT>
-__device__ inline void dequant_lane_pair(const uint8_t* slab, int l, int bb0, uint16_t* dst) {
-  constexpr int POS2[8] = {0, 4, 2, 6, 8, 12, 10, 14};
+__device__ inline void load_rawb(const uint8_t* slab, int l, int bb0, RawB<FMT>& r) {
+  r.sc = *reinterpret_cast<const uint32_t*>(slab + Fmt<FMT>::slab_codes + (l & 15) * 16 + bb0 * 2);
+  if constexpr (FMT == 4) {
+    r.w = *reinterpret_cast<const uint2*>(slab + (bb0 >> 2) * 1024 + l * 16 + (bb0 & 3) * 4);
+  } else {
+    r.w = *reinterpret_cast<const uint32_t*>(slab + l * 16 + (bb0 >> 1) * 4);
+    if constexpr (FMT == 3) r.hi = *reinterpret_cast<const uint32_t*>(slab + 1024 + l * 8 + (bb0 >> 2) * 4);
+  }
+}
+
+// packed FP4 pair SEL of src (nibbles 2SEL, 2SEL+1) times scale, to fp32
+template <int SEL>
+__device__ inline f32x2_t fp4_pair(uint32_t src, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, scale, SEL);
+}
+
+// block B (0 or 1) of the lane-slot: 8 weights
+template <int FMT, int B>
+__device__ inline void dequant_block(const RawB<FMT>& r, int q, int bb0, uint16_t* dst) {
   constexpr int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
   constexpr float C = Fmt<FMT>::c;
-  const int r = l & 15, q = l >> 4;
-  const uint32_t sc = *reinterpret_cast<const uint32_t*>(slab + Fmt<FMT>::slab_codes + r * 16 + bb0 * 2);
-  const float d[2] = {half_bits_to_f32((uint16_t)(sc & 0xffffu)), half_bits_to_f32((uint16_t)(sc >> 16))};
-  float w[16];
+  const float d = half_bits_to_f32((uint16_t)(B ? (r.sc >> 16) : (r.sc & 0xffffu)));
+  const float cd = C * d;
+  float w[8];
   if constexpr (FMT == 4) {
-    const uint2 c = *reinterpret_cast<const uint2*>(slab + (bb0 >> 2) * 1024 + l * 16 + (bb0 & 3) * 4);
+    const uint32_t W = B ? r.w.y : r.w.x;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint32_t W = b ? c.y : c.x;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[8 * b + e] = d[b] * ((float)((W >> (4 * NIB4[e])) & 15u) - C);
-    }
+    for (int e = 0; e < 8; ++e) w[e] = fmaf(d, (float)((W >> (4 * NIB4[e])) & 15u), -cd);
   } else {
-    const uint32_t W = *reinterpret_cast<const uint32_t*>(slab + l * 16 + (bb0 >> 1) * 4);
-    uint32_t Hd = 0;
-    if constexpr (FMT == 3) Hd = *reinterpret_cast<const uint32_t*>(slab + 1024 + l * 8 + (bb0 >> 2) * 4);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t qv = (W >> (16 * b + POS2[e])) & 3u;
-        if constexpr (FMT == 3) qv |= ((Hd >> (4 * e + ((bb0 + b) & 3))) & 1u) << 2;
-        w[8 * b + e] = d[b] * ((float)qv - C);
-      }
+    // 2-bit codes as FP4 nibbles 0b00qq (e2m1 value q/2) at scale 2: exactly q.  The
+    // conversion's scale acts as a power of two, so the block scale d is applied after.
+    const uint32_t E = r.w & 0x33333333u, O = (r.w >> 2) & 0x33333333u;
+    const f32x2_t p0 = fp4_pair<2 * B>(E, 2.0f);
+    const f32x2_t p1 = fp4_pair<2 * B>(O, 2.0f);
+    const f32x2_t p2 = fp4_pair<2 * B + 1>(E, 2.0f);
+    const f32x2_t p3 = fp4_pair<2 * B + 1>(O, 2.0f);
+    w[0] = p0.x; w[1] = p0.y; w[2] = p1.x; w[3] = p1.y;
+    w[4] = p2.x; w[5] = p2.y; w[6] = p3.x; w[7] = p3.y;
+    if constexpr (FMT == 3) {
+      // third bit of weight e at nibble e: FP4 0b000h (0 or 0.5) at scale 8: 4h
+      const uint32_t X = (r.hi >> ((bb0 + B) & 3)) & 0x11111111u;
+      const f32x2_t h0 = fp4_pair<0>(X, 8.0f), h1 = fp4_pair<1>(X, 8.0f);
+      const f32x2_t h2 = fp4_pair<2>(X, 8.0f), h3 = fp4_pair<3>(X, 8.0f);
+      w[0] += h0.x; w[1] += h0.y; w[2] += h1.x; w[3] += h1.y;
+      w[4] += h2.x; w[5] += h2.y; w[6] += h3.x; w[7] += h3.y;
     }
-  }
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-    *reinterpret_cast<uint4*>(dst + 32 * b + 8 * q) = to_bf16x8(w + 8 * b, nullptr);
+    for (int e = 0; e < 8; ++e) w[e] = fmaf(w[e], d, -cd);  // (q - c) d, exact in fp32
+  }
+  *reinterpret_cast<uint4*>(dst + 32 * B + 8 * q) =
+      make_uint4(cvt_bf16x2(w[0], w[1]), cvt_bf16x2(w[2], w[3]), cvt_bf16x2(w[4], w[5]), cvt_bf16x2(w[6], w[7]));
+}
+
+template <int FMT>
+__device__ inline void dequant_rawb(const RawB<FMT>& r, int l, int bb0, uint16_t* dst) {
+  dequant_block<FMT, 0>(r, l >> 4, bb0, dst);
+  dequant_block<FMT, 1>(r, l >> 4, bb0, dst);
 }
 
 // ------------------------------------------------------------------ router GEMM
@@ -331,6 +375,11 @@ struct GemmArgs {
   Work w;
 };
 
+// A-tile chunks of one thread: 4 chunks of 8 bf16 (bf16 input) or of 8 fp32
+template <bool XF32> struct AChunks;
+template <> struct AChunks<false> { u32x4_t v[4]; };
+template <> struct AChunks<true> { f32x4_t v[8]; };
+
 template <int FMT, bool XF32>
 __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
@@ -344,14 +393,11 @@ __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int nsbH = a.H / SB_WEIGHTS;
   if (tid < BM) {
-    const void* p = nullptr;
-    if (tid < rows) {
-      const int slot = slot0 + tid;
-      const int t = slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
-      p = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + (size_t)t * a.H)
-               : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H);
-    }
-    rowsrc[tid] = p;
+    // rows past the tile's end read its first row (in bounds; results not stored)
+    const int slot = slot0 + min(tid, rows - 1);
+    const int t = slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
+    rowsrc[tid] = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + (size_t)t * a.H)
+                       : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H);
   }
   // B columns in groups of 16: column group cg = tid / 32 covers columns 16cg..16cg+15,
   // i.e. matrix (cg % 4) / 2 (0 gate, 1 up) and rows (cg / 4) * 32 + (cg % 2) * 16 of the
@@ -361,36 +407,56 @@ __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
   const int bgroup = itile * 4 + (cg >> 2) * 2 + (cg & 1);
   const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + (bmat ? up_off(FMT, a.H, a.I) : 0);
   __syncthreads();
+  const void* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) src[i] = rowsrc[(tid + 256 * i) >> 3];
+  // the next K-step's operands, in registers: loaded one step ahead
+  AChunks<XF32> an;
+  RawB<FMT> bn[2];
+  auto load_step = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kc = (tid + 256 * i) & 7;
+      if constexpr (XF32) {
+        const float* f = reinterpret_cast<const float*>(src[i]) + k0 + kc * 8;
+        an.v[2 * i] = *reinterpret_cast<const f32x4_t*>(f);
+        an.v[2 * i + 1] = *reinterpret_cast<const f32x4_t*>(f + 4);
+      } else {
+        an.v[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src[i]) + k0 + kc * 8);
+      }
+    }
+    const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
+    const uint8_t* slab = bmat_base + slab_off(FMT, nsbH, bgroup, sb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) load_rawb<FMT>(slab, sub + 32 * h, bb0, bn[h]);
+  };
   f32x16 acc[2][2] = {};
+  load_step(0);
   for (int k0 = 0; k0 < a.H; k0 += BK) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
-      uint4 hv = make_uint4(0, 0, 0, 0);
-      const void* src = rowsrc[r];
-      if (src) {
-        if constexpr (XF32) {
-          const float* f = reinterpret_cast<const float*>(src) + k0 + kc * 8;
-          float v[8];
-          *reinterpret_cast<float4*>(v) = *reinterpret_cast<const float4*>(f);
-          *reinterpret_cast<float4*>(v + 4) = *reinterpret_cast<const float4*>(f + 4);
-          hv = to_bf16x8(v, nullptr);
-        } else {
-          hv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(src) + k0 + kc * 8);
-        }
+      u32x4_t hv;
+      if constexpr (XF32) {
+        const f32x4_t f0 = an.v[2 * i], f1 = an.v[2 * i + 1];
+        hv = u32x4_t{cvt_bf16x2(f0.x, f0.y), cvt_bf16x2(f0.z, f0.w), cvt_bf16x2(f1.x, f1.y),
+                     cvt_bf16x2(f1.z, f1.w)};
+      } else {
+        hv = an.v[i];
       }
-      *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
+      *reinterpret_cast<u32x4_t*>(As + r * LDK + kc * 8) = hv;
     }
     {
-      const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
-      const uint8_t* slab = bmat_base + slab_off(FMT, nsbH, bgroup, sb);
+      const int bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int l = sub + 32 * h;
-        dequant_lane_pair<FMT>(slab, l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
+        dequant_rawb<FMT>(bn[h], l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
       }
     }
     __syncthreads();
+    load_step(min(k0 + BK, a.H - BK));               // in flight during the MFMAs (last step repeats)
+    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the MFMAs
     mma_step(As, Bs, acc, wm, wn, lane);
     __syncthreads();
   }
@@ -424,25 +490,39 @@ __global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
   const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
   const int bgroup = h0 / GROUP_ROWS + cg;
   const uint16_t* act = reinterpret_cast<const uint16_t*>(a.w.act);
+  // rows past the tile's end read its first row (in bounds; results not stored)
+  const uint16_t* src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) src[i] = act + (size_t)(slot0 + min((tid + 256 * i) >> 3, rows - 1)) * a.I;
+  AChunks<false> an;
+  RawB<FMT> bn[2];
+  auto load_step = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) an.v[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0 + ((tid + 256 * i) & 7) * 8);
+    const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
+    const uint8_t* slab = bmat_base + slab_off(FMT, nsbI, bgroup, sb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) load_rawb<FMT>(slab, sub + 32 * h, bb0, bn[h]);
+  };
   f32x16 acc[2][2] = {};
+  load_step(0);
   for (int k0 = 0; k0 < a.I; k0 += BK) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
-      uint4 hv = make_uint4(0, 0, 0, 0);
-      if (r < rows) hv = *reinterpret_cast<const uint4*>(act + (size_t)(slot0 + r) * a.I + k0 + kc * 8);
-      *reinterpret_cast<uint4*>(As + r * LDK + kc * 8) = hv;
+      *reinterpret_cast<u32x4_t*>(As + r * LDK + kc * 8) = an.v[i];
     }
     {
-      const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
-      const uint8_t* slab = bmat_base + slab_off(FMT, nsbI, bgroup, sb);
+      const int bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int l = sub + 32 * h;
-        dequant_lane_pair<FMT>(slab, l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
+        dequant_rawb<FMT>(bn[h], l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
       }
     }
     __syncthreads();
+    load_step(min(k0 + BK, a.I - BK));               // in flight during the MFMAs (last step repeats)
+    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the MFMAs
     mma_step(As, Bs, acc, wm, wn, lane);
     __syncthreads();
   }
