@@ -199,44 +199,16 @@ __device__ inline void topk_emit(uint64_t my_key, uint64_t top_key, int k, int* 
   __builtin_amdgcn_wave_barrier();
 }
 
-// Top-k of one token's logits row[0..E), E <= 64*MAXV, one wave; the row is
-// read once into registers.  Round r takes the best key below round r-1's.
-template <int MAXV>
-__device__ inline void wave_topk(const float* row, int E, int k, int* idx_out, float* w_out,
-                                 int* sel_lds) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  uint64_t key[MAXV];
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + WAVE * i;
-    const float v = row[e < E ? e : E - 1];
-    key[i] = (e < E) ? topk_key(v, e) : 0ull;
-  }
-  uint64_t prev = ~0ull, mine = 0ull, top = 0ull;
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0ull;
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-      const uint64_t c = (key[i] < prev) ? key[i] : 0ull;
-      best = umax64(best, c);
-    }
-    best = wave_max_u64(best);
-    if (r == 0) top = best;
-    mine = (lane == r) ? best : mine;
-    prev = best;
-  }
-  topk_emit(mine, top, k, idx_out, w_out, sel_lds);
-}
-
-// Same selection for any E, re-reading the row each round (E > 512).
-__device__ inline void wave_topk_loop(const float* row, int E, int k, int* idx_out, float* w_out,
-                                      int* sel_lds) {
+// Same selection for any E, re-reading the row (plus bias[e] when bias is not
+// null) each round.
+__device__ inline void wave_topk_loop(const float* row, const float* bias, int E, int k, int* idx_out,
+                                      float* w_out, int* sel_lds) {
   const int lane = threadIdx.x & (WAVE - 1);
   uint64_t prev = ~0ull, mine = 0ull, top = 0ull;
   for (int r = 0; r < k; ++r) {
     uint64_t best = 0ull;
     for (int e = lane; e < E; e += WAVE) {
-      const uint64_t key = topk_key(row[e], e);
+      const uint64_t key = topk_key(row[e] + (bias ? bias[e] : 0.f), e);
       best = umax64(best, (key < prev) ? key : 0ull);
     }
     best = wave_max_u64(best);
@@ -248,29 +220,27 @@ __device__ inline void wave_topk_loop(const float* row, int E, int k, int* idx_o
 }
 
 // Radix select over the order-preserving 32-bit images u of the values
-// (E <= 64*MAXV, one wave): tau = the k-th largest u is fixed bit by bit from
-// the top (population counts of ballots), ties at tau are taken lowest id
-// first, and the selected ids come out in ascending order from prefix counts
-// of the selection ballots.  Same selection as the rounds above.
+// val[i] of ids lane + 64 i (E <= 64*MAXV, one wave): the threshold tau is
+// fixed bit by bit from the top (population counts of ballots) and the
+// descent stops once exactly k values are >= tau; ties at tau are taken lowest
+// id first, and the selected ids come out in ascending order from prefix
+// counts of the selection ballots.  Same selection as the rounds above.
 template <int MAXV>
-__device__ inline void wave_topk_radix(const float* row, int E, int k, int* idx_out, float* w_out) {
+__device__ inline void wave_topk_radix(const float (&val)[MAXV], int E, int k, int* idx_out, float* w_out) {
   const int lane = threadIdx.x & (WAVE - 1);
   uint32_t u[MAXV];
-  float val[MAXV];
 #pragma unroll
-  for (int i = 0; i < MAXV; ++i) {
-    const int e = lane + WAVE * i;
-    const float v = row[e < E ? e : E - 1];
-    val[i] = v;
-    u[i] = (e < E) ? sortable_bits(v) : 0u;    // padding ranks below every value
-  }
+  for (int i = 0; i < MAXV; ++i) u[i] = (lane + WAVE * i < E) ? sortable_bits(val[i]) : 0u;  // padding ranks lowest
   uint32_t tau = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = tau | (1u << b);
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < MAXV; ++i) cnt += __popcll(__ballot(u[i] >= cand));
-    if (cnt >= k) tau = cand;
+    if (cnt >= k) {
+      tau = cand;
+      if (cnt == k) break;                      // {u >= tau} is the selection
+    }
   }
   int gt = 0;
 #pragma unroll
@@ -309,13 +279,6 @@ __device__ inline void wave_topk_radix(const float* row, int E, int k, int* idx_
       w_out[pos[i]] = z[i] * inv;
     }
   }
-}
-
-__device__ inline void wave_topk_any(const float* row, int E, int k, int* idx_out, float* w_out,
-                                     int* sel_lds) {
-  if (E <= 256) wave_topk_radix<4>(row, E, k, idx_out, w_out);
-  else if (E <= 512) wave_topk_radix<8>(row, E, k, idx_out, w_out);
-  else wave_topk_loop(row, E, k, idx_out, w_out, sel_lds);
 }
 
 // Exclusive scan of an int2 over the workgroup (<= 16 waves); *total gets the sum.

@@ -26,7 +26,9 @@ struct Work {
   float* act;         // prefill: bf16 SwiGLU rows [slots][I] (same region as actp)
   _Float16* actp;     // decode: SwiGLU rows as three fp16 parts [active expert][T][3][I]
   _Float16* xparts;   // decode: token rows as three fp16 parts [8][3][H]
-  uint16_t* ybf;      // [slots][H]  prefill: per-pair expert outputs, bf16
+  uint16_t* ybf;      // [slots][H]  prefill: per-pair expert outputs, bf16; before the
+                      //             expert GEMMs it holds the router's split-K partials
+  size_t ybf_bytes;
   int nchunks;
   int max_tiles;
 };

@@ -5,24 +5,29 @@
 // HBM, so the chunk is a grouped, genuinely dense contraction and runs on
 // the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //
-//   k_router_gemm    logits = x Wr^T + b, fp32-accurate from bf16 MFMA by
-//                    splitting Wr (and an fp32 x) into bf16 high + low parts
-//   k_topk_chunks    top-k + renormalised softmax per token (one wave per
-//                    token) and, per chunk of 32 tokens, the expert
-//                    histogram and every pair's rank inside the chunk
-//   k_scan           per-expert chunk bases, counts, offsets and the flat
-//                    list of (expert, 128-row tile) GEMM work items
+//   k_router_gemm    x Wr^T, fp32-accurate from bf16 MFMA by splitting Wr
+//                    (and an fp32 x) into bf16 high + low parts; split over K
+//                    into partial planes when the tile grid is small
+//   k_topk_chunks    logits = sum of the planes + b; top-k + renormalised
+//                    softmax per token (one wave per token) and, per chunk of
+//                    32 tokens, the expert histogram and every pair's rank
+//                    inside the chunk
+//   k_colscan        per-expert bases of the chunks (column scan)
+//   k_scan           expert counts -> offsets and the flat list of
+//                    (expert, 128-row tile) GEMM work items
 //   k_scatter        the stable permutation: slot of pair p =
 //                    offset[e] + base[e][chunk] + rank  (no atomics, so the
 //                    order is (expert, p) on every run)
 //   k_gemm_gateup    per work item: gathered token rows x rows of dequantised
 //                    gate|up weights staged as bf16 in LDS -> SwiGLU -> bf16
 //   k_gemm_down      per work item: SwiGLU rows x dequantised down weights ->
-//                    per-pair fp32 output rows
+//                    per-pair output rows (bf16)
 //   k_combine        out[t] = sum_j w[t, j] y[slot(t, j)] (+ shared, residual)
 //
 // Dequantised weights d (q - c) are rounded to bf16 (8-bit mantissa) before
 // the MFMA; activations are bf16 (exact for bf16 inputs).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,16 +43,11 @@ constexpr int BK = 64;              // reduction step (two quantised blocks)
 constexpr int LDK = BK + 8;         // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
 constexpr int CT = PREFILL_CHUNK_T;
 
-__device__ inline float ld_coherent_f(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ inline bf16x8 lds_frag(const uint16_t* p) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ inline uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -62,17 +62,10 @@ __device__ inline uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// 8 fp32 -> 8 bf16 (RNE) as a 16-B vector; optionally the bf16 of the remainder
-__device__ inline uint4 to_bf16x8(const float* f, uint4* rem) {
-  uint16_t h[8], r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = f32_to_bf16_rne(f[i]);
-    if (rem) r[i] = f32_to_bf16_rne(f[i] - bf16_to_f32(h[i]));
-  }
-  if (rem) *rem = make_uint4(pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7]));
-  return make_uint4(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
-}
+// A-tile chunks of one thread: 4 chunks of 8 bf16 (bf16 input) or of 8 fp32
+template <bool XF32> struct AChunks;
+template <> struct AChunks<false> { u32x4_t v[4]; };
+template <> struct AChunks<true> { f32x4_t v[8]; };
 
 // One wave's 64x64 sub-tile: 2 x 2 MFMA 32x32 tiles over one BK step.
 __device__ inline void mma_step(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[2][2],
@@ -167,13 +160,31 @@ __device__ inline void dequant_rawb(const RawB<FMT>& r, int l, int bb0, uint16_t
 }
 
 // ------------------------------------------------------------------ router GEMM
+// Split-K: workgroup (n, m, z) multiplies K range [z kper, (z+1) kper) of its
+// 128 x 128 tile and writes the fp32 partial to plane z; the top-k kernel sums
+// the planes in order z = 0, 1, ... and adds the bias.  Operands for the next
+// K-step are loaded into registers while the MFMAs of the current one run.
 struct RouterArgs {
   const void* x;
   int x_f32, T, H, E;
+  int kper;               // K range of one split, a multiple of BK
+  size_t plane;           // elements between partial planes
   const uint16_t* whi;
   const uint16_t* wlo;
-  const float* bias;
-  float* logits;
+  float* part;            // [S][T][E]
+};
+
+// fp32 pair -> bf16 pair (RNE) in *hi and the bf16 of the remainders in *lo
+__device__ inline void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = cvt_bf16x2(a, b);
+  *hi = h;
+  *lo = cvt_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+}
+
+template <bool XF32>
+struct RouterStage {
+  AChunks<XF32> x;
+  u32x4_t bh[4], bl[4];
 };
 
 template <bool XF32>
@@ -184,43 +195,65 @@ __global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Blo[BN * LDK];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int t0 = blockIdx.y * BM, e0 = blockIdx.x * BN;
-  f32x16 acc[2][2] = {};
-  for (int k0 = 0; k0 < a.H; k0 += BK) {
-    // A: 128 rows x 64 bf16 (8 chunks of 16 B per row)
+  const int kb = blockIdx.z * a.kper, ke = min(a.H, kb + a.kper);
+  const int kc = tid & 7;
+  // chunk i of this thread: row (tid >> 3) + 32 i, 8 elements at column 8 kc.
+  // Rows past T or E repeat the last row (in bounds; results not stored).
+  const void* xs[4];
+  uint32_t wo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const size_t xo = (size_t)min(t0 + r, a.T - 1) * a.H + kc * 8;
+    xs[i] = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + xo)
+                 : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + xo);
+    wo[i] = (uint32_t)min(e0 + r, a.E - 1) * (uint32_t)a.H + kc * 8;
+  }
+  RouterStage<XF32> st;
+  auto load_step = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
-      const int t = t0 + r;
-      uint4 hv = make_uint4(0, 0, 0, 0), lv = make_uint4(0, 0, 0, 0);
-      if (t < a.T) {
-        if constexpr (XF32) {
-          const float* src = reinterpret_cast<const float*>(a.x) + (size_t)t * a.H + k0 + kc * 8;
-          float f[8];
-          *reinterpret_cast<float4*>(f) = *reinterpret_cast<const float4*>(src);
-          *reinterpret_cast<float4*>(f + 4) = *reinterpret_cast<const float4*>(src + 4);
-          hv = to_bf16x8(f, &lv);
-        } else {
-          hv = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H + k0 + kc * 8);
-        }
+      if constexpr (XF32) {
+        const float* f = reinterpret_cast<const float*>(xs[i]) + k0;
+        st.x.v[2 * i] = *reinterpret_cast<const f32x4_t*>(f);
+        st.x.v[2 * i + 1] = *reinterpret_cast<const f32x4_t*>(f + 4);
+      } else {
+        st.x.v[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(xs[i]) + k0);
       }
-      *reinterpret_cast<uint4*>(Ahi + r * LDK + kc * 8) = hv;
-      if constexpr (XF32) *reinterpret_cast<uint4*>(Alo + r * LDK + kc * 8) = lv;
-      // B: router rows e0 + r, hi and lo planes
-      const int e = e0 + r;
-      uint4 bh = make_uint4(0, 0, 0, 0), bl = make_uint4(0, 0, 0, 0);
-      if (e < a.E) {
-        bh = *reinterpret_cast<const uint4*>(a.whi + (size_t)e * a.H + k0 + kc * 8);
-        bl = *reinterpret_cast<const uint4*>(a.wlo + (size_t)e * a.H + k0 + kc * 8);
+      st.bh[i] = *reinterpret_cast<const u32x4_t*>(a.whi + wo[i] + k0);
+      st.bl[i] = *reinterpret_cast<const u32x4_t*>(a.wlo + wo[i] + k0);
+    }
+  };
+  f32x16 acc[2][2] = {};
+  load_step(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = ((tid >> 3) + 32 * i) * LDK + kc * 8;
+      if constexpr (XF32) {
+        const f32x4_t f0 = st.x.v[2 * i], f1 = st.x.v[2 * i + 1];
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_bf16x2(f0.x, f0.y, &h0, &l0);
+        split_bf16x2(f0.z, f0.w, &h1, &l1);
+        split_bf16x2(f1.x, f1.y, &h2, &l2);
+        split_bf16x2(f1.z, f1.w, &h3, &l3);
+        *reinterpret_cast<u32x4_t*>(Ahi + o) = u32x4_t{h0, h1, h2, h3};
+        *reinterpret_cast<u32x4_t*>(Alo + o) = u32x4_t{l0, l1, l2, l3};
+      } else {
+        *reinterpret_cast<u32x4_t*>(Ahi + o) = st.x.v[i];
       }
-      *reinterpret_cast<uint4*>(Bhi + r * LDK + kc * 8) = bh;
-      *reinterpret_cast<uint4*>(Blo + r * LDK + kc * 8) = bl;
+      *reinterpret_cast<u32x4_t*>(Bhi + o) = st.bh[i];
+      *reinterpret_cast<u32x4_t*>(Blo + o) = st.bl[i];
     }
     __syncthreads();
+    load_step(min(k0 + BK, ke - BK));                // in flight during the MFMAs (last step repeats)
+    __builtin_amdgcn_sched_barrier(0);
     mma_step(Ahi, Bhi, acc, wm, wn, lane);
     mma_step(Ahi, Blo, acc, wm, wn, lane);
     if constexpr (XF32) mma_step(Alo, Bhi, acc, wm, wn, lane);
     __syncthreads();
   }
+  float* out = a.part + blockIdx.z * a.plane;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -229,50 +262,94 @@ __global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
       for (int v = 0; v < 16; ++v) {
         const int t = t0 + 64 * wm + 32 * mt + acc_row(v, lane);
         const int e = e0 + 64 * wn + 32 * nt + (lane & 31);
-        if (t < a.T && e < a.E) a.logits[(size_t)t * a.E + e] = acc[mt][nt][v] + (a.bias ? a.bias[e] : 0.f);
+        if (t < a.T && e < a.E) out[(size_t)t * a.E + e] = acc[mt][nt][v];
       }
 }
 
 // ------------------------------------------------------------------ routing
 struct TopkArgs {
   int T, E, k, nchunks;
+  int S;                  // router partial planes
+  size_t plane;           // elements between planes
+  const float* part;      // [S][T][E] partial logits
+  const float* bias;      // [E] or null
   Work w;
 };
 
-__global__ __launch_bounds__(256) void k_topk_chunks(TopkArgs a) {
+// logits of token t for ids lane + 64 i: the partial planes summed in plane
+// order, then the bias (ids past E read id E - 1 and are masked by the caller)
+template <int MAXV>
+__device__ inline void router_row(const TopkArgs& a, int t, float (&val)[MAXV]) {
+  const int lane = threadIdx.x & 63;
+  int eo[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) eo[i] = min(lane + 64 * i, a.E - 1);
+  const float* p = a.part + (size_t)t * a.E;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) val[i] = p[eo[i]];
+  for (int z = 1; z < a.S; ++z) {
+    const float* pz = p + z * a.plane;
+    float v[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) v[i] = pz[eo[i]];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) val[i] += v[i];
+  }
+  if (a.bias) {
+    float b[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) b[i] = a.bias[eo[i]];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) val[i] += b[i];
+  }
+}
+
+__device__ inline void token_topk(const TopkArgs& a, int t, int* sel, float* w, int* sel_lds) {
+  if (a.E <= 256) {
+    float v[4];
+    router_row<4>(a, t, v);
+    wave_topk_radix<4>(v, a.E, a.k, sel, w);
+  } else if (a.E <= 512) {
+    float v[8];
+    router_row<8>(a, t, v);
+    wave_topk_radix<8>(v, a.E, a.k, sel, w);
+  } else {
+    // one partial plane (the launch guarantees it) re-read per round
+    wave_topk_loop(a.part + (size_t)t * a.E, a.bias, a.E, a.k, sel, w, sel_lds);
+  }
+}
+
+// One chunk of CT tokens per workgroup, one wave per token: top-k ids
+// (ascending) and renormalised weights; then per expert the bitmask of the
+// chunk's tokens that chose it, which gives the chunk's expert histogram and
+// each pair's rank among the chunk's earlier tokens with the same expert.
+constexpr int TOPK_CHUNK_WAVES = 16;
+
+__global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs a) {
   extern __shared__ int lds_i[];
-  int* sel = lds_i;                 // [CT][k]
-  int* hist = sel + CT * a.k;       // [E]
-  __shared__ int s_sel[4][64];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int* sel = lds_i;                                            // [CT][k]
+  uint32_t* tmask = reinterpret_cast<uint32_t*>(sel + CT * a.k);  // [E]
+  __shared__ int s_sel[TOPK_CHUNK_WAVES][64];
+  const int wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x, tb = chunk * CT;
   const int k = a.k, E = a.E;
-  for (int tl = wv; tl < CT; tl += 4) {
+  static_assert(CT <= 32, "token masks are 32-bit");
+  for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
+  for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
     const int t = tb + tl;
-    if (t < a.T) {
-      wave_topk_any(a.w.logits + (size_t)t * E, E, k, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
-    }
+    if (t < a.T) token_topk(a, t, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
   }
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   const int nt = min(CT, a.T - tb);
   for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
     const int e = sel[i];
     a.w.topk_idx[(size_t)tb * k + i] = e;
-    atomicAdd(&hist[e], 1);
-    // rank among this chunk's earlier tokens that chose e (each token's ids are sorted)
-    const int tl = i / k;
-    int rank = 0;
-    for (int t2 = 0; t2 < tl; ++t2) {
-      const int* s2 = sel + t2 * k;
-      int lo = 0, hi = k;
-      while (lo < hi) { const int mid = (lo + hi) >> 1; if (s2[mid] < e) lo = mid + 1; else hi = mid; }
-      rank += (lo < k && s2[lo] == e);
-    }
-    a.w.pair_rank[(size_t)tb * k + i] = rank;
+    atomicOr(&tmask[e], 1u << (i / k));
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = hist[e];
+  for (int i = threadIdx.x; i < nt * k; i += blockDim.x)
+    a.w.pair_rank[(size_t)tb * k + i] = __popc(tmask[sel[i]] & ((1u << (i / k)) - 1u));
+  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = __popc(tmask[e]);
 }
 
 struct ScanArgs {
@@ -374,11 +451,6 @@ struct GemmArgs {
   int x_f32;
   Work w;
 };
-
-// A-tile chunks of one thread: 4 chunks of 8 bf16 (bf16 input) or of 8 fp32
-template <bool XF32> struct AChunks;
-template <> struct AChunks<false> { u32x4_t v[4]; };
-template <> struct AChunks<true> { f32x4_t v[8]; };
 
 template <int FMT, bool XF32>
 __global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
@@ -629,16 +701,31 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
 }  // namespace
 
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
+  // split K until the grid has about two workgroups per CU; the partial planes
+  // live in the per-pair output region, which is dead until the down GEMM
+  const int tiles = ((L.E + BN - 1) / BN) * ((c.T + BM - 1) / BM);
+  const int ksteps = L.H / BK;
+  const size_t plane = (size_t)c.T * L.E;
+  int S = 1;
+  if (L.E <= 512) {
+    S = std::min(std::min(8, ksteps), std::max(1, (512 + tiles - 1) / tiles));
+    while (S > 1 && (size_t)S * plane * 4 > W.ybf_bytes) --S;
+  }
+  const int kper = ((ksteps + S - 1) / S) * BK;
+  S = (L.H + kper - 1) / kper;                       // no empty split
   RouterArgs r;
   r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
-  r.whi = L.router_hi; r.wlo = L.router_lo; r.bias = L.router_b; r.logits = W.logits;
-  dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM);
+  r.kper = kper; r.plane = plane;
+  r.whi = L.router_hi; r.wlo = L.router_lo;
+  r.part = S > 1 ? reinterpret_cast<float*>(W.ybf) : W.logits;
+  dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM, S);
   if (c.x_f32) launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
   else launch(tr, k_router_gemm<false>, grid, dim3(256), 0, s, r);
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
+  t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b;
   const size_t lds = ((size_t)CT * L.k + L.E) * 4;
-  launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(256), lds, s, t);
+  launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(64 * TOPK_CHUNK_WAVES), lds, s, t);
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
   launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);

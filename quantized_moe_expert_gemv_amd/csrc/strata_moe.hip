@@ -55,6 +55,9 @@ int check_config(const strata_moe_config* c) {
   if (c->qfmt != STRATA_Q2 && c->qfmt != STRATA_Q3 && c->qfmt != STRATA_Q4)
     return fail(STRATA_E_INVALID, "qfmt %d is not 2, 3 or 4", c->qfmt);
   if (c->hidden <= 0 || c->inter <= 0) return fail(STRATA_E_INVALID, "hidden and inter must be positive");
+  if (c->hidden > 65536 || c->inter > 65536)
+    return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be at most 65536", c->hidden,
+                c->inter);
   if (c->hidden % 256 || c->inter % 256)
     return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 256",
                 c->hidden, c->inter);
@@ -268,6 +271,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.xparts = reinterpret_cast<_Float16*>(ws + p.xparts);
   W.wtab = reinterpret_cast<float*>(ws + p.wtab);
   W.ybf = reinterpret_cast<uint16_t*>(ws + p.y);
+  W.ybf_bytes = p.total - p.y;                 // the last region
   W.nchunks = p.nchunks;
   W.max_tiles = p.max_tiles;
 
