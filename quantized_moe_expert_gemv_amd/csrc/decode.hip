@@ -11,13 +11,13 @@
 // instructions of one wave, not the bytes):
 //   k_route_gemv  router GEMV, one workgroup per expert row split over its
 //                 waves; each workgroup also writes a slice of the tokens as
-//                 three fp16 parts (x = p0 + p1 + p2 exactly);
+//                 two fp16 parts (x = p0 + p1 to 22 significant bits);
 //   k_topk        one workgroup per token: two-level radix selection of the k
 //                 largest logits and the renormalised softmax weights;
 //   k_gateup      one workgroup per (active expert, 32 rows of I): it finds
 //                 its expert from the top-k ids (experts chosen by any token,
 //                 ascending, then the shared one), its waves split the H
-//                 superblocks; writes silu(g) * u as three fp16 parts per
+//                 superblocks; writes silu(g) * u as two fp16 parts per
 //                 (active expert, token);
 //   k_down        one workgroup per 16 rows of H; waves take (active expert,
 //                 superblock) units with the next units' loads in flight,
@@ -29,13 +29,15 @@
 // token->expert permutation that the expert kernels do not need).
 //
 // The multiply-accumulate runs on the matrix cores (16x16x32 fp16 MFMA, fp32
-// accumulation) with exact operands: the code q of a weight becomes the fp16
-// value q (2-bit codes through the FP4->fp16 conversion, Q3 as a 2-bit and a
-// 1-bit plane) or (q - 8)/16 (Q4, magic-number construction), the
-// activations enter as their three fp16 parts, and the per-block offset
-// -c * sum_j x_j comes from one extra MFMA against a constant operand.  Every
-// product is exact; only the fp32 accumulation rounds.  The fp16 block scale
-// d multiplies each block's 16x16 result in fp32.
+// accumulation): the code q of a weight becomes the fp16 value q (2-bit codes
+// through the FP4->fp16 conversion, Q3 as a 2-bit and a 1-bit plane) or
+// (q - 8)/16 (Q4, magic-number construction), exactly; the activations enter
+// as two fp16 parts (16 A-operand rows: 2 parts x up to 8 tokens, so every
+// decode call is one pass over the weights), which carry 22 significant bits
+// (bf16 inputs exactly); the per-block offset -c * sum_j x_j comes from one
+// extra MFMA against a constant operand.  Every product is exact; the fp32
+// accumulation and the 2^-22 activation split are the only roundings.  The
+// fp16 block scale d multiplies each block's 16x16 result in fp32.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,7 +50,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int DESC = 2;    // ints per active expert for the down kernel: expert id, token mask
 constexpr int WTAB = 8;    // routing weights per active expert, indexed by token
-constexpr int NPART = 3;   // fp16 parts of an fp32 activation
+constexpr int NPART = 2;   // fp16 parts of an fp32 activation
+constexpr uint32_t OOB = 0x80000000u;   // buffer offset past every record: the load returns 0
 
 __device__ inline float4 bf16x4(uint32_t lo, uint32_t hi) {
   return make_float4(__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
@@ -60,23 +63,26 @@ __device__ inline uint32_t comp(const uint4& v, int i) {
 }
 
 // x = p0 + p1 + p2 with fp16 parts (exact for fp32 values of fp16 range)
-__device__ inline void split3(float x, _Float16* p) {
+// x as two fp16 parts: p0 = fp16(x), p1 = fp16(x - p0) (the difference is
+// exact), so |x - p0 - p1| <= 2^-22 |x| while x - p0 is an fp16 normal
+__device__ inline void split2(float x, _Float16* p) {
   p[0] = (_Float16)x;
-  float r = x - (float)p[0];
-  p[1] = (_Float16)r;
-  r -= (float)p[1];
-  p[2] = (_Float16)r;
+  p[1] = (_Float16)(x - (float)p[0]);
 }
+
+// The A operand of the 16x16x32 MFMAs: row r = lane % 16 holds part r / 8 of
+// token r % 8 (every token of a call, T <= 8)
+__device__ inline int arow_token(int lane) { return lane & 7; }
+__device__ inline int arow_part(int lane) { return (lane & 15) >> 3; }
+// D element v of a lane: row 4 (lane / 16) + v, i.e. part lane / 32 of token
+// 4 ((lane / 16) % 2) + v; column lane % 16
+__device__ inline int drow_token(int lane, int v) { return 4 * ((lane >> 4) & 1) + v; }
 
 __device__ inline f32x4 mfma(const f16x8& a, const f16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ inline f16x8 as_f16x8(const uint4& v) { return __builtin_bit_cast(f16x8, v); }
-
-__device__ inline uint4 mask_u4(const uint4& v, uint32_t m) {
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
 
 __device__ inline f16x8 join(half2_t a, half2_t b, half2_t c, half2_t d) {
   f16x8 r;
@@ -261,16 +267,15 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     const float s = wave_sum(acc[t]);
     if (lane == 0) part[wv][t] = s;
   }
-  // this workgroup's slice of the token rows as fp16 parts [t][part][H]
+  // this workgroup's slice of the token rows as fp16 parts [part][t][H]
   const int n = TT * H, chunk = (n + E - 1) / E;
   for (int i = e * chunk + tid; i < min(n, (e + 1) * chunk); i += blockDim.x) {
-    const int t = i / H, h = i - t * H;
     const float v = XF32 ? reinterpret_cast<const float*>(a.x)[i]
                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[i]);
     _Float16 p[NPART];
-    split3(v, p);
+    split2(v, p);
 #pragma unroll
-    for (int q = 0; q < NPART; ++q) a.xparts[((size_t)t * NPART + q) * H + h] = p[q];
+    for (int q = 0; q < NPART; ++q) a.xparts[(size_t)q * n + i] = p[q];
   }
   __syncthreads();
   if (tid < TT) {
@@ -293,7 +298,10 @@ __device__ inline void wave_select(const uint32_t (&u)[V], int k, bool (&sel)[V]
     int cnt = 0;
 #pragma unroll
     for (int i = 0; i < V; ++i) cnt += __popcll(__ballot(u[i] >= cand));
-    if (cnt >= k) tau = cand;
+    if (cnt >= k) {
+      tau = cand;
+      if (cnt == k) break;                 // {u >= tau} is the selection
+    }
   }
   int gt = 0;
 #pragma unroll
@@ -526,7 +534,7 @@ __device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits,
 // expert; its waves split the H superblocks, each wave G gate + G up slabs
 // per superblock (sharing one activation operand); partial sums meet in LDS.
 // The workgroup first finds its expert from the top-k ids.  Output:
-// silu(g) * u as three fp16 parts, rows (active expert, token) of the
+// silu(g) * u as two fp16 parts, rows (active expert, part, token) of the
 // activation buffer.  G = 4 when many experts are active (fewer, larger
 // workgroups: all of them resident at once), else 2.
 
@@ -548,38 +556,51 @@ __device__ inline void gu_aload_lds(rsrc_t xr, uint32_t xvoff, int sb, uint4* ld
                                              (uint32_t)sb * SB_WEIGHTS * 2, 0, 0);
 }
 
+// vector-memory instructions gu_load issues (codes, then the scales, per slab)
+template <int FMT, int G>
+constexpr int gu_load_count() { return 2 * G * (FMT == 2 ? 2 : 3); }
+
+// The weights of one superblock, requested in the order the compute takes
+// them: slab pairs (gate j, up j).
 template <int FMT, int G>
 __device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int sb, int lane, GuStage<FMT, G>& st) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
   const int r = lane & 15;
 #pragma unroll
-  for (int s = 0; s < 2 * G; ++s) {
-    const uint32_t soff = (s < G ? 0u : up_base) + (uint32_t)((G * gp + (s % G)) * nsb + sb) * SLAB;
-    bload_codes<FMT>(wr, soff, lane, st.cd[s]);
-    st.sc[s] = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int s = h * G + j;
+      const uint32_t soff = (h ? up_base : 0u) + (uint32_t)((G * gp + j) * nsb + sb) * SLAB;
+      bload_codes<FMT>(wr, soff, lane, st.cd[s]);
+      st.sc[s] = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
+    }
+    __builtin_amdgcn_sched_barrier(0);               // keep the request order
   }
 }
 
-// One superblock: per block, the activation operand from LDS, the offset
-// MFMA, the 2G product MFMAs, then the 2G x 4 scale FMAs.
-template <int FMT, int G>
-__device__ inline void gu_compute(const GuStage<FMT, G>& st, const uint4* lds_a, int lane, float (&acc)[2 * G][4]) {
-  constexpr int GU_SLABS = 2 * G;
-  // the LDS copies must have landed: the compiler does not track the
-  // buffer->LDS loads against these reads (the memory clobber also keeps
-  // every LDS read below this point)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Slab pairs J0 .. J0 + NJ - 1 of one superblock: per block, the activation
+// operand from LDS, the offset MFMA, the 2 NJ product MFMAs (independent, so
+// their latency overlaps), then their scale FMAs.
+template <int FMT, int G, int J0, int NJ>
+__device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const uint4* lds_a, int lane,
+                                        float (&acc)[2 * G][4]) {
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
     const f16x8 af = as_f16x8(lds_a[BB * 64 + lane]);                             \
     const f32x4 off = block_offset<FMT>(af);                                      \
-    f32x4 d[GU_SLABS];                                                            \
-    _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s)                          \
-      d[s] = block_product<FMT, BB>(af, st.cd[s], off);                           \
-    _Pragma("unroll") for (int s = 0; s < GU_SLABS; ++s) {                        \
-      const float ds = block_scale<FMT, BB>(st.sc[s]);                            \
-      _Pragma("unroll") for (int v = 0; v < 4; ++v)                               \
-        acc[s][v] = fmaf(ds, d[s][v], acc[s][v]);                                 \
+    f32x4 d[2 * NJ];                                                              \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                              \
+      d[2 * j] = block_product<FMT, BB>(af, st.cd[J0 + j], off);                  \
+      d[2 * j + 1] = block_product<FMT, BB>(af, st.cd[G + J0 + j], off);          \
+    }                                                                             \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                              \
+      const float sg = block_scale<FMT, BB>(st.sc[J0 + j]);                       \
+      const float su = block_scale<FMT, BB>(st.sc[G + J0 + j]);                   \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                             \
+        acc[J0 + j][v] = fmaf(sg, d[2 * j][v], acc[J0 + j][v]);                   \
+        acc[G + J0 + j][v] = fmaf(su, d[2 * j + 1][v], acc[G + J0 + j][v]);       \
+      }                                                                           \
     }                                                                             \
   }
   STRATA_BLOCK(0) STRATA_BLOCK(1) STRATA_BLOCK(2) STRATA_BLOCK(3)
@@ -587,25 +608,52 @@ __device__ inline void gu_compute(const GuStage<FMT, G>& st, const uint4* lds_a,
 #undef STRATA_BLOCK
 }
 
-template <int FMT, int NTG, int G>
+// One superblock in halves of G/2 slab pairs, each as soon as its weights
+// have arrived (the compiler waits on the half's registers; the other half
+// stays in flight).
+template <int FMT, int G>
+__device__ inline void gu_compute(const GuStage<FMT, G>& st, const uint4* lds_a, int lane, float (&acc)[2 * G][4]) {
+  // the activation operand was requested by buffer->LDS loads before the
+  // gu_load_count() weight loads: once no more than those are outstanding it
+  // has landed (the compiler does not track these loads; the memory clobber
+  // keeps every LDS read below this point)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(gu_load_count<FMT, G>()) : "memory");
+  gu_compute_pairs<FMT, G, 0, G / 2>(st, lds_a, lane, acc);
+  // (the empty memory clobber makes the second half re-read the operands
+  // from LDS instead of keeping every block's operand in registers)
+  asm volatile("" ::: "memory");
+  gu_compute_pairs<FMT, G, G / 2, G / 2>(st, lds_a, lane, acc);
+}
+
+template <int FMT, int G>
 __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
   // per wave 8 KiB of LDS: its superblock's activation operand, then its
-  // partial sums [GU_SLABS][48 lanes] x 4 tokens
+  // partial sums [GU_SLABS][64 lanes] x 4
   extern __shared__ float4 red4[];
   float* red = reinterpret_cast<float*>(red4);
   __shared__ uint32_t s_bits[128];
   __shared__ int s_info[4];
   __shared__ float s_wts[DECODE_MAX_T];
   const int u = blockIdx.y, gp = blockIdx.x;
-  int e, U;
-  uint32_t mask;
-  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U)) return;
   const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = lane >> 4;                          // K-slice
-  const int part = (lane & 15) >> 2, jj = lane & 3;  // A-operand row of this lane: (part, token)
+  const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(NPART * T * H * 2));
+  uint4* lds_a = reinterpret_cast<uint4*>(red4) + wv * 512;
+  // A row (part, token): rows of tokens past T read past the buffer (zeros)
+  const int tok = arow_token(lane);
+  const uint32_t xvoff = tok < T ? (uint32_t)(((arow_part(lane) * T + tok) * H + 8 * ks) * 2) : OOB;
+  // the first superblock's activation operand does not depend on the expert:
+  // request it before the routing lookup (wv < nw <= nsb)
+  gu_aload_lds(xr, xvoff, wv, lds_a);
+  int e, U;
+  uint32_t mask;
+  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
+    return;
+  }
   if (gp == 0) {
     // routing of this active expert for the down kernel
     if (threadIdx.x == 0) {
@@ -616,59 +664,46 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     if (threadIdx.x < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + threadIdx.x] = s_wts[threadIdx.x];
   }
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
-  const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(T * NPART * H * 2));
   const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
 
-  uint4* lds_a = reinterpret_cast<uint4*>(red4) + wv * 512;
-  for (int tg = 0; tg < NTG; ++tg) {                // token groups of 4
-    if (tg > 0) __syncthreads();                     // the previous group's sums are read
-    float acc[GU_SLABS][4];
+  float acc[GU_SLABS][4];
 #pragma unroll
-    for (int s = 0; s < GU_SLABS; ++s)
+  for (int s = 0; s < GU_SLABS; ++s)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[s][v] = 0.f;
-    // A row (part, token j): rows past T and the unused fourth part read a
-    // real row (same cache lines as other lanes; their results are not used)
-    const int jr = min(4 * tg + jj, T - 1), pr = min(part, NPART - 1);
-    const uint32_t xvoff = (uint32_t)(((jr * NPART + pr) * H + 8 * ks) * 2);
-    for (int sb = wv; sb < nsb; sb += nw) {
-      GuStage<FMT, G> st;
-      gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
-      gu_aload_lds(xr, xvoff, sb, lds_a);
-      __builtin_amdgcn_sched_barrier(0);            // every load of the stage issued before any use
-      gu_compute<FMT, G>(st, lds_a, lane, acc);
+    for (int v = 0; v < 4; ++v) acc[s][v] = 0.f;
+  for (int sb = wv; sb < nsb; sb += nw) {
+    // the activation operand first (the first one is already requested),
+    // then the weights; the compute waits for each part as it needs it
+    if (sb > wv) gu_aload_lds(xr, xvoff, sb, lds_a);
+    __builtin_amdgcn_sched_barrier(0);
+    GuStage<FMT, G> st;
+    gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
+    gu_compute<FMT, G>(st, lds_a, lane, acc);
+  }
+  // raw 16x16 results to this wave's LDS region (its operand is consumed)
+  float4* dst = reinterpret_cast<float4*>(red) + (size_t)wv * 512 + lane;
+#pragma unroll
+  for (int s = 0; s < GU_SLABS; ++s) dst[s * 64] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
+  __syncthreads();
+  // sums over waves and parts, SwiGLU, fp16 parts of the result
+  for (int idx = threadIdx.x; idx < 16 * GU_GROUPS * T; idx += blockDim.x) {
+    const int row = idx & 15, gi = (idx >> 4) % GU_GROUPS, t = idx / (16 * GU_GROUPS);
+    if (!((mask >> t) & 1u)) continue;
+    // D row (part q, token t) sits in lane 16 (2q + t / 4) + row, element t % 4
+    const int l0 = 16 * (t >> 2) + row, l1 = l0 + 32, v = t & 3;
+    float g = 0.f, uu = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float* rg = red + (size_t)w * 2048 + (size_t)gi * 256 + v;
+      const float* ru = red + (size_t)w * 2048 + (size_t)(GU_GROUPS + gi) * 256 + v;
+      g += rg[4 * l0] + rg[4 * l1];
+      uu += ru[4 * l0] + ru[4 * l1];
     }
-    // raw 16x16 results to this wave's LDS region: lane l holds (part l/16,
-    // token v) of row l%16 (lanes 48..63 hold the unused fourth part and are not kept)
-    float4* dst = reinterpret_cast<float4*>(red) + (size_t)wv * 512 + lane;
-    if (lane < 48) {
+    const float act = silu_f(g) * uu;
+    _Float16 p[NPART];
+    split2(act, p);
+    const int i = (GU_GROUPS * gp + gi) * 16 + row;
 #pragma unroll
-      for (int s = 0; s < GU_SLABS; ++s)
-        dst[s * 48] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
-    }
-    __syncthreads();
-    // sums over waves and parts, SwiGLU, fp16 parts of the result
-    for (int idx = threadIdx.x; idx < 4 * GU_GROUPS * 16; idx += blockDim.x) {
-      const int row = idx & 15, gi = (idx >> 4) % GU_GROUPS, v = idx / (16 * GU_GROUPS);
-      const int t = 4 * tg + v;
-      if (t >= T || !((mask >> t) & 1u)) continue;
-      float g = 0.f, uu = 0.f;
-      for (int w = 0; w < nw; ++w) {
-        const float* rg = red + (size_t)w * 2048 + ((size_t)gi * 48 + row) * 4 + v;
-        const float* ru = red + (size_t)w * 2048 + ((size_t)(GU_GROUPS + gi) * 48 + row) * 4 + v;
-#pragma unroll
-        for (int q = 0; q < NPART; ++q) {
-          g += rg[q * 64];
-          uu += ru[q * 64];
-        }
-      }
-      const float act = silu_f(g) * uu;
-      _Float16 p[NPART];
-      split3(act, p);
-      const int i = (GU_GROUPS * gp + gi) * 16 + row;
-#pragma unroll
-      for (int q = 0; q < NPART; ++q) a.w.actp[(((size_t)u * T + t) * NPART + q) * I + i] = p[q];
-    }
+    for (int q = 0; q < NPART; ++q) a.w.actp[(((size_t)u * NPART + q) * T + t) * I + i] = p[q];
   }
 }
 
@@ -686,10 +721,8 @@ template <int FMT> struct DownUnit {
 };
 
 template <int FMT>
-__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, int tg,
-                                 DownUnit<FMT>& du) {
+__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, DownUnit<FMT>& du) {
   const int lane = threadIdx.x & 63, r = lane & 15, ks = lane >> 4;
-  const int part = (lane & 15) >> 2, jj = lane & 3;
   const int u = unit / nsb, sb = unit - u * nsb;
   const int e = __builtin_amdgcn_readfirstlane(ldesc[2 * u]);
   const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[2 * u + 1]);
@@ -697,23 +730,18 @@ __device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit
   const uint32_t soff = (uint32_t)(down_off(FMT, a.H, a.I) + ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256));
   bload_codes<FMT>(wr, soff, lane, du.cd);
   du.sc = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
-  // A row (part, token t = 4tg + jj): the activation of (expert u, token t), if routed
-  // (rows of tokens not routed to u, and the unused fourth part, read the
-  // row of u's first token in the same cache lines, and are zeroed)
-  const int t = 4 * tg + jj;
+  // A row (part, token t): the activation of (expert u, token t); tokens past
+  // T or not routed to u read past the buffer (zeros)
+  const int t = arow_token(lane);
   const bool routed = t < a.T && ((mask >> t) & 1u);
-  const int tr = routed ? t : __builtin_ctz(mask);
   const rsrc_t ar = make_rsrc(a.w.actp, a.actp_bytes);
-  const uint32_t voff = (uint32_t)(((tr * NPART + min(part, NPART - 1)) * a.I + 8 * ks) * 2);
-  const uint32_t asoff = (uint32_t)(((size_t)u * a.T * NPART * a.I + (size_t)sb * SB_WEIGHTS) * 2);
+  const uint32_t voff = routed ? (uint32_t)(((arow_part(lane) * a.T + t) * a.I + 8 * ks) * 2) : OOB;
+  const uint32_t asoff = (uint32_t)(((size_t)u * NPART * a.T * a.I + (size_t)sb * SB_WEIGHTS) * 2);
 #pragma unroll
   for (int bb = 0; bb < 8; ++bb) du.av[bb] = bload4(ar, voff + bb * BLOCK_W * 2, asoff);
-  const uint32_t amask = routed ? ~0u : 0u;
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) du.av[bb] = mask_u4(du.av[bb], amask);
 }
 
-// acc[v] += routing weight of token 4tg + v * (this unit's 16x16 product)
+// out[v] += routing weight of this lane's D-row token v * (this unit's 16x16 product)
 template <int FMT>
 __device__ inline void down_compute(const DownUnit<FMT>& du, const float* wt, float* out) {
   f32x4 dd[2];
@@ -739,7 +767,7 @@ __device__ inline void down_compute(const DownUnit<FMT>& du, const float* wt, fl
   }
 }
 
-template <int FMT, int NTG>
+template <int FMT>
 __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   extern __shared__ float4 lds_dn4[];
   float* lds_dn = reinterpret_cast<float*>(lds_dn4);
@@ -750,39 +778,37 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   const int g = blockIdx.x;
   int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [U][2]: expert, token mask
   float* lwt = reinterpret_cast<float*>(ldesc + 2 * U);         // [U][WTAB]
-  float* red = lds_dn + ((DESC + WTAB) * U + 3) / 4 * 4;        // [nw][NTG][64 lanes][4 tokens], 16-B aligned
+  float* red = lds_dn + ((DESC + WTAB) * U + 3) / 4 * 4;        // [nw][64 lanes][4], 16-B aligned
   for (int i = threadIdx.x; i < DESC * U; i += blockDim.x) ldesc[i] = a.w.udesc[i];
   for (int i = threadIdx.x; i < U * WTAB; i += blockDim.x) lwt[i] = a.w.wtab[i];
   __syncthreads();
 
   const int units = U * nsb;
-  for (int tg = 0; tg < NTG; ++tg) {
-    float out[4] = {0.f, 0.f, 0.f, 0.f};
-    DownUnit<FMT> b[DN_DEPTH];
-    // every load unconditional (unit index clamped; a repeated unit is
-    // loaded but not computed), so the loads of a step are all in flight
+  const int wt_off = 4 * ((lane >> 4) & 1);                     // token of this lane's D element 0
+  float out[4] = {0.f, 0.f, 0.f, 0.f};
+  DownUnit<FMT> b[DN_DEPTH];
+  // every load unconditional (unit index clamped; a repeated unit is
+  // loaded but not computed), so the loads of a step are all in flight
 #pragma unroll
-    for (int q = 0; q < DN_DEPTH; ++q) down_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, tg, b[q]);
-    for (int unit = wv; unit < units; unit += DN_DEPTH * nw) {
+  for (int q = 0; q < DN_DEPTH; ++q) down_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, b[q]);
+  for (int unit = wv; unit < units; unit += DN_DEPTH * nw) {
 #pragma unroll
-      for (int q = 0; q < DN_DEPTH; ++q) {
-        const int cu = unit + q * nw;
-        if (cu < units) down_compute<FMT>(b[q], lwt + (cu / nsb) * WTAB + 4 * tg, out);
-        down_load<FMT>(a, ldesc, min(cu + DN_DEPTH * nw, units - 1), nsb, g, tg, b[q]);
-      }
+    for (int q = 0; q < DN_DEPTH; ++q) {
+      const int cu = unit + q * nw;
+      if (cu < units) down_compute<FMT>(b[q], lwt + (cu / nsb) * WTAB + wt_off, out);
+      down_load<FMT>(a, ldesc, min(cu + DN_DEPTH * nw, units - 1), nsb, g, b[q]);
     }
-    reinterpret_cast<float4*>(red)[((size_t)wv * NTG + tg) * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
   }
+  reinterpret_cast<float4*>(red)[(size_t)wv * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
   __syncthreads();
-  for (int idx = threadIdx.x; idx < NTG * 4 * 16; idx += blockDim.x) {
-    const int row = idx & 15, v = (idx >> 4) & 3, tg = idx >> 6;
-    const int t = 4 * tg + v;
-    if (t >= T) continue;
+  for (int idx = threadIdx.x; idx < 16 * T; idx += blockDim.x) {
+    const int row = idx & 15, t = idx >> 4;
+    // D row (part q, token t) sits in lane 16 (2q + t / 4) + row, element t % 4
+    const int l0 = 16 * (t >> 2) + row, l1 = l0 + 32, v = t & 3;
     float s = 0.f;
     for (int w = 0; w < nw; ++w) {
-      const float* r = red + (((size_t)w * NTG + tg) * 64 + row) * 4 + v;
-#pragma unroll
-      for (int q = 0; q < NPART; ++q) s += r[q * 64];
+      const float* r = red + (size_t)w * 256 + v;
+      s += r[4 * l0] + r[4 * l1];
     }
     const int h = g * 16 + row;
     const size_t o = (size_t)t * H + h;
@@ -795,8 +821,8 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   }
 }
 
-template <int FMT, int NTG>
-hipError_t launch_experts_t(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
+template <int FMT>
+hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   ExpertArgs a;
   a.packed = L.packed;
   a.stride = L.expert_stride;
@@ -815,31 +841,26 @@ hipError_t launch_experts_t(const Layer& L, const Work& W, const Call& c, hipStr
   const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
   const size_t lds_gu = (size_t)nwg * 8192;                     // <= 80 KiB: ceiling raised at create
-  const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * NTG * 64 * 4 * 4;
+  const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * 64 * 4 * 4;
   const dim3 ggu(L.I / (16 * G), umax);
   if constexpr (FMT == 2) {
-    if (wide) launch(tr, k_gateup<FMT, NTG, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
-    else launch(tr, k_gateup<FMT, NTG, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    if (wide) launch(tr, k_gateup<FMT, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    else launch(tr, k_gateup<FMT, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
   } else {
-    launch(tr, k_gateup<FMT, NTG, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    launch(tr, k_gateup<FMT, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
   }
-  launch(tr, k_down<FMT, NTG>, dim3(L.H / 16), dim3(64 * DN_WAVES), lds_dn, s, a);
+  launch(tr, k_down<FMT>, dim3(L.H / 16), dim3(64 * DN_WAVES), lds_dn, s, a);
   return hipGetLastError();
 }
 
 template <int FMT>
-hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
-  return c.T <= 4 ? launch_experts_t<FMT, 1>(L, W, c, s, tr) : launch_experts_t<FMT, 2>(L, W, c, s, tr);
-}
-
-template <int FMT, int NTG>
 hipError_t raise_gateup_lds() {
   const int want = 96 * 1024;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, NTG, 2>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, 2>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, want);
   if constexpr (FMT == 2) {
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, NTG, 4>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, 4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, want);
   }
   return e;
@@ -856,12 +877,9 @@ hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
 
 // The gate/up kernels keep up to 80 KiB of dynamic LDS (8 KiB per wave).
 hipError_t prepare_decode_kernels() {
-  hipError_t e = raise_gateup_lds<2, 1>();
-  if (e == hipSuccess) e = raise_gateup_lds<2, 2>();
-  if (e == hipSuccess) e = raise_gateup_lds<3, 1>();
-  if (e == hipSuccess) e = raise_gateup_lds<3, 2>();
-  if (e == hipSuccess) e = raise_gateup_lds<4, 1>();
-  if (e == hipSuccess) e = raise_gateup_lds<4, 2>();
+  hipError_t e = raise_gateup_lds<2>();
+  if (e == hipSuccess) e = raise_gateup_lds<3>();
+  if (e == hipSuccess) e = raise_gateup_lds<4>();
   return e;
 }
 

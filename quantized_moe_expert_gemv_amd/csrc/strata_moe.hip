@@ -109,9 +109,9 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   const size_t Td = T < STRATA_DECODE_MAX_T ? T : STRATA_DECODE_MAX_T;
   const size_t act_prefill = slots * I * 2;                                   // bf16 rows
   const size_t umax = (Td * k < E ? Td * k : E) + (size_t)c.n_shared;
-  const size_t act_decode = umax * Td * 3 * I * 2;                             // fp16 parts
+  const size_t act_decode = umax * Td * 2 * I * 2;                             // two fp16 parts
   p.act = take(act_prefill > act_decode ? act_prefill : act_decode);
-  p.xparts = take(Td * 3 * H * 2);
+  p.xparts = take(Td * 2 * H * 2);
   p.y = take(slots * H * 2);
   p.total = o;
   return p;
