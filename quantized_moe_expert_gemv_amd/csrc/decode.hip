@@ -9,8 +9,8 @@
 // Four launches per forward call, each with many short waves (the time of a
 // kernel this small is the longest chain of dependent memory round trips and
 // instructions of one wave, not the bytes):
-//   k_route_gemv  router GEMV, one workgroup per expert row split over its
-//                 waves; each workgroup also writes a slice of the tokens as
+//   k_route_gemv  router GEMV, one workgroup per 1 or 2 expert rows split over
+//                 its waves; each workgroup also writes a slice of the tokens as
 //                 two fp16 parts (x = p0 + p1 to 22 significant bits);
 //   k_topk        one workgroup per token: two-level radix selection of the k
 //                 largest logits and the renormalised softmax weights;
@@ -223,29 +223,40 @@ __device__ inline float4 x_quad(const void* x, int H, int t, int q) {
   return bf16x4(v.x, v.y);
 }
 
-// One workgroup per expert row; its waves split the row into float4 columns
-// (strided, so every load instruction of a wave reads 1 KiB contiguously) and
-// meet in LDS.  Workgroup e also writes its slice of the tokens as fp16 parts.
-// TT = T and the input type are template constants so that every load is
-// unconditional (clamped into bounds) and all of a batch are in flight
-// together.
+// Expert rows per router workgroup: every wave reads its columns of the
+// tokens once for all of them (fewer register batches for more tokens)
+constexpr int route_rows(int T) { return T <= 4 ? 2 : 1; }
+
+// route_rows(T) expert rows per workgroup; its waves split the rows into
+// float4 columns (strided, so every load instruction of a wave reads 1 KiB
+// contiguously) and meet in LDS.  Each workgroup also writes its slice of the
+// tokens as fp16 parts.  TT = T and the input type are template constants so
+// that every load is unconditional (clamped into bounds) and all of a batch
+// are in flight together.
 template <int TT, bool XF32>
 __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
-  __shared__ float part[ROUTE_WAVES][TT];
+  constexpr int RR = route_rows(TT);
+  __shared__ float part[ROUTE_WAVES][RR][TT];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.H, E = a.E, e = blockIdx.x;
+  const int H = a.H, E = a.E, e0 = blockIdx.x * RR;
   const int nq = H >> 2;
-  const float4* row = reinterpret_cast<const float4*>(a.Wr + (size_t)e * H);
-  float acc[TT];
+  const float4* rows[RR];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = 0.f;
+  for (int r = 0; r < RR; ++r)      // rows past E repeat the last one (computed, not stored)
+    rows[r] = reinterpret_cast<const float4*>(a.Wr + (size_t)min(e0 + r, E - 1) * H);
+  float acc[RR][TT];
+#pragma unroll
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
   for (int q0 = tid; q0 < nq; q0 += ROUTE_BATCH * 64 * ROUTE_WAVES) {
-    float4 w[ROUTE_BATCH];
+    float4 w[ROUTE_BATCH][RR];
     float4 xv[ROUTE_BATCH][TT];
 #pragma unroll
     for (int j = 0; j < ROUTE_BATCH; ++j) {
       const int q = min(q0 + j * 64 * ROUTE_WAVES, nq - 1);
-      w[j] = row[q];
+#pragma unroll
+      for (int r = 0; r < RR; ++r) w[j][r] = rows[r][q];
 #pragma unroll
       for (int t = 0; t < TT; ++t) xv[j][t] = x_quad<XF32>(a.x, H, t, q);
     }
@@ -253,23 +264,27 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     for (int j = 0; j < ROUTE_BATCH; ++j) {
       const float m = (q0 + j * 64 * ROUTE_WAVES < nq) ? 1.f : 0.f;   // clamped duplicates count 0
 #pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        float d = w[j].x * xv[j][t].x;
-        d = fmaf(w[j].y, xv[j][t].y, d);
-        d = fmaf(w[j].z, xv[j][t].z, d);
-        d = fmaf(w[j].w, xv[j][t].w, d);
-        acc[t] = fmaf(m, d, acc[t]);
-      }
+      for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          float d = w[j][r].x * xv[j][t].x;
+          d = fmaf(w[j][r].y, xv[j][t].y, d);
+          d = fmaf(w[j][r].z, xv[j][t].z, d);
+          d = fmaf(w[j][r].w, xv[j][t].w, d);
+          acc[r][t] = fmaf(m, d, acc[r][t]);
+        }
     }
   }
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const float s = wave_sum(acc[t]);
-    if (lane == 0) part[wv][t] = s;
-  }
+  for (int r = 0; r < RR; ++r)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const float s = wave_sum(acc[r][t]);
+      if (lane == 0) part[wv][r][t] = s;
+    }
   // this workgroup's slice of the token rows as fp16 parts [part][t][H]
-  const int n = TT * H, chunk = (n + E - 1) / E;
-  for (int i = e * chunk + tid; i < min(n, (e + 1) * chunk); i += blockDim.x) {
+  const int n = TT * H, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
+  for (int i = b * chunk + tid; i < min(n, (b + 1) * chunk); i += blockDim.x) {
     const float v = XF32 ? reinterpret_cast<const float*>(a.x)[i]
                          : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[i]);
     _Float16 p[NPART];
@@ -278,11 +293,12 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     for (int q = 0; q < NPART; ++q) a.xparts[(size_t)q * n + i] = p[q];
   }
   __syncthreads();
-  if (tid < TT) {
+  if (tid < RR * TT) {
+    const int r = tid / TT, t = tid - r * TT, e = e0 + r;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < ROUTE_WAVES; ++w) s += part[w][tid];
-    a.logits[(size_t)tid * E + e] = s + (a.bias ? a.bias[e] : 0.f);
+    for (int w = 0; w < ROUTE_WAVES; ++w) s += part[w][r][t];
+    if (e < E) a.logits[(size_t)t * E + e] = s + (a.bias ? a.bias[e] : 0.f);
   }
 }
 
@@ -454,29 +470,43 @@ struct ExpertArgs {
   Work w;
 };
 
+// Workgroup barrier that orders LDS accesses only: global memory requests
+// (prefetches) stay in flight across it.
+__device__ inline void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Active expert u of this call: the experts chosen by any token in ascending
 // id order, then the shared expert (id E, every token, weight 1).  Every
 // thread of the workgroup returns the same values; false when u is past the
-// last one.  LDS: bits[ceil(E/32)], info[4], wts[DECODE_MAX_T].
+// last one.  LDS: bits[ceil(E/32)], info[4], wts[DECODE_MAX_T].  issue() is
+// called once the first pair loads are requested (memory requests that must
+// not delay them go there).
+template <typename F>
 __device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits, int* info, float* wts,
-                                     int& e_out, uint32_t& mask_out, int& n_active) {
+                                     int& e_out, uint32_t& mask_out, int& n_active, F&& issue) {
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
   const int T = a.T, k = a.k, E = a.E, P = T * k, nwords = (E + 31) >> 5;
-  // the pairs: P <= 512 <= ... one per thread when the workgroup has P threads;
-  // loaded unconditionally (clamped) so that the loads are all in flight
+  // the pairs: one per thread for the first blockDim.x; loaded
+  // unconditionally (clamped) so that the loads are all in flight
   const int p0 = min(tid, P - 1);
   const int my_e = a.w.topk_idx[p0];
   const float my_w = a.w.topk_w[p0];
+  __builtin_amdgcn_sched_barrier(0);
+  issue();
+  __builtin_amdgcn_sched_barrier(0);
   for (int i = tid; i < nwords; i += nt) bits[i] = 0u;
   if (tid < DECODE_MAX_T) wts[tid] = 0.f;
   if (tid == 0) info[1] = 0;
-  __syncthreads();
+  lds_sync();
   if (tid < P) atomicOr(&bits[my_e >> 5], 1u << (my_e & 31));
   for (int p = tid + nt; p < P; p += nt) {
     const int e = a.w.topk_idx[p];
     atomicOr(&bits[e >> 5], 1u << (e & 31));
   }
-  __syncthreads();
+  lds_sync();
   if (tid < 64) {
     // words lane and 64 + lane (E <= 4096); inclusive prefix counts in word order
     const uint32_t w0 = lane < nwords ? bits[lane] : 0u;
@@ -500,7 +530,7 @@ __device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits,
     }
     if (lane == 63) info[2] = s1;
   }
-  __syncthreads();
+  lds_sync();
   const int U = __builtin_amdgcn_readfirstlane(info[2]);    // the same in every lane: keep it scalar
   n_active = U + a.n_shared;
   if (u >= n_active) return false;
@@ -517,15 +547,15 @@ __device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits,
         wts[t] = a.w.topk_w[p];
       }
     }
-    __syncthreads();
+    lds_sync();
     e_out = __builtin_amdgcn_readfirstlane(e);
     mask_out = (uint32_t)__builtin_amdgcn_readfirstlane(info[1]);
   } else {
     e_out = E;
     mask_out = (1u << T) - 1u;
-    __syncthreads();
+    lds_sync();
     if (tid < T) wts[tid] = 1.f;
-    __syncthreads();
+    lds_sync();
   }
   return true;
 }
@@ -646,11 +676,11 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   const int tok = arow_token(lane);
   const uint32_t xvoff = tok < T ? (uint32_t)(((arow_part(lane) * T + tok) * H + 8 * ks) * 2) : OOB;
   // the first superblock's activation operand does not depend on the expert:
-  // request it before the routing lookup (wv < nw <= nsb)
-  gu_aload_lds(xr, xvoff, wv, lds_a);
+  // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
   int e, U;
   uint32_t mask;
-  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U)) {
+  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U,
+                     [&]() __attribute__((always_inline)) { gu_aload_lds(xr, xvoff, wv, lds_a); })) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
     return;
   }
@@ -891,8 +921,12 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
   switch (c.T) {
 #define STRATA_ROUTE(TT)                                                                 \
     case TT:                                                                               \
-      if (c.x_f32) launch(tr, k_route_gemv<TT, true>, dim3(L.E), dim3(64 * ROUTE_WAVES), 0, s, a); \
-      else launch(tr, k_route_gemv<TT, false>, dim3(L.E), dim3(64 * ROUTE_WAVES), 0, s, a);        \
+      if (c.x_f32)                                                                         \
+        launch(tr, k_route_gemv<TT, true>, dim3((L.E + route_rows(TT) - 1) / route_rows(TT)), \
+               dim3(64 * ROUTE_WAVES), 0, s, a);                                           \
+      else                                                                                 \
+        launch(tr, k_route_gemv<TT, false>, dim3((L.E + route_rows(TT) - 1) / route_rows(TT)), \
+               dim3(64 * ROUTE_WAVES), 0, s, a);                                           \
       break;
     STRATA_ROUTE(1) STRATA_ROUTE(2) STRATA_ROUTE(3) STRATA_ROUTE(4)
     STRATA_ROUTE(5) STRATA_ROUTE(6) STRATA_ROUTE(7) STRATA_ROUTE(8)

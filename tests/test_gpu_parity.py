@@ -60,6 +60,20 @@ def test_decode_shared_expert_tiny(B, fmt):
         assert rel_l2(out, ref) <= DECODE_TOL
 
 
+@pytest.mark.parametrize("E,k", [(64, 6), (300, 10), (512, 10), (1024, 8)])
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_decode_expert_counts(B, E, k, T):
+    """Expert counts below, at and above 512 (the top-k kernel's per-wave
+    id ranges: 1 to 4 logits per lane, padded ids past E)."""
+    hl, layer = tiny(2, E=E, k=k, max_tokens=16)
+    bits, xf = tokens(hl, 700 + T, T)
+    x = to_device_bf16(bits, DEV)
+    check_route(layer, hl, x, xf)
+    out = layer.forward(x).cpu().numpy()
+    ref, _ = hl.oracle(xf)
+    assert rel_l2(out, ref) <= DECODE_TOL, rel_l2(out, ref)
+
+
 @pytest.mark.parametrize("fmt", [2, 3, 4])
 @pytest.mark.parametrize("T", [1, 9, 130, 300])
 def test_prefill_route_and_forward_tiny(B, fmt, T):
