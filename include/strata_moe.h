@@ -144,6 +144,10 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
  * The full layer: out[T][H] fp32 (device) = moe(x), or with
  * STRATA_ACCUMULATE out += moe(x), or with STRATA_ADD_INPUT out = x + moe(x).
  * x and out must not overlap.  Stream-ordered and asynchronous.
+ * Precision: the decode kernels (T <= 8) multiply exact weight values by the
+ * activations carried as two fp16 parts (22 significant bits) with fp32
+ * accumulation; |x| and the SwiGLU outputs must stay below 65504 there.  The
+ * prefill kernels round weights and activations to bf16 (fp32 accumulation).
  */
 STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
                        float* out, uint32_t flags, void* stream);

@@ -29,15 +29,28 @@ KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_gateup", "gat
            ("k_gemm_down", "down_gemm"), ("k_combine", "combine")]
 
 
-def source_hash():
-    """sha256 over the kernel sources (csrc/*.hip, *.hpp), in name order."""
+# the sources each path's kernels are built from (a counter summary stays
+# valid while these are unchanged)
+PATH_SOURCES = {"decode": ("common.hpp", "decode.hip", "kernels.hpp"),
+                "prefill": ("common.hpp", "kernels.hpp", "prefill.hip")}
+DECODE_KERNELS = ("k_route_gemv", "k_topk", "k_permute", "k_gateup", "k_down")
+
+
+def source_hash(path=None):
+    """sha256 over the kernel sources of one path (all csrc/*.hip, *.hpp when
+    path is None), in name order."""
     h = hashlib.sha256()
     d = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    names = PATH_SOURCES[path] if path else [n for n in os.listdir(d) if n.endswith((".hip", ".hpp"))]
+    for name in sorted(names):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def kernel_path(kernel):
+    m = re.search(r"::(k_[A-Za-z0-9_]+)", kernel)
+    return "decode" if m and m.group(1) in DECODE_KERNELS else "prefill"
 
 
 def bench_name(kernel):
@@ -61,7 +74,7 @@ def stats(out, cmd, stats_csv):
         short = name if len(name) < 90 else name[:87] + "..."
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.2f} |")
-    lines += ["", f"kernel sources: {source_hash()}", ""]
+    lines += ["", f"kernel sources: decode {source_hash('decode')}, prefill {source_hash('prefill')}", ""]
     open(out, "w").write("\n".join(lines))
 
 
@@ -101,14 +114,15 @@ def traffic(out, cmd_f, cmd_w, fetch_csv, write_csv, cfetch_csv, cwrite_csv, cop
         short = k if len(k) < 70 else k[:67] + "..."
         lines.append(f"| `{short}` | {len(fv)} | {fm:.1f} | {wm:.1f} | {b:.0f} |")
         if name:
-            tagged.append((name, b, len(fv)))
-    lines += ["", f"kernel sources: {source_hash()}", ""]
+            tagged.append((name, kernel_path(k), b, len(fv)))
+    lines += ["", f"kernel sources: decode {source_hash('decode')}, prefill {source_hash('prefill')}", ""]
     merged = {}
-    for name, b, n in tagged:               # several instantiations of one kernel: dispatch-weighted mean
-        tb, tn = merged.get(name, (0.0, 0))
-        merged[name] = (tb + b * n, tn + n)
-    for name, (tb, tn) in sorted(merged.items()):
-        lines.append(f"traffic: kernel={name} bytes_per_dispatch={tb / tn:.0f} sources={source_hash()}")
+    for name, kp, b, n in tagged:           # several instantiations of one kernel: dispatch-weighted mean
+        tb, tn = merged.get((name, kp), (0.0, 0))
+        merged[(name, kp)] = (tb + b * n, tn + n)
+    for (name, kp), (tb, tn) in sorted(merged.items()):
+        lines.append(f"traffic: kernel={name} path={kp} bytes_per_dispatch={tb / tn:.0f} "
+                     f"sources={source_hash(kp)}")
     lines.append("")
     open(out, "w").write("\n".join(lines))
 
@@ -118,12 +132,12 @@ def read_traffic(path):
     when it is missing or was taken on other kernel sources."""
     if not os.path.exists(path):
         return {}
-    cur = source_hash()
+    cur = {p: source_hash(p) for p in PATH_SOURCES}
     res = {}
     for line in open(path):
         if line.startswith("traffic:"):
             kv = dict(p.split("=", 1) for p in line.split()[1:])
-            if kv.get("sources") == cur:
+            if kv.get("path") in cur and kv.get("sources") == cur[kv["path"]]:
                 res[kv["kernel"]] = float(kv["bytes_per_dispatch"])
     return res
 
@@ -135,6 +149,6 @@ if __name__ == "__main__":
     elif mode == "traffic":
         traffic(*sys.argv[2:11])
     elif mode == "hash":
-        print(source_hash())
+        print(source_hash(sys.argv[2] if len(sys.argv) > 2 else None))
     else:
         sys.exit(f"unknown mode {mode}")
