@@ -3,11 +3,12 @@
 // (devotd.net "Strata memory tiers", section 读取提示与写出回答时;
 // blog.5616760.com/0039.html, section 七).  Here every expert is resident in
 // HBM, so the chunk is a grouped, genuinely dense contraction and runs on
-// the gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+// the gfx950 matrix cores (fp32 accumulation):
 //
 //   k_router_gemm    x Wr^T, fp32-accurate from bf16 MFMA by splitting Wr
 //                    (and an fp32 x) into bf16 high + low parts; split over K
-//                    into partial planes when the tile grid is small
+//                    into partial planes when the tile grid is small; the
+//                    first column of tiles also writes the tokens as fp16
 //   k_topk_chunks    logits = sum of the planes + b; top-k + renormalised
 //                    softmax per token (one wave per token) and, per chunk of
 //                    32 tokens, the expert histogram and every pair's rank
@@ -18,14 +19,15 @@
 //   k_scatter        the stable permutation: slot of pair p =
 //                    offset[e] + base[e][chunk] + rank  (no atomics, so the
 //                    order is (expert, p) on every run)
-//   k_gemm_gateup    per work item: gathered token rows x rows of dequantised
-//                    gate|up weights staged as bf16 in LDS -> SwiGLU -> bf16
+//   k_gemm_gateup    per work item: gathered fp16 token rows x gate|up
+//                    weights dequantised to fp16 in registers -> SwiGLU -> fp16
 //   k_gemm_down      per work item: SwiGLU rows x dequantised down weights ->
 //                    per-pair output rows (bf16)
 //   k_combine        out[t] = sum_j w[t, j] y[slot(t, j)] (+ shared, residual)
 //
-// Dequantised weights d (q - c) are rounded to bf16 (8-bit mantissa) before
-// the MFMA; activations are bf16 (exact for bf16 inputs).
+// The expert GEMMs run on fp16 MFMA (16x16x32, fp32 accumulation): weights
+// d (q - c) rounded once to fp16 (11-bit mantissa), activations fp16 (bf16
+// inputs exactly, within the fp16 range).
 #include <algorithm>
 
 #include "common.hpp"
@@ -159,6 +161,26 @@ __device__ inline void dequant_rawb(const RawB<FMT>& r, int l, int bb0, uint16_t
   dequant_block<FMT, 1>(r, l >> 4, bb0, dst);
 }
 
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+// 8 bf16 -> 8 fp16 (exact in the fp16 range); 8 fp32 -> 8 fp16 (RNE)
+__device__ inline u32x4_t bf16x8_to_f16(u32x4_t v) {
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t f = {__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xffff0000u)};
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2_t));
+  }
+  return r;
+}
+__device__ inline u32x4_t f32x8_to_f16(f32x4_t lo, f32x4_t hi) {
+  const f32x2_t p0 = {lo.x, lo.y}, p1 = {lo.z, lo.w}, p2 = {hi.x, hi.y}, p3 = {hi.z, hi.w};
+  return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_convertvector(p0, h2_t)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, h2_t)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, h2_t)),
+                 __builtin_bit_cast(uint32_t, __builtin_convertvector(p3, h2_t))};
+}
+
 // ------------------------------------------------------------------ router GEMM
 // Split-K: workgroup (n, m, z) multiplies K range [z kper, (z+1) kper) of its
 // 128 x 128 tile and writes the fp32 partial to plane z; the top-k kernel sums
@@ -172,6 +194,7 @@ struct RouterArgs {
   const uint16_t* whi;
   const uint16_t* wlo;
   float* part;            // [S][T][E]
+  uint16_t* x16;          // [T][H] the tokens as fp16, written by the first column of tiles
 };
 
 // fp32 pair -> bf16 pair (RNE) in *hi and the bf16 of the remainders in *lo
@@ -226,7 +249,20 @@ __global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
   };
   f32x16 acc[2][2] = {};
   load_step(kb);
+  const bool write_x16 = blockIdx.x == 0;
   for (int k0 = kb; k0 < ke; k0 += BK) {
+    if (write_x16) {
+      // the tokens as fp16 for the expert GEMMs (each element once: this
+      // column of tiles covers every (row, K) of the chunk exactly once)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + (tid >> 3) + 32 * i;
+        u32x4_t h;
+        if constexpr (XF32) h = f32x8_to_f16(st.x.v[2 * i], st.x.v[2 * i + 1]);
+        else h = bf16x8_to_f16(st.x.v[i]);
+        if (t < a.T) *reinterpret_cast<u32x4_t*>(a.x16 + (size_t)t * a.H + k0 + kc * 8) = h;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int o = ((tid >> 3) + 32 * i) * LDK + kc * 8;
@@ -443,114 +479,235 @@ __global__ void k_scatter(TopkArgs a) {
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
+// fp16 MFMA 16x16x32 with fp32 accumulation.  The token rows (A) are staged
+// in LDS as fp16, double-buffered, 64 of K per stage.  The weights (B) never
+// touch LDS: the slab layout is the B-operand layout of this MFMA (lane l
+// holds row l % 16, K-slice 8 (l / 16) of every 32-weight block), so each lane
+// dequantises its own operand from the codes it loaded, one superblock ahead.
+// Workgroup: 128 token rows x 128 output columns, four waves of 64 x 64
+// (4 x 4 tiles of 16 x 16).
 struct GemmArgs {
   const uint8_t* packed;
   size_t stride;
   int H, I, E, k, T, P;
-  const void* x;
-  int x_f32;
+  const uint16_t* x16;     // [T][H] the tokens as fp16 (written by the router GEMM)
   Work w;
 };
 
-template <int FMT, bool XF32>
-__global__ __launch_bounds__(256) void k_gemm_gateup(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
-  __shared__ const void* rowsrc[BM];
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int XBK = 64;            // K per A stage: two blocks
+constexpr int LDA = XBK + 8;       // LDS row pitch in halves (144 B)
+
+// one lane's codes and scales of one slab for two A stages (four blocks)
+template <int FMT> struct PairCodes;
+template <> struct PairCodes<2> { uint2 w, sc; };
+template <> struct PairCodes<3> { uint2 w, sc; uint32_t h; };
+template <> struct PairCodes<4> { u32x4_t w; uint2 sc; };
+
+// blocks 4 hp .. 4 hp + 3 (half hp of the superblock) of a slab for this lane
+template <int FMT>
+__device__ inline void load_pair(const uint8_t* slab, int hp, int lane, PairCodes<FMT>& c) {
+  c.sc = *reinterpret_cast<const uint2*>(slab + Fmt<FMT>::slab_codes + (lane & 15) * 16 + 8 * hp);
+  if constexpr (FMT == 4) {
+    c.w = *reinterpret_cast<const u32x4_t*>(slab + hp * 1024 + lane * 16);
+  } else {
+    c.w = *reinterpret_cast<const uint2*>(slab + lane * 16 + 8 * hp);
+    if constexpr (FMT == 3) c.h = *reinterpret_cast<const uint32_t*>(slab + 1024 + lane * 8 + 4 * hp);
+  }
+}
+
+template <int SEL>
+__device__ inline h2_t fp4x2_f16(uint32_t src, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(src, scale, SEL);
+}
+
+// The B operand of block B (of its superblock) for this lane: its 8 weights
+// d (q - c) in K order, as fp16 (one rounding: q d - c d by fused
+// multiply-add with c d rounded to fp16 first; Q4 as ((q - 8) / 16) (16 d),
+// both factors exact).  Codes become fp16 q exactly through the FP4
+// conversions (nibble 0b00qq at scale 2, Q3's third bit 0b000h at scale 8),
+// Q4 through the bit pattern 0x3C00 | q << 6.
+template <int FMT, int B>
+__device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
+  const uint32_t sw = ((B >> 1) & 1) ? c.sc.y : c.sc.x;
+  const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)((B & 1) ? (sw >> 16) : (sw & 0xffffu)));
+  h2_t q[4];
+  if constexpr (FMT == 4) {
+    const uint32_t W = c.w[B & 3];
+    const h2_t off = {(_Float16)-1.5f, (_Float16)-1.5f};
+    const _Float16 s16 = d * (_Float16)16.0f;
+    const h2_t s2 = {s16, s16};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
+      q[k] = (__builtin_bit_cast(h2_t, (t & 0x03C003C0u) | 0x3C003C00u) + off) * s2;
+    }
+  } else {
+    const uint32_t W = ((B >> 1) & 1) ? c.w.y : c.w.x;
+    const uint32_t E = W & 0x33333333u, O = (W >> 2) & 0x33333333u;
+    constexpr int b0 = 2 * (B & 1);
+    q[0] = fp4x2_f16<b0>(E, 2.0f);
+    q[1] = fp4x2_f16<b0>(O, 2.0f);
+    q[2] = fp4x2_f16<b0 + 1>(E, 2.0f);
+    q[3] = fp4x2_f16<b0 + 1>(O, 2.0f);
+    if constexpr (FMT == 3) {
+      const uint32_t X = (c.h >> (B & 3)) & 0x11111111u;
+      q[0] += fp4x2_f16<0>(X, 8.0f);
+      q[1] += fp4x2_f16<1>(X, 8.0f);
+      q[2] += fp4x2_f16<2>(X, 8.0f);
+      q[3] += fp4x2_f16<3>(X, 8.0f);
+    }
+    const _Float16 ncd = -((_Float16)Fmt<FMT>::c * d);
+    const h2_t d2 = {d, d}, n2 = {ncd, ncd};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_elementwise_fma(q[k], d2, n2);
+  }
+  f16x8 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    r[2 * k] = q[k].x;
+    r[2 * k + 1] = q[k].y;
+  }
+  return r;
+}
+
+// A stage in registers: this thread's 4 chunks of 8 fp16 (rows tid / 8 +
+// 32 i, columns 8 (tid % 8) of the stage)
+struct AStage { u32x4_t v[4]; };
+
+// (global address-space loads: a generic pointer's load would also count as
+// an LDS access and hold up every LDS read behind it)
+typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
+
+__device__ inline void a_load(const _Float16* const (&src)[4], int k0, AStage& st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.v[i] = *(gu32x4_t*)(src[i] + k0);
+}
+
+__device__ inline void a_store(const AStage& st, _Float16* buf, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4_t*>(buf + ((tid >> 3) + 32 * i) * LDA + (tid & 7) * 8) = st.v[i];
+}
+
+// Block B (of its superblock) against the wave's 4 slabs: 4 x 4 MFMAs; the
+// block's A columns start at column kb of the stage buffer.
+template <int FMT, int B>
+__device__ inline void gemm_block(const _Float16* buf, int kb, const PairCodes<FMT> (&bc)[4], int wm, int lane,
+                                  f32x4 (&acc)[4][4]) {
+  f16x8 bf[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) bf[n] = dequant_b<FMT, B>(bc[n]);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const f16x8 af = __builtin_bit_cast(
+        f16x8, *reinterpret_cast<const u32x4_t*>(buf + (64 * wm + 16 * m + (lane & 15)) * LDA + kb + 8 * (lane >> 4)));
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[n], acc[m][n], 0, 0, 0);
+  }
+}
+
+// The K loop shared by both GEMMs: A rows from src (this thread's 4 chunk
+// rows), the wave's 4 slabs from slab0[n] (superblock sb at + sb * SLAB).
+// A rows run three stages ahead in four register sets: stage s + 3 is
+// requested while stage s is multiplied, and stage s + 1 (requested two
+// stages earlier) goes to the other LDS buffer after it.  Codes run a
+// superblock half (two stages) ahead, in two sets.
+template <int FMT>
+__device__ inline void gemm_kloop(const _Float16* const (&src)[4], const uint8_t* const (&slab0)[4], int K,
+                                  _Float16 (*As)[BM * LDA], int tid, int wm, int lane, f32x4 (&acc)[4][4]) {
+  constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
+  const int nsb = K / SB_WEIGHTS, ns = K / XBK;
+  // half h of the K loop (stages 2h, 2h + 1); past the end: the last half again (unused)
+  auto load_codes = [&](int h, PairCodes<FMT> (&c)[4]) __attribute__((always_inline)) {
+    const int hc = min(h, 2 * nsb - 1);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
+  };
+  PairCodes<FMT> bc[2][4];
+  load_codes(0, bc[0]);
+  AStage ar[4];
+  a_load(src, 0, ar[0]);
+  a_load(src, XBK, ar[1]);
+  a_load(src, min(2, ns - 1) * XBK, ar[2]);
+  a_store(ar[0], As[0], tid);
+  __syncthreads();
+  for (int sb = 0; sb < nsb; ++sb) {
+#define STRATA_STAGE(ST)                                                           \
+    {                                                                              \
+      const int s = 4 * sb + ST;                                                   \
+      if (ST % 2 == 0) load_codes(2 * sb + ST / 2 + 1, bc[(ST / 2 + 1) & 1]);      \
+      a_load(src, min(s + 3, ns - 1) * XBK, ar[(ST + 3) & 3]);                     \
+      __builtin_amdgcn_sched_barrier(0);                                           \
+      gemm_block<FMT, 2 * ST>(As[ST & 1], 0, bc[(ST / 2) & 1], wm, lane, acc);     \
+      gemm_block<FMT, 2 * ST + 1>(As[ST & 1], 32, bc[(ST / 2) & 1], wm, lane, acc); \
+      a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], tid);                            \
+      __syncthreads();                                                             \
+    }
+    STRATA_STAGE(0) STRATA_STAGE(1) STRATA_STAGE(2) STRATA_STAGE(3)
+#undef STRATA_STAGE
+  }
+}
+
+// token of the pair in slot `slot` (routed pairs, then the shared expert's)
+__device__ inline int slot_token(const GemmArgs& a, int slot) {
+  return slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 2) void k_gemm_gateup(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDA];
+  __shared__ int rowsrc[BM];
   const int j = blockIdx.y;
   if (j >= a.w.meta[1]) return;
   const int4 tl = a.w.tiles[j];
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
-  const int itile = blockIdx.x;                       // 64 intermediate rows: gate + up = 128 columns
+  const int itile = blockIdx.x;                       // 64 rows of I: gate and up
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int nsbH = a.H / SB_WEIGHTS;
   if (tid < BM) {
-    // rows past the tile's end read its first row (in bounds; results not stored)
-    const int slot = slot0 + min(tid, rows - 1);
-    const int t = slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
-    rowsrc[tid] = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + (size_t)t * a.H)
-                       : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + (size_t)t * a.H);
+    // rows past the tile's end read its last row (in bounds; results not stored)
+    rowsrc[tid] = slot_token(a, slot0 + min(tid, rows - 1));
   }
-  // B columns in groups of 16: column group cg = tid / 32 covers columns 16cg..16cg+15,
-  // i.e. matrix (cg % 4) / 2 (0 gate, 1 up) and rows (cg / 4) * 32 + (cg % 2) * 16 of the
-  // 64-row i-tile; each thread dequantises two lane-slots of that slab per K-step.
-  const int cg = tid >> 5, sub = tid & 31;
-  const int bmat = (cg & 3) >> 1;
-  const int bgroup = itile * 4 + (cg >> 2) * 2 + (cg & 1);
-  const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + (bmat ? up_off(FMT, a.H, a.I) : 0);
   __syncthreads();
-  const void* src[4];
+  const _Float16* x16 = reinterpret_cast<const _Float16*>(a.x16);
+  const _Float16* src[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src[i] = rowsrc[(tid + 256 * i) >> 3];
-  // the next K-step's operands, in registers: loaded one step ahead
-  AChunks<XF32> an;
-  RawB<FMT> bn[2];
-  auto load_step = [&](int k0) __attribute__((always_inline)) {
+  for (int i = 0; i < 4; ++i) src[i] = x16 + (size_t)rowsrc[(tid >> 3) + 32 * i] * a.H + 8 * (tid & 7);
+  // this wave's slabs: gate then up for i rows itile * 64 + 32 wn + 16 n (n = 0, 1)
+  const uint8_t* ex = a.packed + (size_t)e * a.stride;
+  const uint8_t* slab0[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int kc = (tid + 256 * i) & 7;
-      if constexpr (XF32) {
-        const float* f = reinterpret_cast<const float*>(src[i]) + k0 + kc * 8;
-        an.v[2 * i] = *reinterpret_cast<const f32x4_t*>(f);
-        an.v[2 * i + 1] = *reinterpret_cast<const f32x4_t*>(f + 4);
-      } else {
-        an.v[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(src[i]) + k0 + kc * 8);
-      }
-    }
-    const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
-    const uint8_t* slab = bmat_base + slab_off(FMT, nsbH, bgroup, sb);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) load_rawb<FMT>(slab, sub + 32 * h, bb0, bn[h]);
-  };
-  f32x16 acc[2][2] = {};
-  load_step(0);
-  for (int k0 = 0; k0 < a.H; k0 += BK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
-      u32x4_t hv;
-      if constexpr (XF32) {
-        const f32x4_t f0 = an.v[2 * i], f1 = an.v[2 * i + 1];
-        hv = u32x4_t{cvt_bf16x2(f0.x, f0.y), cvt_bf16x2(f0.z, f0.w), cvt_bf16x2(f1.x, f1.y),
-                     cvt_bf16x2(f1.z, f1.w)};
-      } else {
-        hv = an.v[i];
-      }
-      *reinterpret_cast<u32x4_t*>(As + r * LDK + kc * 8) = hv;
-    }
-    {
-      const int bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int l = sub + 32 * h;
-        dequant_rawb<FMT>(bn[h], l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
-      }
-    }
-    __syncthreads();
-    load_step(min(k0 + BK, a.H - BK));               // in flight during the MFMAs (last step repeats)
-    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the MFMAs
-    mma_step(As, Bs, acc, wm, wn, lane);
-    __syncthreads();
+  for (int n = 0; n < 2; ++n) {
+    const int g = itile * 4 + 2 * wn + n;
+    slab0[n] = ex + slab_off(FMT, nsbH, g, 0);
+    slab0[2 + n] = ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g, 0);
   }
-  // SwiGLU epilogue: nt = 0 holds gate, nt = 1 up, for the same 32 rows i
-  uint16_t* act = reinterpret_cast<uint16_t*>(a.w.act);        // bf16 rows
-  const int i = itile * 64 + wn * 32 + (lane & 31);
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = 64 * wm + 32 * mt + acc_row(v, lane);
-      if (m < rows) {
-        const float g = acc[mt][0][v], u = acc[mt][1][v];
-        act[(size_t)(slot0 + m) * a.I + i] = f32_to_bf16_rne(silu_f(g) * u);
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_kloop<FMT>(src, slab0, a.H, As, tid, wm, lane, acc);
+  // SwiGLU: tiles n = 0, 1 hold gate and n = 2, 3 up for the same rows i
+  _Float16* act = reinterpret_cast<_Float16*>(a.w.act);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 64 * wm + 16 * m + 4 * (lane >> 4) + v;
+        const int i = itile * 64 + 32 * wn + 16 * n + (lane & 15);
+        if (row < rows) act[(size_t)(slot0 + row) * a.I + i] = (_Float16)(silu_f(acc[m][n][v]) * acc[m][n + 2][v]);
       }
-    }
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDA];
   const int j = blockIdx.y;
   if (j >= a.w.meta[1]) return;
   const int4 tl = a.w.tiles[j];
@@ -558,55 +715,32 @@ __global__ __launch_bounds__(256) void k_gemm_down(GemmArgs a) {
   const int h0 = blockIdx.x * BN;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
   const int nsbI = a.I / SB_WEIGHTS;
-  const int cg = tid >> 5, sub = tid & 31;          // column group: H rows h0 + 16cg .. +15
-  const uint8_t* bmat_base = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
-  const int bgroup = h0 / GROUP_ROWS + cg;
-  const uint16_t* act = reinterpret_cast<const uint16_t*>(a.w.act);
-  // rows past the tile's end read its first row (in bounds; results not stored)
-  const uint16_t* src[4];
+  const _Float16* act = reinterpret_cast<const _Float16*>(a.w.act);
+  // rows past the tile's end read its last row (in bounds; results not stored)
+  const _Float16* src[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src[i] = act + (size_t)(slot0 + min((tid + 256 * i) >> 3, rows - 1)) * a.I;
-  AChunks<false> an;
-  RawB<FMT> bn[2];
-  auto load_step = [&](int k0) __attribute__((always_inline)) {
+  for (int i = 0; i < 4; ++i)
+    src[i] = act + (size_t)(slot0 + min((tid >> 3) + 32 * i, rows - 1)) * a.I + 8 * (tid & 7);
+  // this wave's slabs: H rows h0 + 64 wn + 16 n
+  const uint8_t* dn = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
+  const uint8_t* slab0[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) an.v[i] = *reinterpret_cast<const u32x4_t*>(src[i] + k0 + ((tid + 256 * i) & 7) * 8);
-    const int sb = k0 / SB_WEIGHTS, bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
-    const uint8_t* slab = bmat_base + slab_off(FMT, nsbI, bgroup, sb);
+  for (int n = 0; n < 4; ++n) slab0[n] = dn + slab_off(FMT, nsbI, h0 / GROUP_ROWS + 4 * wn + n, 0);
+  f32x4 acc[4][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) load_rawb<FMT>(slab, sub + 32 * h, bb0, bn[h]);
-  };
-  f32x16 acc[2][2] = {};
-  load_step(0);
-  for (int k0 = 0; k0 < a.I; k0 += BK) {
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4_t*>(As + r * LDK + kc * 8) = an.v[i];
-    }
-    {
-      const int bb0 = (k0 % SB_WEIGHTS) / BLOCK_W;
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_kloop<FMT>(src, slab0, a.I, As, tid, wm, lane, acc);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int l = sub + 32 * h;
-        dequant_rawb<FMT>(bn[h], l, bb0, Bs + (cg * 16 + (l & 15)) * LDK);
-      }
-    }
-    __syncthreads();
-    load_step(min(k0 + BK, a.I - BK));               // in flight during the MFMAs (last step repeats)
-    __builtin_amdgcn_sched_barrier(0);               // keep the loads ahead of the MFMAs
-    mma_step(As, Bs, acc, wm, wn, lane);
-    __syncthreads();
-  }
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int n = 0; n < 4; ++n)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = 64 * wm + 32 * mt + acc_row(v, lane);
-        if (m < rows)
-          a.w.ybf[(size_t)(slot0 + m) * a.H + h0 + 64 * wn + 32 * nt + (lane & 31)] = f32_to_bf16_rne(acc[mt][nt][v]);
+      for (int v = 0; v < 4; ++v) {
+        const int row = 64 * wm + 16 * m + 4 * (lane >> 4) + v;
+        if (row < rows)
+          a.w.ybf[(size_t)(slot0 + row) * a.H + h0 + 64 * wn + 16 * n + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
       }
 }
 
@@ -684,16 +818,45 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   }
 }
 
+// Router split-K plan and the place of the fp16 token rows.  Both live in
+// the per-pair output region, dead until the down GEMM: the partial planes
+// first, then the token rows (which the gate/up GEMM reads).
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct RouterPlan {
+  int S, kper;
+  size_t plane;
+  float* part;
+  uint16_t* x16;
+};
+
+RouterPlan router_plan(const Layer& L, const Work& W, int T) {
+  // split K until the grid has about two workgroups per CU
+  RouterPlan r;
+  const int tiles = ((L.E + BN - 1) / BN) * ((T + BM - 1) / BM);
+  const int ksteps = L.H / BK;
+  const size_t x16_bytes = (size_t)T * L.H * 2;       // <= the region (slots >= T)
+  r.plane = (size_t)T * L.E;
+  int S = 1;
+  if (L.E <= 512) {
+    S = std::min(std::min(8, ksteps), std::max(1, (512 + tiles - 1) / tiles));
+    while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
+  }
+  r.kper = ((ksteps + S - 1) / S) * BK;
+  r.S = (L.H + r.kper - 1) / r.kper;                   // no empty split
+  r.part = r.S > 1 ? reinterpret_cast<float*>(W.ybf) : W.logits;
+  r.x16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(W.ybf) +
+                                      (r.S > 1 ? align256((size_t)r.S * r.plane * 4) : 0));
+  return r;
+}
+
 template <int FMT>
 hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   GemmArgs g;
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
-  g.T = c.T; g.P = c.T * L.k; g.x = c.x; g.x_f32 = c.x_f32; g.w = W;
+  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
   const int max_tiles = W.max_tiles;
-  if (c.x_f32)
-    launch(tr, k_gemm_gateup<FMT, true>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
-  else
-    launch(tr, k_gemm_gateup<FMT, false>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
+  launch(tr, k_gemm_gateup<FMT>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
   launch(tr, k_gemm_down<FMT>, dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
@@ -701,23 +864,15 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
 }  // namespace
 
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
-  // split K until the grid has about two workgroups per CU; the partial planes
-  // live in the per-pair output region, which is dead until the down GEMM
-  const int tiles = ((L.E + BN - 1) / BN) * ((c.T + BM - 1) / BM);
-  const int ksteps = L.H / BK;
-  const size_t plane = (size_t)c.T * L.E;
-  int S = 1;
-  if (L.E <= 512) {
-    S = std::min(std::min(8, ksteps), std::max(1, (512 + tiles - 1) / tiles));
-    while (S > 1 && (size_t)S * plane * 4 > W.ybf_bytes) --S;
-  }
-  const int kper = ((ksteps + S - 1) / S) * BK;
-  S = (L.H + kper - 1) / kper;                       // no empty split
+  const RouterPlan rp = router_plan(L, W, c.T);
+  const int S = rp.S;
+  const size_t plane = rp.plane;
   RouterArgs r;
   r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
-  r.kper = kper; r.plane = plane;
+  r.kper = rp.kper; r.plane = plane;
   r.whi = L.router_hi; r.wlo = L.router_lo;
-  r.part = S > 1 ? reinterpret_cast<float*>(W.ybf) : W.logits;
+  r.part = rp.part;
+  r.x16 = rp.x16;
   dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM, S);
   if (c.x_f32) launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
   else launch(tr, k_router_gemm<false>, grid, dim3(256), 0, s, r);
