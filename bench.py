@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 
 METRIC = "MoE-layer tokens/s (decode, 8K prefill); % HBM peak (decode) / % MFMA peak"
 
@@ -245,10 +245,10 @@ def main():
                 kernels[n]["TFLOPs"] = round(fl[n] / (kern_us[j] * 1e-6) / 1e12, 1)
         dom = max(names, key=lambda n: kernels[n]["us"])
         achieved = kernels[dom].get("TFLOPs", 0.0)
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
         layer_flops = sum(fl.values())
-        layer_frac = layer_flops / (ms_per_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+        layer_frac = layer_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12)
         layer_bytes = None
 
     # ------------------------------------------------------------ CPU oracle baseline
@@ -267,7 +267,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32" if decode else "bf16",
+        "dtype": "fp32" if decode else "fp16",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens_per_step": T, "hidden": w.hidden,
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,

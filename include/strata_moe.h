@@ -147,7 +147,8 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
  * Precision: the decode kernels (T <= 8) multiply exact weight values by the
  * activations carried as two fp16 parts (22 significant bits) with fp32
  * accumulation; |x| and the SwiGLU outputs must stay below 65504 there.  The
- * prefill kernels round weights and activations to bf16 (fp32 accumulation).
+ * prefill expert GEMMs round weights and activations to fp16 (same range
+ * limit) with fp32 accumulation; the prefill router stays fp32-accurate.
  */
 STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
                        float* out, uint32_t flags, void* stream);

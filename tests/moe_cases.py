@@ -8,7 +8,7 @@ import oracle as O
 from moe_synth import generate as G
 
 DECODE_TOL = 1e-5      # rel-L2, fp32 decode path vs fp64 oracle
-PREFILL_TOL = 2e-2     # rel-L2, bf16-MFMA prefill path vs fp64 oracle
+PREFILL_TOL = 2e-2     # rel-L2, 16-bit-MFMA prefill path vs fp64 oracle
 MIN_GAP = 1e-2         # logit gap at rank k required of every generated token
 
 
