@@ -479,13 +479,18 @@ __global__ void k_scatter(TopkArgs a) {
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
-// fp16 MFMA 16x16x32 with fp32 accumulation.  The token rows (A) are staged
-// in LDS as fp16, double-buffered, 64 of K per stage.  The weights (B) never
-// touch LDS: the slab layout is the B-operand layout of this MFMA (lane l
-// holds row l % 16, K-slice 8 (l / 16) of every 32-weight block), so each lane
-// dequantises its own operand from the codes it loaded, one superblock ahead.
-// Workgroup: 128 token rows x 128 output columns, four waves of 64 x 64
-// (4 x 4 tiles of 16 x 16).
+// fp16 MFMA 16x16x32 with fp32 accumulation.  A work item is one 128-slot
+// row tile of an expert (the tile list) times 128 output columns; its four
+// waves each take all 128 token rows and 32 columns, so each weight operand is
+// dequantised once per work item and feeds up to 8 MFMAs (the dequantisation
+// costs VALU time that does not overlap the matrix cores, so it is spread
+// over as many token rows as possible).  Subtiles past a short tile's rows
+// are skipped 32 rows at a time.  The token rows (A) are staged in LDS as
+// fp16, double-buffered, 64 of K per stage, two stages ahead in registers.
+// The weights (B) never touch LDS: the slab layout is the B-operand layout
+// of this MFMA (lane l holds row l % 16, K-slice 8 (l / 16) of every
+// 32-weight block), so each lane dequantises its own operand from the codes
+// it loaded half a superblock ahead.
 struct GemmArgs {
   const uint8_t* packed;
   size_t stride;
@@ -573,99 +578,174 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
   return r;
 }
 
-// A stage in registers: this thread's 4 chunks of 8 fp16 (rows tid / 8 +
-// 32 i, columns 8 (tid % 8) of the stage)
+// A stage: 64 of K (two blocks) of the tile's 128 token rows, kept in LDS
+// fragment-major: fragment f = 2 m + kb (16-row subtile m, block kb) is the
+// 1 KiB A operand of one MFMA; the 16 bytes of its lane p (row 16 m + p % 16,
+// columns 32 kb + 8 (p / 16)) sit in slot a_slot(p), so every operand read is
+// one 16-byte-per-lane LDS read without bank conflicts.  Thread (wave w,
+// lane l) loads the fragments 4 w + i (i = 0..3) of a stage: row 16 m + l / 4,
+// 16 bytes at column 32 kb + 8 (l % 4), so four neighbouring lanes read 64
+// contiguous bytes of one row (one address-unit access instead of four), and
+// stores them at operand lane l / 4 + 16 (l % 4).
+constexpr int AFRAG = 512;          // halves per fragment
+constexpr int ASTAGE = 16 * AFRAG;  // halves per stage (8 subtiles x 2 blocks)
+// slot of operand lane p: the rows of one K-slice rotate by 4 slots per
+// slice, so the lanes that one store instruction writes together (four
+// K-slices of a row, then the next rows) fall into different LDS banks
+__device__ inline int a_slot(int p) { return p ^ (4 * (p >> 4)); }
 struct AStage { u32x4_t v[4]; };
 
 // (global address-space loads: a generic pointer's load would also count as
 // an LDS access and hold up every LDS read behind it)
 typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 
-__device__ inline void a_load(const _Float16* const (&src)[4], int k0, AStage& st) {
+// Every fragment is loaded and stored, also those of subtiles a short tile
+// does not compute (their rows repeat the tile's last row): a load under a
+// condition would make the compiler wait for all outstanding loads before
+// the next store.
+__device__ inline void a_load(const _Float16* const (&src)[2], int k0, AStage& st) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.v[i] = *(gu32x4_t*)(src[i] + k0);
+  for (int i = 0; i < 4; ++i) st.v[i] = *(gu32x4_t*)(src[i >> 1] + k0 + 32 * (i & 1));
 }
 
-__device__ inline void a_store(const AStage& st, _Float16* buf, int tid) {
+__device__ inline void a_store(const AStage& st, _Float16* buf, int wv, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4_t*>(buf + ((tid >> 3) + 32 * i) * LDA + (tid & 7) * 8) = st.v[i];
+    *reinterpret_cast<u32x4_t*>(buf + (4 * wv + i) * AFRAG + 8 * a_slot((lane >> 2) + 16 * (lane & 3))) = st.v[i];
 }
 
-// Block B (of its superblock) against the wave's 4 slabs: 4 x 4 MFMAs; the
-// block's A columns start at column kb of the stage buffer.
-template <int FMT, int B>
-__device__ inline void gemm_block(const _Float16* buf, int kb, const PairCodes<FMT> (&bc)[4], int wm, int lane,
-                                  f32x4 (&acc)[4][4]) {
-  f16x8 bf[4];
+constexpr int GEMM_WAVES = 4;
+constexpr int MT = BM / 16;        // 16-row subtiles of a tile
+
+// One stage (blocks BB and BB + 1 of the superblock) against the wave's 2
+// slabs: each weight operand is dequantised once and feeds MC MFMAs (one per
+// 16-row subtile of the token rows).  The 2 MC token-row operands are read
+// from LDS two steps ahead of their MFMAs, so the read latency stays hidden
+// behind the MFMAs of the steps in between.
+template <int FMT, int BB, int MC>
+__device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc)[2], int lane,
+                                  f32x4 (&acc)[MT][2]) {
+  constexpr int NS = 2 * MC;                          // steps: (block kb, subtile m), kb-major
+  auto rd = [&](int t) __attribute__((always_inline)) {
+    const int m = t % MC, kb = t / MC;
+    return __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4_t*>(buf + (2 * m + kb) * AFRAG + 8 * a_slot(lane)));
+  };
+  f16x8 af[4];
+  af[0] = rd(0);
+  af[1] = rd(1);
+  f16x8 bf[2][2];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) bf[n] = dequant_b<FMT, B>(bc[n]);
+  for (int n = 0; n < 2; ++n) bf[0][n] = dequant_b<FMT, BB>(bc[n]);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const f16x8 af = __builtin_bit_cast(
-        f16x8, *reinterpret_cast<const u32x4_t*>(buf + (64 * wm + 16 * m + (lane & 15)) * LDA + kb + 8 * (lane >> 4)));
+  for (int t = 0; t < NS; ++t) {
+    if (t + 2 < NS) af[(t + 2) & 3] = rd(t + 2);
+    if (t == MC - 1) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[n], acc[m][n], 0, 0, 0);
+      for (int n = 0; n < 2; ++n) bf[1][n] = dequant_b<FMT, BB + 1>(bc[n]);
+    }
+    const int m = t % MC, kb = t / MC;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t & 3], bf[kb][n], acc[m][n], 0, 0, 0);
+  }
+  // keep the reads two steps ahead of the MFMAs that use them
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int t = 0; t < NS; ++t) {
+    if (t + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 }
 
-// The K loop shared by both GEMMs: A rows from src (this thread's 4 chunk
-// rows), the wave's 4 slabs from slab0[n] (superblock sb at + sb * SLAB).
-// A rows run three stages ahead in four register sets: stage s + 3 is
-// requested while stage s is multiplied, and stage s + 1 (requested two
-// stages earlier) goes to the other LDS buffer after it.  Codes run a
-// superblock half (two stages) ahead, in two sets.
-template <int FMT>
-__device__ inline void gemm_kloop(const _Float16* const (&src)[4], const uint8_t* const (&slab0)[4], int K,
-                                  _Float16 (*As)[BM * LDA], int tid, int wm, int lane, f32x4 (&acc)[4][4]) {
+// The K loop shared by both GEMMs, for the first 16 MC token rows: A rows
+// from src (this lane's two rows), the wave's 2 slabs from slab0[n]
+// (superblock sb at + sb * SLAB).  Stage s + 2 of the A rows is requested
+// while stage s is multiplied; stage s + 1 (requested a stage earlier) then
+// goes to the other LDS buffer.  Codes run half a superblock (two stages)
+// ahead, in two sets.
+template <int FMT, int MC>
+__device__ inline void gemm_kloop(const _Float16* const (&src)[2], const uint8_t* const (&slab0)[2], int K,
+                                  _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][2]) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
   const int nsb = K / SB_WEIGHTS, ns = K / XBK;
   // half h of the K loop (stages 2h, 2h + 1); past the end: the last half again (unused)
-  auto load_codes = [&](int h, PairCodes<FMT> (&c)[4]) __attribute__((always_inline)) {
+  auto load_codes = [&](int h, PairCodes<FMT> (&c)[2]) __attribute__((always_inline)) {
     const int hc = min(h, 2 * nsb - 1);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
+    for (int n = 0; n < 2; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
   };
-  PairCodes<FMT> bc[2][4];
+  PairCodes<FMT> bc[2][2];
   load_codes(0, bc[0]);
   AStage ar[4];
   a_load(src, 0, ar[0]);
   a_load(src, XBK, ar[1]);
-  a_load(src, min(2, ns - 1) * XBK, ar[2]);
-  a_store(ar[0], As[0], tid);
+  a_store(ar[0], As[0], wv, lane);
   __syncthreads();
   for (int sb = 0; sb < nsb; ++sb) {
-#define STRATA_STAGE(ST)                                                           \
-    {                                                                              \
-      const int s = 4 * sb + ST;                                                   \
-      if (ST % 2 == 0) load_codes(2 * sb + ST / 2 + 1, bc[(ST / 2 + 1) & 1]);      \
-      a_load(src, min(s + 3, ns - 1) * XBK, ar[(ST + 3) & 3]);                     \
-      __builtin_amdgcn_sched_barrier(0);                                           \
-      gemm_block<FMT, 2 * ST>(As[ST & 1], 0, bc[(ST / 2) & 1], wm, lane, acc);     \
-      gemm_block<FMT, 2 * ST + 1>(As[ST & 1], 32, bc[(ST / 2) & 1], wm, lane, acc); \
-      a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], tid);                            \
-      __syncthreads();                                                             \
+#define STRATA_STAGE(ST)                                                                \
+    {                                                                                   \
+      const int s = 4 * sb + ST;                                                        \
+      if (ST % 2 == 0) load_codes(2 * sb + ST / 2 + 1, bc[(ST / 2 + 1) & 1]);           \
+      a_load(src, min(s + 2, ns - 1) * XBK, ar[(ST + 2) & 3]);                         \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      gemm_stage<FMT, 2 * ST, MC>(As[ST & 1], bc[(ST / 2) & 1], lane, acc);             \
+      a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], wv, lane);                            \
+      __syncthreads();                                                                  \
     }
     STRATA_STAGE(0) STRATA_STAGE(1) STRATA_STAGE(2) STRATA_STAGE(3)
 #undef STRATA_STAGE
   }
 }
 
+// The K loop for a tile of `rows` token rows: subtiles past the rows are not
+// computed (32 rows at a time).
+template <int FMT>
+__device__ inline void gemm_tile(int rows, const _Float16* const (&src)[2], const uint8_t* const (&slab0)[2],
+                                 int K, _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][2]) {
+  if (rows > 96) gemm_kloop<FMT, 8>(src, slab0, K, As, wv, lane, acc);
+  else if (rows > 64) gemm_kloop<FMT, 6>(src, slab0, K, As, wv, lane, acc);
+  else if (rows > 32) gemm_kloop<FMT, 4>(src, slab0, K, As, wv, lane, acc);
+  else gemm_kloop<FMT, 2>(src, slab0, K, As, wv, lane, acc);
+}
+
+// Work item of this workgroup: (row tile j, column tile nt), ntn column tiles
+// per row tile.  The eight XCDs each take a contiguous range of work items
+// (workgroup b runs on XCD b % 8), column tiles of a row tile adjacent.
+__device__ inline bool work_item(int ntiles, int ntn, int& j, int& nt) {
+  const int total = ntiles * ntn, per = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3, w = xcd * per + idx;
+  if (idx >= per || w >= total) return false;
+  j = w / ntn;
+  nt = w - j * ntn;
+  return true;
+}
+
+// workgroups to launch for up to max_tiles row tiles of ntn column tiles
+inline int work_grid(int max_tiles, int ntn) { return 8 * ((max_tiles * ntn + 7) / 8); }
+
 // token of the pair in slot `slot` (routed pairs, then the shared expert's)
 __device__ inline int slot_token(const GemmArgs& a, int slot) {
   return slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
 }
 
+__device__ inline void zero_acc(f32x4 (&acc)[MT][2]) {
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// gate/up: work item = 128 slots x 64 rows of I (gate and up); wave w takes
+// 16 rows of I (one gate and one up slab) and every token row of the tile
 template <int FMT>
-__global__ __launch_bounds__(256, 2) void k_gemm_gateup(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDA];
+__global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm_gateup(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
   __shared__ int rowsrc[BM];
-  const int j = blockIdx.y;
-  if (j >= a.w.meta[1]) return;
+  int j, itile;
+  if (!work_item(a.w.meta[1], a.I / 64, j, itile)) return;
   const int4 tl = a.w.tiles[j];
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
-  const int itile = blockIdx.x;                       // 64 rows of I: gate and up
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nsbH = a.H / SB_WEIGHTS;
   if (tid < BM) {
     // rows past the tile's end read its last row (in bounds; results not stored)
@@ -673,74 +753,61 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gateup(GemmArgs a) {
   }
   __syncthreads();
   const _Float16* x16 = reinterpret_cast<const _Float16*>(a.x16);
-  const _Float16* src[4];
+  const _Float16* src[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) src[i] = x16 + (size_t)rowsrc[(tid >> 3) + 32 * i] * a.H + 8 * (tid & 7);
-  // this wave's slabs: gate then up for i rows itile * 64 + 32 wn + 16 n (n = 0, 1)
+  for (int q = 0; q < 2; ++q)
+    src[q] = x16 + (size_t)rowsrc[16 * (2 * wv + q) + (lane >> 2)] * a.H + 8 * (lane & 3);
+  // this wave's slabs: gate and up for I rows 16 g .. 16 g + 15
+  const int g = itile * GEMM_WAVES + wv;
   const uint8_t* ex = a.packed + (size_t)e * a.stride;
-  const uint8_t* slab0[4];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int g = itile * 4 + 2 * wn + n;
-    slab0[n] = ex + slab_off(FMT, nsbH, g, 0);
-    slab0[2 + n] = ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g, 0);
-  }
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_kloop<FMT>(src, slab0, a.H, As, tid, wm, lane, acc);
-  // SwiGLU: tiles n = 0, 1 hold gate and n = 2, 3 up for the same rows i
+  const uint8_t* slab0[2] = {ex + slab_off(FMT, nsbH, g, 0), ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g, 0)};
+  f32x4 acc[MT][2];
+  zero_acc(acc);
+  gemm_tile<FMT>(rows, src, slab0, a.H, As, wv, lane, acc);
+  // SwiGLU: n = 0 holds gate, n = 1 up, for the same rows i
   _Float16* act = reinterpret_cast<_Float16*>(a.w.act);
+  const int i = 16 * g + (lane & 15);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * m + 4 * (lane >> 4) + v;
+      if (row < rows) act[(size_t)(slot0 + row) * a.I + i] = (_Float16)(silu_f(acc[m][0][v]) * acc[m][1][v]);
+    }
+}
+
+// down: work item = 128 slots x 128 rows of H; wave w takes 32 rows of H
+template <int FMT>
+__global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm_down(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
+  int j, htile;
+  if (!work_item(a.w.meta[1], a.H / 128, j, htile)) return;
+  const int4 tl = a.w.tiles[j];
+  const int e = tl.x, slot0 = tl.y, rows = tl.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nsbI = a.I / SB_WEIGHTS;
+  const _Float16* act = reinterpret_cast<const _Float16*>(a.w.act);
+  // rows past the tile's end read its last row (in bounds; results not stored)
+  const _Float16* src[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    src[q] = act + (size_t)(slot0 + min(16 * (2 * wv + q) + (lane >> 2), rows - 1)) * a.I + 8 * (lane & 3);
+  // this wave's slabs: H rows 16 g0 .. 16 g0 + 31
+  const int g0 = htile * 2 * GEMM_WAVES + 2 * wv;
+  const uint8_t* dn = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
+  const uint8_t* slab0[2] = {dn + slab_off(FMT, nsbI, g0, 0), dn + slab_off(FMT, nsbI, g0 + 1, 0)};
+  f32x4 acc[MT][2];
+  zero_acc(acc);
+  gemm_tile<FMT>(rows, src, slab0, a.I, As, wv, lane, acc);
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = 64 * wm + 16 * m + 4 * (lane >> 4) + v;
-        const int i = itile * 64 + 32 * wn + 16 * n + (lane & 15);
-        if (row < rows) act[(size_t)(slot0 + row) * a.I + i] = (_Float16)(silu_f(acc[m][n][v]) * acc[m][n + 2][v]);
-      }
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDA];
-  const int j = blockIdx.y;
-  if (j >= a.w.meta[1]) return;
-  const int4 tl = a.w.tiles[j];
-  const int e = tl.x, slot0 = tl.y, rows = tl.z;
-  const int h0 = blockIdx.x * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  const int nsbI = a.I / SB_WEIGHTS;
-  const _Float16* act = reinterpret_cast<const _Float16*>(a.w.act);
-  // rows past the tile's end read its last row (in bounds; results not stored)
-  const _Float16* src[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    src[i] = act + (size_t)(slot0 + min((tid >> 3) + 32 * i, rows - 1)) * a.I + 8 * (tid & 7);
-  // this wave's slabs: H rows h0 + 64 wn + 16 n
-  const uint8_t* dn = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
-  const uint8_t* slab0[4];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) slab0[n] = dn + slab_off(FMT, nsbI, h0 / GROUP_ROWS + 4 * wn + n, 0);
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  gemm_kloop<FMT>(src, slab0, a.I, As, tid, wm, lane, acc);
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 64 * wm + 16 * m + 4 * (lane >> 4) + v;
+        const int row = 16 * m + 4 * (lane >> 4) + v;
         if (row < rows)
-          a.w.ybf[(size_t)(slot0 + row) * a.H + h0 + 64 * wn + 16 * n + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
+          a.w.ybf[(size_t)(slot0 + row) * a.H + 16 * (g0 + n) + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
       }
 }
 
@@ -856,8 +923,8 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
   g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
   const int max_tiles = W.max_tiles;
-  launch(tr, k_gemm_gateup<FMT>, dim3(L.I / 64, max_tiles), dim3(256), 0, s, g);
-  launch(tr, k_gemm_down<FMT>, dim3(L.H / BN, max_tiles), dim3(256), 0, s, g);
+  launch(tr, k_gemm_gateup<FMT>, dim3(work_grid(max_tiles, L.I / 64)), dim3(64 * GEMM_WAVES), 0, s, g);
+  launch(tr, k_gemm_down<FMT>, dim3(work_grid(max_tiles, L.H / 128)), dim3(64 * GEMM_WAVES), 0, s, g);
   return hipGetLastError();
 }
 
