@@ -581,18 +581,17 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
 // A stage: 64 of K (two blocks) of the tile's 128 token rows, kept in LDS
 // fragment-major: fragment f = 2 m + kb (16-row subtile m, block kb) is the
 // 1 KiB A operand of one MFMA; the 16 bytes of its lane p (row 16 m + p % 16,
-// columns 32 kb + 8 (p / 16)) sit in slot a_slot(p), so every operand read is
-// one 16-byte-per-lane LDS read without bank conflicts.  Thread (wave w,
-// lane l) loads the fragments 4 w + i (i = 0..3) of a stage: row 16 m + l / 4,
-// 16 bytes at column 32 kb + 8 (l % 4), so four neighbouring lanes read 64
-// contiguous bytes of one row (one address-unit access instead of four), and
-// stores them at operand lane l / 4 + 16 (l % 4).
+// columns 32 kb + 8 (p / 16)) sit in 16-byte slot a_slot(p).  Thread (wave
+// w, lane l) loads the fragments 4 w + i (i = 0..3) of a stage, four
+// neighbouring lanes reading 64 contiguous bytes of one row (one
+// address-unit access instead of four): lane l takes row l / 4 of the
+// subtile, columns 32 kb + 8 (l % 4), i.e. operand lane l / 4 + 16 (l % 4).
+// With the slots XOR 2 (p / 16), both that store and the linear operand
+// read are free of LDS bank conflicts (measured on gfx950 with
+// SQ_LDS_BANK_CONFLICT).
 constexpr int AFRAG = 512;          // halves per fragment
 constexpr int ASTAGE = 16 * AFRAG;  // halves per stage (8 subtiles x 2 blocks)
-// slot of operand lane p: the rows of one K-slice rotate by 4 slots per
-// slice, so the lanes that one store instruction writes together (four
-// K-slices of a row, then the next rows) fall into different LDS banks
-__device__ inline int a_slot(int p) { return p ^ (4 * (p >> 4)); }
+__device__ inline int a_slot(int p) { return p ^ (2 * (p >> 4)); }
 struct AStage { u32x4_t v[4]; };
 
 // (global address-space loads: a generic pointer's load would also count as
