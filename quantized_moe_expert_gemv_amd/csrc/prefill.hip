@@ -582,7 +582,7 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
 // fragment-major: fragment f = 2 m + kb (16-row subtile m, block kb) is the
 // 1 KiB A operand of one MFMA; the 16 bytes of its lane p (row 16 m + p % 16,
 // columns 32 kb + 8 (p / 16)) sit in 16-byte slot a_slot(p).  Thread (wave
-// w, lane l) loads the fragments 4 w + i (i = 0..3) of a stage, four
+// w, lane l) loads the fragments AF w + i (i < AF) of a stage, four
 // neighbouring lanes reading 64 contiguous bytes of one row (one
 // address-unit access instead of four): lane l takes row l / 4 of the
 // subtile, columns 32 kb + 8 (l % 4), i.e. operand lane l / 4 + 16 (l % 4).
@@ -592,7 +592,13 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
 constexpr int AFRAG = 512;          // halves per fragment
 constexpr int ASTAGE = 16 * AFRAG;  // halves per stage (8 subtiles x 2 blocks)
 __device__ inline int a_slot(int p) { return p ^ (2 * (p >> 4)); }
-struct AStage { u32x4_t v[4]; };
+constexpr int GEMM_WAVES = 8;
+// weight slabs (16 output columns each) per wave: 4 for 2-bit codes; the
+// 3- and 4-bit dequantisation needs more registers, so 2 there
+template <int FMT> constexpr int nsl() { return FMT == 2 ? 4 : 2; }
+constexpr int AF = 16 / GEMM_WAVES;   // fragments of a stage per wave
+constexpr int AR = AF / 2;            // token rows per lane
+struct AStage { u32x4_t v[AF]; };
 
 // (global address-space loads: a generic pointer's load would also count as
 // an LDS access and hold up every LDS read behind it)
@@ -602,28 +608,27 @@ typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 // does not compute (their rows repeat the tile's last row): a load under a
 // condition would make the compiler wait for all outstanding loads before
 // the next store.
-__device__ inline void a_load(const _Float16* const (&src)[2], int k0, AStage& st) {
+__device__ inline void a_load(const _Float16* const (&src)[AR], int k0, AStage& st) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.v[i] = *(gu32x4_t*)(src[i >> 1] + k0 + 32 * (i & 1));
+  for (int i = 0; i < AF; ++i) st.v[i] = *(gu32x4_t*)(src[i >> 1] + k0 + 32 * (i & 1));
 }
 
 __device__ inline void a_store(const AStage& st, _Float16* buf, int wv, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<u32x4_t*>(buf + (4 * wv + i) * AFRAG + 8 * a_slot((lane >> 2) + 16 * (lane & 3))) = st.v[i];
+  for (int i = 0; i < AF; ++i)
+    *reinterpret_cast<u32x4_t*>(buf + (AF * wv + i) * AFRAG + 8 * a_slot((lane >> 2) + 16 * (lane & 3))) = st.v[i];
 }
 
-constexpr int GEMM_WAVES = 4;
 constexpr int MT = BM / 16;        // 16-row subtiles of a tile
 
-// One stage (blocks BB and BB + 1 of the superblock) against the wave's 2
+// One stage (blocks BB and BB + 1 of the superblock) against the wave's NSL
 // slabs: each weight operand is dequantised once and feeds MC MFMAs (one per
 // 16-row subtile of the token rows).  The 2 MC token-row operands are read
 // from LDS two steps ahead of their MFMAs, so the read latency stays hidden
 // behind the MFMAs of the steps in between.
-template <int FMT, int BB, int MC>
-__device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc)[2], int lane,
-                                  f32x4 (&acc)[MT][2]) {
+template <int FMT, int BB, int MC, bool TR, int NSL = nsl<FMT>()>
+__device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc)[NSL], int lane,
+                                  f32x4 (&acc)[MT][NSL]) {
   constexpr int NS = 2 * MC;                          // steps: (block kb, subtile m), kb-major
   auto rd = [&](int t) __attribute__((always_inline)) {
     const int m = t % MC, kb = t / MC;
@@ -632,48 +637,49 @@ __device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc
   f16x8 af[4];
   af[0] = rd(0);
   af[1] = rd(1);
-  f16x8 bf[2][2];
+  f16x8 bf[2][NSL];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) bf[0][n] = dequant_b<FMT, BB>(bc[n]);
+  for (int n = 0; n < NSL; ++n) bf[0][n] = dequant_b<FMT, BB>(bc[n]);
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     if (t + 2 < NS) af[(t + 2) & 3] = rd(t + 2);
     if (t == MC - 1) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n) bf[1][n] = dequant_b<FMT, BB + 1>(bc[n]);
+      for (int n = 0; n < NSL; ++n) bf[1][n] = dequant_b<FMT, BB + 1>(bc[n]);
     }
     const int m = t % MC, kb = t / MC;
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-      acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t & 3], bf[kb][n], acc[m][n], 0, 0, 0);
+    for (int n = 0; n < NSL; ++n)
+      acc[m][n] = TR ? __builtin_amdgcn_mfma_f32_16x16x32_f16(bf[kb][n], af[t & 3], acc[m][n], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_16x16x32_f16(af[t & 3], bf[kb][n], acc[m][n], 0, 0, 0);
   }
   // keep the reads two steps ahead of the MFMAs that use them
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
   for (int t = 0; t < NS; ++t) {
     if (t + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NSL, 0);
   }
 }
 
 // The K loop shared by both GEMMs, for the first 16 MC token rows: A rows
-// from src (this lane's two rows), the wave's 2 slabs from slab0[n]
+// from src (this lane's rows), the wave's NSL slabs from slab0[n]
 // (superblock sb at + sb * SLAB).  Stage s + 2 of the A rows is requested
 // while stage s is multiplied; stage s + 1 (requested a stage earlier) then
 // goes to the other LDS buffer.  Codes run half a superblock (two stages)
 // ahead, in two sets.
-template <int FMT, int MC>
-__device__ inline void gemm_kloop(const _Float16* const (&src)[2], const uint8_t* const (&slab0)[2], int K,
-                                  _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][2]) {
+template <int FMT, int MC, bool TR, int NSL = nsl<FMT>()>
+__device__ inline void gemm_kloop(const _Float16* const (&src)[AR], const uint8_t* const (&slab0)[NSL], int K,
+                                  _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][NSL]) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
   const int nsb = K / SB_WEIGHTS, ns = K / XBK;
   // half h of the K loop (stages 2h, 2h + 1); past the end: the last half again (unused)
-  auto load_codes = [&](int h, PairCodes<FMT> (&c)[2]) __attribute__((always_inline)) {
+  auto load_codes = [&](int h, PairCodes<FMT> (&c)[NSL]) __attribute__((always_inline)) {
     const int hc = min(h, 2 * nsb - 1);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
+    for (int n = 0; n < NSL; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
   };
-  PairCodes<FMT> bc[2][2];
+  PairCodes<FMT> bc[2][NSL];
   load_codes(0, bc[0]);
   AStage ar[4];
   a_load(src, 0, ar[0]);
@@ -687,7 +693,7 @@ __device__ inline void gemm_kloop(const _Float16* const (&src)[2], const uint8_t
       if (ST % 2 == 0) load_codes(2 * sb + ST / 2 + 1, bc[(ST / 2 + 1) & 1]);           \
       a_load(src, min(s + 2, ns - 1) * XBK, ar[(ST + 2) & 3]);                         \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      gemm_stage<FMT, 2 * ST, MC>(As[ST & 1], bc[(ST / 2) & 1], lane, acc);             \
+      gemm_stage<FMT, 2 * ST, MC, TR>(As[ST & 1], bc[(ST / 2) & 1], lane, acc);         \
       a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], wv, lane);                            \
       __syncthreads();                                                                  \
     }
@@ -698,13 +704,13 @@ __device__ inline void gemm_kloop(const _Float16* const (&src)[2], const uint8_t
 
 // The K loop for a tile of `rows` token rows: subtiles past the rows are not
 // computed (32 rows at a time).
-template <int FMT>
-__device__ inline void gemm_tile(int rows, const _Float16* const (&src)[2], const uint8_t* const (&slab0)[2],
-                                 int K, _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][2]) {
-  if (rows > 96) gemm_kloop<FMT, 8>(src, slab0, K, As, wv, lane, acc);
-  else if (rows > 64) gemm_kloop<FMT, 6>(src, slab0, K, As, wv, lane, acc);
-  else if (rows > 32) gemm_kloop<FMT, 4>(src, slab0, K, As, wv, lane, acc);
-  else gemm_kloop<FMT, 2>(src, slab0, K, As, wv, lane, acc);
+template <int FMT, bool TR, int NSL = nsl<FMT>()>
+__device__ inline void gemm_tile(int rows, const _Float16* const (&src)[AR], const uint8_t* const (&slab0)[NSL],
+                                 int K, _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][NSL]) {
+  if (rows > 96) gemm_kloop<FMT, 8, TR>(src, slab0, K, As, wv, lane, acc);
+  else if (rows > 64) gemm_kloop<FMT, 6, TR>(src, slab0, K, As, wv, lane, acc);
+  else if (rows > 32) gemm_kloop<FMT, 4, TR>(src, slab0, K, As, wv, lane, acc);
+  else gemm_kloop<FMT, 2, TR>(src, slab0, K, As, wv, lane, acc);
 }
 
 // Work item of this workgroup: (row tile j, column tile nt), ntn column tiles
@@ -727,21 +733,33 @@ __device__ inline int slot_token(const GemmArgs& a, int slot) {
   return slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
 }
 
-__device__ inline void zero_acc(f32x4 (&acc)[MT][2]) {
+template <int NSL>
+__device__ inline void zero_acc(f32x4 (&acc)[MT][NSL]) {
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < NSL; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// gate/up: work item = 128 slots x 64 rows of I (gate and up); wave w takes
-// 16 rows of I (one gate and one up slab) and every token row of the tile
+// silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal
+// (relative error a few ulp; the prefill path rounds its result to fp16)
+__device__ inline float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+constexpr bool DOWN_TR = false;
+
+// Column tiles of a work item: GEMM_WAVES waves of nsl() slabs each.
+template <int FMT> constexpr int gu_rows() { return GEMM_WAVES * nsl<FMT>() / 2 * 16; }  // rows of I, gate/up
+template <int FMT> constexpr int dn_cols() { return GEMM_WAVES * nsl<FMT>() * 16; }      // rows of H, down
+
+// gate/up: work item = 128 slots x gu_rows() rows of I (gate and up); wave w
+// takes NSL/2 row groups of 16 (gate and up slabs) and every token row
 template <int FMT>
-__global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm_gateup(GemmArgs a) {
+__global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) {
+  constexpr int NSL = nsl<FMT>();
   __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
   __shared__ int rowsrc[BM];
   int j, itile;
-  if (!work_item(a.w.meta[1], a.I / 64, j, itile)) return;
+  if (!work_item(a.w.meta[1], a.I / gu_rows<FMT>(), j, itile)) return;
   const int4 tl = a.w.tiles[j];
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -752,62 +770,95 @@ __global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm_gateup(GemmArgs a) 
   }
   __syncthreads();
   const _Float16* x16 = reinterpret_cast<const _Float16*>(a.x16);
-  const _Float16* src[2];
+  const _Float16* src[AR];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    src[q] = x16 + (size_t)rowsrc[16 * (2 * wv + q) + (lane >> 2)] * a.H + 8 * (lane & 3);
-  // this wave's slabs: gate and up for I rows 16 g .. 16 g + 15
-  const int g = itile * GEMM_WAVES + wv;
+  for (int q = 0; q < AR; ++q)
+    src[q] = x16 + (size_t)rowsrc[16 * (AR * wv + q) + (lane >> 2)] * a.H + 8 * (lane & 3);
+  // this wave's slabs: gate and up for I rows 16 g0 .. 16 (g0 + NSL/2) - 1
+  const int g0 = (itile * GEMM_WAVES + wv) * (NSL / 2);
   const uint8_t* ex = a.packed + (size_t)e * a.stride;
-  const uint8_t* slab0[2] = {ex + slab_off(FMT, nsbH, g, 0), ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g, 0)};
-  f32x4 acc[MT][2];
+  const uint8_t* slab0[NSL];
+#pragma unroll
+  for (int n = 0; n < NSL / 2; ++n) {
+    slab0[n] = ex + slab_off(FMT, nsbH, g0 + n, 0);
+    slab0[NSL / 2 + n] = ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g0 + n, 0);
+  }
+  f32x4 acc[MT][NSL];
   zero_acc(acc);
-  gemm_tile<FMT>(rows, src, slab0, a.H, As, wv, lane, acc);
-  // SwiGLU: n = 0 holds gate, n = 1 up, for the same rows i
+  gemm_tile<FMT, true>(rows, src, slab0, a.H, As, wv, lane, acc);
+  // SwiGLU: slabs n < NSL/2 hold gate, n + NSL/2 up, for the same rows i;
+  // the lane's 4 consecutive i of one token row go out as one 8-byte store
   _Float16* act = reinterpret_cast<_Float16*>(a.w.act);
-  const int i = 16 * g + (lane & 15);
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MT; ++m) {
+    const int row = 16 * m + (lane & 15);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = 16 * m + 4 * (lane >> 4) + v;
-      if (row < rows) act[(size_t)(slot0 + row) * a.I + i] = (_Float16)(silu_f(acc[m][0][v]) * acc[m][1][v]);
+    for (int n = 0; n < NSL / 2; ++n) {
+      h2_t h[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+        h[v] = h2_t{(_Float16)(silu_fast(acc[m][n][2 * v]) * acc[m][NSL / 2 + n][2 * v]),
+                    (_Float16)(silu_fast(acc[m][n][2 * v + 1]) * acc[m][NSL / 2 + n][2 * v + 1])};
+      if (row < rows)
+        *reinterpret_cast<uint2*>(act + (size_t)(slot0 + row) * a.I + 16 * (g0 + n) + 4 * (lane >> 4)) =
+            make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]));
     }
+  }
 }
 
-// down: work item = 128 slots x 128 rows of H; wave w takes 32 rows of H
+// down: work item = 128 slots x dn_cols() rows of H; wave w takes NSL row
+// groups of 16 (waves past H, in the last column tile, compute but store nothing)
 template <int FMT>
-__global__ __launch_bounds__(64 * GEMM_WAVES, 2) void k_gemm_down(GemmArgs a) {
+__global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_down(GemmArgs a) {
+  constexpr int NSL = nsl<FMT>();
   __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
   int j, htile;
-  if (!work_item(a.w.meta[1], a.H / 128, j, htile)) return;
+  if (!work_item(a.w.meta[1], (a.H + dn_cols<FMT>() - 1) / dn_cols<FMT>(), j, htile)) return;
   const int4 tl = a.w.tiles[j];
   const int e = tl.x, slot0 = tl.y, rows = tl.z;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nsbI = a.I / SB_WEIGHTS;
   const _Float16* act = reinterpret_cast<const _Float16*>(a.w.act);
   // rows past the tile's end read its last row (in bounds; results not stored)
-  const _Float16* src[2];
+  const _Float16* src[AR];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    src[q] = act + (size_t)(slot0 + min(16 * (2 * wv + q) + (lane >> 2), rows - 1)) * a.I + 8 * (lane & 3);
-  // this wave's slabs: H rows 16 g0 .. 16 g0 + 31
-  const int g0 = htile * 2 * GEMM_WAVES + 2 * wv;
+  for (int q = 0; q < AR; ++q)
+    src[q] = act + (size_t)(slot0 + min(16 * (AR * wv + q) + (lane >> 2), rows - 1)) * a.I + 8 * (lane & 3);
+  // this wave's slabs: H rows 16 g0 .. 16 (g0 + NSL) - 1
+  const int g0w = (htile * GEMM_WAVES + wv) * NSL;
+  const bool on = g0w < a.H / GROUP_ROWS;            // whole waves: H is a multiple of 16 NSL (256)
+  const int g0 = on ? g0w : 0;
   const uint8_t* dn = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
-  const uint8_t* slab0[2] = {dn + slab_off(FMT, nsbI, g0, 0), dn + slab_off(FMT, nsbI, g0 + 1, 0)};
-  f32x4 acc[MT][2];
+  const uint8_t* slab0[NSL];
+#pragma unroll
+  for (int n = 0; n < NSL; ++n) slab0[n] = dn + slab_off(FMT, nsbI, g0 + n, 0);
+  f32x4 acc[MT][NSL];
   zero_acc(acc);
-  gemm_tile<FMT>(rows, src, slab0, a.I, As, wv, lane, acc);
+  gemm_tile<FMT, DOWN_TR>(rows, src, slab0, a.I, As, wv, lane, acc);
+  if (!on) return;
+  if constexpr (DOWN_TR) {
+    // the lane's 4 consecutive h of one token row go out as one 8-byte store
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m) {
+      const int row = 16 * m + (lane & 15);
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 16 * m + 4 * (lane >> 4) + v;
+      for (int n = 0; n < NSL; ++n)
         if (row < rows)
-          a.w.ybf[(size_t)(slot0 + row) * a.H + 16 * (g0 + n) + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
-      }
+          *reinterpret_cast<uint2*>(a.w.ybf + (size_t)(slot0 + row) * a.H + 16 * (g0 + n) + 4 * (lane >> 4)) =
+              make_uint2(cvt_bf16x2(acc[m][n][0], acc[m][n][1]), cvt_bf16x2(acc[m][n][2], acc[m][n][3]));
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < NSL; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = 16 * m + 4 * (lane >> 4) + v;
+          if (row < rows)
+            a.w.ybf[(size_t)(slot0 + row) * a.H + 16 * (g0 + n) + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
+        }
+  }
 }
 
 struct CombineArgs {
@@ -922,8 +973,8 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
   g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
   const int max_tiles = W.max_tiles;
-  launch(tr, k_gemm_gateup<FMT>, dim3(work_grid(max_tiles, L.I / 64)), dim3(64 * GEMM_WAVES), 0, s, g);
-  launch(tr, k_gemm_down<FMT>, dim3(work_grid(max_tiles, L.H / 128)), dim3(64 * GEMM_WAVES), 0, s, g);
+  launch(tr, k_gemm_gateup<FMT>, dim3(work_grid(max_tiles, L.I / gu_rows<FMT>())), dim3(64 * GEMM_WAVES), 0, s, g);
+  launch(tr, k_gemm_down<FMT>, dim3(work_grid(max_tiles, (L.H + dn_cols<FMT>() - 1) / dn_cols<FMT>())), dim3(64 * GEMM_WAVES), 0, s, g);
   return hipGetLastError();
 }
 
