@@ -470,93 +470,107 @@ struct ExpertArgs {
   Work w;
 };
 
-// Workgroup barrier that orders LDS accesses only: global memory requests
-// (prefetches) stay in flight across it.
-__device__ inline void lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Active expert u of this call: the experts chosen by any token in ascending
-// id order, then the shared expert (id E, every token, weight 1).  Every
-// thread of the workgroup returns the same values; false when u is past the
-// last one.  LDS: bits[ceil(E/32)], info[4], wts[DECODE_MAX_T].  issue() is
-// called once the first pair loads are requested (memory requests that must
-// not delay them go there).
+// id order, then the shared expert (id E, every token, weight 1).  Each wave
+// finds it on its own, with no workgroup barrier: it marks the chosen ids in
+// its own 4096-bit LDS mask (bits), counts the set bits below each 64-bit
+// word, and takes the u-th.  Returns false when u is past the last one.
+// wt: in lane t < T, token t's routing weight to this expert (0 when not
+// routed).  issue() is called once the pair loads are requested (memory
+// requests that must not delay them go there).
 template <typename F>
-__device__ inline bool active_expert(const ExpertArgs& a, int u, uint32_t* bits, int* info, float* wts,
-                                     int& e_out, uint32_t& mask_out, int& n_active, F&& issue) {
-  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63;
-  const int T = a.T, k = a.k, E = a.E, P = T * k, nwords = (E + 31) >> 5;
-  // the pairs: one per thread for the first blockDim.x; loaded
-  // unconditionally (clamped) so that the loads are all in flight
-  const int p0 = min(tid, P - 1);
-  const int my_e = a.w.topk_idx[p0];
-  const float my_w = a.w.topk_w[p0];
+__device__ inline bool wave_route(const ExpertArgs& a, int u, uint64_t* bits, int& e_out, uint32_t& mask_out,
+                                  int& n_active, float& wt, F&& issue) {
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, k = a.k, E = a.E, P = T * k, nwords = (E + 63) >> 6;
+  // pairs lane and 64 + lane, loaded unconditionally (clamped) so that both
+  // loads are in flight together; pairs past 128 (T k > 128) are read later
+  int ids[2];
+  float ws[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = min(lane + 64 * i, P - 1);
+    ids[i] = a.w.topk_idx[p];
+    ws[i] = a.w.topk_w[p];
+  }
   __builtin_amdgcn_sched_barrier(0);
   issue();
   __builtin_amdgcn_sched_barrier(0);
-  for (int i = tid; i < nwords; i += nt) bits[i] = 0u;
-  if (tid < DECODE_MAX_T) wts[tid] = 0.f;
-  if (tid == 0) info[1] = 0;
-  lds_sync();
-  if (tid < P) atomicOr(&bits[my_e >> 5], 1u << (my_e & 31));
-  for (int p = tid + nt; p < P; p += nt) {
-    const int e = a.w.topk_idx[p];
-    atomicOr(&bits[e >> 5], 1u << (e & 31));
-  }
-  lds_sync();
-  if (tid < 64) {
-    // words lane and 64 + lane (E <= 4096); inclusive prefix counts in word order
-    const uint32_t w0 = lane < nwords ? bits[lane] : 0u;
-    const uint32_t w1 = lane + 64 < nwords ? bits[lane + 64] : 0u;
-    const int c0 = __popc(w0), c1 = __popc(w1);
-    int s0 = c0, s1 = c1;
+  bits[lane] = 0ull;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y0 = __shfl_up(s0, o, 64), y1 = __shfl_up(s1, o, 64);
-      if (lane >= o) { s0 += y0; s1 += y1; }
-    }
-    const int tot0 = __shfl(s0, 63, 64);
-    s1 += tot0;
-    int word = -1, r = 0;
-    uint32_t wbits = 0u;
-    if (u < s0 && u >= s0 - c0) { word = lane; r = u - (s0 - c0); wbits = w0; }
-    if (u < s1 && u >= s1 - c1) { word = lane + 64; r = u - (s1 - c1); wbits = w1; }
-    if (word >= 0) {
-      for (int j = 0; j < r; ++j) wbits &= wbits - 1u;    // drop the r lowest set bits
-      info[0] = word * 32 + __builtin_ctz(wbits);
-    }
-    if (lane == 63) info[2] = s1;
+  for (int i = 0; i < 2; ++i)
+    if (lane + 64 * i < P) atomicOr(&bits[ids[i] >> 6], 1ull << (ids[i] & 63));
+  for (int p = lane + 128; p < P; p += 64) {
+    const int id = a.w.topk_idx[p];
+    atomicOr(&bits[id >> 6], 1ull << (id & 63));
   }
-  lds_sync();
-  const int U = __builtin_amdgcn_readfirstlane(info[2]);    // the same in every lane: keep it scalar
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  uint64_t w = lane < nwords ? bits[lane] : 0ull;
+  const int c = __popcll(w);
+  int incl = c;                                      // set bits in words 0 .. lane
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  const int U = __builtin_amdgcn_readlane(incl, 63);
   n_active = U + a.n_shared;
   if (u >= n_active) return false;
+  int e = E;                                         // the shared expert past the routed ones
   if (u < U) {
-    const int e = info[0];
-    if (tid < P && my_e == e) {
-      atomicOr(&info[1], 1 << (tid / k));
-      wts[tid / k] = my_w;
+    const bool owner = u >= incl - c && u < incl;    // this lane's word holds the u-th set bit
+    int id = 0;
+    if (owner) {
+      for (int r = u - (incl - c); r > 0; --r) w &= w - 1ull;   // drop the lower set bits
+      id = 64 * lane + __builtin_ctzll(w);
     }
-    for (int p = tid + nt; p < P; p += nt) {
-      if (a.w.topk_idx[p] == e) {
-        const int t = p / k;
-        atomicOr(&info[1], 1 << t);
-        wts[t] = a.w.topk_w[p];
+    e = __builtin_amdgcn_readlane(id, __builtin_ctzll(__ballot(owner)));
+  }
+  // tokens routed to e and their weights (the shared expert: every token, weight 1)
+  uint32_t m = 0u;
+  wt = 0.f;
+  if (e < E) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = lane + 64 * i;
+      const bool hit = p < P && ids[i] == e;
+      if (hit) m |= 1u << (p / k);
+      // the weight of token lane: its pair with e sits in lane p of register i
+      const uint64_t hb = __ballot(hit);
+      for (uint64_t b = hb; b; b &= b - 1ull) {
+        const int src = __builtin_ctzll(b);
+        const float wv = __shfl(ws[i], src, 64);
+        if (lane == (src + 64 * i) / k) wt = wv;
       }
     }
-    lds_sync();
-    e_out = __builtin_amdgcn_readfirstlane(e);
-    mask_out = (uint32_t)__builtin_amdgcn_readfirstlane(info[1]);
+    for (int p = lane + 128; p < P; p += 64) {
+      if (a.w.topk_idx[p] == e) m |= 1u << (p / k);
+    }
+    for (int p0 = 128; p0 < P; p0 += 64) {
+      const int p = min(p0 + lane, P - 1);
+      const bool hit = p0 + lane < P && a.w.topk_idx[p] == e;
+      const float wp = a.w.topk_w[p];
+      const uint64_t hb = __ballot(hit);
+      for (uint64_t b = hb; b; b &= b - 1ull) {
+        const int src = __builtin_ctzll(b);
+        const float wv = __shfl(wp, src, 64);
+        if (lane == (p0 + src) / k) wt = wv;
+      }
+    }
+    // OR over the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m |= (uint32_t)__shfl_xor((int)m, o, 64);
   } else {
-    e_out = E;
-    mask_out = (1u << T) - 1u;
-    lds_sync();
-    if (tid < T) wts[tid] = 1.f;
-    lds_sync();
+    m = (1u << T) - 1u;
+    wt = lane < T ? 1.f : 0.f;
   }
+  e_out = __builtin_amdgcn_readfirstlane(e);
+  mask_out = (uint32_t)__builtin_amdgcn_readfirstlane((int)m);
   return true;
 }
 
@@ -662,9 +676,7 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   // partial sums [GU_SLABS][64 lanes] x 4
   extern __shared__ float4 red4[];
   float* red = reinterpret_cast<float*>(red4);
-  __shared__ uint32_t s_bits[128];
-  __shared__ int s_info[4];
-  __shared__ float s_wts[DECODE_MAX_T];
+  __shared__ uint64_t s_bits[16][64];                // per wave: the chosen-expert mask
   const int u = blockIdx.y, gp = blockIdx.x;
   const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
@@ -679,19 +691,20 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
   int e, U;
   uint32_t mask;
-  if (!active_expert(a, u, s_bits, s_info, s_wts, e, mask, U,
-                     [&]() __attribute__((always_inline)) { gu_aload_lds(xr, xvoff, wv, lds_a); })) {
+  float wt;
+  if (!wave_route(a, u, s_bits[wv], e, mask, U, wt,
+                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, xvoff, wv, lds_a); })) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
     return;
   }
-  if (gp == 0) {
+  if (gp == 0 && wv == 0) {
     // routing of this active expert for the down kernel
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
       a.w.udesc[(size_t)u * DESC] = e;
       a.w.udesc[(size_t)u * DESC + 1] = (int)mask;
       if (u == 0) a.w.meta[0] = U;
     }
-    if (threadIdx.x < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + threadIdx.x] = s_wts[threadIdx.x];
+    if (lane < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + lane] = wt;
   }
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
   const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
