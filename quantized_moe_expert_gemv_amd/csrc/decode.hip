@@ -38,6 +38,8 @@
 // extra MFMA against a constant operand.  Every product is exact; the fp32
 // accumulation and the 2^-22 activation split are the only roundings.  The
 // fp16 block scale d multiplies each block's 16x16 result in fp32.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -463,6 +465,7 @@ struct ExpertArgs {
   size_t stride;
   int H, I, E, k, T, P, n_shared;
   uint32_t actp_bytes;       // bytes of the activation rows of this call
+  int umax;                  // most active experts a call of T tokens can have (+ shared)
   const void* x;
   int x_f32;
   uint32_t flags;
@@ -590,19 +593,39 @@ template <int FMT, int G> struct GuStage {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// the activation operand of superblock sb: 8 blocks x 64 lanes x 16 B,
-// copied by the memory unit straight into this wave's LDS region (lane l's
-// 16 bytes of block b land at b * 1 KiB + 16 l), no registers on the way
-__device__ inline void gu_aload_lds(rsrc_t xr, uint32_t xvoff, int sb, uint4* lds_a) {
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(lds_a + bb * 64), 16, xvoff + bb * BLOCK_W * 2,
-                                             (uint32_t)sb * SB_WEIGHTS * 2, 0, 0);
+// The token rows of superblock sb in this wave's LDS region, compact: row
+// r = q T + t (part q, token t) holds the superblock's 512 bytes of that row;
+// rows 2 i and 2 i + 1 come from one buffer->LDS load (1 KiB, lane j's 16
+// bytes land at 16 j) into slot i of the region (slots 1040 bytes apart).
+// Row 2 i + h keeps its 16-byte chunk g at 512 h + 16 (g ^ 8 h) of the slot,
+// so the 16 rows one operand read touches (a 64-byte block of every row)
+// fall into distinct LDS banks for T <= 8.  Slot T holds a row of zeros for
+// the A-operand rows of tokens past T.  T loads per superblock instead of 8
+// for a 16-row operand.
+constexpr int GU_SLOT = 1040;
+
+__device__ inline int gu_region_bytes(int T) { return max(8192, (T + 1) * GU_SLOT); }
+
+__device__ inline void gu_aload_lds(rsrc_t xr, int T, int H, int sb, int lane, char* region) {
+  const int h = lane >> 5, g = (lane & 31) ^ (8 * h);
+  for (int i = 0; i < T; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(region + i * GU_SLOT), 16,
+                                             (uint32_t)((2 * i + h) * 2 * H + 16 * g), (uint32_t)sb * SB_WEIGHTS * 2,
+                                             0, 0);
 }
 
 // vector-memory instructions gu_load issues (codes, then the scales, per slab)
 template <int FMT, int G>
 constexpr int gu_load_count() { return 2 * G * (FMT == 2 ? 2 : 3); }
+
+// LDS address of this lane's A operand of block BB: row arow (i = arow / 2,
+// h = arow % 2), chunk 4 BB + ks stored at 16 ((4 BB + ks) ^ 8 h); as BB ^ 2 h
+// = BB + 2 h or BB - 2 h by bit 1 of BB, two per-lane bases cover every BB
+struct ALane { const char* plus; const char* minus; };
+template <int BB>
+__device__ inline const uint4* a_operand(const ALane& al) {
+  return reinterpret_cast<const uint4*>(((BB >> 1) & 1 ? al.minus : al.plus) + 64 * BB);
+}
 
 // The weights of one superblock, requested in the order the compute takes
 // them: slab pairs (gate j, up j).
@@ -627,11 +650,10 @@ __device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int
 // operand from LDS, the offset MFMA, the 2 NJ product MFMAs (independent, so
 // their latency overlaps), then their scale FMAs.
 template <int FMT, int G, int J0, int NJ>
-__device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const uint4* lds_a, int lane,
-                                        float (&acc)[2 * G][4]) {
+__device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const ALane& al, float (&acc)[2 * G][4]) {
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
-    const f16x8 af = as_f16x8(lds_a[BB * 64 + lane]);                             \
+    const f16x8 af = as_f16x8(*a_operand<BB>(al));                                \
     const f32x4 off = block_offset<FMT>(af);                                      \
     f32x4 d[2 * NJ];                                                              \
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                              \
@@ -656,26 +678,25 @@ __device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const uint4* 
 // have arrived (the compiler waits on the half's registers; the other half
 // stays in flight).
 template <int FMT, int G>
-__device__ inline void gu_compute(const GuStage<FMT, G>& st, const uint4* lds_a, int lane, float (&acc)[2 * G][4]) {
+__device__ inline void gu_compute(const GuStage<FMT, G>& st, const ALane& al, float (&acc)[2 * G][4]) {
   // the activation operand was requested by buffer->LDS loads before the
   // gu_load_count() weight loads: once no more than those are outstanding it
   // has landed (the compiler does not track these loads; the memory clobber
   // keeps every LDS read below this point)
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(gu_load_count<FMT, G>()) : "memory");
-  gu_compute_pairs<FMT, G, 0, G / 2>(st, lds_a, lane, acc);
+  gu_compute_pairs<FMT, G, 0, G / 2>(st, al, acc);
   // (the empty memory clobber makes the second half re-read the operands
   // from LDS instead of keeping every block's operand in registers)
   asm volatile("" ::: "memory");
-  gu_compute_pairs<FMT, G, G / 2, G / 2>(st, lds_a, lane, acc);
+  gu_compute_pairs<FMT, G, G / 2, G / 2>(st, al, acc);
 }
 
 template <int FMT, int G>
 __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
-  // per wave 8 KiB of LDS: its superblock's activation operand, then its
+  // per wave gu_region_bytes(T) of LDS: its superblock's token rows, then its
   // partial sums [GU_SLABS][64 lanes] x 4
   extern __shared__ float4 red4[];
-  float* red = reinterpret_cast<float*>(red4);
   __shared__ uint64_t s_bits[16][64];                // per wave: the chosen-expert mask
   const int u = blockIdx.y, gp = blockIdx.x;
   const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
@@ -683,17 +704,21 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = lane >> 4;                          // K-slice
   const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(NPART * T * H * 2));
-  uint4* lds_a = reinterpret_cast<uint4*>(red4) + wv * 512;
-  // A row (part, token): rows of tokens past T read past the buffer (zeros)
+  const int wreg = gu_region_bytes(T);
+  char* region = reinterpret_cast<char*>(red4) + wv * wreg;
+  // A row (part, token) of this lane: its token row, the zero row past T
   const int tok = arow_token(lane);
-  const uint32_t xvoff = tok < T ? (uint32_t)(((arow_part(lane) * T + tok) * H + 8 * ks) * 2) : OOB;
+  const int arow = tok < T ? arow_part(lane) * T + tok : 2 * T;
+  const char* rbase = region + (arow >> 1) * GU_SLOT + 512 * (arow & 1) + 16 * ks;
+  const ALane al{rbase + 128 * (arow & 1), rbase - 128 * (arow & 1)};
+  reinterpret_cast<uint2*>(region + T * GU_SLOT)[lane] = make_uint2(0u, 0u);   // the zero row
   // the first superblock's activation operand does not depend on the expert:
   // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
   int e, U;
   uint32_t mask;
   float wt;
   if (!wave_route(a, u, s_bits[wv], e, mask, U, wt,
-                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, xvoff, wv, lds_a); })) {
+                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, T, H, wv, lane, region); })) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
     return;
   }
@@ -717,14 +742,14 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   for (int sb = wv; sb < nsb; sb += nw) {
     // the activation operand first (the first one is already requested),
     // then the weights; the compute waits for each part as it needs it
-    if (sb > wv) gu_aload_lds(xr, xvoff, sb, lds_a);
+    if (sb > wv) gu_aload_lds(xr, T, H, sb, lane, region);
     __builtin_amdgcn_sched_barrier(0);
     GuStage<FMT, G> st;
     gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
-    gu_compute<FMT, G>(st, lds_a, lane, acc);
+    gu_compute<FMT, G>(st, al, acc);
   }
   // raw 16x16 results to this wave's LDS region (its operand is consumed)
-  float4* dst = reinterpret_cast<float4*>(red) + (size_t)wv * 512 + lane;
+  float4* dst = reinterpret_cast<float4*>(region) + lane;
 #pragma unroll
   for (int s = 0; s < GU_SLABS; ++s) dst[s * 64] = make_float4(acc[s][0], acc[s][1], acc[s][2], acc[s][3]);
   __syncthreads();
@@ -736,8 +761,9 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     const int l0 = 16 * (t >> 2) + row, l1 = l0 + 32, v = t & 3;
     float g = 0.f, uu = 0.f;
     for (int w = 0; w < nw; ++w) {
-      const float* rg = red + (size_t)w * 2048 + (size_t)gi * 256 + v;
-      const float* ru = red + (size_t)w * 2048 + (size_t)(GU_GROUPS + gi) * 256 + v;
+      const float* rw = reinterpret_cast<const float*>(reinterpret_cast<const char*>(red4) + w * wreg);
+      const float* rg = rw + (size_t)gi * 256 + v;
+      const float* ru = rw + (size_t)(GU_GROUPS + gi) * 256 + v;
       g += rg[4 * l0] + rg[4 * l1];
       uu += ru[4 * l0] + ru[4 * l1];
     }
@@ -819,11 +845,13 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
-  int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [U][2]: expert, token mask
-  float* lwt = reinterpret_cast<float*>(ldesc + 2 * U);         // [U][WTAB]
-  float* red = lds_dn + ((DESC + WTAB) * U + 3) / 4 * 4;        // [nw][64 lanes][4], 16-B aligned
-  for (int i = threadIdx.x; i < DESC * U; i += blockDim.x) ldesc[i] = a.w.udesc[i];
-  for (int i = threadIdx.x; i < U * WTAB; i += blockDim.x) lwt[i] = a.w.wtab[i];
+  // the routing of the active experts: all umax entries are copied (the
+  // entries past U are stale and unused), so these loads do not wait for U
+  int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [umax][2]: expert, token mask
+  float* lwt = reinterpret_cast<float*>(ldesc + DESC * a.umax); // [umax][WTAB]
+  float* red = lds_dn + ((DESC + WTAB) * a.umax + 3) / 4 * 4;   // [nw][64 lanes][4], 16-B aligned
+  for (int i = threadIdx.x; i < DESC * a.umax; i += blockDim.x) ldesc[i] = a.w.udesc[i];
+  for (int i = threadIdx.x; i < a.umax * WTAB; i += blockDim.x) lwt[i] = a.w.wtab[i];
   __syncthreads();
 
   const int units = U * nsb;
@@ -872,6 +900,7 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.T = c.T; a.P = c.T * L.k; a.n_shared = L.n_shared;
   a.x = c.x; a.x_f32 = c.x_f32; a.flags = c.flags; a.out = c.out; a.w = W;
   const int umax = (a.P < L.E ? a.P : L.E) + L.n_shared;
+  a.umax = umax;
   a.actp_bytes = (uint32_t)((size_t)umax * c.T * NPART * L.I * 2);
   // gate/up waves: the largest divisor of the superblock count that is <= 10,
   // so every wave takes the same number of superblocks.  Row groups per
@@ -883,7 +912,7 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
     if (nsbH % d == 0) nwg = d;
   const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
-  const size_t lds_gu = (size_t)nwg * 8192;                     // <= 80 KiB: ceiling raised at create
+  const size_t lds_gu = (size_t)nwg * std::max(8192, (c.T + 1) * 1040);   // <= 94 KiB: ceiling raised at create
   const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * 64 * 4 * 4;
   const dim3 ggu(L.I / (16 * G), umax);
   if constexpr (FMT == 2) {
