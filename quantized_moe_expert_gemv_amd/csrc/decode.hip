@@ -778,46 +778,60 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
 
 // down + weighted combine: one 16-row group of H per workgroup, every active
 // expert; waves take (expert, superblock) units in turn, with the loads of
-// the next DN_DEPTH - 1 units in flight while one computes.  The routing of
-// all active experts sits in LDS.
+// the next units in flight while one computes.  The routing of all active
+// experts sits in LDS.  A unit's activation rows are staged compactly in the
+// wave's LDS (as the gate/up token rows: 2 T rows in T buffer->LDS loads);
+// lanes of tokens past T or not routed to the unit's expert read the wave's
+// zero row.
 constexpr int DN_WAVES = 8;
-constexpr int DN_DEPTH = 3;
+template <int TT> constexpr int dn_depth() { return TT <= 4 ? 3 : 2; }   // units in flight per wave
+template <int TT> constexpr int dn_wave_bytes() { return (dn_depth<TT>() * TT + 1) * GU_SLOT; }
 
 template <int FMT> struct DownUnit {
   Codes<FMT> cd;
   uint4 sc;
-  uint4 av[8];
 };
 
-template <int FMT>
-__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, DownUnit<FMT>& du) {
-  const int lane = threadIdx.x & 63, r = lane & 15, ks = lane >> 4;
+// vector-memory instructions of one unit: TT activation loads, then codes and scales
+template <int FMT, int TT>
+constexpr int dn_load_count() { return TT + (FMT == 2 ? 2 : 3); }
+
+template <int FMT, int TT>
+__device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, char* slot,
+                                 DownUnit<FMT>& du) {
+  const int lane = threadIdx.x & 63, r = lane & 15;
   const int u = unit / nsb, sb = unit - u * nsb;
   const int e = __builtin_amdgcn_readfirstlane(ldesc[2 * u]);
-  const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[2 * u + 1]);
+  // activation rows (part, token) of expert u, superblock sb: rows 2 i and
+  // 2 i + 1 per load, chunks swizzled as the gate/up token rows
+  const rsrc_t ar = make_rsrc(a.w.actp, a.actp_bytes);
+  const int h = lane >> 5, gch = (lane & 31) ^ (8 * h);
+  const uint32_t asoff = (uint32_t)(((size_t)u * NPART * TT * a.I + (size_t)sb * SB_WEIGHTS) * 2);
+#pragma unroll
+  for (int i = 0; i < TT; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(slot + i * GU_SLOT), 16,
+                                             (uint32_t)((2 * i + h) * a.I * 2 + 16 * gch), asoff, 0, 0);
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
   const uint32_t soff = (uint32_t)(down_off(FMT, a.H, a.I) + ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256));
   bload_codes<FMT>(wr, soff, lane, du.cd);
   du.sc = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
-  // A row (part, token t): the activation of (expert u, token t); tokens past
-  // T or not routed to u read past the buffer (zeros)
-  const int t = arow_token(lane);
-  const bool routed = t < a.T && ((mask >> t) & 1u);
-  const rsrc_t ar = make_rsrc(a.w.actp, a.actp_bytes);
-  const uint32_t voff = routed ? (uint32_t)(((arow_part(lane) * a.T + t) * a.I + 8 * ks) * 2) : OOB;
-  const uint32_t asoff = (uint32_t)(((size_t)u * NPART * a.T * a.I + (size_t)sb * SB_WEIGHTS) * 2);
-#pragma unroll
-  for (int bb = 0; bb < 8; ++bb) du.av[bb] = bload4(ar, voff + bb * BLOCK_W * 2, asoff);
 }
 
 // out[v] += routing weight of this lane's D-row token v * (this unit's 16x16 product)
 template <int FMT>
-__device__ inline void down_compute(const DownUnit<FMT>& du, const float* wt, float* out) {
+__device__ inline void down_compute(const DownUnit<FMT>& du, const ALane& al, const float* wt, float* out) {
   f32x4 dd[2];
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // the 8 operand reads go out together (their latencies overlap)
+  f16x8 afs[8];
+  afs[0] = as_f16x8(*a_operand<0>(al)); afs[1] = as_f16x8(*a_operand<1>(al));
+  afs[2] = as_f16x8(*a_operand<2>(al)); afs[3] = as_f16x8(*a_operand<3>(al));
+  afs[4] = as_f16x8(*a_operand<4>(al)); afs[5] = as_f16x8(*a_operand<5>(al));
+  afs[6] = as_f16x8(*a_operand<6>(al)); afs[7] = as_f16x8(*a_operand<7>(al));
+  __builtin_amdgcn_sched_barrier(0);
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
-    const f16x8 af = as_f16x8(du.av[BB]);                                         \
+    const f16x8 af = afs[BB];                                                     \
     dd[BB & 1] = block_product<FMT, BB>(af, du.cd, block_offset<FMT>(af));        \
     if (BB > 0) {                                                                 \
       const float ds = block_scale<FMT, (BB > 0 ? BB - 1 : 0)>(du.sc);            \
@@ -836,43 +850,73 @@ __device__ inline void down_compute(const DownUnit<FMT>& du, const float* wt, fl
   }
 }
 
-template <int FMT>
+// LDS bytes of the down kernel: routing table, partial sums, staging
+__host__ __device__ inline size_t dn_table_bytes(int umax) { return ((size_t)umax * (DESC + WTAB) * 4 + 15) & ~(size_t)15; }
+
+// dynamic LDS of the down kernel for T tokens (the routing table, partial
+// sums, staged activation rows)
+template <int TT>
+size_t down_lds(int umax) { return dn_table_bytes(umax) + (size_t)DN_WAVES * 1024 + (size_t)DN_WAVES * dn_wave_bytes<TT>(); }
+
+template <int FMT, int TT>
 __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
+  constexpr int DEPTH = dn_depth<TT>();
   extern __shared__ float4 lds_dn4[];
-  float* lds_dn = reinterpret_cast<float*>(lds_dn4);
+  char* lds = reinterpret_cast<char*>(lds_dn4);
   const int U = a.w.meta[0];
-  const int H = a.H, I = a.I, nsb = I / SB_WEIGHTS, T = a.T;
-  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int H = a.H, I = a.I, nsb = I / SB_WEIGHTS;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6, ks = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
   // the routing of the active experts: all umax entries are copied (the
   // entries past U are stale and unused), so these loads do not wait for U
-  int* ldesc = reinterpret_cast<int*>(lds_dn);                  // [umax][2]: expert, token mask
+  int* ldesc = reinterpret_cast<int*>(lds);                     // [umax][2]: expert, token mask
   float* lwt = reinterpret_cast<float*>(ldesc + DESC * a.umax); // [umax][WTAB]
-  float* red = lds_dn + ((DESC + WTAB) * a.umax + 3) / 4 * 4;   // [nw][64 lanes][4], 16-B aligned
+  const size_t tb = dn_table_bytes(a.umax);
+  float* red = reinterpret_cast<float*>(lds + tb);              // [nw][64 lanes][4]
+  char* stage = lds + tb + (size_t)DN_WAVES * 1024 + (size_t)wv * dn_wave_bytes<TT>();
+  char* zrow = stage + DEPTH * TT * GU_SLOT;
+  reinterpret_cast<uint2*>(zrow)[lane] = make_uint2(0u, 0u);
   for (int i = threadIdx.x; i < DESC * a.umax; i += blockDim.x) ldesc[i] = a.w.udesc[i];
   for (int i = threadIdx.x; i < a.umax * WTAB; i += blockDim.x) lwt[i] = a.w.wtab[i];
   __syncthreads();
 
   const int units = U * nsb;
   const int wt_off = 4 * ((lane >> 4) & 1);                     // token of this lane's D element 0
+  const int tok = arow_token(lane), part = arow_part(lane);
   float out[4] = {0.f, 0.f, 0.f, 0.f};
-  DownUnit<FMT> b[DN_DEPTH];
+  DownUnit<FMT> b[DEPTH];
   // every load unconditional (unit index clamped; a repeated unit is
   // loaded but not computed), so the loads of a step are all in flight
 #pragma unroll
-  for (int q = 0; q < DN_DEPTH; ++q) down_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, b[q]);
-  for (int unit = wv; unit < units; unit += DN_DEPTH * nw) {
+  for (int q = 0; q < DEPTH; ++q)
+    down_load<FMT, TT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, stage + q * TT * GU_SLOT, b[q]);
+  for (int unit = wv; unit < units; unit += DEPTH * nw) {
 #pragma unroll
-    for (int q = 0; q < DN_DEPTH; ++q) {
+    for (int q = 0; q < DEPTH; ++q) {
       const int cu = unit + q * nw;
-      if (cu < units) down_compute<FMT>(b[q], lwt + (cu / nsb) * WTAB + wt_off, out);
-      down_load<FMT>(a, ldesc, min(cu + DN_DEPTH * nw, units - 1), nsb, g, b[q]);
+      // this unit's activation rows have landed once no more than the loads
+      // issued after them are outstanding (its own weights and the other
+      // units' loads); the memory clobber keeps the LDS reads below
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(dn_load_count<FMT, TT>() - TT + (DEPTH - 1) * dn_load_count<FMT, TT>())
+                   : "memory");
+      if (cu < units) {
+        const int uu = cu / nsb;
+        const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[2 * uu + 1]);
+        const bool routed = tok < TT && ((mask >> tok) & 1u);
+        const int arow = part * TT + tok;
+        const char* base = routed ? stage + q * TT * GU_SLOT + (arow >> 1) * GU_SLOT + 512 * (arow & 1) : zrow;
+        const int hh = routed ? (arow & 1) : 0;
+        const ALane al{base + 16 * ks + 128 * hh, base + 16 * ks - 128 * hh};
+        down_compute<FMT>(b[q], al, lwt + uu * WTAB + wt_off, out);
+      }
+      asm volatile("" ::: "memory");                // the slot is refilled after its reads
+      down_load<FMT, TT>(a, ldesc, min(cu + DEPTH * nw, units - 1), nsb, g, stage + q * TT * GU_SLOT, b[q]);
     }
   }
   reinterpret_cast<float4*>(red)[(size_t)wv * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * T; idx += blockDim.x) {
+  __syncthreads();                                   // (also drains the last, unused loads)
+  for (int idx = threadIdx.x; idx < 16 * TT; idx += blockDim.x) {
     const int row = idx & 15, t = idx >> 4;
     // D row (part q, token t) sits in lane 16 (2q + t / 4) + row, element t % 4
     const int l0 = 16 * (t >> 2) + row, l1 = l0 + 32, v = t & 3;
@@ -913,7 +957,7 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
   const size_t lds_gu = (size_t)nwg * std::max(8192, (c.T + 1) * 1040);   // <= 94 KiB: ceiling raised at create
-  const size_t lds_dn = (size_t)umax * (DESC + WTAB) * 4 + 16 + (size_t)DN_WAVES * 64 * 4 * 4;
+
   const dim3 ggu(L.I / (16 * G), umax);
   if constexpr (FMT == 2) {
     if (wide) launch(tr, k_gateup<FMT, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
@@ -921,8 +965,36 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   } else {
     launch(tr, k_gateup<FMT, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
   }
-  launch(tr, k_down<FMT>, dim3(L.H / 16), dim3(64 * DN_WAVES), lds_dn, s, a);
+  switch (c.T) {
+#define STRATA_DOWN(TT)                                                                            \
+    case TT:                                                                                       \
+      launch(tr, k_down<FMT, TT>, dim3(L.H / 16), dim3(64 * DN_WAVES), down_lds<TT>(umax), s, a);    \
+      break;
+    STRATA_DOWN(1) STRATA_DOWN(2) STRATA_DOWN(3) STRATA_DOWN(4)
+    STRATA_DOWN(5) STRATA_DOWN(6) STRATA_DOWN(7) STRATA_DOWN(8)
+#undef STRATA_DOWN
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+template <int FMT, int TT>
+hipError_t raise_down_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_down<FMT, TT>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)DECODE_LDS_MAX);
+}
+
+template <int FMT>
+hipError_t raise_down_lds_all() {
+  hipError_t e = raise_down_lds<FMT, 1>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 2>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 3>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 4>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 5>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 6>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 7>();
+  if (e == hipSuccess) e = raise_down_lds<FMT, 8>();
+  return e;
 }
 
 template <int FMT>
@@ -948,10 +1020,30 @@ hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
 }  // namespace
 
 // The gate/up kernels keep up to 80 KiB of dynamic LDS (8 KiB per wave).
+bool decode_fits(int T, int k, int E, int n_shared) {
+  if (T < 1 || T > DECODE_MAX_T) return false;
+  const int umax = (T * k < E ? T * k : E) + n_shared;
+  size_t need = 0;
+  switch (T) {
+    case 1: need = down_lds<1>(umax); break;
+    case 2: need = down_lds<2>(umax); break;
+    case 3: need = down_lds<3>(umax); break;
+    case 4: need = down_lds<4>(umax); break;
+    case 5: need = down_lds<5>(umax); break;
+    case 6: need = down_lds<6>(umax); break;
+    case 7: need = down_lds<7>(umax); break;
+    default: need = down_lds<8>(umax); break;
+  }
+  return need <= DECODE_LDS_MAX;
+}
+
 hipError_t prepare_decode_kernels() {
   hipError_t e = raise_gateup_lds<2>();
   if (e == hipSuccess) e = raise_gateup_lds<3>();
   if (e == hipSuccess) e = raise_gateup_lds<4>();
+  if (e == hipSuccess) e = raise_down_lds_all<2>();
+  if (e == hipSuccess) e = raise_down_lds_all<3>();
+  if (e == hipSuccess) e = raise_down_lds_all<4>();
   return e;
 }
 

@@ -80,6 +80,11 @@ hipError_t launch_router_split(const Layer& L, hipStream_t s);
 // gate/up and down + combine; prepare_decode_kernels raises the gate/up
 // kernels' dynamic-LDS ceiling (once per process is enough)
 hipError_t prepare_decode_kernels();
+// LDS ceiling of the decode kernels, and whether the decode path covers T
+// tokens of a layer with top-k k over E experts (+ n_shared): its down kernel
+// keeps the routing table and the staged activation rows in LDS
+constexpr size_t DECODE_LDS_MAX = 160 * 1024;
+bool decode_fits(int T, int k, int E, int n_shared);
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);

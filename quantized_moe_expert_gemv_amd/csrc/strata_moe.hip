@@ -140,18 +140,22 @@ int check_call(strata_moe* h, const void* x, int32_t x_dtype, int32_t T) {
   return STRATA_OK;
 }
 
-bool use_decode(int T, uint32_t flags) {
+bool fits(const strata_moe_config& c, int T) { return decode_fits(T, c.top_k, c.n_experts, c.n_shared); }
+
+bool use_decode(const strata_moe_config& c, int T, uint32_t flags) {
   if (flags & STRATA_FORCE_PREFILL) return false;
-  return T <= STRATA_DECODE_MAX_T;
+  return fits(c, T);
 }
 
-int check_flags(int T, uint32_t flags) {
+int check_flags(const strata_moe_config& c, int T, uint32_t flags) {
   const uint32_t known = STRATA_ACCUMULATE | STRATA_ADD_INPUT | STRATA_FORCE_DECODE | STRATA_FORCE_PREFILL;
   if (flags & ~known) return fail(STRATA_E_INVALID, "unknown flag bits 0x%x", flags & ~known);
   if ((flags & STRATA_FORCE_DECODE) && (flags & STRATA_FORCE_PREFILL))
     return fail(STRATA_E_INVALID, "FORCE_DECODE and FORCE_PREFILL are exclusive");
   if ((flags & STRATA_FORCE_DECODE) && T > STRATA_DECODE_MAX_T)
     return fail(STRATA_E_UNSUPPORTED, "the decode path takes at most %d tokens", STRATA_DECODE_MAX_T);
+  if ((flags & STRATA_FORCE_DECODE) && !fits(c, T))
+    return fail(STRATA_E_UNSUPPORTED, "the decode path's LDS does not hold %d tokens at top_k %d", T, c.top_k);
   if ((flags & STRATA_ACCUMULATE) && (flags & STRATA_ADD_INPUT))
     return fail(STRATA_E_INVALID, "ACCUMULATE and ADD_INPUT are exclusive");
   return STRATA_OK;
@@ -313,13 +317,13 @@ int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, i
                      float* topk_w, int32_t* perm, int32_t* offsets, uint32_t flags, void* stream) {
   int rc = check_call(h, x, x_dtype, T);
   if (rc) return rc;
-  if ((rc = check_flags(T, flags))) return rc;
+  if ((rc = check_flags(h->cfg, T, flags))) return rc;
   if (!topk_idx || !topk_w || !perm || !offsets)
     return fail(STRATA_E_INVALID, "route outputs must be non-NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Call c = make_call(x, x_dtype, T, nullptr, flags);
   TraceScope ts(h);
-  if ((rc = run_route(h, c, use_decode(T, flags), true, s, ts.ptr))) return rc;
+  if ((rc = run_route(h, c, use_decode(h->cfg, T, flags), true, s, ts.ptr))) return rc;
   const size_t P = (size_t)T * h->cfg.top_k;
   hipError_t e = hipMemcpyAsync(topk_idx, h->W.topk_idx, P * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(topk_w, h->W.topk_w, P * 4, hipMemcpyDeviceToDevice, s);
@@ -334,7 +338,7 @@ int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
                        uint32_t flags, void* stream) {
   int rc = check_call(h, x, x_dtype, T);
   if (rc) return rc;
-  if ((rc = check_flags(T, flags))) return rc;
+  if ((rc = check_flags(h->cfg, T, flags))) return rc;
   if (!out) return fail(STRATA_E_INVALID, "out is NULL");
   if (!aligned(out, 16)) return fail(STRATA_E_INVALID, "out must be 16-byte aligned");
   const size_t xb = (size_t)T * h->cfg.hidden * (x_dtype == STRATA_FP32 ? 4 : 2);
@@ -343,7 +347,7 @@ int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
   if (xa < oa + ob && oa < xa + xb) return fail(STRATA_E_INVALID, "x and out overlap");
   hipStream_t s = static_cast<hipStream_t>(stream);
   TraceScope ts(h);
-  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(T, flags), s, ts.ptr))) return rc;
+  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(h->cfg, T, flags), s, ts.ptr))) return rc;
   return ok();
 }
 
@@ -373,7 +377,7 @@ int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const 
     float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
     const Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
     TraceScope ts(layers[l]);
-    int rc = run_forward(layers[l], c, use_decode(T, 0), s, ts.ptr);
+    int rc = run_forward(layers[l], c, use_decode(layers[l]->cfg, T, 0), s, ts.ptr);
     if (rc) return rc;
     cur = dst;
     cur_dtype = STRATA_FP32;
