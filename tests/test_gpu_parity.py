@@ -74,6 +74,25 @@ def test_decode_expert_counts(B, E, k, T):
     assert rel_l2(out, ref) <= DECODE_TOL, rel_l2(out, ref)
 
 
+def test_decode_lds_limit_falls_back_to_prefill(B):
+    """Top-64 of 512 experts: at 8 tokens the decode down kernel's routing
+    table and staged rows do not fit in LDS, so the call takes the grouped-GEMM
+    path (and forcing decode is refused); at 4 tokens decode still fits."""
+    hl, layer = tiny(2, E=512, k=64, max_tokens=16)
+    bits, xf = tokens(hl, 950, 8)
+    x = to_device_bf16(bits, DEV)
+    ref, _ = hl.oracle(xf)
+    out = layer.forward(x).cpu().numpy()
+    assert rel_l2(out, ref) <= PREFILL_TOL, rel_l2(out, ref)
+    with pytest.raises(B.StrataError) as e:
+        B.strata_moe_forward(layer.handle, x, 8, torch.empty((8, hl.H), device=DEV), B.STRATA_FORCE_DECODE)
+    assert e.value.code == B.STRATA_E_UNSUPPORTED
+    bits4, xf4 = tokens(hl, 951, 4)
+    out4 = layer.forward(to_device_bf16(bits4, DEV), flags=B.STRATA_FORCE_DECODE).cpu().numpy()
+    ref4, _ = hl.oracle(xf4)
+    assert rel_l2(out4, ref4) <= DECODE_TOL, rel_l2(out4, ref4)
+
+
 @pytest.mark.parametrize("fmt", [2, 3, 4])
 @pytest.mark.parametrize("T", [1, 9, 130, 300])
 def test_prefill_route_and_forward_tiny(B, fmt, T):
