@@ -83,7 +83,10 @@ typedef struct {
     int32_t top_k;       /* k: 1..min(E, 64)                                  */
     int32_t n_shared;    /* 0 or 1 always-on shared expert (weight 1)         */
     int32_t qfmt;        /* STRATA_Q2 / STRATA_Q3 / STRATA_Q4                 */
-    int32_t max_tokens;  /* largest T any call on the handle will pass, >= 1  */
+    int32_t max_tokens;  /* largest T any call on the handle will pass, >= 1; */
+                         /* max_tokens * top_k <= 2^28 and                   */
+                         /* max_tokens * hidden * 2 < 4 GiB (else            */
+                         /* STRATA_E_UNSUPPORTED)                            */
 } strata_moe_config;
 
 typedef struct strata_moe strata_moe;   /* opaque; one per MoE layer */

@@ -84,6 +84,27 @@ __device__ inline float half_bits_to_f32(uint16_t h) {
   return (float)v;
 }
 
+// Buffer loads: one descriptor (SGPRs) per expert record or workspace
+// buffer, a per-lane byte offset (one VGPR) and a wave-uniform byte offset
+// (SGPR), so a wave's many slab loads cost no per-slab address registers.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
+}
+__device__ inline uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ inline uint32_t bload1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // DPP lane permutations (gfx9 encodings): xor-1 and xor-2 inside quads,
 // mirror inside half-rows of 8 and rows of 16.
 constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,

@@ -100,24 +100,6 @@ template <> struct Codes<2> { uint4 lo; };
 template <> struct Codes<3> { uint4 lo; uint2 hi; };
 template <> struct Codes<4> { uint4 v0, v1; };
 
-// Buffer loads: one descriptor (SGPRs) per expert record or workspace
-// buffer, a per-lane byte offset (one VGPR) and a wave-uniform byte offset
-// (SGPR), so a wave's many slab loads cost no per-slab address registers.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
-
-__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, RSRC_WORD3);
-}
-__device__ inline uint4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ inline uint2 bload2(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-  return make_uint2(v[0], v[1]);
-}
-
 // Codes of one lane of the slab at byte soff of an expert record.
 template <int FMT>
 __device__ inline void bload_codes(rsrc_t r, uint32_t soff, int lane, Codes<FMT>& c) {

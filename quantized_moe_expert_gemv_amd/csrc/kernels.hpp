@@ -17,12 +17,14 @@ struct Work {
   int* offsets;       // [E+1]
   int* perm;          // [Tmax*k]   sorted slot -> pair
   int* inv;           // [Tmax*k]   pair -> sorted slot
+  int* slot_tok;      // [Tmax*k]   prefill: sorted slot -> token
   int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
   float* wtab;        // [E+1][8]   decode: routing weight per (active expert, token), 0 if not routed
   int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill)
   int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
-  int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}
+  int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}, in XCD segments,
+                      //             each sorted by row class (see k_scan)
   float* act;         // prefill: bf16 SwiGLU rows [slots][I] (same region as actp)
   _Float16* actp;     // decode: SwiGLU rows as two fp16 parts [active expert][2][T][I]
   _Float16* xparts;   // decode: token rows as two fp16 parts [2][T][H]

@@ -433,37 +433,126 @@ __global__ __launch_bounds__(64 * COLSCAN_GROUPS) void k_colscan(ScanArgs a) {
   if (g == COLSCAN_GROUPS - 1 && e < E) a.w.counts[e] = run;    // the last range ends at the total
 }
 
-// Offsets (exclusive scan of the expert counts) and the flat tile list.
-// One workgroup.
+// row class of a tile: 0 for more than 96 rows, 1 for 65..96, 2 for 33..64,
+// 3 for up to 32 (the GEMMs compute 128, 96, 64 and 32 rows for them)
+__device__ inline int row_class(int rows) { return rows > 96 ? 0 : rows > 64 ? 1 : rows > 32 ? 2 : 3; }
+
+// Workgroup-wide exclusive scan of an int4 per thread (blockDim a multiple
+// of 64, at most 1024); *total gets the sum over the workgroup.
+__device__ inline int4 block_exclusive_scan4(int4 v, int4* tmp /* >= 16 */, int4* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int4 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ax = __shfl_up(inc.x, o, 64), ay = __shfl_up(inc.y, o, 64);
+    const int az = __shfl_up(inc.z, o, 64), aw = __shfl_up(inc.w, o, 64);
+    if (lane >= o) { inc.x += ax; inc.y += ay; inc.z += az; inc.w += aw; }
+  }
+  if (lane == 63) tmp[wv] = inc;
+  __syncthreads();
+  int4 pre = make_int4(0, 0, 0, 0), tot = make_int4(0, 0, 0, 0);
+  for (int i = 0; i < nw; ++i) {
+    const int4 t = tmp[i];
+    if (i < wv) { pre.x += t.x; pre.y += t.y; pre.z += t.z; pre.w += t.w; }
+    tot.x += t.x; tot.y += t.y; tot.z += t.z; tot.w += t.w;
+  }
+  *total = tot;
+  __syncthreads();
+  return make_int4(pre.x + inc.x - v.x, pre.y + inc.y - v.y, pre.z + inc.z - v.z, pre.w + inc.w - v.w);
+}
+
+__device__ inline int4 class_unit(int c) {
+  return make_int4(c == 0, c == 1, c == 2, c == 3);
+}
+__device__ inline int class_of(const int4& v, int c) { return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w; }
+
+// Offsets (exclusive scan of the expert counts) and the tile list.  One
+// workgroup.  In expert order an entry's tiles are full 128-row tiles and
+// then its remainder; that order is cut into 8 contiguous segments of
+// ceil(n / 8) tiles (one per XCD in the GEMMs) and each segment is stably
+// sorted by row class, so a GEMM workgroup walking its segment in order meets
+// the classes in turn.  Each thread places the tiles of its own entries:
+// tile j (expert order) of class c in segment x goes to
+//   x tp + (segment x's tiles of classes below c) + (class-c tiles in [x tp, j)).
 __global__ __launch_bounds__(1024) void k_scan(ScanArgs a) {
   __shared__ int2 tmp[16];
+  __shared__ int4 tmp4[16];
+  __shared__ int4 bnd[9];          // class counts of the expert-order tiles before each segment start
   const int E = a.E, P = a.T * a.k;
   // exclusive scan over experts (the shared expert is entry E) of (count, tiles)
+  // and of the per-class tile counts
   const int n_ent = E + (a.n_shared ? 1 : 0);
   const int per = (n_ent + blockDim.x - 1) / blockDim.x;
-  const int e0 = threadIdx.x * per;
+  const int e0 = min(n_ent, (int)threadIdx.x * per), e1 = min(n_ent, e0 + per);
   auto cnt_of = [&](int e) { return e < E ? a.w.counts[e] : a.T; };
   int2 loc = make_int2(0, 0);
-  for (int e = e0; e < min(n_ent, e0 + per); ++e) {
-    const int c = cnt_of(e);
+  int4 cls = make_int4(0, 0, 0, 0);
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt_of(e), full = c / BM, rem = c - full * BM;
     loc.x += (e < E) ? c : 0;
-    loc.y += (c + BM - 1) / BM;
+    loc.y += full + (rem > 0);
+    cls.x += full;
+    if (rem > 0) {
+      const int4 u = class_unit(row_class(rem));
+      cls.x += u.x; cls.y += u.y; cls.z += u.z; cls.w += u.w;
+    }
   }
   int2 total;
   int2 base = block_exclusive_scan(loc, tmp, &total);
-  for (int e = e0; e < min(n_ent, e0 + per); ++e) {
-    const int c = cnt_of(e);
-    const int first = (e < E) ? base.x : P;
-    if (e < E) a.w.offsets[e] = base.x;
-    const int nt = (c + BM - 1) / BM;
-    for (int q = 0; q < nt; ++q)
-      a.w.tiles[base.y + q] = make_int4(e, first + q * BM, min(BM, c - q * BM), 0);
-    if (e < E) base.x += c;
-    base.y += nt;
+  int4 ctot;
+  const int4 cpre = block_exclusive_scan4(cls, tmp4, &ctot);
+  const int n = total.y, tp = (n + 7) / 8;
+  // class counts at the segment starts that fall in this thread's tiles
+  // (inside an entry only its full tiles precede the start)
+  {
+    int j = base.y;
+    int4 run = cpre;
+    for (int e = e0; e < e1; ++e) {
+      const int c = cnt_of(e), full = c / BM, rem = c - full * BM, nt = full + (rem > 0);
+      for (int x = (j + tp - 1) / tp; x * tp < j + nt; ++x) {
+        bnd[x] = make_int4(run.x + (x * tp - j), run.y, run.z, run.w);
+      }
+      run.x += full;
+      if (rem > 0) {
+        const int4 u = class_unit(row_class(rem));
+        run.x += u.x; run.y += u.y; run.z += u.z; run.w += u.w;
+      }
+      j += nt;
+    }
   }
   if (threadIdx.x == 0) {
+    for (int x = (n + tp - 1) / tp; x <= 8; ++x) bnd[x] = ctot;
     a.w.offsets[E] = P;
-    a.w.meta[1] = total.y;
+    a.w.meta[1] = n;
+  }
+  __syncthreads();
+  // full tiles (class 0) of a segment are placed consecutively from
+  // x tp + (class-0 tiles of the segment before them); only an entry's
+  // remainder tile needs the lower classes' counts
+  int4 run = cpre;
+  int x = base.y / tp;
+  int4 b0 = bnd[x];
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt_of(e), full = c / BM, rem = c - full * BM;
+    const int first = (e < E) ? base.x : P;
+    if (e < E) a.w.offsets[e] = base.x;
+    for (int q = 0; q < full; ++q, ++base.y) {
+      if (base.y >= (x + 1) * tp) b0 = bnd[++x];
+      a.w.tiles[x * tp + run.x - b0.x] = make_int4(e, first + q * BM, BM, 0);
+      ++run.x;
+    }
+    if (rem > 0) {
+      if (base.y >= (x + 1) * tp) b0 = bnd[++x];
+      const int k = row_class(rem);
+      const int4 b1 = bnd[x + 1];
+      int pos = x * tp + class_of(run, k) - class_of(b0, k);
+      for (int kk = 0; kk < k; ++kk) pos += class_of(b1, kk) - class_of(b0, kk);
+      a.w.tiles[pos] = make_int4(e, first + full * BM, rem, 0);
+      const int4 u = class_unit(k);
+      run.x += u.x; run.y += u.y; run.z += u.z; run.w += u.w;
+      ++base.y;
+    }
+    if (e < E) base.x += c;
   }
 }
 
@@ -476,6 +565,7 @@ __global__ void k_scatter(TopkArgs a) {
   const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)chunk * a.E + e] + a.w.pair_rank[p];
   a.w.perm[slot] = p;
   a.w.inv[p] = slot;
+  a.w.slot_tok[slot] = p / a.k;
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
@@ -511,15 +601,17 @@ template <> struct PairCodes<2> { uint2 w, sc; };
 template <> struct PairCodes<3> { uint2 w, sc; uint32_t h; };
 template <> struct PairCodes<4> { u32x4_t w; uint2 sc; };
 
-// blocks 4 hp .. 4 hp + 3 (half hp of the superblock) of a slab for this lane
+// blocks 4 hp .. 4 hp + 3 (half hp of the superblock) of a slab for this
+// lane: the slab at byte soff of the expert record r
 template <int FMT>
-__device__ inline void load_pair(const uint8_t* slab, int hp, int lane, PairCodes<FMT>& c) {
-  c.sc = *reinterpret_cast<const uint2*>(slab + Fmt<FMT>::slab_codes + (lane & 15) * 16 + 8 * hp);
+__device__ inline void load_pair(rsrc_t r, uint32_t soff, int hp, int lane, PairCodes<FMT>& c) {
+  c.sc = bload2(r, Fmt<FMT>::slab_codes + (lane & 15) * 16 + 8 * hp, soff);
   if constexpr (FMT == 4) {
-    c.w = *reinterpret_cast<const u32x4_t*>(slab + hp * 1024 + lane * 16);
+    const uint4 v = bload4(r, hp * 1024 + lane * 16, soff);
+    c.w = u32x4_t{v.x, v.y, v.z, v.w};
   } else {
-    c.w = *reinterpret_cast<const uint2*>(slab + lane * 16 + 8 * hp);
-    if constexpr (FMT == 3) c.h = *reinterpret_cast<const uint32_t*>(slab + 1024 + lane * 8 + 4 * hp);
+    c.w = bload2(r, lane * 16 + 8 * hp, soff);
+    if constexpr (FMT == 3) c.h = bload1(r, 1024 + lane * 8 + 4 * hp, soff);
   }
 }
 
@@ -607,10 +699,14 @@ typedef __attribute__((address_space(1))) const u32x4_t gu32x4_t;
 // Every fragment is loaded and stored, also those of subtiles a short tile
 // does not compute (their rows repeat the tile's last row): a load under a
 // condition would make the compiler wait for all outstanding loads before
-// the next store.
-__device__ inline void a_load(const _Float16* const (&src)[AR], int k0, AStage& st) {
+// the next store.  The lane's row is at byte va of the buffer ra; k0 is in
+// elements.
+__device__ inline void a_load(rsrc_t ra, uint32_t va, int k0, AStage& st) {
 #pragma unroll
-  for (int i = 0; i < AF; ++i) st.v[i] = *(gu32x4_t*)(src[i >> 1] + k0 + 32 * (i & 1));
+  for (int i = 0; i < AF; ++i) {
+    const uint4 v = bload4(ra, va + 64 * (i & 1), 2 * k0);
+    st.v[i] = u32x4_t{v.x, v.y, v.z, v.w};
+  }
 }
 
 __device__ inline void a_store(const AStage& st, _Float16* buf, int wv, int lane) {
@@ -628,7 +724,7 @@ constexpr int MT = BM / 16;        // 16-row subtiles of a tile
 // behind the MFMAs of the steps in between.
 template <int FMT, int BB, int MC, bool TR, int NSL = nsl<FMT>()>
 __device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc)[NSL], int lane,
-                                  f32x4 (&acc)[MT][NSL]) {
+                                  f32x4 (&acc)[MC][NSL]) {
   constexpr int NS = 2 * MC;                          // steps: (block kb, subtile m), kb-major
   auto rd = [&](int t) __attribute__((always_inline)) {
     const int m = t % MC, kb = t / MC;
@@ -662,135 +758,173 @@ __device__ inline void gemm_stage(const _Float16* buf, const PairCodes<FMT> (&bc
   }
 }
 
-// The K loop shared by both GEMMs, for the first 16 MC token rows: A rows
-// from src (this lane's rows), the wave's NSL slabs from slab0[n]
-// (superblock sb at + sb * SLAB).  Stage s + 2 of the A rows is requested
-// while stage s is multiplied; stage s + 1 (requested a stage earlier) then
-// goes to the other LDS buffer.  Codes run half a superblock (two stages)
-// ahead, in two sets.
-template <int FMT, int MC, bool TR, int NSL = nsl<FMT>()>
-__device__ inline void gemm_kloop(const _Float16* const (&src)[AR], const uint8_t* const (&slab0)[NSL], int K,
-                                  _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][NSL]) {
+// Operand sources of one work item for this lane: its token row (A, byte va
+// of buffer ra) and the wave's NSL weight slabs (byte slab[n] of the expert
+// record rw; superblock sb of a slab SLAB bytes further per sb).  Buffer
+// loads keep the addresses in scalar registers but for one per-lane offset.
+static_assert(AR == 1, "one token row per lane");
+template <int NSL>
+struct ItemSrc {
+  rsrc_t ra;
+  uint32_t va;
+  rsrc_t rw;
+  uint32_t slab[NSL];
+};
+
+// codes and scales of half h of the K loop (stages 2h, 2h + 1)
+template <int FMT, int NSL>
+__device__ inline void codes_load(const ItemSrc<NSL>& is, int h, int lane, PairCodes<FMT> (&c)[NSL]) {
   constexpr int SLAB = Fmt<FMT>::slab_codes + 256;
-  const int nsb = K / SB_WEIGHTS, ns = K / XBK;
-  // half h of the K loop (stages 2h, 2h + 1); past the end: the last half again (unused)
-  auto load_codes = [&](int h, PairCodes<FMT> (&c)[NSL]) __attribute__((always_inline)) {
-    const int hc = min(h, 2 * nsb - 1);
 #pragma unroll
-    for (int n = 0; n < NSL; ++n) load_pair<FMT>(slab0[n] + (size_t)(hc >> 1) * SLAB, hc & 1, lane, c[n]);
-  };
-  PairCodes<FMT> bc[2][NSL];
-  load_codes(0, bc[0]);
-  AStage ar[4];
-  a_load(src, 0, ar[0]);
-  a_load(src, XBK, ar[1]);
+  for (int n = 0; n < NSL; ++n) load_pair<FMT>(is.rw, is.slab[n] + (uint32_t)(h >> 1) * SLAB, h & 1, lane, c[n]);
+}
+
+// The K loop of one work item, for its first 16 MC token rows.  On entry
+// stage 0 of A is in LDS buffer 0, stage 1 in flight in ar[1] and the codes of
+// stages 0 and 1 in flight in bc[0].  Stage s + 2 of A is requested while
+// stage s is multiplied; stage s + 1 (requested a stage earlier) then goes to
+// the other LDS buffer.  Codes run half a superblock (two stages) ahead, in
+// two sets.  The last two stages request the next work item's first two A
+// stages and first codes (from next(), called only there), which leaves the
+// next item's loop the same entry state: the next item's operands are in
+// flight while this one's epilogue runs.  K is a multiple of 256, so the
+// stage ring positions line up across items.
+template <int FMT, int MC, bool TR, int NSL, typename Next>
+__device__ inline void gemm_kloop(const ItemSrc<NSL>& cur, Next next, int K, _Float16 (*As)[ASTAGE], int wv,
+                                  int lane, AStage (&ar)[4], PairCodes<FMT> (&bc)[2][NSL],
+                                  f32x4 (&acc)[MC][NSL]) {
+  const int nsb = K / SB_WEIGHTS;
+#define STRATA_STAGE(ST, SRC, K0, CODES)                                                \
+  {                                                                                     \
+    CODES;                                                                              \
+    a_load(SRC.ra, SRC.va, K0, ar[(ST + 2) & 3]);                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    gemm_stage<FMT, 2 * ST, MC, TR>(As[ST & 1], bc[(ST / 2) & 1], lane, acc);           \
+    a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], wv, lane);                              \
+    __syncthreads();                                                                    \
+  }
+  for (int sb = 0; sb < nsb - 1; ++sb) {
+    const int s = 4 * sb;
+    STRATA_STAGE(0, cur, (s + 2) * XBK, codes_load<FMT>(cur, 2 * sb + 1, lane, bc[1]))
+    STRATA_STAGE(1, cur, (s + 3) * XBK, (void)0)
+    STRATA_STAGE(2, cur, (s + 4) * XBK, codes_load<FMT>(cur, 2 * sb + 2, lane, bc[0]))
+    STRATA_STAGE(3, cur, (s + 5) * XBK, (void)0)
+  }
+  {
+    const int sb = nsb - 1, s = 4 * sb;
+    STRATA_STAGE(0, cur, (s + 2) * XBK, codes_load<FMT>(cur, 2 * sb + 1, lane, bc[1]))
+    STRATA_STAGE(1, cur, (s + 3) * XBK, (void)0)
+    const ItemSrc<NSL> nx = next();
+    STRATA_STAGE(2, nx, 0, codes_load<FMT>(nx, 0, lane, bc[0]))
+    STRATA_STAGE(3, nx, XBK, (void)0)
+  }
+#undef STRATA_STAGE
+}
+
+// first entry state of the K loop (see gemm_kloop)
+template <int FMT, int NSL>
+__device__ inline void gemm_prologue(const ItemSrc<NSL>& cur, _Float16 (*As)[ASTAGE], int wv, int lane,
+                                     AStage (&ar)[4], PairCodes<FMT> (&bc)[2][NSL]) {
+  codes_load<FMT>(cur, 0, lane, bc[0]);
+  a_load(cur.ra, cur.va, 0, ar[0]);
+  a_load(cur.ra, cur.va, XBK, ar[1]);
   a_store(ar[0], As[0], wv, lane);
   __syncthreads();
-  for (int sb = 0; sb < nsb; ++sb) {
-#define STRATA_STAGE(ST)                                                                \
-    {                                                                                   \
-      const int s = 4 * sb + ST;                                                        \
-      if (ST % 2 == 0) load_codes(2 * sb + ST / 2 + 1, bc[(ST / 2 + 1) & 1]);           \
-      a_load(src, min(s + 2, ns - 1) * XBK, ar[(ST + 2) & 3]);                         \
-      __builtin_amdgcn_sched_barrier(0);                                                \
-      gemm_stage<FMT, 2 * ST, MC, TR>(As[ST & 1], bc[(ST / 2) & 1], lane, acc);         \
-      a_store(ar[(ST + 1) & 3], As[(ST + 1) & 1], wv, lane);                            \
-      __syncthreads();                                                                  \
-    }
-    STRATA_STAGE(0) STRATA_STAGE(1) STRATA_STAGE(2) STRATA_STAGE(3)
-#undef STRATA_STAGE
+}
+
+// The work items of a persistent workgroup.  The tile list is cut into 8
+// contiguous segments of ceil(n / 8) tiles, one per XCD (the workgroups b
+// with b % 8 == x), each sorted by row class; an item is (tile, column tile),
+// column tiles of a tile adjacent, and the G = gridDim / 8 workgroups of an
+// XCD take every G-th item of its segment.  at(i) is clamped to the
+// workgroup's last item, so look-ahead loads past the end stay in bounds.
+struct ItemSeq {
+  int seg0, n, w0, step, ntn;
+  __device__ ItemSeq(int ntiles, int ntn_) {
+    const int tp = (ntiles + 7) >> 3;
+    seg0 = min(ntiles, (int)(blockIdx.x & 7) * tp);
+    n = (min(ntiles, seg0 + tp) - seg0) * ntn_;
+    w0 = blockIdx.x >> 3;
+    step = gridDim.x >> 3;
+    ntn = ntn_;
   }
-}
+  __device__ bool valid(int i) const { return w0 + i * step < n; }
+  __device__ int at(int i) const { return min(w0 + i * step, w0 + max(0, (n - 1 - w0) / step) * step); }
+  __device__ int tile(int i) const { return seg0 + at(i) / ntn; }
+  __device__ int col(int i) const { return at(i) % ntn; }
+};
 
-// The K loop for a tile of `rows` token rows: subtiles past the rows are not
-// computed (32 rows at a time).
-template <int FMT, bool TR, int NSL = nsl<FMT>()>
-__device__ inline void gemm_tile(int rows, const _Float16* const (&src)[AR], const uint8_t* const (&slab0)[NSL],
-                                 int K, _Float16 (*As)[ASTAGE], int wv, int lane, f32x4 (&acc)[MT][NSL]) {
-  if (rows > 96) gemm_kloop<FMT, 8, TR>(src, slab0, K, As, wv, lane, acc);
-  else if (rows > 64) gemm_kloop<FMT, 6, TR>(src, slab0, K, As, wv, lane, acc);
-  else if (rows > 32) gemm_kloop<FMT, 4, TR>(src, slab0, K, As, wv, lane, acc);
-  else gemm_kloop<FMT, 2, TR>(src, slab0, K, As, wv, lane, acc);
+// tile entry j, read through the scalar cache (the tile list is read-only
+// while the GEMMs run), so the entries and everything derived from them stay
+// in scalar registers
+typedef const __attribute__((address_space(4))) int* cint_ptr;
+__device__ inline int4 tile_entry(const GemmArgs& a, int j) {
+  const cint_ptr p = (cint_ptr)(a.w.tiles + j);
+  return make_int4(p[0], p[1], p[2], p[3]);
 }
-
-// Work item of this workgroup: (row tile j, column tile nt), ntn column tiles
-// per row tile.  The eight XCDs each take a contiguous range of work items
-// (workgroup b runs on XCD b % 8), column tiles of a row tile adjacent.
-__device__ inline bool work_item(int ntiles, int ntn, int& j, int& nt) {
-  const int total = ntiles * ntn, per = (total + 7) >> 3;
-  const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3, w = xcd * per + idx;
-  if (idx >= per || w >= total) return false;
-  j = w / ntn;
-  nt = w - j * ntn;
-  return true;
-}
-
-// workgroups to launch for up to max_tiles row tiles of ntn column tiles
-inline int work_grid(int max_tiles, int ntn) { return 8 * ((max_tiles * ntn + 7) / 8); }
-
-// token of the pair in slot `slot` (routed pairs, then the shared expert's)
-__device__ inline int slot_token(const GemmArgs& a, int slot) {
-  return slot < a.P ? a.w.perm[slot] / a.k : slot - a.P;
-}
-
-template <int NSL>
-__device__ inline void zero_acc(f32x4 (&acc)[MT][NSL]) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int n = 0; n < NSL; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
+__device__ inline int tile_count(const GemmArgs& a) { return *(cint_ptr)(a.w.meta + 1); }
 
 // silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal
 // (relative error a few ulp; the prefill path rounds its result to fp16)
 __device__ inline float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-constexpr bool DOWN_TR = false;
-
 // Column tiles of a work item: GEMM_WAVES waves of nsl() slabs each.
 template <int FMT> constexpr int gu_rows() { return GEMM_WAVES * nsl<FMT>() / 2 * 16; }  // rows of I, gate/up
 template <int FMT> constexpr int dn_cols() { return GEMM_WAVES * nsl<FMT>() * 16; }      // rows of H, down
 
-// gate/up: work item = 128 slots x gu_rows() rows of I (gate and up); wave w
-// takes NSL/2 row groups of 16 (gate and up slabs) and every token row
-template <int FMT>
-__global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) {
-  constexpr int NSL = nsl<FMT>();
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
-  __shared__ int rowsrc[BM];
-  int j, itile;
-  if (!work_item(a.w.meta[1], a.I / gu_rows<FMT>(), j, itile)) return;
-  const int4 tl = a.w.tiles[j];
-  const int e = tl.x, slot0 = tl.y, rows = tl.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nsbH = a.H / SB_WEIGHTS;
-  if (tid < BM) {
-    // rows past the tile's end read its last row (in bounds; results not stored)
-    rowsrc[tid] = slot_token(a, slot0 + min(tid, rows - 1));
+// Epilogue staging.  A work item's results are written to an LDS tile of
+// [BM rows][NC halves] (16-byte granules of a row XOR-swizzled by row % 8,
+// which spreads the 16 rows of one transposed-layout write over the banks)
+// and, after a barrier, stored as whole rows: 16 bytes per lane, full
+// 128-byte lines.  Stored straight from the MFMA layout, each lane would
+// write 8 bytes of 16 different rows per instruction, and the partial-line
+// writes cost the expert GEMMs about a third of their time.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// 8 bytes (4 halves starting at column c, a multiple of 4) of row `row`
+template <int NC>
+__device__ inline void stage_put(char* stg, int row, int c, uint2 v) {
+  const int g = c >> 3;
+  *reinterpret_cast<uint2*>(stg + row * (2 * NC) + ((g ^ (row & 7)) << 4) + ((c & 4) << 1)) = v;
+}
+
+// rows [0, rows) of the staged tile to dst (row r at dst + r * pitch halves),
+// columns below ncols (a multiple of 8); wave w takes every 8th row group.
+// UNR: loop unrolling (a register budget choice of the caller)
+template <int NC, int UNR>
+__device__ inline void stage_store(const char* stg, int rows, int ncols, _Float16* dst, size_t pitch, int wv,
+                                   int lane) {
+  constexpr int LPR = NC / 8, RPI = 64 / LPR;         // lanes per row, rows per instruction
+  static_assert(LPR <= 64 && 64 % LPR == 0, "staged row width");
+  const int gg = lane % LPR, c = 8 * gg;
+#pragma unroll UNR
+  for (int q = 0; q < BM / (8 * RPI); ++q) {
+    const int row = RPI * (wv + 8 * q) + lane / LPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * (2 * NC) + ((gg ^ (row & 7)) << 4));
+    if (row < rows && c < ncols) *reinterpret_cast<uint4*>(dst + (size_t)row * pitch + c) = v;
   }
-  __syncthreads();
-  const _Float16* x16 = reinterpret_cast<const _Float16*>(a.x16);
-  const _Float16* src[AR];
+}
+
+// One gate/up work item with 16 MC computed token rows: K loop, then SwiGLU
+// (slabs n < NSL/2 hold gate, n + NSL/2 up, for the same rows i); the lane's
+// 4 consecutive i of one token row go out as one 8-byte store.
+template <int FMT, int MC, int NSL, typename Next>
+__device__ inline void gateup_item(const GemmArgs& a, const ItemSrc<NSL>& cur, Next next, int slot0, int rows,
+                                   int col, _Float16 (*As)[ASTAGE], char* stg, int wv, int lane, AStage (&ar)[4],
+                                   PairCodes<FMT> (&bc)[2][NSL]) {
+  constexpr int NC = gu_rows<FMT>();
+  f32x4 acc[MC][NSL];
 #pragma unroll
-  for (int q = 0; q < AR; ++q)
-    src[q] = x16 + (size_t)rowsrc[16 * (AR * wv + q) + (lane >> 2)] * a.H + 8 * (lane & 3);
-  // this wave's slabs: gate and up for I rows 16 g0 .. 16 (g0 + NSL/2) - 1
-  const int g0 = (itile * GEMM_WAVES + wv) * (NSL / 2);
-  const uint8_t* ex = a.packed + (size_t)e * a.stride;
-  const uint8_t* slab0[NSL];
+  for (int m = 0; m < MC; ++m)
 #pragma unroll
-  for (int n = 0; n < NSL / 2; ++n) {
-    slab0[n] = ex + slab_off(FMT, nsbH, g0 + n, 0);
-    slab0[NSL / 2 + n] = ex + up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g0 + n, 0);
-  }
-  f32x4 acc[MT][NSL];
-  zero_acc(acc);
-  gemm_tile<FMT, true>(rows, src, slab0, a.H, As, wv, lane, acc);
-  // SwiGLU: slabs n < NSL/2 hold gate, n + NSL/2 up, for the same rows i;
-  // the lane's 4 consecutive i of one token row go out as one 8-byte store
-  _Float16* act = reinterpret_cast<_Float16*>(a.w.act);
+    for (int n = 0; n < NSL; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_kloop<FMT, MC, true>(cur, next, a.H, As, wv, lane, ar, bc, acc);
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+  for (int m = 0; m < MC; ++m) {
     const int row = 16 * m + (lane & 15);
 #pragma unroll
     for (int n = 0; n < NSL / 2; ++n) {
@@ -799,65 +933,282 @@ __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) 
       for (int v = 0; v < 2; ++v)
         h[v] = h2_t{(_Float16)(silu_fast(acc[m][n][2 * v]) * acc[m][NSL / 2 + n][2 * v]),
                     (_Float16)(silu_fast(acc[m][n][2 * v + 1]) * acc[m][NSL / 2 + n][2 * v + 1])};
-      if (row < rows)
-        *reinterpret_cast<uint2*>(act + (size_t)(slot0 + row) * a.I + 16 * (g0 + n) + 4 * (lane >> 4)) =
-            make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1]));
+      stage_put<NC>(stg, row, 16 * (wv * (NSL / 2) + n) + 4 * (lane >> 4),
+                    make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1])));
     }
   }
+  lds_barrier();
+  stage_store<NC, 2>(stg, rows, NC, reinterpret_cast<_Float16*>(a.w.act) + (size_t)slot0 * a.I + col * NC, a.I, wv,
+                  lane);
+}
+
+// One down work item with 16 MC computed token rows: K loop (transposed, so
+// the lane's 4 results are consecutive h of one token row), then the bf16
+// per-pair rows through the staging tile (columns past H, computed by the
+// waves past H of the last column tile, are not stored).
+template <int FMT, int MC, int NSL, typename Next>
+__device__ inline void down_item(const GemmArgs& a, const ItemSrc<NSL>& cur, Next next, int slot0, int rows, int col,
+                                 _Float16 (*As)[ASTAGE], char* stg, int wv, int lane, AStage (&ar)[4],
+                                 PairCodes<FMT> (&bc)[2][NSL]) {
+  constexpr int NC = dn_cols<FMT>();
+  f32x4 acc[MC][NSL];
+#pragma unroll
+  for (int m = 0; m < MC; ++m)
+#pragma unroll
+    for (int n = 0; n < NSL; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  gemm_kloop<FMT, MC, true>(cur, next, a.I, As, wv, lane, ar, bc, acc);
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    const int row = 16 * m + (lane & 15);
+#pragma unroll
+    for (int n = 0; n < NSL; ++n)
+      stage_put<NC>(stg, row, 16 * (wv * NSL + n) + 4 * (lane >> 4),
+                    make_uint2(cvt_bf16x2(acc[m][n][0], acc[m][n][1]), cvt_bf16x2(acc[m][n][2], acc[m][n][3])));
+  }
+  lds_barrier();
+  stage_store<NC, BM>(stg, rows, min(NC, a.H - col * NC),
+                  reinterpret_cast<_Float16*>(a.w.ybf) + (size_t)slot0 * a.H + col * NC, a.H, wv, lane);
+}
+
+// gate/up: work item = 128 slots x gu_rows() rows of I (gate and up); wave w
+// takes NSL/2 row groups of 16 (gate and up slabs) and every token row.
+// Persistent: one workgroup per CU walks its items (ItemSeq); the tile entry
+// of item i + 2 and the pair of this lane's token row in item i + 1 are
+// requested while item i starts, so the next item's operand addresses are
+// known by the time its loads are issued (two stages before this item ends).
+template <int FMT>
+__global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) {
+  constexpr int NSL = nsl<FMT>();
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
+  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * gu_rows<FMT>()];
+  const ItemSeq seq(tile_count(a), a.I / gu_rows<FMT>());
+  if (!seq.valid(0)) return;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = 16 * wv + (lane >> 2);                 // this lane's token row of a tile
+  const int nsbH = a.H / SB_WEIGHTS;
+  // slot of this lane's row (rows past the tile's end repeat its last row);
+  // its token (routed slots), read for every slot at an in-bounds index
+  auto row_slot = [&](int4 tl) { return tl.y + min(r, tl.z - 1); };
+  auto slot_pair = [&](int slot) { return a.w.slot_tok[min(slot, a.P - 1)]; };
+  const rsrc_t rx = make_rsrc(a.x16, (uint32_t)((size_t)a.T * a.H * 2));
+  auto make_src = [&](int4 tl, int pair, int col) __attribute__((always_inline)) {
+    const int slot = row_slot(tl);
+    const int tok = slot < a.P ? pair : slot - a.P;
+    const int g0 = (col * GEMM_WAVES + wv) * (NSL / 2);
+    ItemSrc<NSL> is;
+    is.ra = rx;
+    is.va = (uint32_t)tok * (uint32_t)(2 * a.H) + 16 * (lane & 3);
+    is.rw = make_rsrc(a.packed + (size_t)tl.x * a.stride, (uint32_t)a.stride);
+#pragma unroll
+    for (int n = 0; n < NSL / 2; ++n) {
+      is.slab[n] = (uint32_t)slab_off(FMT, nsbH, g0 + n, 0);
+      is.slab[NSL / 2 + n] = (uint32_t)(up_off(FMT, a.H, a.I) + slab_off(FMT, nsbH, g0 + n, 0));
+    }
+    return is;
+  };
+  int4 tl0 = tile_entry(a, seq.tile(0));
+  int4 tl1 = tile_entry(a, seq.tile(1));
+  ItemSrc<NSL> cur = make_src(tl0, slot_pair(row_slot(tl0)), seq.col(0));
+  AStage ar[4];
+  PairCodes<FMT> bc[2][NSL];
+  gemm_prologue<FMT>(cur, As, wv, lane, ar, bc);
+  // one loop per row class (the segment is sorted by class): each loop body
+  // has a single MC, which keeps the register allocation of each tight
+  int i = 0;
+#define STRATA_GU_CLASS(MCV, CLS)                                                              \
+  for (; seq.valid(i) && row_class(tl0.z) == CLS; ++i) {                                       \
+    const int pair1 = slot_pair(row_slot(tl1));                                                \
+    const int4 tl2 = tile_entry(a, seq.tile(i + 2));                                           \
+    const int c1 = seq.col(i + 1);                                                             \
+    auto next = [&]() __attribute__((always_inline)) { return make_src(tl1, pair1, c1); };     \
+    gateup_item<FMT, MCV>(a, cur, next, tl0.y, tl0.z, seq.col(i), As, stg, wv, lane, ar, bc);  \
+    cur = next();                                                                              \
+    tl0 = tl1;                                                                                 \
+    tl1 = tl2;                                                                                 \
+  }
+  STRATA_GU_CLASS(8, 0)
+  STRATA_GU_CLASS(6, 1)
+  STRATA_GU_CLASS(4, 2)
+  STRATA_GU_CLASS(2, 3)
+#undef STRATA_GU_CLASS
 }
 
 // down: work item = 128 slots x dn_cols() rows of H; wave w takes NSL row
-// groups of 16 (waves past H, in the last column tile, compute but store nothing)
+// groups of 16.  Persistent as the gate/up GEMM; its A rows are the slots
+// themselves, so only the tile entries are looked up ahead.
 template <int FMT>
 __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_down(GemmArgs a) {
   constexpr int NSL = nsl<FMT>();
   __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
-  int j, htile;
-  if (!work_item(a.w.meta[1], (a.H + dn_cols<FMT>() - 1) / dn_cols<FMT>(), j, htile)) return;
-  const int4 tl = a.w.tiles[j];
-  const int e = tl.x, slot0 = tl.y, rows = tl.z;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * dn_cols<FMT>()];
+  const ItemSeq seq(tile_count(a), (a.H + dn_cols<FMT>() - 1) / dn_cols<FMT>());
+  if (!seq.valid(0)) return;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = 16 * wv + (lane >> 2);
   const int nsbI = a.I / SB_WEIGHTS;
-  const _Float16* act = reinterpret_cast<const _Float16*>(a.w.act);
-  // rows past the tile's end read its last row (in bounds; results not stored)
-  const _Float16* src[AR];
+  // this wave's slabs: H rows 16 g0 .. 16 (g0 + NSL) - 1; waves past H (in
+  // the last column tile; whole waves, H being a multiple of 16 NSL) read
+  // the first slabs instead and store nothing
+  auto wave_g0 = [&](int col) { return (col * GEMM_WAVES + wv) * NSL; };
+  auto make_src = [&](int4 tl, int col) __attribute__((always_inline)) {
+    const int g0w = wave_g0(col);
+    const int g0 = g0w < a.H / GROUP_ROWS ? g0w : 0;
+    ItemSrc<NSL> is;
+    is.ra = make_rsrc(reinterpret_cast<const char*>(a.w.act) + (size_t)tl.y * a.I * 2, (uint32_t)(BM * a.I * 2));
+    is.va = (uint32_t)min(r, tl.z - 1) * (uint32_t)(2 * a.I) + 16 * (lane & 3);
+    is.rw = make_rsrc(a.packed + (size_t)tl.x * a.stride, (uint32_t)a.stride);
+    const uint32_t dn = (uint32_t)down_off(FMT, a.H, a.I);
 #pragma unroll
-  for (int q = 0; q < AR; ++q)
-    src[q] = act + (size_t)(slot0 + min(16 * (AR * wv + q) + (lane >> 2), rows - 1)) * a.I + 8 * (lane & 3);
-  // this wave's slabs: H rows 16 g0 .. 16 (g0 + NSL) - 1
-  const int g0w = (htile * GEMM_WAVES + wv) * NSL;
-  const bool on = g0w < a.H / GROUP_ROWS;            // whole waves: H is a multiple of 16 NSL (256)
-  const int g0 = on ? g0w : 0;
-  const uint8_t* dn = a.packed + (size_t)e * a.stride + down_off(FMT, a.H, a.I);
-  const uint8_t* slab0[NSL];
+    for (int n = 0; n < NSL; ++n) is.slab[n] = dn + (uint32_t)slab_off(FMT, nsbI, g0 + n, 0);
+    return is;
+  };
+  int4 tl0 = tile_entry(a, seq.tile(0));
+  int4 tl1 = tile_entry(a, seq.tile(1));
+  ItemSrc<NSL> cur = make_src(tl0, seq.col(0));
+  AStage ar[4];
+  PairCodes<FMT> bc[2][NSL];
+  gemm_prologue<FMT>(cur, As, wv, lane, ar, bc);
+  int i = 0;
+#define STRATA_DN_CLASS(MCV, CLS)                                                              \
+  for (; seq.valid(i) && row_class(tl0.z) == CLS; ++i) {                                       \
+    const int4 tl2 = tile_entry(a, seq.tile(i + 2));                                           \
+    const int c1 = seq.col(i + 1);                                                             \
+    auto next = [&]() __attribute__((always_inline)) { return make_src(tl1, c1); };            \
+    down_item<FMT, MCV>(a, cur, next, tl0.y, tl0.z, seq.col(i), As, stg, wv, lane, ar, bc);   \
+    cur = next();                                                                              \
+    tl0 = tl1;                                                                                 \
+    tl1 = tl2;                                                                                 \
+  }
+  STRATA_DN_CLASS(8, 0)
+  STRATA_DN_CLASS(6, 1)
+  STRATA_DN_CLASS(4, 2)
+  STRATA_DN_CLASS(2, 3)
+#undef STRATA_DN_CLASS
+}
+
+// ------------------------------------------------------------------ router GEMM (bf16 tokens)
+// Router logits for bf16 tokens on the 16x16x32 bf16 MFMA: the tokens (exact
+// in bf16) times the bf16 high and low parts of Wr (together Wr to about
+// 2^-16 relative), fp32 accumulation: two products per weight.  Work item:
+// 128 tokens x 128 experts, split over K into partial planes when the tile
+// grid is small.  8 waves, each all 128 token rows x 16 experts; computed
+// transposed (experts as the A operand) so each lane's 4 results are
+// consecutive experts of one token (16-byte stores).  Both operands are staged
+// in LDS fragment-major with coalesced loads and XOR-swizzled slots (as the
+// expert GEMMs' token rows), 64 of K per stage, loaded two stages ahead in
+// registers.  The first column of expert tiles also writes the tokens as fp16.
+constexpr int RT_WAVES = 8;
+struct RouterMArgs {
+  const uint16_t* x;      // [T][H] bf16
+  int T, H, E;
+  int kper;               // K range of one split, a multiple of 64
+  int S;                  // K splits
+  size_t plane;           // elements between partial planes
+  const uint16_t* whi;
+  const uint16_t* wlo;
+  float* part;            // [S][T][E]
+  uint16_t* x16;          // [T][H] the tokens as fp16
+};
+
+// a stage: 16 token fragments (8 subtiles x 2 blocks), then 32 router
+// fragments (8 expert subtiles x 2 blocks x high, low), 1 KiB each
+constexpr int RT_AFR = 16, RT_FR = 48;
+
+__device__ inline bf16x8 rt_frag(const uint16_t* stage, int f, int lane) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(stage + f * 512 + 8 * a_slot(lane)));
+}
+
+__global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router_mfma(RouterMArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][RT_FR * 512];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // XCD-contiguous items, expert tiles fastest: the expert tiles of one token
+  // tile run on one XCD, so each token row is fetched into one L2
+  const int ne = (a.E + 127) / 128, nt = (a.T + 127) / 128, total = ne * nt * a.S;
+  const int per = (total + 7) >> 3, idx = blockIdx.x >> 3, w = (blockIdx.x & 7) * per + idx;
+  if (idx >= per || w >= total) return;
+  const int ex = w % ne, ty = (w / ne) % nt, kz = w / (ne * nt);
+  const int t0 = ty * 128, e0 = ex * 128;
+  const int kb0 = kz * a.kper, ke = min(a.H, kb0 + a.kper), ns = (ke - kb0) / XBK;
+  // loads of this lane: token fragments 2w, 2w+1 (subtile w, blocks 0/1) and
+  // router fragments 16 + 4w + i (expert subtile w, block i/2, part i%2); row
+  // l/4 of the subtile, 16 bytes at column 8 (l % 4) of the block
+  const int r4 = lane >> 2, c4 = 8 * (lane & 3);
+  const int trow = min(t0 + 16 * wv + r4, a.T - 1), erow = min(e0 + 16 * wv + r4, a.E - 1);
+  const uint16_t* xs = a.x + (size_t)trow * a.H + c4;
+  const uint16_t* hs = a.whi + (size_t)erow * a.H + c4;
+  const uint16_t* ls = a.wlo + (size_t)erow * a.H + c4;
+  const int slot = 8 * a_slot(r4 + 16 * (lane & 3));
+  struct St { u32x4_t v[6]; };
+  auto load = [&](int k0, St& st) __attribute__((always_inline)) {
+    st.v[0] = *(gu32x4_t*)(xs + k0);
+    st.v[1] = *(gu32x4_t*)(xs + k0 + 32);
+    st.v[2] = *(gu32x4_t*)(hs + k0);
+    st.v[3] = *(gu32x4_t*)(ls + k0);
+    st.v[4] = *(gu32x4_t*)(hs + k0 + 32);
+    st.v[5] = *(gu32x4_t*)(ls + k0 + 32);
+  };
+  auto store = [&](const St& st, uint16_t* buf) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4_t*>(buf + (2 * wv) * 512 + slot) = st.v[0];
+    *reinterpret_cast<u32x4_t*>(buf + (2 * wv + 1) * 512 + slot) = st.v[1];
 #pragma unroll
-  for (int n = 0; n < NSL; ++n) slab0[n] = dn + slab_off(FMT, nsbI, g0 + n, 0);
-  f32x4 acc[MT][NSL];
-  zero_acc(acc);
-  gemm_tile<FMT, DOWN_TR>(rows, src, slab0, a.I, As, wv, lane, acc);
-  if (!on) return;
-  if constexpr (DOWN_TR) {
-    // the lane's 4 consecutive h of one token row go out as one 8-byte store
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int row = 16 * m + (lane & 15);
-#pragma unroll
-      for (int n = 0; n < NSL; ++n)
-        if (row < rows)
-          *reinterpret_cast<uint2*>(a.w.ybf + (size_t)(slot0 + row) * a.H + 16 * (g0 + n) + 4 * (lane >> 4)) =
-              make_uint2(cvt_bf16x2(acc[m][n][0], acc[m][n][1]), cvt_bf16x2(acc[m][n][2], acc[m][n][3]));
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(buf + (RT_AFR + 4 * wv + i) * 512 + slot) = st.v[2 + i];
+  };
+  const bool write_x16 = ex == 0 && t0 + 16 * wv + r4 < a.T;
+  auto put_x16 = [&](const St& st, int k0) __attribute__((always_inline)) {
+    if (write_x16) {
+      uint16_t* d = a.x16 + (size_t)(t0 + 16 * wv + r4) * a.H + c4 + k0;
+      *reinterpret_cast<u32x4_t*>(d) = bf16x8_to_f16(st.v[0]);
+      *reinterpret_cast<u32x4_t*>(d + 32) = bf16x8_to_f16(st.v[1]);
     }
-  } else {
+  };
+  f32x4 acc[8];
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  St ar[4];
+  load(kb0, ar[0]);
+  load(kb0 + min(1, ns - 1) * XBK, ar[1]);
+  store(ar[0], Ls[0]);
+  put_x16(ar[0], kb0);
+  __syncthreads();
+  for (int s4 = 0; s4 < ns; s4 += 4) {
+#define STRATA_RSTAGE(ST)                                                                  \
+    if (s4 + ST < ns) {                                                                    \
+      const int s = s4 + ST;                                                               \
+      load(kb0 + min(s + 2, ns - 1) * XBK, ar[(ST + 2) & 3]);                              \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      const uint16_t* buf = Ls[ST & 1];                                                    \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                   \
+        const bf16x8 bh = rt_frag(buf, RT_AFR + 4 * wv + 2 * kb, lane);                    \
+        const bf16x8 bl = rt_frag(buf, RT_AFR + 4 * wv + 2 * kb + 1, lane);                \
+        _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                    \
+          const bf16x8 af = rt_frag(buf, 2 * m + kb, lane);                                \
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, af, acc[m], 0, 0, 0);       \
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, af, acc[m], 0, 0, 0);       \
+        }                                                                                  \
+      }                                                                                    \
+      if (s + 1 < ns) {                                                                    \
+        store(ar[(ST + 1) & 3], Ls[(ST + 1) & 1]);                                         \
+        put_x16(ar[(ST + 1) & 3], kb0 + (s + 1) * XBK);                                    \
+      }                                                                                    \
+      __syncthreads();                                                                     \
+    }
+    STRATA_RSTAGE(0) STRATA_RSTAGE(1) STRATA_RSTAGE(2) STRATA_RSTAGE(3)
+#undef STRATA_RSTAGE
+  }
+  // D[e][t]: lane l holds experts 4 (l / 16) .. + 3 of its subtile for token 16 m + l % 16
+  float* out = a.part + kz * a.plane;
+  const int e = e0 + 16 * wv + 4 * (lane >> 4);
 #pragma unroll
-      for (int n = 0; n < NSL; ++n)
+  for (int m = 0; m < 8; ++m) {
+    const int t = t0 + 16 * m + (lane & 15);
+    if (t >= a.T) continue;
+    if ((a.E & 3) == 0) {
+      if (e < a.E) *reinterpret_cast<f32x4*>(out + (size_t)t * a.E + e) = acc[m];
+    } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = 16 * m + 4 * (lane >> 4) + v;
-          if (row < rows)
-            a.w.ybf[(size_t)(slot0 + row) * a.H + 16 * (g0 + n) + (lane & 15)] = f32_to_bf16_rne(acc[m][n][v]);
-        }
+      for (int j = 0; j < 4; ++j)
+        if (e + j < a.E) out[(size_t)t * a.E + e + j] = acc[m][j];
+    }
   }
 }
 
@@ -947,16 +1298,18 @@ struct RouterPlan {
   uint16_t* x16;
 };
 
-RouterPlan router_plan(const Layer& L, const Work& W, int T) {
-  // split K until the grid has about two workgroups per CU
+RouterPlan router_plan(const Layer& L, const Work& W, int T, bool x_f32) {
+  // split K until the grid has about one workgroup per resident slot: two per
+  // CU for the fp32-token kernel, one for the bf16 one (its LDS and registers)
   RouterPlan r;
+  const int slots = x_f32 ? 512 : 256;
   const int tiles = ((L.E + BN - 1) / BN) * ((T + BM - 1) / BM);
   const int ksteps = L.H / BK;
   const size_t x16_bytes = (size_t)T * L.H * 2;       // <= the region (slots >= T)
   r.plane = (size_t)T * L.E;
   int S = 1;
   if (L.E <= 512) {
-    S = std::min(std::min(8, ksteps), std::max(1, (512 + tiles - 1) / tiles));
+    S = std::min(std::min(8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
     while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
   }
   r.kper = ((ksteps + S - 1) / S) * BK;
@@ -967,21 +1320,43 @@ RouterPlan router_plan(const Layer& L, const Work& W, int T) {
   return r;
 }
 
+// compute units of the current device (cached per device)
+int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int* c = &cache[dev & 63];
+  if (*c == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 8;
+    *c = n;
+  }
+  return *c;
+}
+
+// persistent GEMM grid: one workgroup per CU (a multiple of 8, one group per
+// XCD), fewer when there are fewer items
+int persistent_grid(int max_items) {
+  return 8 * std::max(1, std::min(cu_count() / 8, (max_items + 7) / 8));
+}
+
 template <int FMT>
 hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   GemmArgs g;
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
-  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
+  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T, c.x_f32).x16; g.w = W;
   const int max_tiles = W.max_tiles;
-  launch(tr, k_gemm_gateup<FMT>, dim3(work_grid(max_tiles, L.I / gu_rows<FMT>())), dim3(64 * GEMM_WAVES), 0, s, g);
-  launch(tr, k_gemm_down<FMT>, dim3(work_grid(max_tiles, (L.H + dn_cols<FMT>() - 1) / dn_cols<FMT>())), dim3(64 * GEMM_WAVES), 0, s, g);
+  launch(tr, k_gemm_gateup<FMT>, dim3(persistent_grid(max_tiles * (L.I / gu_rows<FMT>()))), dim3(64 * GEMM_WAVES), 0,
+         s, g);
+  launch(tr, k_gemm_down<FMT>, dim3(persistent_grid(max_tiles * ((L.H + dn_cols<FMT>() - 1) / dn_cols<FMT>()))),
+         dim3(64 * GEMM_WAVES), 0, s, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
-  const RouterPlan rp = router_plan(L, W, c.T);
+  const RouterPlan rp = router_plan(L, W, c.T, c.x_f32);
   const int S = rp.S;
   const size_t plane = rp.plane;
   RouterArgs r;
@@ -991,8 +1366,15 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   r.part = rp.part;
   r.x16 = rp.x16;
   dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM, S);
-  if (c.x_f32) launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
-  else launch(tr, k_router_gemm<false>, grid, dim3(256), 0, s, r);
+  if (c.x_f32) {
+    launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
+  } else {
+    RouterMArgs m;
+    m.x = reinterpret_cast<const uint16_t*>(c.x); m.T = c.T; m.H = L.H; m.E = L.E;
+    m.kper = rp.kper; m.S = S; m.plane = plane; m.whi = L.router_hi; m.wlo = L.router_lo;
+    m.part = rp.part; m.x16 = rp.x16;
+    launch(tr, k_router_mfma, dim3(8 * ((grid.x * grid.y * S + 7) / 8)), dim3(64 * RT_WAVES), 0, s, m);
+  }
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b;

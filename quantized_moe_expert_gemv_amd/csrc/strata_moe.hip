@@ -69,11 +69,13 @@ int check_config(const strata_moe_config* c) {
   if (c->max_tokens < 1) return fail(STRATA_E_INVALID, "max_tokens must be >= 1");
   if ((long long)c->max_tokens * c->top_k > (1LL << 30) / 4)
     return fail(STRATA_E_UNSUPPORTED, "max_tokens * top_k too large");
+  if ((long long)c->max_tokens * c->hidden * 2 > 0xFFFFFFFFLL)
+    return fail(STRATA_E_UNSUPPORTED, "max_tokens * hidden * 2 bytes of fp16 token rows exceed 4 GiB");
   return STRATA_OK;
 }
 
 struct WsPlan {
-  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, udesc, wtab, meta,
+  size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, slot_tok, udesc, wtab, meta,
       chunk_base, pair_rank, tiles, act, xparts, y, total;
   int nchunks, max_tiles;
 };
@@ -100,6 +102,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.offsets = take((E + 1) * 4);
   p.perm = take(P * 4);
   p.inv = take(P * 4);
+  p.slot_tok = take(P * 4);
   p.udesc = take((E + 1) * 2 * 4);
   p.wtab = take((E + 1) * 8 * 4);
   p.meta = take(16 * 4);
@@ -265,6 +268,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   W.offsets = reinterpret_cast<int*>(ws + p.offsets);
   W.perm = reinterpret_cast<int*>(ws + p.perm);
   W.inv = reinterpret_cast<int*>(ws + p.inv);
+  W.slot_tok = reinterpret_cast<int*>(ws + p.slot_tok);
   W.udesc = reinterpret_cast<int*>(ws + p.udesc);
   W.meta = reinterpret_cast<int*>(ws + p.meta);
   W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
