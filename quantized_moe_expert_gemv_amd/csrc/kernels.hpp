@@ -41,8 +41,8 @@ struct Layer {
   const float* router_b;        // [E] or null
   const uint8_t* packed;        // experts (routed then shared) in the packed layout
   size_t expert_stride;         // bytes per expert
-  const uint16_t* router_hi;    // [E][H] bf16 high part of router_w
-  const uint16_t* router_lo;    // [E][H] bf16 remainder
+  const uint16_t* router_hi;    // bf16 high part of router_w, MFMA operand order (k_router_split)
+  const uint16_t* router_lo;    // bf16 remainder, same order
 };
 
 struct Call {

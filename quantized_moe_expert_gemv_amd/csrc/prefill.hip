@@ -5,10 +5,10 @@
 // HBM, so the chunk is a grouped, genuinely dense contraction and runs on
 // the gfx950 matrix cores (fp32 accumulation):
 //
-//   k_router_gemm    x Wr^T, fp32-accurate from bf16 MFMA by splitting Wr
+//   k_router         x Wr^T, fp32-accurate from bf16 MFMA by splitting Wr
 //                    (and an fp32 x) into bf16 high + low parts; split over K
-//                    into partial planes when the tile grid is small; the
-//                    first column of tiles also writes the tokens as fp16
+//                    into partial planes when the item grid is small; the
+//                    first expert tile also writes the tokens as fp16
 //   k_topk_chunks    logits = sum of the planes + b; top-k + renormalised
 //                    softmax per token (one wave per token) and, per chunk of
 //                    32 tokens, the expert histogram and every pair's rank
@@ -37,18 +37,10 @@ namespace strata {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int BM = PREFILL_BM;      // 128 token rows
-constexpr int BN = 128;             // output columns per tile
-constexpr int BK = 64;              // reduction step (two quantised blocks)
-constexpr int LDK = BK + 8;         // LDS row pitch in bf16 (144 B: conflict-free 16-B reads)
 constexpr int CT = PREFILL_CHUNK_T;
 
-__device__ inline bf16x8 lds_frag(const uint16_t* p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -62,103 +54,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ inline uint32_t cvt_bf16x2(float a, float b) {
   const f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// A-tile chunks of one thread: 4 chunks of 8 bf16 (bf16 input) or of 8 fp32
-template <bool XF32> struct AChunks;
-template <> struct AChunks<false> { u32x4_t v[4]; };
-template <> struct AChunks<true> { f32x4_t v[8]; };
-
-// One wave's 64x64 sub-tile: 2 x 2 MFMA 32x32 tiles over one BK step.
-__device__ inline void mma_step(const uint16_t* As, const uint16_t* Bs, f32x16 (&acc)[2][2],
-                                int wm, int wn, int lane) {
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int kof = ks * 16 + 8 * (lane >> 5);
-    bf16x8 af[2], bfr[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) af[mt] = lds_frag(As + (64 * wm + 32 * mt + (lane & 31)) * LDK + kof);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) bfr[nt] = lds_frag(Bs + (64 * wn + 32 * nt + (lane & 31)) * LDK + kof);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
-  }
-}
-
-// row of element v of a 32x32 accumulator held by `lane`
-__device__ inline int acc_row(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
-
-// One lane-slot l of a slab for blocks bb0 and bb0 + 1 (bb0 even): row l % 16,
-// K-slice 8*(l/16) of each block.  RawB holds its codes and the two scales as
-// loaded; dequant_rawb writes the 16 weights d (q - c), rounded to bf16, to
-// the LDS row dst (columns (b - bb0)*32 + 8*(l/16) + e).  The raw loads are
-// issued a K-step ahead of the conversion.
-template <int FMT> struct RawB;
-template <> struct RawB<2> { uint32_t w, sc; };
-template <> struct RawB<3> { uint32_t w, hi, sc; };
-template <> struct RawB<4> { uint2 w; uint32_t sc; };
-
-template <int FMT>
-__device__ inline void load_rawb(const uint8_t* slab, int l, int bb0, RawB<FMT>& r) {
-  r.sc = *reinterpret_cast<const uint32_t*>(slab + Fmt<FMT>::slab_codes + (l & 15) * 16 + bb0 * 2);
-  if constexpr (FMT == 4) {
-    r.w = *reinterpret_cast<const uint2*>(slab + (bb0 >> 2) * 1024 + l * 16 + (bb0 & 3) * 4);
-  } else {
-    r.w = *reinterpret_cast<const uint32_t*>(slab + l * 16 + (bb0 >> 1) * 4);
-    if constexpr (FMT == 3) r.hi = *reinterpret_cast<const uint32_t*>(slab + 1024 + l * 8 + (bb0 >> 2) * 4);
-  }
-}
-
-// packed FP4 pair SEL of src (nibbles 2SEL, 2SEL+1) times scale, to fp32
-template <int SEL>
-__device__ inline f32x2_t fp4_pair(uint32_t src, float scale) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(src, scale, SEL);
-}
-
-// block B (0 or 1) of the lane-slot: 8 weights
-template <int FMT, int B>
-__device__ inline void dequant_block(const RawB<FMT>& r, int q, int bb0, uint16_t* dst) {
-  constexpr int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-  constexpr float C = Fmt<FMT>::c;
-  const float d = half_bits_to_f32((uint16_t)(B ? (r.sc >> 16) : (r.sc & 0xffffu)));
-  const float cd = C * d;
-  float w[8];
-  if constexpr (FMT == 4) {
-    const uint32_t W = B ? r.w.y : r.w.x;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = fmaf(d, (float)((W >> (4 * NIB4[e])) & 15u), -cd);
-  } else {
-    // 2-bit codes as FP4 nibbles 0b00qq (e2m1 value q/2) at scale 2: exactly q.  The
-    // conversion's scale acts as a power of two, so the block scale d is applied after.
-    const uint32_t E = r.w & 0x33333333u, O = (r.w >> 2) & 0x33333333u;
-    const f32x2_t p0 = fp4_pair<2 * B>(E, 2.0f);
-    const f32x2_t p1 = fp4_pair<2 * B>(O, 2.0f);
-    const f32x2_t p2 = fp4_pair<2 * B + 1>(E, 2.0f);
-    const f32x2_t p3 = fp4_pair<2 * B + 1>(O, 2.0f);
-    w[0] = p0.x; w[1] = p0.y; w[2] = p1.x; w[3] = p1.y;
-    w[4] = p2.x; w[5] = p2.y; w[6] = p3.x; w[7] = p3.y;
-    if constexpr (FMT == 3) {
-      // third bit of weight e at nibble e: FP4 0b000h (0 or 0.5) at scale 8: 4h
-      const uint32_t X = (r.hi >> ((bb0 + B) & 3)) & 0x11111111u;
-      const f32x2_t h0 = fp4_pair<0>(X, 8.0f), h1 = fp4_pair<1>(X, 8.0f);
-      const f32x2_t h2 = fp4_pair<2>(X, 8.0f), h3 = fp4_pair<3>(X, 8.0f);
-      w[0] += h0.x; w[1] += h0.y; w[2] += h1.x; w[3] += h1.y;
-      w[4] += h2.x; w[5] += h2.y; w[6] += h3.x; w[7] += h3.y;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = fmaf(w[e], d, -cd);  // (q - c) d, exact in fp32
-  }
-  *reinterpret_cast<uint4*>(dst + 32 * B + 8 * q) =
-      make_uint4(cvt_bf16x2(w[0], w[1]), cvt_bf16x2(w[2], w[3]), cvt_bf16x2(w[4], w[5]), cvt_bf16x2(w[6], w[7]));
-}
-
-template <int FMT>
-__device__ inline void dequant_rawb(const RawB<FMT>& r, int l, int bb0, uint16_t* dst) {
-  dequant_block<FMT, 0>(r, l >> 4, bb0, dst);
-  dequant_block<FMT, 1>(r, l >> 4, bb0, dst);
 }
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -179,127 +74,6 @@ __device__ inline u32x4_t f32x8_to_f16(f32x4_t lo, f32x4_t hi) {
                  __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, h2_t)),
                  __builtin_bit_cast(uint32_t, __builtin_convertvector(p2, h2_t)),
                  __builtin_bit_cast(uint32_t, __builtin_convertvector(p3, h2_t))};
-}
-
-// ------------------------------------------------------------------ router GEMM
-// Split-K: workgroup (n, m, z) multiplies K range [z kper, (z+1) kper) of its
-// 128 x 128 tile and writes the fp32 partial to plane z; the top-k kernel sums
-// the planes in order z = 0, 1, ... and adds the bias.  Operands for the next
-// K-step are loaded into registers while the MFMAs of the current one run.
-struct RouterArgs {
-  const void* x;
-  int x_f32, T, H, E;
-  int kper;               // K range of one split, a multiple of BK
-  size_t plane;           // elements between partial planes
-  const uint16_t* whi;
-  const uint16_t* wlo;
-  float* part;            // [S][T][E]
-  uint16_t* x16;          // [T][H] the tokens as fp16, written by the first column of tiles
-};
-
-// fp32 pair -> bf16 pair (RNE) in *hi and the bf16 of the remainders in *lo
-__device__ inline void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
-  const uint32_t h = cvt_bf16x2(a, b);
-  *hi = h;
-  *lo = cvt_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
-}
-
-template <bool XF32>
-struct RouterStage {
-  AChunks<XF32> x;
-  u32x4_t bh[4], bl[4];
-};
-
-template <bool XF32>
-__global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ahi[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Alo[XF32 ? BM * LDK : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Bhi[BN * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Blo[BN * LDK];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wm = wv >> 1, wn = wv & 1;
-  const int t0 = blockIdx.y * BM, e0 = blockIdx.x * BN;
-  const int kb = blockIdx.z * a.kper, ke = min(a.H, kb + a.kper);
-  const int kc = tid & 7;
-  // chunk i of this thread: row (tid >> 3) + 32 i, 8 elements at column 8 kc.
-  // Rows past T or E repeat the last row (in bounds; results not stored).
-  const void* xs[4];
-  uint32_t wo[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    const size_t xo = (size_t)min(t0 + r, a.T - 1) * a.H + kc * 8;
-    xs[i] = XF32 ? (const void*)(reinterpret_cast<const float*>(a.x) + xo)
-                 : (const void*)(reinterpret_cast<const uint16_t*>(a.x) + xo);
-    wo[i] = (uint32_t)min(e0 + r, a.E - 1) * (uint32_t)a.H + kc * 8;
-  }
-  RouterStage<XF32> st;
-  auto load_step = [&](int k0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (XF32) {
-        const float* f = reinterpret_cast<const float*>(xs[i]) + k0;
-        st.x.v[2 * i] = *reinterpret_cast<const f32x4_t*>(f);
-        st.x.v[2 * i + 1] = *reinterpret_cast<const f32x4_t*>(f + 4);
-      } else {
-        st.x.v[i] = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint16_t*>(xs[i]) + k0);
-      }
-      st.bh[i] = *reinterpret_cast<const u32x4_t*>(a.whi + wo[i] + k0);
-      st.bl[i] = *reinterpret_cast<const u32x4_t*>(a.wlo + wo[i] + k0);
-    }
-  };
-  f32x16 acc[2][2] = {};
-  load_step(kb);
-  const bool write_x16 = blockIdx.x == 0;
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    if (write_x16) {
-      // the tokens as fp16 for the expert GEMMs (each element once: this
-      // column of tiles covers every (row, K) of the chunk exactly once)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + (tid >> 3) + 32 * i;
-        u32x4_t h;
-        if constexpr (XF32) h = f32x8_to_f16(st.x.v[2 * i], st.x.v[2 * i + 1]);
-        else h = bf16x8_to_f16(st.x.v[i]);
-        if (t < a.T) *reinterpret_cast<u32x4_t*>(a.x16 + (size_t)t * a.H + k0 + kc * 8) = h;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = ((tid >> 3) + 32 * i) * LDK + kc * 8;
-      if constexpr (XF32) {
-        const f32x4_t f0 = st.x.v[2 * i], f1 = st.x.v[2 * i + 1];
-        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-        split_bf16x2(f0.x, f0.y, &h0, &l0);
-        split_bf16x2(f0.z, f0.w, &h1, &l1);
-        split_bf16x2(f1.x, f1.y, &h2, &l2);
-        split_bf16x2(f1.z, f1.w, &h3, &l3);
-        *reinterpret_cast<u32x4_t*>(Ahi + o) = u32x4_t{h0, h1, h2, h3};
-        *reinterpret_cast<u32x4_t*>(Alo + o) = u32x4_t{l0, l1, l2, l3};
-      } else {
-        *reinterpret_cast<u32x4_t*>(Ahi + o) = st.x.v[i];
-      }
-      *reinterpret_cast<u32x4_t*>(Bhi + o) = st.bh[i];
-      *reinterpret_cast<u32x4_t*>(Blo + o) = st.bl[i];
-    }
-    __syncthreads();
-    load_step(min(k0 + BK, ke - BK));                // in flight during the MFMAs (last step repeats)
-    __builtin_amdgcn_sched_barrier(0);
-    mma_step(Ahi, Bhi, acc, wm, wn, lane);
-    mma_step(Ahi, Blo, acc, wm, wn, lane);
-    if constexpr (XF32) mma_step(Alo, Bhi, acc, wm, wn, lane);
-    __syncthreads();
-  }
-  float* out = a.part + blockIdx.z * a.plane;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 64 * wm + 32 * mt + acc_row(v, lane);
-        const int e = e0 + 64 * wn + 32 * nt + (lane & 31);
-        if (t < a.T && e < a.E) out[(size_t)t * a.E + e] = acc[mt][nt][v];
-      }
 }
 
 // ------------------------------------------------------------------ routing
@@ -1086,128 +860,246 @@ __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_down(GemmArgs a) {
 #undef STRATA_DN_CLASS
 }
 
-// ------------------------------------------------------------------ router GEMM (bf16 tokens)
-// Router logits for bf16 tokens on the 16x16x32 bf16 MFMA: the tokens (exact
-// in bf16) times the bf16 high and low parts of Wr (together Wr to about
-// 2^-16 relative), fp32 accumulation: two products per weight.  Work item:
-// 128 tokens x 128 experts, split over K into partial planes when the tile
-// grid is small.  8 waves, each all 128 token rows x 16 experts; computed
-// transposed (experts as the A operand) so each lane's 4 results are
-// consecutive experts of one token (16-byte stores).  Both operands are staged
-// in LDS fragment-major with coalesced loads and XOR-swizzled slots (as the
-// expert GEMMs' token rows), 64 of K per stage, loaded two stages ahead in
-// registers.  The first column of expert tiles also writes the tokens as fp16.
+// ------------------------------------------------------------------ router GEMM
+// Router logits x Wr^T on the 16x16x32 bf16 MFMA with fp32 accumulation,
+// fp32-accurate: Wr is held as bf16 high parts and bf16 remainders (together
+// Wr to about 2^-16 relative).  bf16 tokens are exact in bf16 (two products
+// per weight); fp32 tokens are split the same way (three products: high x
+// high, high x low, low x high).
+//
+// Work item: 128 tokens x 256 experts over a K range; the K range is split
+// into partial planes when the item grid is small (the top-k kernel sums the
+// planes in plane order, then adds the bias).  8 waves: wave w takes experts
+// [32 w, 32 w + 32) of the item and all 128 tokens, computed transposed
+// (experts as the A operand), so a lane's 4 results are consecutive experts
+// of one token (16-byte stores).
+//  - Router weights are laid out at create time in MFMA operand order
+//    (1 KiB fragments of 16 experts x 32 of K, lane-major; see
+//    k_router_split), so a wave loads its operands straight into registers,
+//    one whole fragment per instruction, a stage (64 of K) ahead.  No wave
+//    shares them, so they never pass through LDS.
+//  - Token rows are staged in LDS fragment-major with coalesced row loads and
+//    XOR-swizzled slots (as the expert GEMMs' token rows), two stages ahead in
+//    registers; all 8 waves read them.
+// Items are XCD-contiguous with token tiles fastest, so each XCD works on one
+// (expert tile, K range) slice of the router weights at a time, which its L2
+// holds.  The items of the first expert tile also write the tokens as fp16
+// for the expert GEMMs (each element once).
+constexpr int RT_E = 256;          // experts per work item
 constexpr int RT_WAVES = 8;
-struct RouterMArgs {
-  const uint16_t* x;      // [T][H] bf16
-  int T, H, E;
+
+struct RouterArgs {
+  const void* x;          // [T][H] bf16 or fp32
+  int T, H, E, S;
   int kper;               // K range of one split, a multiple of 64
-  int S;                  // K splits
   size_t plane;           // elements between partial planes
-  const uint16_t* whi;
-  const uint16_t* wlo;
+  const uint16_t* whi;    // Wr high parts, operand order
+  const uint16_t* wlo;    // Wr remainders, operand order
   float* part;            // [S][T][E]
   uint16_t* x16;          // [T][H] the tokens as fp16
 };
 
-// a stage: 16 token fragments (8 subtiles x 2 blocks), then 32 router
-// fragments (8 expert subtiles x 2 blocks x high, low), 1 KiB each
-constexpr int RT_AFR = 16, RT_FR = 48;
-
-__device__ inline bf16x8 rt_frag(const uint16_t* stage, int f, int lane) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(stage + f * 512 + 8 * a_slot(lane)));
+// fp32 pair -> bf16 pair (RNE) in *hi and the bf16 of the remainders in *lo
+__device__ inline void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = cvt_bf16x2(a, b);
+  *hi = h;
+  *lo = cvt_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
 }
 
-__global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router_mfma(RouterMArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][RT_FR * 512];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // XCD-contiguous items, expert tiles fastest: the expert tiles of one token
-  // tile run on one XCD, so each token row is fetched into one L2
-  const int ne = (a.E + 127) / 128, nt = (a.T + 127) / 128, total = ne * nt * a.S;
+__device__ inline bf16x8 rt_frag(const uint16_t* stage, int f, int lane) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4_t*>(stage + f * AFRAG + 8 * a_slot(lane)));
+}
+
+// One stage (two 32-wide K blocks) of a router work item for one wave:
+// token subtiles in pairs, their fragments read from LDS a pair ahead; for a
+// pair, the products of the weight high parts, then of the remainders (then
+// of the token low parts): the same accumulator comes back every 4th MFMA,
+// never back to back.
+template <bool XF32>
+__device__ inline void router_stage(const uint16_t* buf, const u32x4_t (&b)[2][2][2], int lane,
+                                    f32x4 (&acc)[8][2]) {
+  constexpr int NP = XF32 ? 2 : 1;                     // token parts
+  constexpr int NMF = 4 * (XF32 ? 3 : 2);              // MFMAs per subtile pair
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    bf16x8 af[2][2][NP];                               // [buffer][subtile of the pair][part]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) af[0][i][p] = rt_frag(buf, 16 * p + 2 * i + q, lane);
+#pragma unroll
+    for (int mp = 0; mp < 4; ++mp) {
+      const int cb = mp & 1;
+      if (mp < 3) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int p = 0; p < NP; ++p) af[cb ^ 1][i][p] = rt_frag(buf, 16 * p + 2 * (2 * mp + 2 + i) + q, lane);
+      }
+#pragma unroll
+      for (int pass = 0; pass < (XF32 ? 3 : 2); ++pass)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) {
+            // pass 0: W high x token high, 1: W low x token high, 2: W high x token low
+            const bf16x8 w = __builtin_bit_cast(bf16x8, b[q][n][pass == 1 ? 1 : 0]);
+            const bf16x8 x = af[cb][i][pass == 2 ? NP - 1 : 0];
+            acc[2 * mp + i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, x, acc[2 * mp + i][n], 0, 0, 0);
+          }
+    }
+    // reads a pair ahead of the MFMAs that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NP, 0);
+#pragma unroll
+    for (int mp = 0; mp < 4; ++mp) {
+      if (mp < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2 * NP, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    }
+  }
+}
+
+template <bool XF32>
+__global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
+  constexpr int NA = XF32 ? 2 : 1;                    // token parts in LDS: high (and low)
+  constexpr int NX = XF32 ? 4 : 2;                    // 16-byte token loads per lane and stage
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][NA * 16 * AFRAG];
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ne = (a.E + RT_E - 1) / RT_E, nt = (a.T + BM - 1) / BM, total = ne * nt * a.S;
   const int per = (total + 7) >> 3, idx = blockIdx.x >> 3, w = (blockIdx.x & 7) * per + idx;
   if (idx >= per || w >= total) return;
-  const int ex = w % ne, ty = (w / ne) % nt, kz = w / (ne * nt);
-  const int t0 = ty * 128, e0 = ex * 128;
+  const int ty = w % nt, ex = (w / nt) % ne, kz = w / (nt * ne);
+  const int t0 = ty * BM, e0 = ex * RT_E;
   const int kb0 = kz * a.kper, ke = min(a.H, kb0 + a.kper), ns = (ke - kb0) / XBK;
-  // loads of this lane: token fragments 2w, 2w+1 (subtile w, blocks 0/1) and
-  // router fragments 16 + 4w + i (expert subtile w, block i/2, part i%2); row
-  // l/4 of the subtile, 16 bytes at column 8 (l % 4) of the block
+  // token loads of this lane: row l/4 of subtile w, 8 elements at column
+  // 8 (l % 4) of each 32-wide block (operand lane l / 4 + 16 (l % 4))
   const int r4 = lane >> 2, c4 = 8 * (lane & 3);
-  const int trow = min(t0 + 16 * wv + r4, a.T - 1), erow = min(e0 + 16 * wv + r4, a.E - 1);
-  const uint16_t* xs = a.x + (size_t)trow * a.H + c4;
-  const uint16_t* hs = a.whi + (size_t)erow * a.H + c4;
-  const uint16_t* ls = a.wlo + (size_t)erow * a.H + c4;
+  const int trow = min(t0 + 16 * wv + r4, a.T - 1);
+  const size_t xoff = (size_t)trow * a.H + c4;
   const int slot = 8 * a_slot(r4 + 16 * (lane & 3));
-  struct St { u32x4_t v[6]; };
-  auto load = [&](int k0, St& st) __attribute__((always_inline)) {
-    st.v[0] = *(gu32x4_t*)(xs + k0);
-    st.v[1] = *(gu32x4_t*)(xs + k0 + 32);
-    st.v[2] = *(gu32x4_t*)(hs + k0);
-    st.v[3] = *(gu32x4_t*)(ls + k0);
-    st.v[4] = *(gu32x4_t*)(hs + k0 + 32);
-    st.v[5] = *(gu32x4_t*)(ls + k0 + 32);
-  };
-  auto store = [&](const St& st, uint16_t* buf) __attribute__((always_inline)) {
-    *reinterpret_cast<u32x4_t*>(buf + (2 * wv) * 512 + slot) = st.v[0];
-    *reinterpret_cast<u32x4_t*>(buf + (2 * wv + 1) * 512 + slot) = st.v[1];
+  // router operands of this wave: expert groups of 16 (clamped to the last)
+  const int ng = (a.E + 15) / 16, nkb = a.H / 32;
+  const uint16_t* bsrc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(buf + (RT_AFR + 4 * wv + i) * 512 + slot) = st.v[2 + i];
+  for (int n = 0; n < 2; ++n) {
+    const size_t g = (size_t)min(e0 / 16 + 2 * wv + n, ng - 1);
+    bsrc[n][0] = a.whi + g * nkb * AFRAG + 8 * lane;
+    bsrc[n][1] = a.wlo + g * nkb * AFRAG + 8 * lane;
+  }
+  struct BSt { u32x4_t v[2][2][2]; };                 // [block][group][part]
+  auto bload = [&](int s, BSt& b) __attribute__((always_inline)) {
+    const int kb = kb0 / 32 + 2 * s;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) b.v[q][n][p] = *(gu32x4_t*)(bsrc[n][p] + (size_t)(kb + q) * AFRAG);
   };
-  const bool write_x16 = ex == 0 && t0 + 16 * wv + r4 < a.T;
-  auto put_x16 = [&](const St& st, int k0) __attribute__((always_inline)) {
-    if (write_x16) {
-      uint16_t* d = a.x16 + (size_t)(t0 + 16 * wv + r4) * a.H + c4 + k0;
-      *reinterpret_cast<u32x4_t*>(d) = bf16x8_to_f16(st.v[0]);
-      *reinterpret_cast<u32x4_t*>(d + 32) = bf16x8_to_f16(st.v[1]);
+  struct XSt { u32x4_t v[NX]; };
+  auto xload = [&](int s, XSt& st) __attribute__((always_inline)) {
+    const int k0 = kb0 + s * XBK;
+    if constexpr (XF32) {
+      const float* p = reinterpret_cast<const float*>(a.x) + xoff + k0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st.v[i] = *(gu32x4_t*)(p + 32 * (i >> 1) + 4 * (i & 1));
+    } else {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(a.x) + xoff + k0;
+      st.v[0] = *(gu32x4_t*)(p);
+      st.v[1] = *(gu32x4_t*)(p + 32);
     }
   };
-  f32x4 acc[8];
+  // this lane's 8 token values of block q as bf16 (high part) and, for fp32
+  // tokens, the low parts
+  auto xparts = [&](const XSt& st, int q, u32x4_t& hi, u32x4_t& lo) __attribute__((always_inline)) {
+    if constexpr (XF32) {
+      const u32x4_t f0 = st.v[2 * q], f1 = st.v[2 * q + 1];
+      uint32_t h[4], l[4];
+      split_bf16x2(__uint_as_float(f0[0]), __uint_as_float(f0[1]), &h[0], &l[0]);
+      split_bf16x2(__uint_as_float(f0[2]), __uint_as_float(f0[3]), &h[1], &l[1]);
+      split_bf16x2(__uint_as_float(f1[0]), __uint_as_float(f1[1]), &h[2], &l[2]);
+      split_bf16x2(__uint_as_float(f1[2]), __uint_as_float(f1[3]), &h[3], &l[3]);
+      hi = u32x4_t{h[0], h[1], h[2], h[3]};
+      lo = u32x4_t{l[0], l[1], l[2], l[3]};
+    } else {
+      hi = st.v[q];
+    }
+  };
+  auto xstore = [&](const XSt& st, uint16_t* buf) __attribute__((always_inline)) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  St ar[4];
-  load(kb0, ar[0]);
-  load(kb0 + min(1, ns - 1) * XBK, ar[1]);
-  store(ar[0], Ls[0]);
-  put_x16(ar[0], kb0);
+    for (int q = 0; q < 2; ++q) {
+      u32x4_t hi, lo;
+      xparts(st, q, hi, lo);
+      *reinterpret_cast<u32x4_t*>(buf + (2 * wv + q) * AFRAG + slot) = hi;
+      if constexpr (XF32) *reinterpret_cast<u32x4_t*>(buf + (16 + 2 * wv + q) * AFRAG + slot) = lo;
+    }
+  };
+  const bool write_x16 = ex == 0 && t0 + 16 * wv + r4 < a.T;
+  auto put_x16 = [&](const XSt& st, int s) __attribute__((always_inline)) {
+    if (write_x16) {
+      uint16_t* d = a.x16 + xoff + kb0 + s * XBK;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        u32x4_t h;
+        if constexpr (XF32) {
+          h = f32x8_to_f16(__builtin_bit_cast(f32x4_t, st.v[2 * q]), __builtin_bit_cast(f32x4_t, st.v[2 * q + 1]));
+        } else {
+          h = bf16x8_to_f16(st.v[q]);
+        }
+        *reinterpret_cast<u32x4_t*>(d + 32 * q) = h;
+      }
+    }
+  };
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // router operands BD stages ahead (2 for bf16 tokens; the fp32-token
+  // kernel has no registers to spare for the second)
+  constexpr int BD = XF32 ? 1 : 2, RB = 2 * BD;
+  XSt ar[4];
+  BSt br[RB];
+  bload(0, br[0]);
+  if constexpr (BD == 2) bload(min(1, ns - 1), br[1]);
+  xload(0, ar[0]);
+  xload(min(1, ns - 1), ar[1]);
+  xstore(ar[0], Ls[0]);
+  put_x16(ar[0], 0);
   __syncthreads();
   for (int s4 = 0; s4 < ns; s4 += 4) {
-#define STRATA_RSTAGE(ST)                                                                  \
-    if (s4 + ST < ns) {                                                                    \
-      const int s = s4 + ST;                                                               \
-      load(kb0 + min(s + 2, ns - 1) * XBK, ar[(ST + 2) & 3]);                              \
-      __builtin_amdgcn_sched_barrier(0);                                                   \
-      const uint16_t* buf = Ls[ST & 1];                                                    \
-      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                   \
-        const bf16x8 bh = rt_frag(buf, RT_AFR + 4 * wv + 2 * kb, lane);                    \
-        const bf16x8 bl = rt_frag(buf, RT_AFR + 4 * wv + 2 * kb + 1, lane);                \
-        _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                    \
-          const bf16x8 af = rt_frag(buf, 2 * m + kb, lane);                                \
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, af, acc[m], 0, 0, 0);       \
-          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, af, acc[m], 0, 0, 0);       \
-        }                                                                                  \
-      }                                                                                    \
-      if (s + 1 < ns) {                                                                    \
-        store(ar[(ST + 1) & 3], Ls[(ST + 1) & 1]);                                         \
-        put_x16(ar[(ST + 1) & 3], kb0 + (s + 1) * XBK);                                    \
-      }                                                                                    \
-      __syncthreads();                                                                     \
+#define STRATA_RSTAGE(ST)                                                                    \
+    if (s4 + ST < ns) {                                                                      \
+      const int s = s4 + ST;                                                                 \
+      bload(min(s + BD, ns - 1), br[(ST + BD) & (RB - 1)]);                                  \
+      xload(min(s + 2, ns - 1), ar[(ST + 2) & 3]);                                           \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+      router_stage<XF32>(Ls[ST & 1], br[ST & (RB - 1)].v, lane, acc);                        \
+      if (s + 1 < ns) {                                                                      \
+        xstore(ar[(ST + 1) & 3], Ls[(ST + 1) & 1]);                                          \
+        put_x16(ar[(ST + 1) & 3], s + 1);                                                    \
+      }                                                                                      \
+      __syncthreads();                                                                       \
     }
     STRATA_RSTAGE(0) STRATA_RSTAGE(1) STRATA_RSTAGE(2) STRATA_RSTAGE(3)
 #undef STRATA_RSTAGE
   }
-  // D[e][t]: lane l holds experts 4 (l / 16) .. + 3 of its subtile for token 16 m + l % 16
-  float* out = a.part + kz * a.plane;
-  const int e = e0 + 16 * wv + 4 * (lane >> 4);
+  // D[e][t]: lane l holds experts 4 (l / 16) .. + 3 of group n for token 16 m + l % 16
+  float* out = a.part + (size_t)kz * a.plane;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int t = t0 + 16 * m + (lane & 15);
-    if (t >= a.T) continue;
-    if ((a.E & 3) == 0) {
-      if (e < a.E) *reinterpret_cast<f32x4*>(out + (size_t)t * a.E + e) = acc[m];
-    } else {
+  for (int n = 0; n < 2; ++n) {
+    const int e = e0 + 32 * wv + 16 * n + 4 * (lane >> 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (e + j < a.E) out[(size_t)t * a.E + e + j] = acc[m][j];
+    for (int m = 0; m < 8; ++m) {
+      const int t = t0 + 16 * m + (lane & 15);
+      if (t >= a.T) continue;
+      if ((a.E & 3) == 0) {
+        if (e < a.E) *reinterpret_cast<f32x4*>(out + (size_t)t * a.E + e) = acc[m][n];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (e + j < a.E) out[(size_t)t * a.E + e + j] = acc[m][n][j];
+      }
     }
   }
 }
@@ -1291,35 +1183,6 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // first, then the token rows (which the gate/up GEMM reads).
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-struct RouterPlan {
-  int S, kper;
-  size_t plane;
-  float* part;
-  uint16_t* x16;
-};
-
-RouterPlan router_plan(const Layer& L, const Work& W, int T, bool x_f32) {
-  // split K until the grid has about one workgroup per resident slot: two per
-  // CU for the fp32-token kernel, one for the bf16 one (its LDS and registers)
-  RouterPlan r;
-  const int slots = x_f32 ? 512 : 256;
-  const int tiles = ((L.E + BN - 1) / BN) * ((T + BM - 1) / BM);
-  const int ksteps = L.H / BK;
-  const size_t x16_bytes = (size_t)T * L.H * 2;       // <= the region (slots >= T)
-  r.plane = (size_t)T * L.E;
-  int S = 1;
-  if (L.E <= 512) {
-    S = std::min(std::min(8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
-    while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
-  }
-  r.kper = ((ksteps + S - 1) / S) * BK;
-  r.S = (L.H + r.kper - 1) / r.kper;                   // no empty split
-  r.part = r.S > 1 ? reinterpret_cast<float*>(W.ybf) : W.logits;
-  r.x16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(W.ybf) +
-                                      (r.S > 1 ? align256((size_t)r.S * r.plane * 4) : 0));
-  return r;
-}
-
 // compute units of the current device (cached per device)
 int cu_count() {
   static int cache[64] = {};
@@ -1340,11 +1203,41 @@ int persistent_grid(int max_items) {
   return 8 * std::max(1, std::min(cu_count() / 8, (max_items + 7) / 8));
 }
 
+struct RouterPlan {
+  int S, kper;
+  size_t plane;
+  float* part;
+  uint16_t* x16;
+};
+
+RouterPlan router_plan(const Layer& L, const Work& W, int T) {
+  // split K until the grid has about one workgroup per CU (at most 8 splits:
+  // top-k reads every plane; one plane past 512 experts, where top-k re-reads
+  // its plane)
+  RouterPlan r;
+  const int slots = cu_count();
+  const int tiles = ((L.E + RT_E - 1) / RT_E) * ((T + BM - 1) / BM);
+  const int ksteps = L.H / XBK;
+  const size_t x16_bytes = (size_t)T * L.H * 2;       // <= the region (slots >= T)
+  r.plane = (size_t)T * L.E;
+  int S = 1;
+  if (L.E <= 512) {
+    S = std::min(std::min(8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
+    while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
+  }
+  r.kper = ((ksteps + S - 1) / S) * XBK;
+  r.S = (L.H + r.kper - 1) / r.kper;                   // no empty split
+  r.part = r.S > 1 ? reinterpret_cast<float*>(W.ybf) : W.logits;
+  r.x16 = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(W.ybf) +
+                                      (r.S > 1 ? align256((size_t)r.S * r.plane * 4) : 0));
+  return r;
+}
+
 template <int FMT>
 hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   GemmArgs g;
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
-  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T, c.x_f32).x16; g.w = W;
+  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
   const int max_tiles = W.max_tiles;
   launch(tr, k_gemm_gateup<FMT>, dim3(persistent_grid(max_tiles * (L.I / gu_rows<FMT>()))), dim3(64 * GEMM_WAVES), 0,
          s, g);
@@ -1356,25 +1249,19 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
 }  // namespace
 
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
-  const RouterPlan rp = router_plan(L, W, c.T, c.x_f32);
+  const RouterPlan rp = router_plan(L, W, c.T);
   const int S = rp.S;
   const size_t plane = rp.plane;
   RouterArgs r;
-  r.x = c.x; r.x_f32 = c.x_f32; r.T = c.T; r.H = L.H; r.E = L.E;
+  r.x = c.x; r.T = c.T; r.H = L.H; r.E = L.E; r.S = S;
   r.kper = rp.kper; r.plane = plane;
   r.whi = L.router_hi; r.wlo = L.router_lo;
   r.part = rp.part;
   r.x16 = rp.x16;
-  dim3 grid((L.E + BN - 1) / BN, (c.T + BM - 1) / BM, S);
-  if (c.x_f32) {
-    launch(tr, k_router_gemm<true>, grid, dim3(256), 0, s, r);
-  } else {
-    RouterMArgs m;
-    m.x = reinterpret_cast<const uint16_t*>(c.x); m.T = c.T; m.H = L.H; m.E = L.E;
-    m.kper = rp.kper; m.S = S; m.plane = plane; m.whi = L.router_hi; m.wlo = L.router_lo;
-    m.part = rp.part; m.x16 = rp.x16;
-    launch(tr, k_router_mfma, dim3(8 * ((grid.x * grid.y * S + 7) / 8)), dim3(64 * RT_WAVES), 0, s, m);
-  }
+  const int items = ((L.E + RT_E - 1) / RT_E) * ((c.T + BM - 1) / BM) * S;
+  const dim3 grid(8 * ((items + 7) / 8)), block(64 * RT_WAVES);
+  if (c.x_f32) launch(tr, k_router<true>, grid, block, 0, s, r);
+  else launch(tr, k_router<false>, grid, block, 0, s, r);
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b;

@@ -100,11 +100,22 @@ __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict_
   }
 }
 
+// Router split: Wr (fp32 [E][H]) -> bf16 high parts and bf16 remainders,
+// each in MFMA operand order for the prefill router: fragment (g, kb) of 16
+// experts (group g) x 32 of K (block kb) is 1 KiB at element
+// (g * H / 32 + kb) * 512, and its lane l holds the 8 weights of expert
+// 16 g + l % 16 at K = 32 kb + 8 (l / 16) + j in element 8 l + j.  Experts
+// past E (padding of the last group) are zero.  One thread per element of
+// the output.
 __global__ void k_router_split(const float* __restrict__ w, uint16_t* __restrict__ hi,
-                               uint16_t* __restrict__ lo, long long n) {
+                               uint16_t* __restrict__ lo, int E, int H, long long n) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  const float v = w[i];
+  const int j = (int)(i & 7), l = (int)((i >> 3) & 63);
+  const long long f = i >> 9;
+  const int nkb = H / 32, kb = (int)(f % nkb), g = (int)(f / nkb);
+  const int e = 16 * g + (l & 15), k = 32 * kb + 8 * (l >> 4) + j;
+  const float v = e < E ? w[(size_t)e * H + k] : 0.0f;
   const uint16_t h = f32_to_bf16_rne(v);
   hi[i] = h;
   lo[i] = f32_to_bf16_rne(v - bf16_to_f32(h));
@@ -124,11 +135,11 @@ hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in,
 }
 
 hipError_t launch_router_split(const Layer& L, hipStream_t s) {
-  const long long n = (long long)L.E * L.H;
+  const long long n = (long long)((L.E + 15) / 16) * 16 * L.H;
   const int bs = 256;
   hipLaunchKernelGGL(k_router_split, dim3((unsigned)((n + bs - 1) / bs)), dim3(bs), 0, s,
                      L.router_w, const_cast<uint16_t*>(L.router_hi),
-                     const_cast<uint16_t*>(L.router_lo), n);
+                     const_cast<uint16_t*>(L.router_lo), L.E, L.H, n);
   return hipGetLastError();
 }
 

@@ -120,12 +120,17 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   return p;
 }
 
+// one part (high or low) of the router split: experts padded to groups of 16
+size_t router_part_bytes(const strata_moe_config& c) {
+  return align256((size_t)((c.n_experts + 15) / 16) * 16 * c.hidden * 2);
+}
+
 size_t packed_experts_bytes(const strata_moe_config& c) {
   return align256((size_t)(c.n_experts + c.n_shared) * expert_bytes(c.qfmt, c.hidden, c.inter));
 }
 
 size_t packed_total(const strata_moe_config& c) {
-  return packed_experts_bytes(c) + 2 * align256((size_t)c.n_experts * c.hidden * 2);
+  return packed_experts_bytes(c) + 2 * router_part_bytes(c);
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -259,7 +264,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   L.expert_stride = expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
   const size_t rh = packed_experts_bytes(*cfg);
   L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
-  L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + align256((size_t)cfg->n_experts * cfg->hidden * 2));
+  L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + router_part_bytes(*cfg));
   Work& W = h->W;
   W.logits = reinterpret_cast<float*>(ws + p.logits);
   W.topk_idx = reinterpret_cast<int*>(ws + p.topk_idx);
