@@ -245,8 +245,14 @@ def main():
                 kernels[n]["TFLOPs"] = round(fl[n] / (kern_us[j] * 1e-6) / 1e12, 1)
         dom = max(names, key=lambda n: kernels[n]["us"])
         achieved = kernels[dom].get("TFLOPs", 0.0)
+        # HBM bytes per launch of that kernel (FETCH_SIZE + WRITE_SIZE summary
+        # taken on the current kernel sources), for reference next to the flops
+        from quantized_moe_expert_gemv_amd import prof_summary
+        measured = prof_summary.read_traffic(
+            os.path.join(ROOT, "profiles", f"prefill_hbm_traffic_{args.workload}.md"))
         roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": int(measured[dom]) if dom in measured else None}
         layer_flops = sum(fl.values())
         layer_frac = layer_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12)
         layer_bytes = None

@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 # library kernel name fragment -> benchmark name
 KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_gateup", "gateup"),
-           ("k_down", "down_combine"), ("k_router_gemm", "router_gemm"), ("k_topk_chunks", "topk"),
+           ("k_down", "down_combine"), ("k_router", "router_gemm"), ("k_topk_chunks", "topk"),
            ("k_colscan", "colscan"), ("k_scan", "scan"), ("k_scatter", "scatter"), ("k_gemm_gateup", "gateup_gemm"),
            ("k_gemm_down", "down_gemm"), ("k_combine", "combine")]
 
