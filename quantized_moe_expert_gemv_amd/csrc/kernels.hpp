@@ -25,7 +25,7 @@ struct Work {
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
   int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}, in XCD segments,
                       //             each sorted by row class (see k_scan)
-  float* act;         // prefill: bf16 SwiGLU rows [slots][I] (same region as actp)
+  float* act;         // prefill: fp16 SwiGLU rows [slots][I] (same region as actp)
   _Float16* actp;     // decode: SwiGLU rows as two fp16 parts [active expert][2][T][I]
   _Float16* xparts;   // decode: token rows as two fp16 parts [2][T][H]
   uint16_t* ybf;      // [slots][H]  prefill: per-pair expert outputs, bf16; before the
