@@ -64,6 +64,11 @@ WORKLOADS: Dict[str, Workload] = {
     # overflows fp32 by about layer 8; at 0.005 each layer moves h by ~2%)
     "stack48_q3_decode": Workload("stack48_q3_decode", 2560, 512, 512, 10, 3, 1, True,
                                   n_layers=48, steps=256, d_sigma=0.005),
+    # skinny batches between the one-pass decode and the 8K chunk (batched
+    # slots, longer verify windows), same layer and Zipf-skewed router
+    "skinny_t16_q2": Workload("skinny_t16_q2", 2560, 512, 512, 10, 2, 16, True),
+    "skinny_t32_q2": Workload("skinny_t32_q2", 2560, 512, 512, 10, 2, 32, True),
+    "skinny_t64_q2": Workload("skinny_t64_q2", 2560, 512, 512, 10, 2, 64, True),
     # 8192-token prefill chunk through one Q2 layer, Zipf-skewed router
     "prefill_t8192_q2": Workload("prefill_t8192_q2", 2560, 512, 512, 10, 2, 8192, True),
     # DeepSeek-V4-Flash-shaped layer, Q4, 256 routed + 1 shared, top-6

@@ -29,6 +29,7 @@
 // d (q - c) rounded once to fp16 (11-bit mantissa), activations fp16 (bf16
 // inputs exactly, within the fp16 range).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -643,8 +644,8 @@ __device__ inline int tile_count(const GemmArgs& a) { return *(cint_ptr)(a.w.met
 __device__ inline float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // Column tiles of a work item: GEMM_WAVES waves of nsl() slabs each.
-template <int FMT> constexpr int gu_rows() { return GEMM_WAVES * nsl<FMT>() / 2 * 16; }  // rows of I, gate/up
-template <int FMT> constexpr int dn_cols() { return GEMM_WAVES * nsl<FMT>() * 16; }      // rows of H, down
+template <int NSL> constexpr int gu_rows() { return GEMM_WAVES * NSL / 2 * 16; }  // rows of I, gate/up
+template <int NSL> constexpr int dn_cols() { return GEMM_WAVES * NSL * 16; }      // rows of H, down
 
 // Epilogue staging.  A work item's results are written to an LDS tile of
 // [BM rows][NC halves] (16-byte granules of a row XOR-swizzled by row % 8,
@@ -690,7 +691,7 @@ template <int FMT, int MC, int NSL, typename Next>
 __device__ inline void gateup_item(const GemmArgs& a, const ItemSrc<NSL>& cur, Next next, int slot0, int rows,
                                    int col, _Float16 (*As)[ASTAGE], char* stg, int wv, int lane, AStage (&ar)[4],
                                    PairCodes<FMT> (&bc)[2][NSL]) {
-  constexpr int NC = gu_rows<FMT>();
+  constexpr int NC = gu_rows<NSL>();
   f32x4 acc[MC][NSL];
 #pragma unroll
   for (int m = 0; m < MC; ++m)
@@ -724,7 +725,7 @@ template <int FMT, int MC, int NSL, typename Next>
 __device__ inline void down_item(const GemmArgs& a, const ItemSrc<NSL>& cur, Next next, int slot0, int rows, int col,
                                  _Float16 (*As)[ASTAGE], char* stg, int wv, int lane, AStage (&ar)[4],
                                  PairCodes<FMT> (&bc)[2][NSL]) {
-  constexpr int NC = dn_cols<FMT>();
+  constexpr int NC = dn_cols<NSL>();
   f32x4 acc[MC][NSL];
 #pragma unroll
   for (int m = 0; m < MC; ++m)
@@ -750,12 +751,11 @@ __device__ inline void down_item(const GemmArgs& a, const ItemSrc<NSL>& cur, Nex
 // of item i + 2 and the pair of this lane's token row in item i + 1 are
 // requested while item i starts, so the next item's operand addresses are
 // known by the time its loads are issued (two stages before this item ends).
-template <int FMT>
+template <int FMT, int NSL>
 __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) {
-  constexpr int NSL = nsl<FMT>();
   __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
-  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * gu_rows<FMT>()];
-  const ItemSeq seq(tile_count(a), a.I / gu_rows<FMT>());
+  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * gu_rows<NSL>()];
+  const ItemSeq seq(tile_count(a), a.I / gu_rows<NSL>());
   if (!seq.valid(0)) return;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = 16 * wv + (lane >> 2);                 // this lane's token row of a tile
@@ -810,12 +810,11 @@ __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_gateup(GemmArgs a) 
 // down: work item = 128 slots x dn_cols() rows of H; wave w takes NSL row
 // groups of 16.  Persistent as the gate/up GEMM; its A rows are the slots
 // themselves, so only the tile entries are looked up ahead.
-template <int FMT>
+template <int FMT, int NSL>
 __global__ __launch_bounds__(64 * GEMM_WAVES, 1) void k_gemm_down(GemmArgs a) {
-  constexpr int NSL = nsl<FMT>();
   __shared__ __attribute__((aligned(16))) _Float16 As[2][ASTAGE];
-  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * dn_cols<FMT>()];
-  const ItemSeq seq(tile_count(a), (a.H + dn_cols<FMT>() - 1) / dn_cols<FMT>());
+  __shared__ __attribute__((aligned(16))) char stg[BM * 2 * dn_cols<NSL>()];
+  const ItemSeq seq(tile_count(a), (a.H + dn_cols<NSL>() - 1) / dn_cols<NSL>());
   if (!seq.valid(0)) return;
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = 16 * wv + (lane >> 2);
@@ -1183,6 +1182,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 // first, then the token rows (which the gate/up GEMM reads).
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// calls of up to this many tokens use the narrow expert-GEMM work items
+constexpr int SKINNY_T = 64;
+
 // compute units of the current device (cached per device)
 int cu_count() {
   static int cache[64] = {};
@@ -1197,10 +1199,10 @@ int cu_count() {
   return *c;
 }
 
-// persistent GEMM grid: one workgroup per CU (a multiple of 8, one group per
-// XCD), fewer when there are fewer items
-int persistent_grid(int max_items) {
-  return 8 * std::max(1, std::min(cu_count() / 8, (max_items + 7) / 8));
+// persistent GEMM grid: per_cu workgroups per CU (a multiple of 8, one
+// group per XCD), fewer when there are fewer items
+int persistent_grid(int max_items, int per_cu = 1) {
+  return 8 * std::max(1, std::min(per_cu * cu_count() / 8, (max_items + 7) / 8));
 }
 
 struct RouterPlan {
@@ -1239,10 +1241,22 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
   g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
   const int max_tiles = W.max_tiles;
-  launch(tr, k_gemm_gateup<FMT>, dim3(persistent_grid(max_tiles * (L.I / gu_rows<FMT>()))), dim3(64 * GEMM_WAVES), 0,
-         s, g);
-  launch(tr, k_gemm_down<FMT>, dim3(persistent_grid(max_tiles * ((L.H + dn_cols<FMT>() - 1) / dn_cols<FMT>()))),
-         dim3(64 * GEMM_WAVES), 0, s, g);
+  // Skinny calls (up to 64 tokens: tiles of a few rows, one or two per
+  // touched expert) are bound by streaming each expert's weights through one
+  // workgroup; narrower work items (2 slabs per wave for gate/up, 1 for down)
+  // spread those streams over 2 and 4 times as many CUs.
+  auto gemms = [&](auto gu_nsl, auto dn_nsl) {
+    constexpr int GN = decltype(gu_nsl)::value, DN = decltype(dn_nsl)::value;
+    launch(tr, k_gemm_gateup<FMT, GN>, dim3(persistent_grid(max_tiles * (L.I / gu_rows<GN>()))),
+           dim3(64 * GEMM_WAVES), 0, s, g);
+    // (the one-slab down kernel fits two workgroups per CU: under 128 VGPRs,
+    // 64 KiB of LDS)
+    launch(tr, k_gemm_down<FMT, DN>,
+           dim3(persistent_grid(max_tiles * ((L.H + dn_cols<DN>() - 1) / dn_cols<DN>()), DN == 1 ? 2 : 1)),
+           dim3(64 * GEMM_WAVES), 0, s, g);
+  };
+  if (c.T <= SKINNY_T) gemms(std::integral_constant<int, 2>(), std::integral_constant<int, 1>());
+  else gemms(std::integral_constant<int, nsl<FMT>()>(), std::integral_constant<int, nsl<FMT>()>());
   return hipGetLastError();
 }
 

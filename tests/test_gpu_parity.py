@@ -257,6 +257,23 @@ def test_workload_prefill_t8192_q2(B):
     assert rel_l2(out[sample], ref) <= PREFILL_TOL
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["skinny_t16_q2", "skinny_t32_q2", "skinny_t64_q2"])
+def test_workload_skinny_q2(B, name):
+    """Skinny batches (16-64 tokens) of the verify/prefill layer: the
+    grouped-GEMM path with tiles of a few rows; routing exact for every
+    token, outputs sampled."""
+    T = WORKLOADS[name].tokens
+    hl, layer = full_layer(name, 8192)
+    bits, xf = tokens(hl, 300 + T, T)
+    x = to_device_bf16(bits, DEV)
+    check_route(layer, hl, x, xf, w_atol=5e-5)
+    out = layer.forward(x).cpu().numpy()
+    sample = np.random.default_rng(T).choice(T, 8, replace=False)
+    ref, _ = hl.oracle(xf[sample])
+    assert rel_l2(out[sample], ref) <= PREFILL_TOL
+
+
 @pytest.mark.timeout(900)
 def test_workload_deepseek_q4(B):
     hl, layer = full_layer("deepseek_q4_t2048", 2048)
