@@ -11,12 +11,16 @@ Recipe (the value distributions of the workloads):
                     workload is unbiased
   * expert codes    uniform random bytes: every 2/3/4-bit code is then
                     uniform and independent, whatever the bit layout
-  * expert scales   d = fp16(|N(0, 0.02^2)|), round-to-nearest-even
+  * expert scales   d = fp16(|N(0, 0.02^2)|), round-to-nearest-even; for
+                    MXFP4 the E8M0 byte 127 + floor(log2 |N(0, 0.02^2)|) - 2,
+                    clipped to [1, 254] (so 6 x 2^(e-127), the largest
+                    element magnitude, is 0.75 to 1.5 times the drawn value)
   * tokens          x = bf16(fp32(N(0, 1))), round-to-nearest-even
 
 Canonical expert record (the storage layout the library's create call
 consumes): gate [I rows][H/32 blocks], up [I][H/32], down [H][I/32]; each
-block is its code bytes followed by the little-endian fp16 scale.
+block is its code bytes followed by the little-endian fp16 scale (MXFP4: the
+E8M0 scale byte).
 """
 
 import os
@@ -24,7 +28,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .workloads import FORMATS, BLOCK, canonical_block_bytes
+from .workloads import FORMATS, BLOCK, MXFP4, canonical_block_bytes
 
 TAG_ROUTER, TAG_BIAS, TAG_EXPERT, TAG_SHARED, TAG_TOKEN = 1, 2, 3, 4, 5
 
@@ -59,10 +63,15 @@ def router_bias(seed: int, layer: int, n_experts: int, s: float = 1.1) -> np.nda
 def _blocks(g, n_blocks: int, fmt: int, d_sigma: float = 0.02) -> np.ndarray:
     cb = FORMATS[fmt][1]
     codes = g.integers(0, 256, size=(n_blocks, cb), dtype=np.uint8)
-    d = np.abs(d_sigma * g.standard_normal(n_blocks)).astype(np.float16)
     out = np.empty((n_blocks, canonical_block_bytes(fmt)), dtype=np.uint8)
     out[:, :cb] = codes
-    out[:, cb:] = d.astype("<f2").view(np.uint8).reshape(n_blocks, 2)
+    if fmt == MXFP4:
+        a = np.abs(d_sigma * g.standard_normal(n_blocks))
+        e = 127 + np.floor(np.log2(np.maximum(a, 1e-30))) - 2
+        out[:, cb] = np.clip(e, 1, 254).astype(np.uint8)
+    else:
+        d = np.abs(d_sigma * g.standard_normal(n_blocks)).astype(np.float16)
+        out[:, cb:] = d.astype("<f2").view(np.uint8).reshape(n_blocks, 2)
     return out
 
 

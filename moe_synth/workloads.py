@@ -18,15 +18,19 @@ by each implementation.
 from dataclasses import dataclass
 from typing import Dict
 
-# fmt -> (bits per code, code bytes per 32-weight block)
-FORMATS: Dict[int, tuple] = {2: (2, 8), 3: (3, 12), 4: (4, 16)}
+# fmt -> (bits per code, code bytes per 32-weight block); 5 is MXFP4 (4-bit
+# E2M1 elements with one E8M0 scale byte per block of 32, OCP Microscaling
+# Formats v1.0), the others the Q2/Q3/Q4 blocks with an fp16 scale
+FORMATS: Dict[int, tuple] = {2: (2, 8), 3: (3, 12), 4: (4, 16), 5: (4, 16)}
+MXFP4 = 5
 BLOCK = 32          # weights per quantised block
-SCALE_BYTES = 2     # one fp16 scale per block, stored after the codes
+# bytes of the per-block scale stored after the codes: fp16, or E8M0 for MXFP4
+SCALE_BYTES: Dict[int, int] = {2: 2, 3: 2, 4: 2, 5: 1}
 
 
 def canonical_block_bytes(fmt: int) -> int:
-    """Bytes of one canonical block: codes followed by the fp16 scale."""
-    return FORMATS[fmt][1] + SCALE_BYTES
+    """Bytes of one canonical block: codes followed by the scale."""
+    return FORMATS[fmt][1] + SCALE_BYTES[fmt]
 
 
 @dataclass(frozen=True)
@@ -75,4 +79,9 @@ WORKLOADS: Dict[str, Workload] = {
     "deepseek_q4_t1": Workload("deepseek_q4_t1", 4096, 2048, 256, 6, 4, 1, True, n_shared=1),
     "deepseek_q4_t2048": Workload("deepseek_q4_t2048", 4096, 2048, 256, 6, 4, 2048, True,
                                   n_shared=1),
+    # the same layer with MXFP4 experts (the format of the pages' DeepSeek
+    # suites): E2M1 codes, E8M0 block scales 2^(floor(log2 |N(0, 0.02^2)|) - 2)
+    "deepseek_mxfp4_t1": Workload("deepseek_mxfp4_t1", 4096, 2048, 256, 6, 5, 1, True, n_shared=1),
+    "deepseek_mxfp4_t2048": Workload("deepseek_mxfp4_t2048", 4096, 2048, 256, 6, 5, 2048, True,
+                                     n_shared=1),
 }

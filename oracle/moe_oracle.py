@@ -11,7 +11,8 @@ the results, ai-coding.wiselychen.com "Strata two weeks", section
 成功思路一; the always-on shared expert of the DeepSeek layer, lcz.me/topic/2153
 section 一):
 
-  O1 unpack   w = d * (q - c) per 32-weight block, c = 1.5 / 3.5 / 8
+  O1 unpack   w = d * (q - c) per 32-weight block, c = 1.5 / 3.5 / 8;
+              MXFP4 (format 5): w = 2^(e - 127) * E2M1(q)
   O2 router   l[t, e] = sum_h x[t, h] * Wr[e, h] + b[e]
   O3 select   S_t = the k largest l[t, .]  (ids returned in ascending order)
   O4 weights  w[t, j] = softmax of l[t, .] restricted to S_t
@@ -32,18 +33,48 @@ renormalisation or the tie order; the readings used here are:
   * the shared expert enters the sum with weight 1.
 Every quantity is fp64; the stored inputs (bf16 x, fp32 router, fp16 d) are
 taken exactly.
+
+MXFP4 experts.  The pages name the format (lcz.me/topic/2153, the DeepSeek
+suites of section 一) but give no layout; the element and scale encodings are
+those of the OCP Microscaling Formats (MX) v1.0 specification: a block of 32
+FP4 E2M1 elements (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+exponent field 0 is subnormal: m * 0.5) sharing one E8M0 scale byte e (the
+value 2^(e - 127); e = 255 is NaN).  Readings: element j of a block is the
+4-bit code j in the block's little-endian bit string (as for the other
+formats, so byte j / 2, low nibble first), followed by the scale byte; there
+is no offset term.
 """
 
 import numpy as np
 
 # code offset c of each format (w = d * (q - c))
 OFFSET = {2: 1.5, 3: 3.5, 4: 8.0}
-CODE_BYTES = {2: 8, 3: 12, 4: 16}
+CODE_BYTES = {2: 8, 3: 12, 4: 16, 5: 16}
+CODE_BITS = {2: 2, 3: 3, 4: 4, 5: 4}
+SCALE_BYTES = {2: 2, 3: 2, 4: 2, 5: 1}
+MXFP4 = 5
 BLOCK = 32
 
 
 def block_bytes(fmt):
-    return CODE_BYTES[fmt] + 2
+    return CODE_BYTES[fmt] + SCALE_BYTES[fmt]
+
+
+def e2m1_value(q):
+    """FP4 E2M1 code(s) -> value: sign bit 3, exponent bits 1-2 (bias 1),
+    mantissa bit 0; exponent field 0 is subnormal (m * 2^(1 - 1) * 0.5)."""
+    q = np.asarray(q, dtype=np.int64)
+    sign = np.where(q & 8, -1.0, 1.0)
+    ex = (q >> 1) & 3
+    m = (q & 1).astype(np.float64)
+    mag = np.where(ex == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(ex.astype(np.float64) - 1.0))
+    return sign * mag
+
+
+def e8m0_value(e):
+    """E8M0 scale byte(s) -> 2^(e - 127); 255 is NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e.astype(np.float64) - 127.0))
 
 
 # ---------------------------------------------------------------- O1 unpack
@@ -63,9 +94,12 @@ def dequant_blocks(blocks, fmt):
     """blocks uint8 [..., nblk, Bq] -> fp64 weights [..., nblk*32]."""
     cb = CODE_BYTES[fmt]
     blocks = np.asarray(blocks, dtype=np.uint8)
-    q = unpack_codes(blocks[..., :cb], fmt)                       # [..., nblk, 32]
-    d = np.ascontiguousarray(blocks[..., cb:cb + 2]).view("<f2")[..., 0].astype(np.float64)
-    w = d[..., None] * (q.astype(np.float64) - OFFSET[fmt])
+    q = unpack_codes(blocks[..., :cb], CODE_BITS[fmt])            # [..., nblk, 32]
+    if fmt == MXFP4:
+        w = e8m0_value(blocks[..., cb])[..., None] * e2m1_value(q)
+    else:
+        d = np.ascontiguousarray(blocks[..., cb:cb + 2]).view("<f2")[..., 0].astype(np.float64)
+        w = d[..., None] * (q.astype(np.float64) - OFFSET[fmt])
     return w.reshape(*w.shape[:-2], w.shape[-2] * BLOCK)
 
 

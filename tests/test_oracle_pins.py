@@ -19,7 +19,15 @@ from moe_synth import generate as G
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 OFFSETS = {2: 1.5, 3: 3.5, 4: 8.0}        # w = d * (q - c), from the format definitions
-CODE_BYTES = {2: 8, 3: 12, 4: 16}
+CODE_BYTES = {2: 8, 3: 12, 4: 16, 5: 16}
+BITS = {2: 2, 3: 3, 4: 4, 5: 4}
+SCALE_BYTES = {2: 2, 3: 2, 4: 2, 5: 1}
+MXFP4 = 5
+
+# FP4 E2M1 element values of codes 0..15 as tabulated in the OCP Microscaling
+# Formats (MX) v1.0 specification (section 5.3.3): 0, 0.5, 1, 1.5, 2, 3, 4, 6,
+# then the same with the sign bit set
+E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
 
 
 # ------------------------------------------------------------------ O1 unpack
@@ -40,47 +48,104 @@ def _pack_codes(codes, bits):
     return v.to_bytes(len(codes) * bits // 8, "little")
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_pack_unpack_roundtrip(fmt):
     rng = np.random.default_rng(7 + fmt)
-    codes = rng.integers(0, 1 << fmt, size=(50, 32))
-    packed = np.stack([np.frombuffer(_pack_codes(c, fmt), dtype=np.uint8) for c in codes])
+    codes = rng.integers(0, 1 << BITS[fmt], size=(50, 32))
+    packed = np.stack([np.frombuffer(_pack_codes(c, BITS[fmt]), dtype=np.uint8) for c in codes])
     assert packed.shape == (50, CODE_BYTES[fmt])
-    np.testing.assert_array_equal(O.unpack_codes(packed, fmt), codes)
+    np.testing.assert_array_equal(O.unpack_codes(packed, BITS[fmt]), codes)
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+# ------------------------------------------------------------------ MXFP4 (OCP MX v1.0)
+def _torch_fp4_reference():
+    """PyTorch's own FP4 unpacking reference (its testing helpers import
+    expecttest only for test-case classes; a stand-in module is enough)."""
+    import sys
+    import types
+    if "expecttest" not in sys.modules:
+        stub = types.ModuleType("expecttest")
+        stub.TestCase = object
+        sys.modules["expecttest"] = stub
+    from torch.testing._internal.common_quantized import _floatx_unpacked_to_f32
+    return _floatx_unpacked_to_f32
+
+
+def test_e2m1_matches_pytorch_reference():
+    torch = pytest.importorskip("torch")
+    try:
+        ref_fn = _torch_fp4_reference()
+    except Exception as e:                      # pragma: no cover - depends on the torch build
+        pytest.skip(f"PyTorch FP4 reference unavailable: {e}")
+    ref = ref_fn(torch.arange(16, dtype=torch.uint8), 2, 1).double().numpy()
+    got = O.e2m1_value(np.arange(16))
+    np.testing.assert_array_equal(got, ref)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_e2m1_matches_the_spec_table():
+    got = O.e2m1_value(np.arange(16))
+    np.testing.assert_array_equal(got, np.array(E2M1_SPEC))
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(np.array(E2M1_SPEC)))
+
+
+def test_e8m0_matches_pytorch_float8_e8m0fnu():
+    torch = pytest.importorskip("torch")
+    e = np.arange(255, dtype=np.uint8)             # 255 is NaN in both
+    ref = torch.from_numpy(e).view(torch.float8_e8m0fnu).float().double().numpy()
+    np.testing.assert_array_equal(O.e8m0_value(e), ref)
+    assert np.isnan(O.e8m0_value(255))
+
+
+def test_mxfp4_block_golden():
+    # hand-built blocks: codes 0..15 twice; scale bytes 127 (x1), 130 (x8), 120 (x2^-7)
+    codes = bytes((2 * j) | ((2 * j + 1) << 4) for j in range(8)) * 2
+    for e, scale in [(127, 1.0), (130, 8.0), (120, 2.0 ** -7)]:
+        blk = np.frombuffer(codes + bytes([e]), dtype=np.uint8)
+        w = O.dequant_blocks(blk[None, :], MXFP4)
+        np.testing.assert_array_equal(w, scale * np.array(E2M1_SPEC * 2))
+
+
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_levels_are_the_stated_grid(fmt):
     # every reachable weight is d*(q-c) for an integer code 0 <= q < 2^b
+    # (MXFP4: 2^(e-127) times an E2M1 value)
     rng = np.random.default_rng(fmt)
-    blocks = rng.integers(0, 256, size=(400, CODE_BYTES[fmt] + 2), dtype=np.uint8)
-    blocks[:, -2:] = np.frombuffer(np.float16(1.0).tobytes(), dtype=np.uint8)
+    blocks = rng.integers(0, 256, size=(400, CODE_BYTES[fmt] + SCALE_BYTES[fmt]), dtype=np.uint8)
+    if fmt == MXFP4:
+        blocks[:, -1] = 127
+    else:
+        blocks[:, -2:] = np.frombuffer(np.float16(1.0).tobytes(), dtype=np.uint8)
     w = O.dequant_blocks(blocks, fmt)
     levels = np.unique(w)
-    np.testing.assert_array_equal(levels, np.arange(1 << fmt) - OFFSETS[fmt])
+    want = np.unique(np.array(E2M1_SPEC)) if fmt == MXFP4 else np.arange(1 << fmt) - OFFSETS[fmt]
+    np.testing.assert_array_equal(levels, want)
 
 
 # ------------------------------------------------------------------ dense scalar reference
 def _scalar_matrix(blocks, fmt):
     """Scalar, per-weight expansion of a [rows][nblk][Bq] block array."""
-    cb = CODE_BYTES[fmt]
+    cb, bits = CODE_BYTES[fmt], BITS[fmt]
     rows, nblk, _ = blocks.shape
     out = np.zeros((rows, nblk * 32))
     for r in range(rows):
         for b in range(nblk):
             raw = bytes(blocks[r, b])
             bitval = int.from_bytes(raw[:cb], "little")
-            (d,) = struct.unpack("<e", raw[cb:cb + 2])
             for j in range(32):
-                q = (bitval >> (fmt * j)) & ((1 << fmt) - 1)
-                out[r, b * 32 + j] = d * (q - OFFSETS[fmt])
+                q = (bitval >> (bits * j)) & ((1 << bits) - 1)
+                if fmt == MXFP4:
+                    out[r, b * 32 + j] = 2.0 ** (raw[cb] - 127) * E2M1_SPEC[q]
+                else:
+                    (d,) = struct.unpack("<e", raw[cb:cb + 2])
+                    out[r, b * 32 + j] = d * (q - OFFSETS[fmt])
     return out
 
 
 def _dense_reference(x, wr, b, records, shared, H, I, k, fmt, residual):
     """Every expert on every token, then masked by the top-k set."""
     T, E = x.shape[0], wr.shape[0]
-    bq = CODE_BYTES[fmt] + 2
+    bq = CODE_BYTES[fmt] + SCALE_BYTES[fmt]
     n_gu = I * (H // 32) * bq
 
     def expand(rec):
@@ -117,7 +182,8 @@ def _dense_reference(x, wr, b, records, shared, H, I, k, fmt, residual):
 
 
 @pytest.mark.parametrize("fmt,biased,shared,residual", [
-    (2, False, False, False), (2, True, False, True), (3, True, False, False), (4, True, True, False)])
+    (2, False, False, False), (2, True, False, True), (3, True, False, False), (4, True, True, False),
+    (5, True, True, True)])
 def test_oracle_matches_scalar_dense_reference(fmt, biased, shared, residual):
     H, I, E, k, T = 64, 32, 5, 2, 3
     wr = G.router_weights(11, 0, H, E)
@@ -179,7 +245,7 @@ def _tiny_layer(fmt, E=6, H=64, I=32, T=4, seed=21):
     return wr, b, recs, x
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_k_equals_E_is_the_dense_softmax_mixture(fmt):
     H, I, E = 64, 32, 6
     wr, b, recs, x = _tiny_layer(fmt, E, H, I)
@@ -190,7 +256,7 @@ def test_k_equals_E_is_the_dense_softmax_mixture(fmt):
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_k1_is_the_argmax_expert_exactly(fmt):
     H, I, E = 64, 32, 6
     wr, b, recs, x = _tiny_layer(fmt, E, H, I)

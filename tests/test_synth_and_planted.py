@@ -35,6 +35,12 @@ def test_value_distributions():
     assert abs(rec[:, :8].mean() - 127.5) < 0.5
     x = G.bf16_bits_to_f32(G.token_candidates(0, 0, 0, 4096))
     assert abs(x.std() - 1) < 0.05
+    # MXFP4: 16 code bytes then one E8M0 byte 127 + floor(log2 |N(0, 0.02^2)|) - 2
+    mx = G.expert_canonical(0, 0, 0, 2560, 512, 5).reshape(-1, 17)
+    e = mx[:, 16].astype(np.int64)
+    assert e.min() >= 1 and e.max() <= 254
+    assert abs(np.median(e) - (127 + np.floor(np.log2(0.02 * 0.6745)) - 2)) <= 1
+    assert abs(mx[:, :16].mean() - 127.5) < 0.5
     # bf16 rounding is nearest-even: the rounded value is within half a bf16 ulp
     f = np.random.default_rng(0).standard_normal(1000).astype(np.float32)
     r = G.bf16_bits_to_f32(G.f32_to_bf16_bits(f))
@@ -108,4 +114,44 @@ def test_planted_mistake_is_caught(monkeypatch, mistake):
     elif mistake == "k_plus_one":
         real = OM.select_topk
         monkeypatch.setattr(OM, "select_topk", lambda l, k: real(l, k + 1))
+    assert not _agrees(*args)
+
+
+# ------------------------------------------------------------------ planted MXFP4 mistakes
+def _tiny_mx():
+    H, I, E, k, T, fmt = 64, 32, 5, 2, 3, 5
+    wr = G.router_weights(12, 0, H, E)
+    b = G.router_bias(12, 0, E)
+    recs = [G.expert_canonical(12, 0, e, H, I, fmt) for e in range(E)]
+    x = G.bf16_bits_to_f32(np.stack([G.token_candidates(12, 0, t, H) for t in range(T)])).astype(np.float64)
+    return H, I, E, k, T, fmt, wr, b, recs, x
+
+
+def test_unplanted_mxfp4_oracle_agrees():
+    assert _agrees(*_tiny_mx())
+
+
+@pytest.mark.parametrize("mistake", ["e2m1_bias", "e2m1_no_subnormal", "e8m0_bias", "sign_bit"])
+def test_planted_mxfp4_mistake_is_caught(monkeypatch, mistake):
+    args = _tiny_mx()
+    if mistake == "e2m1_bias":                  # exponent bias 0 instead of 1
+        def v(q):
+            q = np.asarray(q, dtype=np.int64)
+            ex, m = (q >> 1) & 3, (q & 1).astype(np.float64)
+            mag = np.where(ex == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(ex.astype(np.float64)))
+            return np.where(q & 8, -1.0, 1.0) * mag
+        monkeypatch.setattr(OM, "e2m1_value", v)
+    elif mistake == "e2m1_no_subnormal":        # exponent field 0 read as a normal number
+        def v(q):
+            q = np.asarray(q, dtype=np.int64)
+            ex, m = (q >> 1) & 3, (q & 1).astype(np.float64)
+            mag = (1.0 + 0.5 * m) * np.exp2(ex.astype(np.float64) - 1.0)
+            return np.where(q & 8, -1.0, 1.0) * mag
+        monkeypatch.setattr(OM, "e2m1_value", v)
+    elif mistake == "e8m0_bias":                # scale 2^(e - 128)
+        monkeypatch.setattr(OM, "e8m0_value", lambda e: np.exp2(np.asarray(e, dtype=np.float64) - 128.0))
+    elif mistake == "sign_bit":                 # sign taken from bit 0
+        real = OM.e2m1_value
+        monkeypatch.setattr(OM, "e2m1_value",
+                            lambda q: real(((np.asarray(q) & 1) << 3) | (np.asarray(q) & 6) | ((np.asarray(q) >> 3) & 1)))
     assert not _agrees(*args)
