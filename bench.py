@@ -297,7 +297,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens_per_step": T, "hidden": w.hidden,
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
-                   "shared": w.n_shared, "format": f"Q{w.fmt}", "layers_rotated": n_inst,
+                   "shared": w.n_shared, "format": ("MXFP4" if w.fmt == 5 else f"Q{w.fmt}"), "layers_rotated": n_inst,
                    "stack_layers": w.n_layers, "launch": "hip_graph" if use_graph else "eager",
                    "unique_experts_per_step": round(u_mean, 2)},
         "roofline": roofline,

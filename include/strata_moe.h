@@ -18,11 +18,16 @@
  * Expert weights are 32-weight blocks: b-bit codes q then an fp16 scale d,
  * w = d (q - c): Q2 (8 code bytes, c = 1.5), Q3 (12 bytes, c = 3.5),
  * Q4 (16 bytes, c = 8).  Code j of a block occupies bits [b*j, b*j+b) of
- * the code bytes read as one little-endian bit string.
+ * the code bytes read as one little-endian bit string.  MXFP4 (OCP
+ * Microscaling Formats v1.0, a format the pages name for their DeepSeek
+ * suites): 16 bytes of FP4 E2M1 codes in the same bit order, then one E8M0
+ * scale byte e, w = 2^(e - 127) E2M1(q); e = 0 (2^-127) is read as 0 and
+ * e = 255 (NaN) is not supported.
  *
  * Canonical expert record (the input of strata_moe_create): gate
  * [I rows][H/32 blocks], up [I][H/32], down [H rows][I/32 blocks], each
- * block = code bytes followed by the little-endian fp16 scale, no padding.
+ * block = code bytes followed by the little-endian fp16 scale (MXFP4: the
+ * scale byte), no padding.
  * Routed experts are stored back to back in expert-id order.
  *
  * Conventions
@@ -61,7 +66,8 @@ enum {
     STRATA_E_HIP = -3           /* a HIP runtime call or launch failed       */
 };
 
-enum { STRATA_Q2 = 2, STRATA_Q3 = 3, STRATA_Q4 = 4 };      /* expert block format */
+enum { STRATA_Q2 = 2, STRATA_Q3 = 3, STRATA_Q4 = 4,        /* expert block format */
+       STRATA_MXFP4 = 5 };
 enum { STRATA_BF16 = 0, STRATA_FP32 = 1 };                 /* activation dtype    */
 
 /* forward flags */
@@ -82,7 +88,7 @@ typedef struct {
     int32_t n_experts;   /* E: routed experts, 1..4096                        */
     int32_t top_k;       /* k: 1..min(E, 64)                                  */
     int32_t n_shared;    /* 0 or 1 always-on shared expert (weight 1)         */
-    int32_t qfmt;        /* STRATA_Q2 / STRATA_Q3 / STRATA_Q4                 */
+    int32_t qfmt;        /* STRATA_Q2 / STRATA_Q3 / STRATA_Q4 / STRATA_MXFP4  */
     int32_t max_tokens;  /* largest T any call on the handle will pass, >= 1; */
                          /* max_tokens * top_k <= 2^28 and                   */
                          /* max_tokens * hidden * 2 < 4 GiB (else            */
@@ -91,14 +97,15 @@ typedef struct {
 
 typedef struct strata_moe strata_moe;   /* opaque; one per MoE layer */
 
-/* Bytes of one canonical expert record, 3 * I * (H/32) * (code bytes + 2).
- * Returns 0 for an invalid config. */
+/* Bytes of one canonical expert record, 3 * I * (H/32) * (code bytes +
+ * scale bytes: 2, or 1 for MXFP4).  Returns 0 for an invalid config. */
 STRATA_API size_t strata_moe_expert_bytes(const strata_moe_config* cfg);
 
 /* Bytes of the device buffer `packed` that strata_moe_create fills: the
  * experts (routed, then shared) repacked into the kernels' layout (the same
- * byte count as the canonical records) plus a bf16 hi/lo split of the
- * router rows.  Returns 0 for an invalid config. */
+ * byte count as the canonical records; for MXFP4 one byte more per block,
+ * the scale taking a 16-bit slot) plus a bf16 hi/lo split of the router
+ * rows.  Returns 0 for an invalid config. */
 STRATA_API size_t strata_moe_packed_bytes(const strata_moe_config* cfg);
 
 /* Bytes of the device buffer `workspace` (router logits, top-k, counts,

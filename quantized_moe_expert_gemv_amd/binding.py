@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libstrata_moe.so")
 
 STRATA_OK, STRATA_E_INVALID, STRATA_E_UNSUPPORTED, STRATA_E_HIP = 0, -1, -2, -3
-STRATA_Q2, STRATA_Q3, STRATA_Q4 = 2, 3, 4
+STRATA_Q2, STRATA_Q3, STRATA_Q4, STRATA_MXFP4 = 2, 3, 4, 5
 STRATA_BF16, STRATA_FP32 = 0, 1
 STRATA_ACCUMULATE, STRATA_ADD_INPUT, STRATA_FORCE_DECODE, STRATA_FORCE_PREFILL = 1, 2, 4, 8
 STRATA_DECODE_MAX_T = 8

@@ -50,15 +50,32 @@ template <> struct Fmt<4> {
   static constexpr int bits = 4, code_bytes = 16, slab_codes = 2048;
   static constexpr float c = 8.0f;
 };
+// MXFP4 (OCP Microscaling Formats v1.0): 4-bit E2M1 elements, one E8M0 scale
+// per block, no offset
+constexpr int FMT_MXFP4 = 5;
+template <> struct Fmt<5> {
+  static constexpr int bits = 4, code_bytes = 16, slab_codes = 2048;
+  static constexpr float c = 0.0f;
+};
 
-__host__ __device__ inline int fmt_code_bytes(int fmt) { return fmt == 2 ? 8 : (fmt == 3 ? 12 : 16); }
-__host__ __device__ inline int slab_code_bytes(int fmt) { return 16 * 32 * fmt; }   // 16 rows x 256 codes
+__host__ __device__ inline int fmt_bits(int fmt) { return fmt == FMT_MXFP4 ? 4 : fmt; }
+__host__ __device__ inline int fmt_code_bytes(int fmt) { return 4 * fmt_bits(fmt); }
+// canonical block: codes, then the scale (fp16; one E8M0 byte for MXFP4)
+__host__ __device__ inline int canon_block_bytes(int fmt) { return fmt_code_bytes(fmt) + (fmt == FMT_MXFP4 ? 1 : 2); }
+__host__ __device__ inline int slab_code_bytes(int fmt) { return 16 * 32 * fmt_bits(fmt); }   // 16 rows x 256 codes
+// a slab's scales are 16-bit slots (fp16 d, or the E8M0 byte zero-extended)
 __host__ __device__ inline int slab_bytes(int fmt) { return slab_code_bytes(fmt) + 256; }
 __host__ __device__ inline size_t matrix_bytes(int fmt, int R, int K) {
   return (size_t)(R / GROUP_ROWS) * (K / SB_WEIGHTS) * slab_bytes(fmt);
 }
-__host__ __device__ inline size_t expert_bytes(int fmt, int H, int I) {
-  return (size_t)3 * I * (H / BLOCK_W) * (fmt_code_bytes(fmt) + 2);
+// bytes of one canonical expert record (gate, up, down blocks)
+__host__ __device__ inline size_t canon_expert_bytes(int fmt, int H, int I) {
+  return (size_t)3 * I * (H / BLOCK_W) * canon_block_bytes(fmt);
+}
+// bytes of one packed expert (the canonical count, but for MXFP4's 16-bit
+// scale slots: one byte more per block)
+__host__ __device__ inline size_t packed_expert_bytes(int fmt, int H, int I) {
+  return 2 * matrix_bytes(fmt, I, H) + matrix_bytes(fmt, H, I);
 }
 // byte offsets of the three matrices inside an expert
 __host__ __device__ inline size_t gate_off(int, int, int) { return 0; }

@@ -99,11 +99,12 @@ template <int FMT> struct Codes;
 template <> struct Codes<2> { uint4 lo; };
 template <> struct Codes<3> { uint4 lo; uint2 hi; };
 template <> struct Codes<4> { uint4 v0, v1; };
+template <> struct Codes<5> { uint4 v0, v1; };
 
 // Codes of one lane of the slab at byte soff of an expert record.
 template <int FMT>
 __device__ inline void bload_codes(rsrc_t r, uint32_t soff, int lane, Codes<FMT>& c) {
-  if constexpr (FMT == 4) {
+  if constexpr (FMT == 4 || FMT == FMT_MXFP4) {
     c.v0 = bload4(r, lane * 16, soff);
     c.v1 = bload4(r, 1024 + lane * 16, soff);
   } else {
@@ -151,11 +152,25 @@ __device__ inline f16x8 q4_operand(const Codes<4>& c) {
   return join(p[0], p[1], p[2], p[3]);
 }
 
-// scale of block BB of this lane's row; Q4 folds in the factor 16
+// MXFP4 codes of block BB as their E2M1 values (exact in fp16): byte j of
+// the block's word holds elements 2j (low nibble) and 2j + 1
+template <int BB>
+__device__ inline f16x8 mx_operand(const Codes<5>& c) {
+  const uint32_t W = comp((BB >> 2) ? c.v1 : c.v0, BB & 3);
+  return join(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, 0),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, 1),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, 2),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, 3));
+}
+
+// scale of block BB of this lane's row; Q4 folds in the factor 16; MXFP4's
+// 16-bit slot holds the E8M0 byte e: 2^(e - 127) (e = 0 reads as 0)
 template <int FMT, int BB>
 __device__ inline float block_scale(const uint4& sc) {
   const uint32_t w = comp(sc, BB >> 1);
-  const float d = half_bits_to_f32((uint16_t)((BB & 1) ? (w >> 16) : (w & 0xffffu)));
+  const uint32_t h = (BB & 1) ? (w >> 16) : (w & 0xffffu);
+  if constexpr (FMT == FMT_MXFP4) return __uint_as_float(h << 23);
+  const float d = half_bits_to_f32((uint16_t)h);
   return FMT == 4 ? 16.0f * d : d;
 }
 
@@ -164,6 +179,8 @@ template <int FMT, int BB>
 __device__ inline f32x4 block_product(const f16x8& a, const Codes<FMT>& c, const f32x4& doff) {
   if constexpr (FMT == 4) {
     return mfma(a, q4_operand<BB>(c), doff);
+  } else if constexpr (FMT == FMT_MXFP4) {
+    return mfma(a, mx_operand<BB>(c), doff);
   } else {
     f32x4 d = mfma(a, lo2_operand<BB>(c.lo), doff);
     if constexpr (FMT == 3) d = mfma(a, hi3_operand<BB>(c.hi), d);
@@ -175,7 +192,7 @@ __device__ inline f32x4 block_product(const f16x8& a, const Codes<FMT>& c, const
 template <int FMT>
 __device__ inline f32x4 block_offset(const f16x8& a) {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (FMT == 4) {
+  if constexpr (FMT == 4 || FMT == FMT_MXFP4) {   // no offset term (Q4 folds it into the operand)
     return z;
   } else {
     f16x8 cst;
@@ -1023,9 +1040,11 @@ hipError_t prepare_decode_kernels() {
   hipError_t e = raise_gateup_lds<2>();
   if (e == hipSuccess) e = raise_gateup_lds<3>();
   if (e == hipSuccess) e = raise_gateup_lds<4>();
+  if (e == hipSuccess) e = raise_gateup_lds<FMT_MXFP4>();
   if (e == hipSuccess) e = raise_down_lds_all<2>();
   if (e == hipSuccess) e = raise_down_lds_all<3>();
   if (e == hipSuccess) e = raise_down_lds_all<4>();
+  if (e == hipSuccess) e = raise_down_lds_all<FMT_MXFP4>();
   return e;
 }
 
@@ -1067,7 +1086,8 @@ hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, h
   switch (L.fmt) {
     case 2: return launch_experts_fmt<2>(L, W, c, s, tr);
     case 3: return launch_experts_fmt<3>(L, W, c, s, tr);
-    default: return launch_experts_fmt<4>(L, W, c, s, tr);
+    case 4: return launch_experts_fmt<4>(L, W, c, s, tr);
+    default: return launch_experts_fmt<FMT_MXFP4>(L, W, c, s, tr);
   }
 }
 

@@ -375,13 +375,14 @@ template <int FMT> struct PairCodes;
 template <> struct PairCodes<2> { uint2 w, sc; };
 template <> struct PairCodes<3> { uint2 w, sc; uint32_t h; };
 template <> struct PairCodes<4> { u32x4_t w; uint2 sc; };
+template <> struct PairCodes<5> { u32x4_t w; uint2 sc; };
 
 // blocks 4 hp .. 4 hp + 3 (half hp of the superblock) of a slab for this
 // lane: the slab at byte soff of the expert record r
 template <int FMT>
 __device__ inline void load_pair(rsrc_t r, uint32_t soff, int hp, int lane, PairCodes<FMT>& c) {
   c.sc = bload2(r, Fmt<FMT>::slab_codes + (lane & 15) * 16 + 8 * hp, soff);
-  if constexpr (FMT == 4) {
+  if constexpr (FMT == 4 || FMT == FMT_MXFP4) {
     const uint4 v = bload4(r, hp * 1024 + lane * 16, soff);
     c.w = u32x4_t{v.x, v.y, v.z, v.w};
   } else {
@@ -404,6 +405,18 @@ __device__ inline h2_t fp4x2_f16(uint32_t src, float scale) {
 template <int FMT, int B>
 __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
   const uint32_t sw = ((B >> 1) & 1) ? c.sc.y : c.sc.x;
+  if constexpr (FMT == FMT_MXFP4) {
+    // E2M1 codes times the block's power-of-two scale 2^(e - 127), one
+    // conversion per pair (the conversion's scale is exactly that power)
+    const uint32_t e = (B & 1) ? (sw >> 16) : (sw & 0xffffu);
+    const float s = __uint_as_float(e << 23);
+    const uint32_t W = c.w[B & 3];
+    const h2_t q0 = fp4x2_f16<0>(W, s), q1 = fp4x2_f16<1>(W, s), q2 = fp4x2_f16<2>(W, s), q3 = fp4x2_f16<3>(W, s);
+    f16x8 r;
+    r[0] = q0.x; r[1] = q0.y; r[2] = q1.x; r[3] = q1.y;
+    r[4] = q2.x; r[5] = q2.y; r[6] = q3.x; r[7] = q3.y;
+    return r;
+  }
   const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)((B & 1) ? (sw >> 16) : (sw & 0xffffu)));
   h2_t q[4];
   if constexpr (FMT == 4) {
@@ -1295,7 +1308,8 @@ hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, 
   switch (L.fmt) {
     case 2: err = launch_gemms_fmt<2>(L, W, c, s, tr); break;
     case 3: err = launch_gemms_fmt<3>(L, W, c, s, tr); break;
-    default: err = launch_gemms_fmt<4>(L, W, c, s, tr); break;
+    case 4: err = launch_gemms_fmt<4>(L, W, c, s, tr); break;
+    default: err = launch_gemms_fmt<FMT_MXFP4>(L, W, c, s, tr); break;
   }
   if (err != hipSuccess) return err;
   CombineArgs cb;

@@ -2,9 +2,9 @@
 // layout, and the bf16 hi/lo split of the router rows used by the prefill
 // router.
 //
-// The repack only moves bits: every code and every fp16 scale of the
-// canonical record lands in exactly one place, so an expert keeps its byte
-// count.  It follows the one-time re-layout of the expert set into a
+// The repack only moves bits: every code and every scale of the canonical
+// record lands in exactly one place, so an expert keeps its byte count (but
+// for MXFP4, whose one-byte scales take 16-bit slots).  It follows the one-time re-layout of the expert set into a
 // compute-friendly copy that the pages describe for the CPU path
 // (devotd.net "Strata memory tiers", section 小模型包不等于合适的模型: a
 // one-time ~40 GB copy written for AVX-512 Q2_0) and the contiguous
@@ -22,20 +22,20 @@ __constant__ int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};      // Q4 nibble of offset
 
 // code j (0..31) of a canonical block: bits [b*j, b*j + b) of the code bytes
 // read as one little-endian bit string
-__device__ inline uint32_t canon_code(const uint8_t* blk, int fmt, int j) {
-  const int p = fmt * j;
+__device__ inline uint32_t canon_code(const uint8_t* blk, int bits, int j) {
+  const int p = bits * j;
   uint32_t v = blk[p >> 3] >> (p & 7);
-  if ((p & 7) + fmt > 8) v |= (uint32_t)blk[(p >> 3) + 1] << (8 - (p & 7));
-  return v & ((1u << fmt) - 1u);
+  if ((p & 7) + bits > 8) v |= (uint32_t)blk[(p >> 3) + 1] << (8 - (p & 7));
+  return v & ((1u << bits) - 1u);
 }
 
 // One thread per (expert, matrix, row, superblock): 8 canonical blocks in,
 // the row's share of one slab out (4 lanes' code bits and one scale row).
 __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict__ packed, int fmt,
-                         int H, int I, size_t stride, long long n_items, int first_expert) {
+                         int H, int I, size_t canon_stride, size_t stride, long long n_items, int first_expert) {
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= n_items) return;
-  const int bq = fmt_code_bytes(fmt) + 2;
+  const int bq = canon_block_bytes(fmt);
   const long long gu_items = (long long)I * (H / SB_WEIGHTS);     // per gate or up matrix
   const long long dn_items = (long long)H * (I / SB_WEIGHTS);
   const long long per = 2 * gu_items + dn_items;
@@ -57,7 +57,7 @@ __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict_
   // canonical: gate blocks [I][H/32], up [I][H/32], down [H][I/32]
   const size_t mat_canon = (m == 0) ? 0 : (m == 1 ? (size_t)I * (H / BLOCK_W) * bq
                                                    : (size_t)2 * I * (H / BLOCK_W) * bq);
-  const uint8_t* src = canon + (size_t)x * stride + mat_canon + ((size_t)row * (K / BLOCK_W) + sb * 8) * bq;
+  const uint8_t* src = canon + (size_t)x * canon_stride + mat_canon + ((size_t)row * (K / BLOCK_W) + sb * 8) * bq;
   const size_t mat_packed = (m == 0) ? 0 : (m == 1 ? up_off(fmt, H, I) : down_off(fmt, H, I));
   uint8_t* slab = packed + (size_t)(first_expert + x) * stride + mat_packed +
                   slab_off(fmt, nsb, row / GROUP_ROWS, sb);
@@ -65,11 +65,15 @@ __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict_
 
   for (int q = 0; q < 4; ++q) {                 // K-slice -> lane q*16 + r
     const int lane = q * 16 + r;
-    if (fmt == 4) {
+    if (fmt == 4 || fmt == FMT_MXFP4) {
+      // Q4: nibbles in the order of its magic-number conversion; MXFP4: in K
+      // order (byte j = elements 2j, 2j + 1, low nibble first), the order of
+      // the FP4 -> fp16 conversion
       uint32_t w[8];
       for (int bb = 0; bb < 8; ++bb) {
         uint32_t d = 0;
-        for (int e = 0; e < 8; ++e) d |= canon_code(src + bb * bq, 4, 8 * q + e) << (4 * NIB4[e]);
+        for (int e = 0; e < 8; ++e)
+          d |= canon_code(src + bb * bq, 4, 8 * q + e) << (4 * (fmt == 4 ? NIB4[e] : e));
         w[bb] = d;
       }
       uint32_t* v0 = reinterpret_cast<uint32_t*>(slab + lane * 16);
@@ -95,8 +99,13 @@ __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict_
   }
   uint8_t* sc = slab + slab_code_bytes(fmt) + r * 16;
   for (int bb = 0; bb < 8; ++bb) {
-    sc[2 * bb] = src[bb * bq + bq - 2];
-    sc[2 * bb + 1] = src[bb * bq + bq - 1];
+    if (fmt == FMT_MXFP4) {                    // the E8M0 byte, zero-extended
+      sc[2 * bb] = src[bb * bq + bq - 1];
+      sc[2 * bb + 1] = 0;
+    } else {
+      sc[2 * bb] = src[bb * bq + bq - 2];
+      sc[2 * bb + 1] = src[bb * bq + bq - 1];
+    }
   }
 }
 
@@ -130,7 +139,8 @@ hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in,
   if (n == 0) return hipSuccess;
   const int bs = 256;
   hipLaunchKernelGGL(k_repack, dim3((unsigned)((n + bs - 1) / bs)), dim3(bs), 0, s, canon,
-                     const_cast<uint8_t*>(L.packed), L.fmt, L.H, L.I, L.expert_stride, n, first_expert);
+                     const_cast<uint8_t*>(L.packed), L.fmt, L.H, L.I, canon_expert_bytes(L.fmt, L.H, L.I),
+                     L.expert_stride, n, first_expert);
   return hipGetLastError();
 }
 

@@ -52,8 +52,8 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_config(const strata_moe_config* c) {
   if (!c) return fail(STRATA_E_INVALID, "config is NULL");
-  if (c->qfmt != STRATA_Q2 && c->qfmt != STRATA_Q3 && c->qfmt != STRATA_Q4)
-    return fail(STRATA_E_INVALID, "qfmt %d is not 2, 3 or 4", c->qfmt);
+  if (c->qfmt != STRATA_Q2 && c->qfmt != STRATA_Q3 && c->qfmt != STRATA_Q4 && c->qfmt != STRATA_MXFP4)
+    return fail(STRATA_E_INVALID, "qfmt %d is not 2, 3, 4 or 5 (MXFP4)", c->qfmt);
   if (c->hidden <= 0 || c->inter <= 0) return fail(STRATA_E_INVALID, "hidden and inter must be positive");
   if (c->hidden > 65536 || c->inter > 65536)
     return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be at most 65536", c->hidden,
@@ -126,7 +126,7 @@ size_t router_part_bytes(const strata_moe_config& c) {
 }
 
 size_t packed_experts_bytes(const strata_moe_config& c) {
-  return align256((size_t)(c.n_experts + c.n_shared) * expert_bytes(c.qfmt, c.hidden, c.inter));
+  return align256((size_t)(c.n_experts + c.n_shared) * packed_expert_bytes(c.qfmt, c.hidden, c.inter));
 }
 
 size_t packed_total(const strata_moe_config& c) {
@@ -220,7 +220,7 @@ extern "C" {
 
 size_t strata_moe_expert_bytes(const strata_moe_config* cfg) {
   if (check_config(cfg)) return 0;
-  return expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
+  return canon_expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
 }
 
 size_t strata_moe_packed_bytes(const strata_moe_config* cfg) {
@@ -261,7 +261,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   L.n_shared = cfg->n_shared; L.fmt = cfg->qfmt;
   L.router_w = router_w; L.router_b = router_bias;
   L.packed = static_cast<const uint8_t*>(packed);
-  L.expert_stride = expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
+  L.expert_stride = packed_expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
   const size_t rh = packed_experts_bytes(*cfg);
   L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
   L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + router_part_bytes(*cfg));

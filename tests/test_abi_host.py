@@ -52,6 +52,15 @@ def test_expert_bytes_match_the_block_format(B):
     assert B.strata_moe_expert_bytes(_cfg(B)) == 1228800
     assert B.strata_moe_expert_bytes(_cfg(B, qfmt=3)) == 1720320
     assert B.strata_moe_expert_bytes(_cfg(B, hidden=4096, inter=2048, n_experts=256, top_k=6, qfmt=4)) == 14155776
+    # MXFP4 (OCP MX v1.0): 16 bytes of E2M1 codes + one E8M0 scale byte per block
+    assert B.strata_moe_expert_bytes(_cfg(B, hidden=7168, inter=2048, n_experts=256, top_k=8, qfmt=5)) == \
+        3 * 2048 * (7168 // 32) * 17
+
+
+def test_mxfp4_packed_bytes_widen_the_scale_to_a_16_bit_slot(B):
+    c = _cfg(B, hidden=7168, inter=2048, n_experts=256, top_k=8, qfmt=5)
+    blocks = 3 * 2048 * (7168 // 32)
+    assert B.strata_moe_packed_bytes(c) >= 256 * blocks * 18 + 2 * 256 * 7168 * 2
 
 
 def test_packed_bytes_cover_experts_and_router_split(B):
@@ -67,7 +76,7 @@ def test_workspace_grows_with_max_tokens(B):
     assert small > 0 and big > 8192 * 10 * 2560 * 2 > small
 
 
-@pytest.mark.parametrize("bad", [dict(qfmt=5), dict(hidden=2500), dict(inter=100), dict(top_k=0),
+@pytest.mark.parametrize("bad", [dict(qfmt=6), dict(qfmt=1), dict(hidden=2500), dict(inter=100), dict(top_k=0),
                                  dict(top_k=513), dict(top_k=65, n_experts=100), dict(n_experts=0),
                                  dict(n_experts=5000), dict(n_shared=2), dict(max_tokens=0)])
 def test_invalid_configs_are_rejected(B, bad):

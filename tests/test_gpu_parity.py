@@ -38,7 +38,7 @@ def tiny(fmt, biased=True, n_shared=0, H=256, I=256, E=16, k=4, max_tokens=320, 
 
 
 # ------------------------------------------------------------------ small shapes, every format
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 @pytest.mark.parametrize("T", [1, 3, 8])
 def test_decode_route_and_forward_tiny(B, fmt, T):
     hl, layer = tiny(fmt)
@@ -50,7 +50,7 @@ def test_decode_route_and_forward_tiny(B, fmt, T):
     assert rel_l2(out, ref) <= DECODE_TOL, rel_l2(out, ref)
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_decode_shared_expert_tiny(B, fmt):
     hl, layer = tiny(fmt, n_shared=1)
     for T in (1, 4):
@@ -93,10 +93,10 @@ def test_decode_lds_limit_falls_back_to_prefill(B):
     assert rel_l2(out4, ref4) <= DECODE_TOL, rel_l2(out4, ref4)
 
 
-@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 @pytest.mark.parametrize("T", [1, 9, 130, 300])
 def test_prefill_route_and_forward_tiny(B, fmt, T):
-    hl, layer = tiny(fmt, n_shared=1 if fmt == 4 else 0)
+    hl, layer = tiny(fmt, n_shared=1 if fmt >= 4 else 0)
     bits, xf = tokens(hl, 50 + T, T)
     x = to_device_bf16(bits, DEV)
     check_route(layer, hl, x, xf, flags=B.STRATA_FORCE_PREFILL, w_atol=5e-5)
@@ -288,6 +288,26 @@ def test_workload_deepseek_q4(B):
     check_route(layer, hl, x, xf, w_atol=5e-5)
     out = layer.forward(x).cpu().numpy()
     sample = np.random.default_rng(1).choice(2048, 8, replace=False)
+    ref, _ = hl.oracle(xf[sample])
+    assert rel_l2(out[sample], ref) <= PREFILL_TOL
+
+
+@pytest.mark.timeout(900)
+def test_workload_deepseek_mxfp4(B):
+    """MXFP4 experts (E2M1 codes, one E8M0 scale per 32 weights) at the
+    DeepSeek-shaped layer with its shared expert: one decode token and a
+    2048-token prefill."""
+    hl, layer = full_layer("deepseek_mxfp4_t2048", 2048)
+    bits, xf = tokens(hl, 13, 2048)
+    for t in range(2):
+        x1 = to_device_bf16(bits[t:t + 1], DEV)
+        check_route(layer, hl, x1, xf[t:t + 1])
+        ref1, _ = hl.oracle(xf[t:t + 1])
+        assert rel_l2(layer.forward(x1).cpu().numpy(), ref1) <= DECODE_TOL
+    x = to_device_bf16(bits, DEV)
+    check_route(layer, hl, x, xf, w_atol=5e-5)
+    out = layer.forward(x).cpu().numpy()
+    sample = np.random.default_rng(2).choice(2048, 8, replace=False)
     ref, _ = hl.oracle(xf[sample])
     assert rel_l2(out[sample], ref) <= PREFILL_TOL
 
