@@ -75,6 +75,8 @@ WORKLOADS: Dict[str, Workload] = {
     "skinny_t64_q2": Workload("skinny_t64_q2", 2560, 512, 512, 10, 2, 64, True),
     # 8192-token prefill chunk through one Q2 layer, Zipf-skewed router
     "prefill_t8192_q2": Workload("prefill_t8192_q2", 2560, 512, 512, 10, 2, 8192, True),
+    # the opt-in 32768-token prefill chunk through the same layer
+    "prefill_t32768_q2": Workload("prefill_t32768_q2", 2560, 512, 512, 10, 2, 32768, True),
     # DeepSeek-V4-Flash-shaped layer, Q4, 256 routed + 1 shared, top-6
     "deepseek_q4_t1": Workload("deepseek_q4_t1", 4096, 2048, 256, 6, 4, 1, True, n_shared=1),
     "deepseek_q4_t2048": Workload("deepseek_q4_t2048", 4096, 2048, 256, 6, 4, 2048, True,

@@ -208,7 +208,7 @@ _full = {}
 
 def full_layer(name, max_tokens):
     w = WORKLOADS[name]
-    key = (w.hidden, w.inter, w.n_experts, w.top_k, w.fmt, w.biased, w.n_shared)
+    key = (w.hidden, w.inter, w.n_experts, w.top_k, w.fmt, w.biased, w.n_shared, max_tokens)
     if key not in _full:
         _full.clear()
         hl = HostLayer(2026, 0, w.hidden, w.inter, w.n_experts, w.top_k, w.fmt, w.biased, w.n_shared)
@@ -270,6 +270,23 @@ def test_workload_skinny_q2(B, name):
     check_route(layer, hl, x, xf, w_atol=5e-5)
     out = layer.forward(x).cpu().numpy()
     sample = np.random.default_rng(T).choice(T, 8, replace=False)
+    ref, _ = hl.oracle(xf[sample])
+    assert rel_l2(out[sample], ref) <= PREFILL_TOL
+
+
+@pytest.mark.timeout(900)
+def test_workload_prefill_t32768_q2(B):
+    """The 32768-token chunk: four times the rows per expert of the 8K chunk
+    (327,680 token-expert pairs); routing exact for every token, outputs
+    sampled across the whole chunk."""
+    hl, layer = full_layer("prefill_t32768_q2", 32768)
+    bits, xf = tokens(hl, 17, 32768)
+    x = to_device_bf16(bits, DEV)
+    oidx = check_route(layer, hl, x, xf, w_atol=5e-5)
+    counts = np.bincount(oidx.reshape(-1), minlength=hl.E)
+    assert counts.max() > 8 * 128                          # the hottest expert spans many row tiles
+    out = layer.forward(x).cpu().numpy()
+    sample = np.random.default_rng(5).choice(32768, 40, replace=False)
     ref, _ = hl.oracle(xf[sample])
     assert rel_l2(out[sample], ref) <= PREFILL_TOL
 
