@@ -98,13 +98,21 @@ __device__ inline void router_row(const TopkArgs& a, int t, float (&val)[MAXV]) 
   const float* p = a.part + (size_t)t * a.E;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) val[i] = p[eo[i]];
-  for (int z = 1; z < a.S; ++z) {
-    const float* pz = p + z * a.plane;
-    float v[MAXV];
+  // the other planes four at a time, every load of a group in flight
+  // together; a plane index past the last re-reads the last plane and is not
+  // added, so the sum runs over the planes in order
+  for (int z0 = 1; z0 < a.S; z0 += 4) {
+    float v[4][MAXV];
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) v[i] = pz[eo[i]];
+    for (int j = 0; j < 4; ++j) {
+      const float* pz = p + (size_t)min(z0 + j, a.S - 1) * a.plane;
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) val[i] += v[i];
+      for (int i = 0; i < MAXV; ++i) v[j][i] = pz[eo[i]];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i) val[i] = (z0 + j < a.S) ? val[i] + v[j][i] : val[i];
   }
   if (a.bias) {
     float b[MAXV];
@@ -1226,9 +1234,10 @@ struct RouterPlan {
 };
 
 RouterPlan router_plan(const Layer& L, const Work& W, int T) {
-  // split K until the grid has about one workgroup per CU (at most 8 splits:
-  // top-k reads every plane; one plane past 512 experts, where top-k re-reads
-  // its plane)
+  // split K until the grid has about one workgroup per CU (at most 8 splits,
+  // 32 for calls of up to 64 tokens, whose one or two expert tiles would
+  // otherwise stream the router through a handful of CUs: top-k reads every
+  // plane; one plane past 512 experts, where top-k re-reads its plane)
   RouterPlan r;
   const int slots = cu_count();
   const int tiles = ((L.E + RT_E - 1) / RT_E) * ((T + BM - 1) / BM);
@@ -1237,7 +1246,7 @@ RouterPlan router_plan(const Layer& L, const Work& W, int T) {
   r.plane = (size_t)T * L.E;
   int S = 1;
   if (L.E <= 512) {
-    S = std::min(std::min(8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
+    S = std::min(std::min(T <= 64 ? 32 : 8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
     while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
   }
   r.kper = ((ksteps + S - 1) / S) * XBK;
