@@ -60,6 +60,26 @@ def test_decode_shared_expert_tiny(B, fmt):
         assert rel_l2(out, ref) <= DECODE_TOL
 
 
+@pytest.mark.parametrize("T", [3, 130])
+def test_mxfp4_extreme_scales(B, T):
+    """MXFP4 blocks whose E8M0 scale byte is 0 (read as zero by the kernels,
+    2^-127 by the oracle: below every tolerance), 1 (2^-126, the smallest
+    normal float; zero once rounded to fp16 in the prefill operands) and 127
+    (scale 1: weights up to 6, ~300 times the drawn ones), each on about 5%
+    of the blocks, through both paths."""
+    hl = HostLayer(103, 5, 256, 256, 16, 4, 5, True, 1)
+    rng = np.random.default_rng(7)
+    for rec in (hl.canon.reshape(hl.E, -1, 17), hl.shared.reshape(1, -1, 17)):
+        u = rng.random(rec.shape[:2])
+        rec[..., 16] = np.where(u < 0.05, 0, np.where(u < 0.10, 1, np.where(u < 0.15, 127, rec[..., 16])))
+    layer = device_layer(hl, 320, DEV)
+    bits, xf = tokens(hl, 40 + T, T)
+    x = to_device_bf16(bits, DEV)
+    check_route(layer, hl, x, xf, w_atol=5e-5)
+    ref, _ = hl.oracle(xf)
+    assert rel_l2(layer.forward(x).cpu().numpy(), ref) <= (DECODE_TOL if T <= 8 else PREFILL_TOL)
+
+
 @pytest.mark.parametrize("E,k", [(64, 6), (300, 10), (512, 10), (1024, 8)])
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_decode_expert_counts(B, E, k, T):
