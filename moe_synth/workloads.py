@@ -62,6 +62,8 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_t1_q2": Workload("decode_t1_q2", 2560, 512, 512, 10, 2, 1, False),
     # same layer, 1+3-token MTP verify batch, Zipf-skewed router
     "mtp_verify_t4_q2": Workload("mtp_verify_t4_q2", 2560, 512, 512, 10, 2, 4, True),
+    # same layer, 6-token verify of a prompt-lookup draft (1 + 5 tokens)
+    "lookup_verify_t6_q2": Workload("lookup_verify_t6_q2", 2560, 512, 512, 10, 2, 6, True),
     # 48-layer Q3 stack, single-token decode stream of 256 steps
     # (scales a quarter of the single-layer ones: with d ~ |N(0, 0.02^2)| each
     # layer's output grows as the square of its input and the residual stream

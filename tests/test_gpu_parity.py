@@ -251,10 +251,14 @@ def test_workload_decode_t1_q2(B):
 
 
 @pytest.mark.timeout(600)
-def test_workload_mtp_verify_t4_q2(B):
-    hl, layer = full_layer("mtp_verify_t4_q2", 8192)
+@pytest.mark.parametrize("name", ["mtp_verify_t4_q2", "lookup_verify_t6_q2"])
+def test_workload_verify_q2(B, name):
+    """Verify windows through the decode path: 1 + 3 MTP drafts and 1 + 5
+    prompt-lookup drafts, four batches each."""
+    T = WORKLOADS[name].tokens
+    hl, layer = full_layer(name, 8192)
     for s in range(4):
-        bits, xf = tokens(hl, 100 + s, 4)
+        bits, xf = tokens(hl, 100 + s, T)
         x = to_device_bf16(bits, DEV)
         oidx = check_route(layer, hl, x, xf)
         assert np.unique(oidx).size < 40                  # the Zipf bias shares experts
