@@ -168,7 +168,16 @@ __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs 
   __syncthreads();
   for (int i = threadIdx.x; i < nt * k; i += blockDim.x)
     a.w.pair_rank[(size_t)tb * k + i] = __popc(tmask[sel[i]] & ((1u << (i / k)) - 1u));
-  for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = __popc(tmask[e]);
+  if (a.nchunks == 1) {
+    // a single chunk (T <= CT) is its own column scan: every base is 0 and
+    // the chunk's histogram is the expert counts
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      a.w.chunk_base[e] = 0;
+      a.w.counts[e] = __popc(tmask[e]);
+    }
+  } else {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = __popc(tmask[e]);
+  }
 }
 
 struct ScanArgs {
@@ -1305,7 +1314,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(64 * TOPK_CHUNK_WAVES), lds, s, t);
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
-  launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);
+  if (t.nchunks > 1) launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);
   launch(tr, k_scan, dim3(1), dim3(1024), 0, s, sa);
   const int P = c.T * L.k;
   launch(tr, k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
