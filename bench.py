@@ -193,8 +193,8 @@ def main():
         names = ["route_gemv", "topk", "gateup", "down_combine"]
     else:
         names = ["router_gemm", "topk", "colscan", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
-        if T <= 32:
-            names.remove("colscan")        # one top-k chunk is its own column scan
+        if T <= 32:                        # one top-k chunk also scans and scatters
+            names = ["router_gemm", "topk_scan_scatter", "gateup_gemm", "down_gemm", "combine"]
     # each kernel's own dispatch start/end, bound to a pair of events on the
     # launch stream (eager launches of the same steps, after the timed replay)
     n_trace = min(steps, 256)

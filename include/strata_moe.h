@@ -183,9 +183,10 @@ STRATA_API int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_lay
  * the pair is that kernel's execution, without launch gaps.  Kernels beyond
  * n_events / 2 are not traced.  Kernel order: decode forward = router GEMV,
  * top-k + permutation, gate/up + SwiGLU, down + weighted combine; prefill
- * forward = router GEMM, top-k, column scan (only for T > 32), scan, scatter,
- * gate/up GEMM, down GEMM, combine (route-only calls stop after the routing
- * kernels).  A stack call
+ * forward = router GEMM, top-k, column scan, scan, scatter, gate/up GEMM,
+ * down GEMM, combine, where for T <= 32 the top-k kernel also does the
+ * column scan, the scan and the scatter (5 kernels); route-only calls stop
+ * after the routing kernels.  A stack call
  * traces the handle's layer only.  n_events even, in
  * [0, STRATA_MAX_TRACE_EVENTS]; 0 disarms.  The events must outlive the
  * call's completion on its stream.

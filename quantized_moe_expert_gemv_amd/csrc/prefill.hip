@@ -12,7 +12,9 @@
 //   k_topk_chunks    logits = sum of the planes + b; top-k + renormalised
 //                    softmax per token (one wave per token) and, per chunk of
 //                    32 tokens, the expert histogram and every pair's rank
-//                    inside the chunk
+//                    inside the chunk; a call of at most 32 tokens (one
+//                    chunk) also does the three steps below in the same
+//                    workgroup
 //   k_colscan        per-expert bases of the chunks (column scan)
 //   k_scan           expert counts -> offsets and the flat list of
 //                    (expert, 128-row tile) GEMM work items
@@ -79,7 +81,7 @@ __device__ inline u32x4_t f32x8_to_f16(f32x4_t lo, f32x4_t hi) {
 
 // ------------------------------------------------------------------ routing
 struct TopkArgs {
-  int T, E, k, nchunks;
+  int T, E, k, nchunks, n_shared;
   int S;                  // router partial planes
   size_t plane;           // elements between planes
   const float* part;      // [S][T][E] partial logits
@@ -144,6 +146,13 @@ __device__ inline void token_topk(const TopkArgs& a, int t, int* sel, float* w, 
 // each pair's rank among the chunk's earlier tokens with the same expert.
 constexpr int TOPK_CHUNK_WAVES = 16;
 
+struct ScanArgs {
+  int T, E, k, n_shared, nchunks;
+  Work w;
+};
+__device__ inline void scan_tiles(const ScanArgs& a);
+__device__ inline void scatter_pair(const TopkArgs& a, int p);
+
 __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs a) {
   extern __shared__ int lds_i[];
   int* sel = lds_i;                                            // [CT][k]
@@ -170,20 +179,24 @@ __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs 
     a.w.pair_rank[(size_t)tb * k + i] = __popc(tmask[sel[i]] & ((1u << (i / k)) - 1u));
   if (a.nchunks == 1) {
     // a single chunk (T <= CT) is its own column scan: every base is 0 and
-    // the chunk's histogram is the expert counts
+    // the chunk's histogram is the expert counts.  This workgroup then holds
+    // every pair of the call, so it also takes the scan (offsets, tile list)
+    // and the scatter, which would otherwise be two more launches; the
+    // barriers order its own global writes for its own reads.
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       a.w.chunk_base[e] = 0;
       a.w.counts[e] = __popc(tmask[e]);
     }
+    __syncthreads();
+    ScanArgs sa;
+    sa.T = a.T; sa.E = E; sa.k = k; sa.n_shared = a.n_shared; sa.nchunks = 1; sa.w = a.w;
+    scan_tiles(sa);
+    __syncthreads();
+    for (int p = threadIdx.x; p < a.T * k; p += blockDim.x) scatter_pair(a, p);
   } else {
     for (int e = threadIdx.x; e < E; e += blockDim.x) a.w.chunk_base[(size_t)chunk * E + e] = __popc(tmask[e]);
   }
 }
-
-struct ScanArgs {
-  int T, E, k, n_shared, nchunks;
-  Work w;
-};
 
 // Column scan of the per-chunk expert histograms (chunk-major [nch][E]): each
 // count becomes the number of that expert's pairs in earlier chunks, and
@@ -266,7 +279,7 @@ __device__ inline int class_of(const int4& v, int c) { return c == 0 ? v.x : c =
 // the classes in turn.  Each thread places the tiles of its own entries:
 // tile j (expert order) of class c in segment x goes to
 //   x tp + (segment x's tiles of classes below c) + (class-c tiles in [x tp, j)).
-__global__ __launch_bounds__(1024) void k_scan(ScanArgs a) {
+__device__ inline void scan_tiles(const ScanArgs& a) {
   __shared__ int2 tmp[16];
   __shared__ int4 tmp4[16];
   __shared__ int4 bnd[9];          // class counts of the expert-order tiles before each segment start
@@ -348,16 +361,22 @@ __global__ __launch_bounds__(1024) void k_scan(ScanArgs a) {
   }
 }
 
-__global__ void k_scatter(TopkArgs a) {
-  const int p = blockIdx.x * blockDim.x + threadIdx.x;
-  const int P = a.T * a.k;
-  if (p >= P) return;
+__global__ __launch_bounds__(1024) void k_scan(ScanArgs a) { scan_tiles(a); }
+
+// slot of pair p: its expert's offset + the pairs of that expert in earlier
+// chunks + its rank in its own chunk
+__device__ inline void scatter_pair(const TopkArgs& a, int p) {
   const int e = a.w.topk_idx[p];
   const int chunk = (p / a.k) / CT;
   const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)chunk * a.E + e] + a.w.pair_rank[p];
   a.w.perm[slot] = p;
   a.w.inv[p] = slot;
   a.w.slot_tok[slot] = p / a.k;
+}
+
+__global__ void k_scatter(TopkArgs a) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < a.T * a.k) scatter_pair(a, p);
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
@@ -1309,12 +1328,13 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   else launch(tr, k_router<false>, grid, block, 0, s, r);
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
-  t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b;
+  t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b; t.n_shared = L.n_shared;
   const size_t lds = ((size_t)CT * L.k + L.E) * 4;
   launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(64 * TOPK_CHUNK_WAVES), lds, s, t);
+  if (t.nchunks == 1) return hipGetLastError();   // the one chunk did the scan and the scatter
   ScanArgs sa;
   sa.T = c.T; sa.E = L.E; sa.k = L.k; sa.n_shared = L.n_shared; sa.nchunks = t.nchunks; sa.w = W;
-  if (t.nchunks > 1) launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);
+  launch(tr, k_colscan, dim3((L.E + 63) / 64), dim3(64 * COLSCAN_GROUPS), 0, s, sa);
   launch(tr, k_scan, dim3(1), dim3(1024), 0, s, sa);
   const int P = c.T * L.k;
   launch(tr, k_scatter, dim3((P + 255) / 256), dim3(256), 0, s, t);
