@@ -173,14 +173,17 @@ __device__ inline void wave_argmax(float& v, int& i) {
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------ top-k
-// Selection order: value descending, then expert id ascending; NaN ranks as
-// -inf.  Each entry becomes one 64-bit key (order-preserving integer image of
-// the float, then the complemented id), so "better" is plain unsigned ">"
-// and every comparison below is branch-free.
+// Selection order: value descending, then expert id ascending; NaN ranks
+// below every number (-inf included).  Each entry becomes one 64-bit key
+// (order-preserving integer image of the float, then the complemented id),
+// so "better" is plain unsigned ">" and every comparison below is
+// branch-free.  A NaN's image is 0, the image of padding entries (ids past
+// E), below -inf's 0x007FFFFF; ties at 0 go to the lower id, so a real
+// expert always wins over padding.
 __device__ inline uint32_t sortable_bits(float v) {
-  if (v != v) v = -INFINITY;
   const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t s = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (v != v) ? 0u : s;
 }
 __device__ inline float unsortable_bits(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);

@@ -75,6 +75,55 @@ def rel_l2(got, ref):
     return float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
 
 
+def row_rel_l2(got, ref):
+    """Relative L2 error of every token row: ||got_t - ref_t|| / ||ref_t||."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+
+
+def check_rows(got, ref, tol, what=""):
+    """The call's rel-L2 over all compared rows and the worst single row, both
+    within tol (a token with a wrong row cannot hide in the pooled norm).
+    Returns (pooled, worst row)."""
+    pooled = rel_l2(got, ref)
+    rows = row_rel_l2(got, ref)
+    worst = float(rows.max())
+    print(f"{what} rows {rows.size}: rel-L2 {pooled:.3e}, worst row {worst:.3e} "
+          f"(token {int(rows.argmax())}), bound {tol:g}", flush=True)
+    assert np.isfinite(pooled) and pooled <= tol, (what, pooled)
+    assert np.isfinite(worst) and worst <= tol, (what, worst, int(rows.argmax()))
+    return pooled, worst
+
+
+def tile_tokens(idx, n_experts, n_shared=0, rows=128, seed=0):
+    """Tokens that put at least one row into every 128-slot GEMM tile.
+
+    The expert GEMMs of the grouped path work on tiles of `rows` consecutive
+    slots of one expert in the stable (expert, pair) order (the permutation
+    of the routing), full tiles first and then the expert's remainder; the
+    shared expert's slots follow, one per token.  For every such tile this
+    picks a random slot and the last slot, and returns the sorted tokens that
+    own them."""
+    rng = np.random.default_rng(seed)
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    counts, offsets, perm, _ = O.permute(idx, n_experts)
+    toks = set()
+    for e in range(n_experts):
+        c = int(counts[e])
+        for j0 in range(0, c, rows):
+            n = min(rows, c - j0)
+            for slot in (offsets[e] + j0 + int(rng.integers(n)), offsets[e] + j0 + n - 1):
+                toks.add(int(perm[slot]) // k)
+    if n_shared:
+        for j0 in range(0, T, rows):
+            n = min(rows, T - j0)
+            toks.add(j0 + int(rng.integers(n)))
+            toks.add(j0 + n - 1)
+    return np.array(sorted(toks), dtype=np.int64)
+
+
 def check_route(layer, hl, x_dev, x_f64, flags=0, w_atol=2e-6):
     """Route outputs vs the oracle: ids, permutation and offsets bit-exact."""
     idx, w, perm, offs = layer.route(x_dev, flags=flags)
