@@ -909,7 +909,12 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
         const ALane al{base + 16 * ks + 128 * hh, base + 16 * ks - 128 * hh};
         down_compute<FMT>(b[q], al, lwt + uu * WTAB + wt_off, out);
       }
-      asm volatile("" ::: "memory");                // the slot is refilled after its reads
+      // the slot is refilled only once its operand reads have completed: a
+      // buffer->LDS load issued while a read of the same bytes is still
+      // queued can land first (L2-resident rows return quickly), and the
+      // compiler moves the refill up among this unit's MFMAs, so the wait
+      // must be a hardware one, not only a compiler barrier
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       down_load<FMT, TT>(a, ldesc, min(cu + DEPTH * nw, units - 1), nsb, g, stage + q * TT * GU_SLOT, b[q]);
     }
   }

@@ -340,11 +340,15 @@ def against_decode(layer, x, out, tol=PREFILL_TOL, what=""):
     tests above and on the sampled rows of each caller)."""
     from quantized_moe_expert_gemv_amd import binding as Bn
     T = x.shape[0]
-    dec = torch.empty((T, out.shape[1]), dtype=torch.float32, device=DEV)
-    for t0 in range(0, T, 8):
-        n = min(8, T - t0)
-        Bn.strata_moe_forward(layer.handle, x[t0:t0 + n], n, dec[t0:t0 + n], Bn.STRATA_FORCE_DECODE)
-    dec = dec.cpu().numpy()
+    runs = []
+    for _ in range(2):                  # twice: the decode path must be bit-identical run to run
+        dec = torch.empty((T, out.shape[1]), dtype=torch.float32, device=DEV)
+        for t0 in range(0, T, 8):
+            n = min(8, T - t0)
+            Bn.strata_moe_forward(layer.handle, x[t0:t0 + n], n, dec[t0:t0 + n], Bn.STRATA_FORCE_DECODE)
+        runs.append(dec.cpu().numpy())
+    dec = runs[0]
+    assert np.array_equal(runs[0], runs[1]), f"{what}: decode path differs between two runs"
     check_rows(out, dec, tol, f"{what} vs decode path")
     return dec
 
