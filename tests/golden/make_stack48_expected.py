@@ -26,7 +26,7 @@ from moe_synth import WORKLOADS, generate as G       # noqa: E402
 
 SEED = 2026
 STREAM = 48
-STEPS = 2
+STEPS = 8
 MIN_GAP = 1e-3
 OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "stack48_q3_expected.npz")
 
