@@ -164,6 +164,26 @@ STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype,
                        float* out, uint32_t flags, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as strata_moe_forward, same arguments, kernels and results, but the
+ * per-call regions (logits, top-k, permutation, activation and per-pair rows)
+ * live in a fixed array inside the library, STRATA_STATIC_SCRATCH_BYTES per
+ * device, instead of the handle's workspace.  It allocates nothing (no
+ * hipMalloc/hipFree, no allocating library call).  The array is resolved for
+ * the device current at strata_moe_create and kept until the process ends.
+ * Calls whose regions exceed the array (more tokens than fit; a 2560-wide,
+ * 512-expert, top-10 layer fits up to about 256 tokens, every decode call of
+ * 8 tokens or fewer fits) return STRATA_E_UNSUPPORTED before anything is
+ * enqueued.  Every handle on a device shares that device's one array:
+ * static calls that overlap in time on one device (different streams, or
+ * different threads) race and give wrong results; order them on one stream.
+ */
+#define STRATA_STATIC_SCRATCH_BYTES (16u << 20)
+STRATA_API int strata_moe_forward_static(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
+                              float* out, uint32_t flags, void* stream);
+
+/*
  * A stack of MoE layers with residual adds (48 layers x 512 experts is the
  * Qwen3.8-Flash-Next expert set of the pages: ai-coding.wiselychen.com
  * "Strata two weeks", Table 1):  h_0 = x,  h_{l+1} = h_l + moe_l(h_l),

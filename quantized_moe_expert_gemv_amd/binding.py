@@ -22,9 +22,10 @@ STRATA_DECODE_MAX_T = 8
 
 EXPORTS = ("strata_moe_expert_bytes", "strata_moe_packed_bytes", "strata_moe_workspace_bytes",
            "strata_moe_create", "strata_moe_route", "strata_moe_forward",
-           "strata_moe_stack_forward", "strata_moe_trace_next_call", "strata_moe_destroy",
+           "strata_moe_forward_static", "strata_moe_stack_forward", "strata_moe_trace_next_call", "strata_moe_destroy",
            "strata_moe_last_error")
 STRATA_MAX_TRACE_EVENTS = 16
+STRATA_STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class strata_moe_config(ctypes.Structure):
@@ -53,6 +54,7 @@ def _load():
         "strata_moe_create": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, ctypes.POINTER(P)]),
         "strata_moe_route": (ctypes.c_int, [P, P, I32, I32, P, P, P, P, U32, P]),
         "strata_moe_forward": (ctypes.c_int, [P, P, I32, I32, P, U32, P]),
+        "strata_moe_forward_static": (ctypes.c_int, [P, P, I32, I32, P, U32, P]),
         "strata_moe_stack_forward": (ctypes.c_int, [ctypes.POINTER(P), I32, P, I32, I32, P, P, P]),
         "strata_moe_trace_next_call": (ctypes.c_int, [P, ctypes.POINTER(P), I32]),
         "strata_moe_destroy": (None, [P]),
@@ -122,6 +124,10 @@ def strata_moe_route(h, x, T, topk_idx, topk_w, perm, offsets, flags=0, stream=N
 
 def strata_moe_forward(h, x, T, out, flags=0, stream=None):
     _check(_lib.strata_moe_forward(h, _ptr(x), _dtype_code(x), T, _ptr(out), flags, _stream(stream)))
+
+
+def strata_moe_forward_static(h, x, T, out, flags=0, stream=None):
+    _check(_lib.strata_moe_forward_static(h, _ptr(x), _dtype_code(x), T, _ptr(out), flags, _stream(stream)))
 
 
 def strata_moe_stack_forward(handles, x, T, out, tmp, stream=None):

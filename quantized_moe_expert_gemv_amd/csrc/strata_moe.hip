@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 #include <string>
+#include <mutex>
 #include <new>
 
 #include "strata_moe.h"
@@ -23,6 +24,8 @@ struct strata_moe {
   Work W;          // regions sized for cfg.max_tokens (max_tiles set per call)
   uint8_t* ws;
   size_t ws_bytes;
+  int device;                // the device current at create
+  uint8_t* scratch;          // device address of that device's static scratch array
   hipEvent_t trace[STRATA_MAX_TRACE_EVENTS];   // armed by strata_moe_trace_next_call
   int n_trace;
 };
@@ -120,6 +123,62 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   return p;
 }
 
+// The workspace regions of a plan at base ws.
+Work layout_work(uint8_t* ws, const WsPlan& p) {
+  Work W;
+  W.logits = reinterpret_cast<float*>(ws + p.logits);
+  W.topk_idx = reinterpret_cast<int*>(ws + p.topk_idx);
+  W.topk_w = reinterpret_cast<float*>(ws + p.topk_w);
+  W.counts = reinterpret_cast<int*>(ws + p.counts);
+  W.offsets = reinterpret_cast<int*>(ws + p.offsets);
+  W.perm = reinterpret_cast<int*>(ws + p.perm);
+  W.inv = reinterpret_cast<int*>(ws + p.inv);
+  W.slot_tok = reinterpret_cast<int*>(ws + p.slot_tok);
+  W.udesc = reinterpret_cast<int*>(ws + p.udesc);
+  W.meta = reinterpret_cast<int*>(ws + p.meta);
+  W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
+  W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
+  W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
+  W.act = reinterpret_cast<float*>(ws + p.act);
+  W.actp = reinterpret_cast<_Float16*>(ws + p.act);
+  W.xparts = reinterpret_cast<_Float16*>(ws + p.xparts);
+  W.wtab = reinterpret_cast<float*>(ws + p.wtab);
+  W.ybf = reinterpret_cast<uint16_t*>(ws + p.y);
+  W.ybf_bytes = p.total - p.y;                 // the last region
+  W.nchunks = p.nchunks;
+  W.max_tiles = p.max_tiles;
+  return W;
+}
+
+// ------------------------------------------------------------------ static scratch
+// The allocation-free entry point keeps its per-call regions in this array
+// instead of a caller's workspace.  Each device holds its own copy (at its
+// own address) from the first use until the process ends.  In host code the
+// array's name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current (at
+// the first create on the device) and kept in g_scratch.  Nothing in it
+// needs to start at zero: every region a call reads is written earlier in
+// the same call.
+static __device__ __align__(256) uint8_t scratch[STRATA_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[MAX_DEVICES] = {};
+
+// the current device's scratch address (looked up on the first call per device)
+hipError_t scratch_address(int dev, uint8_t** out) {
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 // one part (high or low) of the router split: experts padded to groups of 16
 size_t router_part_bytes(const strata_moe_config& c) {
   return align256((size_t)((c.n_experts + 15) / 16) * 16 * c.hidden * 2);
@@ -169,6 +228,19 @@ int check_flags(const strata_moe_config& c, int T, uint32_t flags) {
   return STRATA_OK;
 }
 
+int check_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, const float* out, uint32_t flags) {
+  int rc = check_call(h, x, x_dtype, T);
+  if (rc) return rc;
+  if ((rc = check_flags(h->cfg, T, flags))) return rc;
+  if (!out) return fail(STRATA_E_INVALID, "out is NULL");
+  if (!aligned(out, 16)) return fail(STRATA_E_INVALID, "out must be 16-byte aligned");
+  const size_t xb = (size_t)T * h->cfg.hidden * (x_dtype == STRATA_FP32 ? 4 : 2);
+  const size_t ob = (size_t)T * h->cfg.hidden * 4;
+  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
+  if (xa < oa + ob && oa < xa + xb) return fail(STRATA_E_INVALID, "x and out overlap");
+  return STRATA_OK;
+}
+
 Call make_call(const void* x, int32_t x_dtype, int32_t T, float* out, uint32_t flags) {
   Call c;
   c.x = x;
@@ -195,8 +267,9 @@ struct TraceScope {
 
 // permutation: the decode path computes the token->expert permutation only
 // when the caller asks for it (route()); its expert kernels do without.
-int run_route(strata_moe* h, const Call& c, bool decode, bool permutation, hipStream_t s, Tracer* tr) {
-  Work W = h->W;
+int run_route(strata_moe* h, const Work& W0, const Call& c, bool decode, bool permutation, hipStream_t s,
+              Tracer* tr) {
+  Work W = W0;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
   hipError_t e = decode ? launch_decode_route(h->L, W, c, s, tr, permutation)
                         : launch_prefill_route(h->L, W, c, s, tr);
@@ -204,10 +277,10 @@ int run_route(strata_moe* h, const Call& c, bool decode, bool permutation, hipSt
   return STRATA_OK;
 }
 
-int run_forward(strata_moe* h, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
-  int rc = run_route(h, c, decode, false, s, tr);
+int run_forward(strata_moe* h, const Work& W0, const Call& c, bool decode, hipStream_t s, Tracer* tr) {
+  int rc = run_route(h, W0, c, decode, false, s, tr);
   if (rc) return rc;
-  Work W = h->W;
+  Work W = W0;
   W.max_tiles = max_tiles_for(h->cfg, c.T);
   hipError_t e = decode ? launch_decode_experts(h->L, W, c, s, tr) : launch_prefill_experts(h->L, W, c, s, tr);
   if (e != hipSuccess) return hip_fail(e, "expert launch");
@@ -265,28 +338,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   const size_t rh = packed_experts_bytes(*cfg);
   L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
   L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + router_part_bytes(*cfg));
-  Work& W = h->W;
-  W.logits = reinterpret_cast<float*>(ws + p.logits);
-  W.topk_idx = reinterpret_cast<int*>(ws + p.topk_idx);
-  W.topk_w = reinterpret_cast<float*>(ws + p.topk_w);
-  W.counts = reinterpret_cast<int*>(ws + p.counts);
-  W.offsets = reinterpret_cast<int*>(ws + p.offsets);
-  W.perm = reinterpret_cast<int*>(ws + p.perm);
-  W.inv = reinterpret_cast<int*>(ws + p.inv);
-  W.slot_tok = reinterpret_cast<int*>(ws + p.slot_tok);
-  W.udesc = reinterpret_cast<int*>(ws + p.udesc);
-  W.meta = reinterpret_cast<int*>(ws + p.meta);
-  W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
-  W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
-  W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
-  W.act = reinterpret_cast<float*>(ws + p.act);
-  W.actp = reinterpret_cast<_Float16*>(ws + p.act);
-  W.xparts = reinterpret_cast<_Float16*>(ws + p.xparts);
-  W.wtab = reinterpret_cast<float*>(ws + p.wtab);
-  W.ybf = reinterpret_cast<uint16_t*>(ws + p.y);
-  W.ybf_bytes = p.total - p.y;                 // the last region
-  W.nchunks = p.nchunks;
-  W.max_tiles = p.max_tiles;
+  h->W = layout_work(ws, p);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* step = "zeroing counters";
@@ -306,6 +358,14 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   if (e == hipSuccess) {
     step = "kernel attributes";
     e = prepare_decode_kernels();
+  }
+  if (e == hipSuccess) {
+    step = "current device";
+    e = hipGetDevice(&h->device);
+  }
+  if (e == hipSuccess) {
+    step = "static scratch address";
+    e = scratch_address(h->device, &h->scratch);
   }
   if (e == hipSuccess) {
     step = "stream synchronize";
@@ -332,7 +392,7 @@ int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, i
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Call c = make_call(x, x_dtype, T, nullptr, flags);
   TraceScope ts(h);
-  if ((rc = run_route(h, c, use_decode(h->cfg, T, flags), true, s, ts.ptr))) return rc;
+  if ((rc = run_route(h, h->W, c, use_decode(h->cfg, T, flags), true, s, ts.ptr))) return rc;
   const size_t P = (size_t)T * h->cfg.top_k;
   hipError_t e = hipMemcpyAsync(topk_idx, h->W.topk_idx, P * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = hipMemcpyAsync(topk_w, h->W.topk_w, P * 4, hipMemcpyDeviceToDevice, s);
@@ -345,18 +405,32 @@ int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, i
 
 int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, float* out,
                        uint32_t flags, void* stream) {
-  int rc = check_call(h, x, x_dtype, T);
+  int rc = check_forward(h, x, x_dtype, T, out, flags);
   if (rc) return rc;
-  if ((rc = check_flags(h->cfg, T, flags))) return rc;
-  if (!out) return fail(STRATA_E_INVALID, "out is NULL");
-  if (!aligned(out, 16)) return fail(STRATA_E_INVALID, "out must be 16-byte aligned");
-  const size_t xb = (size_t)T * h->cfg.hidden * (x_dtype == STRATA_FP32 ? 4 : 2);
-  const size_t ob = (size_t)T * h->cfg.hidden * 4;
-  const uintptr_t xa = (uintptr_t)x, oa = (uintptr_t)out;
-  if (xa < oa + ob && oa < xa + xb) return fail(STRATA_E_INVALID, "x and out overlap");
   hipStream_t s = static_cast<hipStream_t>(stream);
   TraceScope ts(h);
-  if ((rc = run_forward(h, make_call(x, x_dtype, T, out, flags), use_decode(h->cfg, T, flags), s, ts.ptr))) return rc;
+  if ((rc = run_forward(h, h->W, make_call(x, x_dtype, T, out, flags), use_decode(h->cfg, T, flags), s, ts.ptr)))
+    return rc;
+  return ok();
+}
+
+int strata_moe_forward_static(strata_moe* h, const void* x, int32_t x_dtype, int32_t T, float* out,
+                              uint32_t flags, void* stream) {
+  int rc = check_forward(h, x, x_dtype, T, out, flags);
+  if (rc) return rc;
+  strata_moe_config c = h->cfg;
+  c.max_tokens = T;
+  const WsPlan p = plan_workspace(c);
+  if (p.total > STRATA_STATIC_SCRATCH_BYTES)
+    return fail(STRATA_E_UNSUPPORTED,
+                "a call of %d tokens needs %zu bytes of scratch, more than the static array's %zu", T, p.total,
+                (size_t)STRATA_STATIC_SCRATCH_BYTES);
+  if (!h->scratch) return fail(STRATA_E_HIP, "the static scratch of device %d was not resolved", h->device);
+  const Work W = layout_work(h->scratch, p);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TraceScope ts(h);
+  if ((rc = run_forward(h, W, make_call(x, x_dtype, T, out, flags), use_decode(h->cfg, T, flags), s, ts.ptr)))
+    return rc;
   return ok();
 }
 
@@ -386,7 +460,7 @@ int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const 
     float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
     const Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
     TraceScope ts(layers[l]);
-    int rc = run_forward(layers[l], c, use_decode(layers[l]->cfg, T, 0), s, ts.ptr);
+    int rc = run_forward(layers[l], layers[l]->W, c, use_decode(layers[l]->cfg, T, 0), s, ts.ptr);
     if (rc) return rc;
     cur = dst;
     cur_dtype = STRATA_FP32;

@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert set(names) == {"strata_moe_expert_bytes", "strata_moe_packed_bytes",
                           "strata_moe_workspace_bytes", "strata_moe_create", "strata_moe_route",
-                          "strata_moe_forward", "strata_moe_stack_forward", "strata_moe_trace_next_call",
+                          "strata_moe_forward", "strata_moe_forward_static", "strata_moe_stack_forward", "strata_moe_trace_next_call",
                           "strata_moe_destroy", "strata_moe_last_error"}
 
 
