@@ -83,10 +83,13 @@ enum {
 #define STRATA_DECODE_MAX_T 8
 
 typedef struct {
-    int32_t hidden;      /* H: multiple of 256                                */
-    int32_t inter;       /* I: expert intermediate width, multiple of 256     */
+    int32_t hidden;      /* H: multiple of 32 (whole blocks), <= 65536        */
+    int32_t inter;       /* I: expert intermediate width, multiple of 32,     */
+                         /*    <= 65536 (widths that are not whole 256-weight */
+                         /*    superblocks are zero-padded inside the packed  */
+                         /*    layout; one packed expert must stay < 2 GiB)   */
     int32_t n_experts;   /* E: routed experts, 1..4096                        */
-    int32_t top_k;       /* k: 1..min(E, 64)                                  */
+    int32_t top_k;       /* k: 1..E                                           */
     int32_t n_shared;    /* 0 or 1 always-on shared expert (weight 1)         */
     int32_t qfmt;        /* STRATA_Q2 / STRATA_Q3 / STRATA_Q4 / STRATA_MXFP4  */
     int32_t max_tokens;  /* largest T any call on the handle will pass, >= 1; */
@@ -103,18 +106,23 @@ STRATA_API size_t strata_moe_expert_bytes(const strata_moe_config* cfg);
 
 /* Bytes of the device buffer `packed` that strata_moe_create fills: the
  * experts (routed, then shared) repacked into the kernels' layout (the same
- * byte count as the canonical records; for MXFP4 one byte more per block,
+ * byte count as the canonical records when H and I are multiples of 256,
+ * else with the padding rows and blocks; for MXFP4 one byte more per block,
  * the scale taking a 16-bit slot) plus a bf16 hi/lo split of the router
  * rows.  Returns 0 for an invalid config. */
 STRATA_API size_t strata_moe_packed_bytes(const strata_moe_config* cfg);
 
 /* Bytes of the device buffer `workspace` (router logits, top-k, counts,
- * offsets, permutation, per-pair activations and outputs, ticket counters),
- * sized for cfg->max_tokens.  Returns 0 for an invalid config. */
+ * offsets, permutation, per-pair activations and outputs), sized for
+ * cfg->max_tokens.  Returns 0 for an invalid config. */
 STRATA_API size_t strata_moe_workspace_bytes(const strata_moe_config* cfg);
 
 /*
- * Build a layer handle.
+ * Build a layer handle: one MoE layer's router and experts, repacked once
+ * into the kernels' layout (the one-time re-layout of the expert set into a
+ * compute-friendly copy: devotd.net "Strata memory tiers", section
+ * 小模型包不等于合适的模型; one contiguous record per expert: lcz.me/topic/2153,
+ * section 三 item 4).  Every expert stays resident in `packed`.
  *   router_w       device, fp32 [E][H] row-major; borrowed for the handle's life
  *   router_bias    device, fp32 [E], or NULL for no bias; borrowed
  *   experts_canon  device, E canonical records back to back; read during the
@@ -136,7 +144,13 @@ STRATA_API int strata_moe_create(const strata_moe_config* cfg, const float* rout
 
 /*
  * Routing only (router logits, top-k, renormalised weights, stable
- * token->expert permutation).  All outputs are device buffers:
+ * token->expert permutation): the router scores of every expert, the top-k
+ * selection and the softmax merge weights of blog.5616760.com/0039.html,
+ * section 五 "MoE 的本质", and the grouping of tokens by expert that lets one
+ * read of an expert's weights serve all its tokens (same page, section 十二;
+ * devotd.net "Strata memory tiers", section 读取提示与写出回答时).  Ties
+ * between equal logits go to the lower expert id; a NaN logit ranks below
+ * every number.  All outputs are device buffers:
  *   x          device, [T][H] of x_dtype (STRATA_BF16 or STRATA_FP32)
  *   topk_idx   int32 [T][k], expert ids of S_t in ascending order
  *   topk_w     fp32  [T][k], weights matching topk_idx
@@ -151,7 +165,11 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
                      int32_t* offsets, uint32_t flags, void* stream);
 
 /*
- * The full layer: out[T][H] fp32 (device) = moe(x), or with
+ * The full layer (blog.5616760.com/0039.html, section 五: router scores,
+ * top-k, softmax-weighted merge of the selected experts' outputs;
+ * ai-coding.wiselychen.com "Strata two weeks", section 成功思路一: each
+ * selected expert computed and the results summed; lcz.me/topic/2153,
+ * section 一: the always-on shared expert): out[T][H] fp32 (device) = moe(x), or with
  * STRATA_ACCUMULATE out += moe(x), or with STRATA_ADD_INPUT out = x + moe(x).
  * x and out must not overlap.  Stream-ordered and asynchronous.
  * Precision: the decode kernels (T <= 8) multiply exact weight values by the
@@ -206,7 +224,11 @@ STRATA_API int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_lay
  * forward = router GEMM, top-k, column scan, scan, scatter, gate/up GEMM,
  * down GEMM, combine, where for T <= 32 the top-k kernel also does the
  * column scan, the scan and the scatter (5 kernels); route-only calls stop
- * after the routing kernels.  A stack call
+ * after the routing kernels.  A layer whose H is not a multiple of 256 runs
+ * one more kernel first in the grouped path (the tokens widened with zero
+ * columns); a top-k above 64 runs its selection as one more kernel before
+ * the top-k / histogram kernel (grouped path) or in place of the top-k
+ * kernel (decode path).  A stack call
  * traces the handle's layer only.  n_events even, in
  * [0, STRATA_MAX_TRACE_EVENTS]; 0 disarms.  The events must outlive the
  * call's completion on its stream.

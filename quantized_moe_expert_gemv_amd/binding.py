@@ -91,6 +91,36 @@ def _dtype_code(x):
     raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
 
 
+def check_tensor(t, name, shape=None, dtypes=None, device=None, nbytes=None):
+    """Raise ValueError unless t is a contiguous tensor of one of `dtypes`
+    with the given shape (None entries match anything), on `device`, of
+    `nbytes` bytes.  The library sees only data pointers, so a wrong
+    argument here would read or write past an allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor, got {type(t).__name__}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and w != g for w, g in zip(shape, t.shape)):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if nbytes is not None and t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{name} must hold {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
+def _check_call_tensors(x, T, out=None, hidden=None, max_tokens=None, device=None):
+    if T < 1 or (max_tokens is not None and T > max_tokens):
+        raise ValueError(f"T = {T} outside [1, {max_tokens}]")
+    check_tensor(x, "x", (T, hidden), (torch.bfloat16, torch.float32), device if device is not None else None)
+    if device is None and x.device.type != "cuda":
+        raise ValueError(f"x must be on the HIP device, got {x.device}")
+    if out is not None:
+        check_tensor(out, "out", (T, x.shape[1]), (torch.float32,), x.device)
+
+
 def make_config(hidden, inter, n_experts, top_k, n_shared, qfmt, max_tokens):
     return strata_moe_config(hidden, inter, n_experts, top_k, n_shared, qfmt, max_tokens)
 
@@ -118,19 +148,29 @@ def strata_moe_create(cfg, router_w, router_bias, experts_canon, shared_canon, p
 
 
 def strata_moe_route(h, x, T, topk_idx, topk_w, perm, offsets, flags=0, stream=None):
+    _check_call_tensors(x, T)
+    check_tensor(topk_idx, "topk_idx", (T, None), (torch.int32,), x.device)
+    k = topk_idx.shape[1]
+    check_tensor(topk_w, "topk_w", (T, k), (torch.float32,), x.device)
+    check_tensor(perm, "perm", (T * k,), (torch.int32,), x.device)
+    check_tensor(offsets, "offsets", (None,), (torch.int32,), x.device)
     _check(_lib.strata_moe_route(h, _ptr(x), _dtype_code(x), T, _ptr(topk_idx), _ptr(topk_w),
                                  _ptr(perm), _ptr(offsets), flags, _stream(stream)))
 
 
 def strata_moe_forward(h, x, T, out, flags=0, stream=None):
+    _check_call_tensors(x, T, out)
     _check(_lib.strata_moe_forward(h, _ptr(x), _dtype_code(x), T, _ptr(out), flags, _stream(stream)))
 
 
 def strata_moe_forward_static(h, x, T, out, flags=0, stream=None):
+    _check_call_tensors(x, T, out)
     _check(_lib.strata_moe_forward_static(h, _ptr(x), _dtype_code(x), T, _ptr(out), flags, _stream(stream)))
 
 
 def strata_moe_stack_forward(handles, x, T, out, tmp, stream=None):
+    _check_call_tensors(x, T, out)
+    check_tensor(tmp, "tmp", tuple(out.shape), (torch.float32,), x.device)
     arr = (ctypes.c_void_p * len(handles))(*[h.value for h in handles])
     _check(_lib.strata_moe_stack_forward(arr, len(handles), _ptr(x), _dtype_code(x), T, _ptr(out),
                                          _ptr(tmp), _stream(stream)))
@@ -162,6 +202,23 @@ class StrataMoE:
 
     def __init__(self, cfg, router_w, router_bias, experts_canon, shared_canon=None, stream=None):
         dev = router_w.device
+        if dev.type != "cuda":
+            raise ValueError(f"router_w must be on the HIP device, got {dev}")
+        E, H = cfg.n_experts, cfg.hidden
+        rec = strata_moe_expert_bytes(cfg)
+        if rec == 0:
+            raise StrataError(STRATA_E_INVALID, strata_moe_last_error())
+        check_tensor(router_w, "router_w", (E, H), (torch.float32,), dev)
+        if router_bias is not None:
+            check_tensor(router_bias, "router_bias", (E,), (torch.float32,), dev)
+        check_tensor(experts_canon, "experts_canon", None, None, dev, E * rec)
+        if cfg.n_shared:
+            if shared_canon is None:
+                raise ValueError("n_shared = 1 needs shared_canon")
+            check_tensor(shared_canon, "shared_canon", None, None, dev, rec)
+        elif shared_canon is not None:
+            raise ValueError("shared_canon given but n_shared = 0")
+        self.device = dev
         self.cfg = cfg
         self.router_w = router_w.contiguous()
         self.router_bias = None if router_bias is None else router_bias.contiguous()
@@ -172,6 +229,7 @@ class StrataMoE:
 
     def route(self, x, flags=0, stream=None):
         T = x.shape[0]
+        _check_call_tensors(x, T, None, self.cfg.hidden, self.cfg.max_tokens, self.device)
         k, E = self.cfg.top_k, self.cfg.n_experts
         dev = x.device
         idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -183,6 +241,7 @@ class StrataMoE:
 
     def forward(self, x, out=None, flags=0, stream=None):
         T = x.shape[0]
+        _check_call_tensors(x, T, None, self.cfg.hidden, self.cfg.max_tokens, self.device)
         if out is None:
             out = torch.empty((T, self.cfg.hidden), dtype=torch.float32, device=x.device)
         strata_moe_forward(self.handle, x, T, out, flags, stream)
@@ -203,7 +262,14 @@ class StrataMoE:
 
 
 def stack_forward(layers, x, out=None, tmp=None, stream=None):
-    T, H = x.shape
+    if not layers:
+        raise ValueError("need at least one layer")
+    T = x.shape[0]
+    H = layers[0].cfg.hidden
+    for l in layers:
+        if l.cfg.hidden != H:
+            raise ValueError("every layer of a stack must have the same hidden width")
+        _check_call_tensors(x, T, None, H, l.cfg.max_tokens, l.device)
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=x.device)
     if tmp is None:

@@ -322,6 +322,41 @@ __device__ inline void wave_topk_radix(const float (&val)[MAXV], int E, int k, i
   }
 }
 
+// Sum / maximum over the workgroup (<= 16 waves, blockDim a multiple of 64);
+// every thread receives the result.  tmp: >= 16 entries of LDS, reused by
+// the next call only after the barrier at the end.
+__device__ inline int block_sum_i(int v, int* tmp) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) tmp[wv] = v;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < nw; ++i) t += tmp[i];
+  __syncthreads();
+  return t;
+}
+__device__ inline float block_sum_f(float v, float* tmp) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) tmp[wv] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += tmp[i];
+  __syncthreads();
+  return t;
+}
+__device__ inline uint32_t block_max_u(uint32_t v, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = (uint32_t)wave_max_u64(v);
+  if (lane == 0) tmp[wv] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int i = 0; i < nw; ++i) t = tmp[i] > t ? tmp[i] : t;
+  __syncthreads();
+  return t;
+}
+
 // Exclusive scan of an int2 over the workgroup (<= 16 waves); *total gets the sum.
 __device__ inline int2 block_exclusive_scan(int2 v, int2* tmp /* >= 16 */, int2* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
@@ -342,6 +377,79 @@ __device__ inline int2 block_exclusive_scan(int2 v, int2* tmp /* >= 16 */, int2*
   *total = tot;
   __syncthreads();
   return make_int2(pre.x + inc.x - v.x, pre.y + inc.y - v.y);
+}
+
+// Top-k of one row for any k <= E (E <= 4 * blockDim), one workgroup: thread
+// i holds the ids 4 i .. 4 i + 3 (so thread order is id order).  The
+// threshold key tau is fixed bit by bit from the top (workgroup counts of
+// keys >= the candidate) and the descent stops once exactly k keys are >=
+// tau; ties at tau are taken lowest id first (ranks from a scan of the tie
+// counts in id order), and each selected id's place in the ascending output
+// is a scan of the selection counts.  Same selection and weights as the wave
+// versions above (values row[e] + bias[e], bias optional).
+__device__ inline void block_topk(const float* row, const float* bias, int E, int k, int* idx_out, float* w_out) {
+  __shared__ int s_i[16];
+  __shared__ float s_f[16];
+  __shared__ int2 s_scan[16];
+  const int e0 = 4 * threadIdx.x;
+  float v[4];
+  uint32_t u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = min(e0 + i, E - 1);
+    v[i] = row[e] + (bias ? bias[e] : 0.f);
+    u[i] = e0 + i < E ? sortable_bits(v[i]) : 0u;   // padding ranks lowest
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = u[i] > m ? u[i] : m;
+  const float top = unsortable_bits(block_max_u(m, reinterpret_cast<uint32_t*>(s_i)));
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c += u[i] >= cand;
+    const int cnt = block_sum_i(c, s_i);
+    if (cnt >= k) {
+      tau = cand;
+      if (cnt == k) break;                  // {u >= tau} is the selection
+    }
+  }
+  int gt = 0, ties = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gt += u[i] > tau;
+    ties += (u[i] == tau) && (e0 + i < E);
+  }
+  int2 tot;
+  const int need = k - block_sum_i(gt, s_i);
+  int trank = block_exclusive_scan(make_int2(ties, 0), s_scan, &tot).x;
+  bool sel[4];
+  int nsel = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool tie = (u[i] == tau) && (e0 + i < E);
+    sel[i] = (u[i] > tau) || (tie && trank < need);
+    trank += tie;
+    nsel += sel[i];
+  }
+  int pos = block_exclusive_scan(make_int2(nsel, 0), s_scan, &tot).x;
+  float z[4], zs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = sel[i] ? expf(v[i] - top) : 0.f;
+    zs += z[i];
+  }
+  const float inv = 1.0f / block_sum_f(zs, s_f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (sel[i]) {
+      idx_out[pos] = e0 + i;
+      w_out[pos] = z[i] * inv;
+      ++pos;
+    }
+  }
 }
 
 }  // namespace strata

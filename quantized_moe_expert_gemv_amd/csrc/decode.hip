@@ -205,12 +205,13 @@ __device__ inline f32x4 block_offset(const f16x8& a) {
 
 // ------------------------------------------------------------------ router
 struct RouteArgs {
-  const float* Wr;
+  const float* Wr;           // [E][Ho]
   const float* bias;
-  const void* x;
-  int x_f32, T, H, E;
+  const void* x;             // [T][Ho]
+  int x_f32, T, H, E;        // H: the token-part rows' width (whole superblocks)
+  int Ho;                    // the layer's hidden width
   float* logits;
-  _Float16* xparts;
+  _Float16* xparts;          // [2][T][H], zero past Ho
 };
 
 constexpr int ROUTE_WAVES = 4;
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
   constexpr int RR = route_rows(TT);
   __shared__ float part[ROUTE_WAVES][RR][TT];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.H, E = a.E, e0 = blockIdx.x * RR;
+  const int H = a.Ho, E = a.E, e0 = blockIdx.x * RR;
   const int nq = H >> 2;
   const float4* rows[RR];
 #pragma unroll
@@ -283,11 +284,15 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
       const float s = wave_sum(acc[r][t]);
       if (lane == 0) part[wv][r][t] = s;
     }
-  // this workgroup's slice of the token rows as fp16 parts [part][t][H]
-  const int n = TT * H, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
+  // this workgroup's slice of the token rows as fp16 parts [part][t][a.H]
+  // (columns past the layer's width are zero)
+  const int Hp = a.H, n = TT * Hp, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
   for (int i = b * chunk + tid; i < min(n, (b + 1) * chunk); i += blockDim.x) {
-    const float v = XF32 ? reinterpret_cast<const float*>(a.x)[i]
-                         : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[i]);
+    const int t = i / Hp, h = i - t * Hp;
+    const int src = t * H + min(h, H - 1);
+    float v = XF32 ? reinterpret_cast<const float*>(a.x)[src]
+                   : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[src]);
+    v = h < H ? v : 0.f;
     _Float16 p[NPART];
     split2(v, p);
 #pragma unroll
@@ -417,20 +422,32 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void k_topk(TopkArgs a) {
   }
 }
 
+// Top-k for any k (used when k > 64, past the candidate slots of k_topk):
+// one 1024-thread workgroup per token over its logit row (+ bias).
+__global__ __launch_bounds__(1024) void k_topk_block(const float* rows, size_t stride, const float* bias, int E,
+                                                     int k, int* idx, float* w) {
+  const size_t t = blockIdx.x;
+  block_topk(rows + t * stride, bias, E, k, idx + t * k, w + t * k);
+}
+
 // The stable token->expert permutation of the routing (route() only): counts,
 // offsets (exclusive scan over experts), and for every pair p = t * k + j its
-// slot, earlier tokens of the same expert first.  One workgroup.
+// slot, earlier tokens of the same expert first: its rank is the number of
+// earlier tokens in the expert's token bitmask (T <= 8).  One workgroup.
 __global__ __launch_bounds__(512) void k_permute(TopkArgs a) {
   extern __shared__ int lds_i[];
   __shared__ int2 tmp[16];
   const int tid = threadIdx.x, nt = blockDim.x;
   const int E = a.E, k = a.k, T = a.T, P = T * k;
-  int* sel = lds_i;        // [P]
-  int* hist = sel + P;     // [E] counts, then offsets
-  for (int e = tid; e < E; e += nt) hist[e] = 0;
-  for (int p = tid; p < P; p += nt) sel[p] = a.w.topk_idx[p];
+  int* hist = lds_i;                                           // [E] counts, then offsets
+  uint32_t* tmask = reinterpret_cast<uint32_t*>(hist + E);     // [E] tokens of each expert
+  for (int e = tid; e < E; e += nt) { hist[e] = 0; tmask[e] = 0u; }
   __syncthreads();
-  for (int p = tid; p < P; p += nt) atomicAdd(&hist[sel[p]], 1);
+  for (int p = tid; p < P; p += nt) {
+    const int e = a.w.topk_idx[p];
+    atomicAdd(&hist[e], 1);
+    atomicOr(&tmask[e], 1u << (p / k));
+  }
   __syncthreads();
   const int per = (E + nt - 1) / nt;
   const int e0 = tid * per, e1 = min(E, e0 + per);
@@ -447,11 +464,8 @@ __global__ __launch_bounds__(512) void k_permute(TopkArgs a) {
   }
   __syncthreads();
   for (int p = tid; p < P; p += nt) {
-    const int t = p / k, e = sel[p];
-    int rank = 0;
-    for (int t2 = 0; t2 < t; ++t2)
-      for (int j = 0; j < k; ++j) rank += (sel[t2 * k + j] == e);
-    const int slot = hist[e] + rank;
+    const int t = p / k, e = a.w.topk_idx[p];
+    const int slot = hist[e] + __popc(tmask[e] & ((1u << t) - 1u));
     a.w.perm[slot] = p;
     a.w.inv[p] = slot;
   }
@@ -462,7 +476,8 @@ __global__ __launch_bounds__(512) void k_permute(TopkArgs a) {
 struct ExpertArgs {
   const uint8_t* packed;
   size_t stride;
-  int H, I, E, k, T, P, n_shared;
+  int H, I, E, k, T, P, n_shared;   // H, I: whole superblocks (the packed geometry)
+  int Ho;                            // the layer's hidden width (x, out)
   uint32_t actp_bytes;       // bytes of the activation rows of this call
   int umax;                  // most active experts a call of T tokens can have (+ shared)
   const void* x;
@@ -863,7 +878,7 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   extern __shared__ float4 lds_dn4[];
   char* lds = reinterpret_cast<char*>(lds_dn4);
   const int U = a.w.meta[0];
-  const int H = a.H, I = a.I, nsb = I / SB_WEIGHTS;
+  const int nsb = a.I / SB_WEIGHTS;
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6, ks = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.x;
@@ -930,7 +945,7 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
       s += r[4 * l0] + r[4 * l1];
     }
     const int h = g * 16 + row;
-    const size_t o = (size_t)t * H + h;
+    const size_t o = (size_t)t * a.Ho + h;
     if (a.flags & 2u) {
       s += a.x_f32 ? reinterpret_cast<const float*>(a.x)[o]
                    : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[o]);
@@ -946,6 +961,7 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   a.packed = L.packed;
   a.stride = L.expert_stride;
   a.H = L.H; a.I = L.I; a.E = L.E; a.k = L.k; a.T = c.T; a.P = c.T * L.k; a.n_shared = L.n_shared;
+  a.Ho = L.Ho;
   a.x = c.x; a.x_f32 = c.x_f32; a.flags = c.flags; a.out = c.out; a.w = W;
   const int umax = (a.P < L.E ? a.P : L.E) + L.n_shared;
   a.umax = umax;
@@ -972,7 +988,7 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   switch (c.T) {
 #define STRATA_DOWN(TT)                                                                            \
     case TT:                                                                                       \
-      launch(tr, k_down<FMT, TT>, dim3(L.H / 16), dim3(64 * DN_WAVES), down_lds<TT>(umax), s, a);    \
+      launch(tr, k_down<FMT, TT>, dim3(L.Ho / 16), dim3(64 * DN_WAVES), down_lds<TT>(umax), s, a);   \
       break;
     STRATA_DOWN(1) STRATA_DOWN(2) STRATA_DOWN(3) STRATA_DOWN(4)
     STRATA_DOWN(5) STRATA_DOWN(6) STRATA_DOWN(7) STRATA_DOWN(8)
@@ -1053,11 +1069,17 @@ hipError_t prepare_decode_kernels() {
   return e;
 }
 
+hipError_t launch_topk_block(const float* rows, size_t stride, const float* bias, int T, int E, int k, int* idx,
+                             float* w, hipStream_t s, Tracer* tr) {
+  launch(tr, k_topk_block, dim3(T), dim3(1024), 0, s, rows, stride, bias, E, k, idx, w);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation) {
   RouteArgs a;
   a.Wr = L.router_w; a.bias = L.router_b; a.x = c.x; a.x_f32 = c.x_f32; a.T = c.T;
-  a.H = L.H; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts;
+  a.H = L.H; a.Ho = L.Ho; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts;
   switch (c.T) {
 #define STRATA_ROUTE(TT)                                                                 \
     case TT:                                                                               \
@@ -1077,13 +1099,13 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
   t.T = c.T; t.E = L.E; t.k = L.k; t.n_shared = L.n_shared; t.w = W;
   const int per_wave = (L.E + 64 * TOPK_WAVES - 1) / (64 * TOPK_WAVES);
   hipError_t e;
-  if (per_wave <= 1) e = launch_topk_v1<1>(t, s, tr);
+  if (L.k > 64) e = launch_topk_block(W.logits, L.E, nullptr, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
+  else if (per_wave <= 1) e = launch_topk_v1<1>(t, s, tr);
   else if (per_wave <= 2) e = launch_topk_v1<2>(t, s, tr);
   else if (per_wave <= 4) e = launch_topk_v1<4>(t, s, tr);
   else e = launch_topk_v1<8>(t, s, tr);
   if (e != hipSuccess) return e;
-  if (permutation)
-    launch(tr, k_permute, dim3(1), dim3(512), ((size_t)c.T * L.k + (size_t)L.E) * 4, s, t);
+  if (permutation) launch(tr, k_permute, dim3(1), dim3(512), (size_t)L.E * 8, s, t);
   return hipGetLastError();
 }
 

@@ -31,12 +31,20 @@ struct Work {
   uint16_t* ybf;      // [slots][H]  prefill: per-pair expert outputs, bf16; before the
                       //             expert GEMMs it holds the router's split-K partials
   size_t ybf_bytes;
+  void* xpad;         // [Tmax][H]   prefill: the tokens with zero columns past Ho (only
+                      //             when Ho < H), in the call's activation type
   int nchunks;
   int max_tiles;
 };
 
+// Kernel geometry.  H and I are the hidden and intermediate widths rounded up
+// to whole 256-weight superblocks; Ho and Io are the layer's own widths (the
+// canonical records, x, out and the router rows).  The padded rows and
+// columns of every packed matrix hold zero codes with zero scales, so they
+// contribute exactly zero (a padded gate/up row gives silu(0) * 0 = 0).
 struct Layer {
   int H, I, E, k, n_shared, fmt;
+  int Ho, Io;
   const float* router_w;        // [E][H] fp32
   const float* router_b;        // [E] or null
   const uint8_t* packed;        // experts (routed then shared) in the packed layout
@@ -90,6 +98,11 @@ bool decode_fits(int T, int k, int E, int n_shared);
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);
+
+// top-k of T logit rows (row t at rows + t * stride, + bias[e] when bias is
+// not null) for any k <= E <= 4096: one workgroup per token
+hipError_t launch_topk_block(const float* rows, size_t stride, const float* bias, int T, int E, int k, int* idx,
+                             float* w, hipStream_t s, Tracer* tr);
 
 // prefill path
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);

@@ -82,6 +82,7 @@ __device__ inline u32x4_t f32x8_to_f16(f32x4_t lo, f32x4_t hi) {
 // ------------------------------------------------------------------ routing
 struct TopkArgs {
   int T, E, k, nchunks, n_shared;
+  int presel;             // 1: the selection is already in topk_idx / topk_w (k > 64)
   int S;                  // router partial planes
   size_t plane;           // elements between planes
   const float* part;      // [S][T][E] partial logits
@@ -155,23 +156,27 @@ __device__ inline void scatter_pair(const TopkArgs& a, int p);
 
 __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs a) {
   extern __shared__ int lds_i[];
-  int* sel = lds_i;                                            // [CT][k]
-  uint32_t* tmask = reinterpret_cast<uint32_t*>(sel + CT * a.k);  // [E]
+  uint32_t* tmask = reinterpret_cast<uint32_t*>(lds_i);         // [E]
+  // the chunk's selections: [CT][k] in LDS after tmask, or (preselected, any
+  // k) the chunk's rows of topk_idx
+  int* sel = a.presel ? a.w.topk_idx + (size_t)blockIdx.x * CT * a.k : reinterpret_cast<int*>(tmask + a.E);
   __shared__ int s_sel[TOPK_CHUNK_WAVES][64];
   const int wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x, tb = chunk * CT;
   const int k = a.k, E = a.E;
   static_assert(CT <= 32, "token masks are 32-bit");
   for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
-  for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
-    const int t = tb + tl;
-    if (t < a.T) token_topk(a, t, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
+  if (!a.presel) {
+    for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
+      const int t = tb + tl;
+      if (t < a.T) token_topk(a, t, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
+    }
   }
   __syncthreads();
   const int nt = min(CT, a.T - tb);
   for (int i = threadIdx.x; i < nt * k; i += blockDim.x) {
     const int e = sel[i];
-    a.w.topk_idx[(size_t)tb * k + i] = e;
+    if (!a.presel) a.w.topk_idx[(size_t)tb * k + i] = e;
     atomicOr(&tmask[e], 1u << (i / k));
   }
   __syncthreads();
@@ -1152,8 +1157,23 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
   }
 }
 
+// The tokens widened to whole superblocks (zero columns past Ho) for the
+// router GEMM, in their own type (2 or 4 bytes per element), when the
+// layer's width is not a multiple of 256.
+__global__ void k_pad_tokens(const void* __restrict__ x, void* __restrict__ xpad, int T, int Ho, int H, int esize) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)T * H) return;
+  const int t = (int)(i / H), h = (int)(i - (long long)t * H);
+  if (esize == 4) {
+    reinterpret_cast<float*>(xpad)[i] = h < Ho ? reinterpret_cast<const float*>(x)[(size_t)t * Ho + h] : 0.f;
+  } else {
+    reinterpret_cast<uint16_t*>(xpad)[i] = h < Ho ? reinterpret_cast<const uint16_t*>(x)[(size_t)t * Ho + h] : 0;
+  }
+}
+
 struct CombineArgs {
-  int T, H, k, P, n_shared;
+  int T, H, k, P, n_shared;   // H: the per-pair rows' width (whole superblocks)
+  int Ho;                      // the layer's hidden width (x, out)
   const void* x;
   int x_f32;
   uint32_t flags;
@@ -1166,25 +1186,27 @@ struct CombineArgs {
 // the bf16 per-pair rows are read in batches of 8 unconditional loads.
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   const int t = blockIdx.x;
-  const int k = a.k;
-  __shared__ int s_slot[64];
-  __shared__ float s_w[64];
-  if (threadIdx.x < 64) {
-    const int j = min((int)threadIdx.x, k - 1);
-    s_slot[threadIdx.x] = a.w.inv[t * k + j];
-    s_w[threadIdx.x] = (threadIdx.x < (unsigned)k) ? a.w.topk_w[t * k + j] : 0.f;
+  const int k = a.k, kp = (k + 7) & ~7;
+  // the token's slots and weights, padded to a multiple of 8 with weight 0
+  extern __shared__ int s_cmb[];
+  int* s_slot = s_cmb;                                   // [kp]
+  float* s_w = reinterpret_cast<float*>(s_cmb + kp);     // [kp]
+  for (int j = threadIdx.x; j < kp; j += blockDim.x) {
+    const int jj = min(j, k - 1);
+    s_slot[j] = a.w.inv[(size_t)t * k + jj];
+    s_w[j] = j < k ? a.w.topk_w[(size_t)t * k + jj] : 0.f;
   }
   __syncthreads();
-  for (int h = threadIdx.x * 8; h < a.H; h += blockDim.x * 8) {
+  for (int h = threadIdx.x * 8; h < a.Ho; h += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += 8) {
       uint4 y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        y[j] = *reinterpret_cast<const uint4*>(a.w.ybf + (size_t)s_slot[min(j0 + j, 63)] * a.H + h);
+        y[j] = *reinterpret_cast<const uint4*>(a.w.ybf + (size_t)s_slot[j0 + j] * a.H + h);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float wj = s_w[min(j0 + j, 63)];                 // 0 past k
+        const float wj = s_w[j0 + j];                          // 0 past k
         const uint32_t q[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1206,7 +1228,7 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     for (int half = 0; half < 2; ++half) {
       const int hh = h + 4 * half;
       float4 r = make_float4(acc[4 * half], acc[4 * half + 1], acc[4 * half + 2], acc[4 * half + 3]);
-      const size_t o = (size_t)t * a.H + hh;
+      const size_t o = (size_t)t * a.Ho + hh;
       if (a.flags & 2u) {
         if (a.x_f32) {
           const float4 xv = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + o);
@@ -1268,12 +1290,13 @@ RouterPlan router_plan(const Layer& L, const Work& W, int T) {
   // plane; one plane past 512 experts, where top-k re-reads its plane)
   RouterPlan r;
   const int slots = cu_count();
+  // (a selection past 64 per token runs the block top-k on one plane)
   const int tiles = ((L.E + RT_E - 1) / RT_E) * ((T + BM - 1) / BM);
   const int ksteps = L.H / XBK;
   const size_t x16_bytes = (size_t)T * L.H * 2;       // <= the region (slots >= T)
   r.plane = (size_t)T * L.E;
   int S = 1;
-  if (L.E <= 512) {
+  if (L.E <= 512 && L.k <= 64) {
     S = std::min(std::min(T <= 64 ? 32 : 8, ksteps), std::max(1, (slots + tiles - 1) / tiles));
     while (S > 1 && align256((size_t)S * r.plane * 4) + x16_bytes > W.ybf_bytes) --S;
   }
@@ -1318,6 +1341,12 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   const size_t plane = rp.plane;
   RouterArgs r;
   r.x = c.x; r.T = c.T; r.H = L.H; r.E = L.E; r.S = S;
+  if (L.Ho != L.H) {
+    const long long n = (long long)c.T * L.H;
+    launch(tr, k_pad_tokens, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, c.x, W.xpad, c.T, L.Ho, L.H,
+           c.x_f32 ? 4 : 2);
+    r.x = W.xpad;
+  }
   r.kper = rp.kper; r.plane = plane;
   r.whi = L.router_hi; r.wlo = L.router_lo;
   r.part = rp.part;
@@ -1329,7 +1358,12 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b; t.n_shared = L.n_shared;
-  const size_t lds = ((size_t)CT * L.k + L.E) * 4;
+  t.presel = L.k > 64;
+  if (t.presel) {
+    const hipError_t e = launch_topk_block(r.part, L.E, L.router_b, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
+    if (e != hipSuccess) return e;
+  }
+  const size_t lds = ((t.presel ? 0 : (size_t)CT * L.k) + L.E) * 4;
   launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(64 * TOPK_CHUNK_WAVES), lds, s, t);
   if (t.nchunks == 1) return hipGetLastError();   // the one chunk did the scan and the scatter
   ScanArgs sa;
@@ -1351,9 +1385,9 @@ hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, 
   }
   if (err != hipSuccess) return err;
   CombineArgs cb;
-  cb.T = c.T; cb.H = L.H; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
+  cb.T = c.T; cb.H = L.H; cb.Ho = L.Ho; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
   cb.x = c.x; cb.x_f32 = c.x_f32; cb.flags = c.flags; cb.out = c.out; cb.w = W;
-  launch(tr, k_combine, dim3(c.T), dim3(256), 0, s, cb);
+  launch(tr, k_combine, dim3(c.T), dim3(256), (size_t)((L.k + 7) & ~7) * 8, s, cb);
   return hipGetLastError();
 }
 

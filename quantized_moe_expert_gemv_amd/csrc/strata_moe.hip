@@ -53,33 +53,39 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+size_t pad256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 int check_config(const strata_moe_config* c) {
   if (!c) return fail(STRATA_E_INVALID, "config is NULL");
   if (c->qfmt != STRATA_Q2 && c->qfmt != STRATA_Q3 && c->qfmt != STRATA_Q4 && c->qfmt != STRATA_MXFP4)
     return fail(STRATA_E_INVALID, "qfmt %d is not 2, 3, 4 or 5 (MXFP4)", c->qfmt);
   if (c->hidden <= 0 || c->inter <= 0) return fail(STRATA_E_INVALID, "hidden and inter must be positive");
+  if (c->hidden % 32 || c->inter % 32)
+    return fail(STRATA_E_INVALID, "hidden (%d) and inter (%d) must be multiples of 32 (one block)", c->hidden,
+                c->inter);
   if (c->hidden > 65536 || c->inter > 65536)
     return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be at most 65536", c->hidden,
                 c->inter);
-  if (c->hidden % 256 || c->inter % 256)
-    return fail(STRATA_E_UNSUPPORTED, "hidden (%d) and inter (%d) must be multiples of 256",
-                c->hidden, c->inter);
   if (c->n_experts < 1 || c->n_experts > 4096)
     return fail(STRATA_E_INVALID, "n_experts %d outside [1, 4096]", c->n_experts);
-  if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 64)
-    return fail(STRATA_E_INVALID, "top_k %d outside [1, min(n_experts, 64)]", c->top_k);
+  if (c->top_k < 1 || c->top_k > c->n_experts)
+    return fail(STRATA_E_INVALID, "top_k %d outside [1, n_experts = %d]", c->top_k, c->n_experts);
   if (c->n_shared != 0 && c->n_shared != 1) return fail(STRATA_E_INVALID, "n_shared must be 0 or 1");
   if (c->max_tokens < 1) return fail(STRATA_E_INVALID, "max_tokens must be >= 1");
   if ((long long)c->max_tokens * c->top_k > (1LL << 30) / 4)
     return fail(STRATA_E_UNSUPPORTED, "max_tokens * top_k too large");
-  if ((long long)c->max_tokens * c->hidden * 2 > 0xFFFFFFFFLL)
+  if ((long long)c->max_tokens * (long long)pad256(c->hidden) * 2 > 0xFFFFFFFFLL)
     return fail(STRATA_E_UNSUPPORTED, "max_tokens * hidden * 2 bytes of fp16 token rows exceed 4 GiB");
+  // the kernels address an expert record and its matrices with 32-bit byte
+  // offsets inside one buffer descriptor
+  if (packed_expert_bytes(c->qfmt, (int)pad256(c->hidden), (int)pad256(c->inter)) >= (1ull << 31))
+    return fail(STRATA_E_UNSUPPORTED, "one packed expert of %d x %d exceeds 2 GiB", c->hidden, c->inter);
   return STRATA_OK;
 }
 
 struct WsPlan {
   size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, slot_tok, udesc, wtab, meta,
-      chunk_base, pair_rank, tiles, act, xparts, y, total;
+      chunk_base, pair_rank, tiles, act, xparts, xpad, y, total;
   int nchunks, max_tiles;
 };
 
@@ -92,7 +98,8 @@ int max_tiles_for(const strata_moe_config& c, int T) {
 
 WsPlan plan_workspace(const strata_moe_config& c) {
   WsPlan p;
-  const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  // H, I: the kernels' widths (whole superblocks)
+  const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = pad256(c.hidden), I = pad256(c.inter);
   const size_t P = T * k, slots = P + (size_t)c.n_shared * T;
   p.nchunks = (int)((T + PREFILL_CHUNK_T - 1) / PREFILL_CHUNK_T);
   p.max_tiles = max_tiles_for(c, (int)T);
@@ -118,6 +125,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   const size_t act_decode = umax * Td * 2 * I * 2;                             // two fp16 parts
   p.act = take(act_prefill > act_decode ? act_prefill : act_decode);
   p.xparts = take(Td * 2 * H * 2);
+  p.xpad = take(H != (size_t)c.hidden ? T * H * 4 : 0);
   p.y = take(slots * H * 2);
   p.total = o;
   return p;
@@ -145,6 +153,7 @@ Work layout_work(uint8_t* ws, const WsPlan& p) {
   W.wtab = reinterpret_cast<float*>(ws + p.wtab);
   W.ybf = reinterpret_cast<uint16_t*>(ws + p.y);
   W.ybf_bytes = p.total - p.y;                 // the last region
+  W.xpad = ws + p.xpad;
   W.nchunks = p.nchunks;
   W.max_tiles = p.max_tiles;
   return W;
@@ -181,11 +190,12 @@ hipError_t scratch_address(int dev, uint8_t** out) {
 
 // one part (high or low) of the router split: experts padded to groups of 16
 size_t router_part_bytes(const strata_moe_config& c) {
-  return align256((size_t)((c.n_experts + 15) / 16) * 16 * c.hidden * 2);
+  return align256((size_t)((c.n_experts + 15) / 16) * 16 * pad256(c.hidden) * 2);
 }
 
 size_t packed_experts_bytes(const strata_moe_config& c) {
-  return align256((size_t)(c.n_experts + c.n_shared) * packed_expert_bytes(c.qfmt, c.hidden, c.inter));
+  return align256((size_t)(c.n_experts + c.n_shared) *
+                  packed_expert_bytes(c.qfmt, (int)pad256(c.hidden), (int)pad256(c.inter)));
 }
 
 size_t packed_total(const strata_moe_config& c) {
@@ -330,11 +340,12 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   h->ws = ws;
   h->ws_bytes = p.total;
   Layer& L = h->L;
-  L.H = cfg->hidden; L.I = cfg->inter; L.E = cfg->n_experts; L.k = cfg->top_k;
+  L.H = (int)pad256(cfg->hidden); L.I = (int)pad256(cfg->inter); L.Ho = cfg->hidden; L.Io = cfg->inter;
+  L.E = cfg->n_experts; L.k = cfg->top_k;
   L.n_shared = cfg->n_shared; L.fmt = cfg->qfmt;
   L.router_w = router_w; L.router_b = router_bias;
   L.packed = static_cast<const uint8_t*>(packed);
-  L.expert_stride = packed_expert_bytes(cfg->qfmt, cfg->hidden, cfg->inter);
+  L.expert_stride = packed_expert_bytes(cfg->qfmt, L.H, L.I);
   const size_t rh = packed_experts_bytes(*cfg);
   L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
   L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + router_part_bytes(*cfg));

@@ -76,9 +76,23 @@ def test_workspace_grows_with_max_tokens(B):
     assert small > 0 and big > 8192 * 10 * 2560 * 2 > small
 
 
-@pytest.mark.parametrize("bad", [dict(qfmt=6), dict(qfmt=1), dict(hidden=2500), dict(inter=100), dict(top_k=0),
-                                 dict(top_k=513), dict(top_k=65, n_experts=100), dict(n_experts=0),
-                                 dict(n_experts=5000), dict(n_shared=2), dict(max_tokens=0)])
+@pytest.mark.parametrize("good", [dict(hidden=2592, inter=800), dict(hidden=32, inter=32, n_experts=4, top_k=4),
+                                  dict(top_k=512), dict(n_experts=4096, top_k=4096, max_tokens=4),
+                                  dict(hidden=7168, inter=2048, n_experts=256, top_k=8, qfmt=5)])
+def test_block_multiples_and_any_k_up_to_e_are_accepted(B, good):
+    """Hidden and intermediate widths only need whole 32-weight blocks, and
+    top_k may be anything in [1, E]."""
+    c = _cfg(B, **good)
+    assert B.strata_moe_expert_bytes(c) == 3 * c.inter * (c.hidden // 32) * (17 if c.qfmt == 5 else 2 + 4 * c.qfmt)
+    assert B.strata_moe_packed_bytes(c) >= c.n_experts * B.strata_moe_expert_bytes(c)
+    assert B.strata_moe_workspace_bytes(c) > 0
+
+
+@pytest.mark.parametrize("bad", [dict(qfmt=6), dict(qfmt=1), dict(hidden=2500), dict(hidden=2576), dict(inter=100),
+                                 dict(inter=48), dict(top_k=0), dict(top_k=513), dict(top_k=101, n_experts=100),
+                                 dict(n_experts=0), dict(n_experts=5000), dict(n_shared=2), dict(max_tokens=0),
+                                 # one packed Q4 expert past 2 GiB (32-bit offsets inside a record)
+                                 dict(hidden=65536, inter=65536, qfmt=4, max_tokens=1)])
 def test_invalid_configs_are_rejected(B, bad):
     c = _cfg(B, **bad)
     assert B.strata_moe_packed_bytes(c) == 0
@@ -113,3 +127,34 @@ def test_calls_on_null_handle_fail_cleanly(B):
     rc = B._lib.strata_moe_trace_next_call(None, None, 0)
     assert rc == B.STRATA_E_INVALID
     B.strata_moe_destroy(None)            # NULL-safe
+
+
+def test_binding_checks_tensors_before_the_library(B):
+    """The binding refuses, before any library call, tensors whose dtype,
+    shape, layout or byte size would let the kernels read or write past an
+    allocation (checked here on host tensors)."""
+    import torch
+    cpu = torch.device("cpu")
+    B.check_tensor(torch.zeros(4, 8), "t", (4, 8), (torch.float32,), cpu, 128)
+    B.check_tensor(torch.zeros(4, 8), "t", (None, 8), (torch.float32,), cpu)
+    bad = [
+        dict(t=torch.zeros(4, 8, dtype=torch.bfloat16), dtypes=(torch.float32,)),      # dtype
+        dict(t=torch.zeros(4, 7), shape=(4, 8)),                                        # width
+        dict(t=torch.zeros(3, 8), shape=(4, 8)),                                        # rows
+        dict(t=torch.zeros(4, 8, 1), shape=(4, 8)),                                     # rank
+        dict(t=torch.zeros(8, 4).t(), shape=(4, 8)),                                    # not contiguous
+        dict(t=torch.zeros(4, 8), nbytes=64),                                           # byte size
+        dict(t=torch.zeros(4, 8), device=torch.device("meta")),                         # device
+        dict(t=[0.0] * 8),                                                              # not a tensor
+    ]
+    for kw in bad:
+        t = kw.pop("t")
+        with pytest.raises(ValueError):
+            B.check_tensor(t, "t", **kw)
+    # the call helpers: x must be on the HIP device, T within max_tokens
+    with pytest.raises(ValueError):
+        B.strata_moe_forward(None, torch.zeros(2, 256, dtype=torch.bfloat16), 2, torch.zeros(2, 256))
+    with pytest.raises(ValueError):
+        B._check_call_tensors(torch.zeros(9, 256, dtype=torch.bfloat16), 9, None, 256, 8, cpu)
+    with pytest.raises(ValueError):
+        B._check_call_tensors(torch.zeros(2, 256, dtype=torch.float16), 2, None, 256, 8, cpu)

@@ -209,6 +209,48 @@ def test_exact_ties_and_nan_logits(B, path):
                DECODE_TOL if path == "decode" else PREFILL_TOL, f"ties {path}")
 
 
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
+@pytest.mark.parametrize("H,I", [(96, 160), (2592, 800)])
+def test_widths_in_whole_blocks(B, fmt, H, I):
+    """Hidden and intermediate widths that are whole 32-weight blocks but not
+    whole 256-weight superblocks (zero-padded inside the library): decode and
+    grouped paths, with the shared expert and the residual add, every row
+    against the oracle."""
+    hl = HostLayer(31, 0, H, I, 16, 4, fmt, True, 1 if fmt >= 4 else 0)
+    layer = device_layer(hl, 64, DEV)
+    for T in (3, 40):
+        bits, xf = tokens(hl, 600 + T, T)
+        x = to_device_bf16(bits, DEV)
+        check_route(layer, hl, x, xf, w_atol=5e-5)
+        ref, _ = hl.oracle(xf)
+        tol = DECODE_TOL if T <= 8 else PREFILL_TOL
+        check_rows(layer.forward(x).cpu().numpy(), ref, tol, f"H {H} I {I} fmt {fmt} T {T}")
+        out = torch.zeros((T, H), dtype=torch.float32, device=DEV)
+        layer.forward(x, out=out, flags=B.STRATA_ADD_INPUT)
+        check_rows(out.cpu().numpy(), ref + xf, tol, f"H {H} I {I} fmt {fmt} T {T} + x")
+    if fmt == 2:                            # fp32 tokens through the padded router rows
+        xf32 = torch.from_numpy(xf.astype(np.float32)).to(DEV)
+        check_rows(layer.forward(xf32).cpu().numpy(), ref, PREFILL_TOL, f"H {H} I {I} fp32 tokens")
+
+
+@pytest.mark.parametrize("E,k,T,path", [(512, 100, 4, "decode"), (512, 100, 40, "prefill"),
+                                        (96, 96, 3, "decode"), (96, 96, 50, "prefill"),
+                                        (4096, 300, 2, "decode"), (4096, 300, 9, "prefill"),
+                                        (1024, 65, 70, "prefill")])
+def test_top_k_beyond_64(B, E, k, T, path):
+    """Selections past 64 experts per token (block top-k, any k up to E):
+    ids, weights, permutation and offsets exact, every output row within the
+    path's bound."""
+    hl, layer = tiny(2, E=E, k=k, max_tokens=80)
+    bits, xf = tokens(hl, 880 + T, T, min_gap=0.0 if k == E else 1e-2)
+    x = to_device_bf16(bits, DEV)
+    flags = B.STRATA_FORCE_PREFILL if path == "prefill" else B.STRATA_FORCE_DECODE
+    check_route(layer, hl, x, xf, flags=flags, w_atol=5e-5)
+    ref, _ = hl.oracle(xf)
+    check_rows(layer.forward(x, flags=flags).cpu().numpy(), ref, DECODE_TOL if path == "decode" else PREFILL_TOL,
+               f"E {E} k {k} T {T} {path}")
+
+
 @pytest.mark.parametrize("flags_name", ["STRATA_ADD_INPUT", "STRATA_ACCUMULATE"])
 @pytest.mark.parametrize("T", [2, 40])
 def test_residual_flags(B, flags_name, T):
@@ -277,9 +319,19 @@ def test_bad_calls_on_a_live_handle(B):
     hl, layer = tiny(2)
     x = torch.zeros((4, hl.H), dtype=torch.bfloat16, device=DEV)
     out = torch.empty((4, hl.H), dtype=torch.float32, device=DEV)
-    with pytest.raises(B.StrataError) as e:
-        B.strata_moe_forward(layer.handle, x, 400, out)          # T > max_tokens
-    assert e.value.code == B.STRATA_E_INVALID
+    # T > max_tokens: refused by the library itself (raw call) and by the binding
+    import ctypes
+    rc = B._lib.strata_moe_forward(layer.handle, ctypes.c_void_p(x.data_ptr()), B.STRATA_BF16, 400,
+                                   ctypes.c_void_p(out.data_ptr()), 0, None)
+    assert rc == B.STRATA_E_INVALID and "max_tokens" in B.strata_moe_last_error()
+    with pytest.raises(ValueError):
+        B.strata_moe_forward(layer.handle, x, 400, out)
+    with pytest.raises(ValueError):                           # out not fp32 / wrong width
+        layer.forward(x, out=torch.empty((4, hl.H), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        layer.forward(torch.zeros((4, hl.H - 32), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):                           # a strided view
+        layer.forward(torch.zeros((4, 2 * hl.H), dtype=torch.bfloat16, device=DEV)[:, ::2])
     big = torch.zeros((9, hl.H), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(B.StrataError) as e:
         B.strata_moe_forward(layer.handle, big, 9, torch.empty((9, hl.H), device=DEV), B.STRATA_FORCE_DECODE)
