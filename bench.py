@@ -1,19 +1,26 @@
 #!/usr/bin/env python3
 """Throughput benchmark of the MI355X routed-MoE expert layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...]
 
 A step is one full MoE-layer call (router GEMV/GEMM, top-k + renormalised
 softmax, token->expert permutation, dequantising gate/up + SwiGLU, down,
 weighted combine) over one batch of seeded synthetic tokens, with every
 expert resident in HBM.  Decode workloads rotate over many resident layer
 instances of the same shape (as consecutive layers of a stack would), so
-repeated steps do not re-read one layer's experts from the on-die caches.
-The timed region replays a captured HIP graph of a full rotation.
+repeated steps do not re-read one layer's experts from the on-die caches;
+their timed region replays captured HIP graphs of exactly K steps.
+
+With no --workload the run measures the metric's three configurations: the
+4-token MTP verify (the headline line), the single-token decode and the
+8192-token prefill chunk, each with its own step time, roofline and CPU
+oracle baseline; the last two go under "also" in the same JSON line.
 
 Prints ONE JSON line: the throughput (tokens/s), the roofline of the
-dominant kernel from HIP events recorded between kernels on the launch
-stream, and the CPU oracle timed on a bounded sample of the same workload.
+dominant kernel from HIP events bound to each kernel's own dispatch on the
+launch stream, the counter summaries committed under profiles/ when they
+were taken on the current kernel sources, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 import argparse
@@ -31,17 +38,19 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
 
 METRIC = "MoE-layer tokens/s (decode, 8K prefill); % HBM peak (decode) / % MFMA peak"
+DEFAULT_WORKLOADS = ["mtp_verify_t4_q2", "decode_t1_q2", "prefill_t8192_q2"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=0, help="timed steps (0: workload default)")
+    ap.add_argument("--steps", type=int, default=0, help="timed steps per workload (0: workload default)")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mtp_verify_t4_q2")
+    ap.add_argument("--workload", action="append", default=None,
+                    help="workload to time (repeatable; default: " + ", ".join(DEFAULT_WORKLOADS) + ")")
     ap.add_argument("--layers", type=int, default=0, help="resident layer instances to rotate over")
     ap.add_argument("--seed", type=int, default=2026)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -65,12 +74,38 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    torch.cuda.set_device(torch.device("cuda:0"))
+    names = args.workload or DEFAULT_WORKLOADS
+    results, baselines = [], []
+    # every GPU measurement first (back to back, so the clocks stay up), then
+    # the CPU oracle baselines
+    for name in names:
+        r, cpu_job = run_workload(args, name)
+        results.append(r)
+        baselines.append(cpu_job)
+        torch.cuda.empty_cache()
+    for r, job in zip(results, baselines):
+        r["cpu_baseline"] = job() if job is not None else None
+    res = dict(results[0])
+    res["metric"] = METRIC
+    props = torch.cuda.get_device_properties(0)
+    res["system"] = {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+                     "compute_units": props.multi_processor_count, "hip": torch.version.hip,
+                     "torch": torch.__version__}
+    if len(results) > 1:
+        res["also"] = {r["config"]["workload"]: {k: v for k, v in r.items() if k not in ("metric",)}
+                       for r in results[1:]}
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(args, name):
+    import torch
     from moe_synth import WORKLOADS, generate as G, canonical_block_bytes
     from quantized_moe_expert_gemv_amd import binding as B
+    from quantized_moe_expert_gemv_amd import prof_summary
 
-    w = WORKLOADS[args.workload]
+    w = WORKLOADS[name]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     stack = w.n_layers > 1
     decode = w.tokens <= B.STRATA_DECODE_MAX_T
     # skinny batches (up to 64 tokens) take the grouped-GEMM path but, like
@@ -103,7 +138,7 @@ def main():
             host0 = (canon_h, sh_h)
         del canon, sh, canon_h
     torch.cuda.synchronize()
-    log(f"{n_inst} layer instances of {args.workload} resident in "
+    log(f"{n_inst} layer instances of {name} resident in "
         f"{sum(l.packed.numel() for l in layers) / 1e9:.1f} GB ({time.time() - t_setup:.0f} s)")
 
     # token batches (bf16, seeded)
@@ -130,13 +165,12 @@ def main():
     # unique experts per step, from the library's own routing of each (layer, batch) pair
     period = int(np.lcm(n_inst if not stack else 1, n_batches))
     uniq = []
-    for i in range(min(period, steps)):
-        if stack:
-            break
-        idx, _, _, offs = layers[i % n_inst].route(xs[i % n_batches])
-        uniq.append(int((offs[1:] - offs[:-1] > 0).sum().item()))
-    if stack:
-        uniq = [w.top_k]          # per layer; refined below from the trace of layer 0
+    if not stack:
+        for i in range(min(period, steps)):
+            _, _, _, offs = layers[i % n_inst].route(xs[i % n_batches])
+            uniq.append(int((offs[1:] - offs[:-1] > 0).sum().item()))
+    else:
+        uniq = [w.top_k]          # per layer of a single-token stack step
     u_mean = float(np.mean(uniq))
 
     # ------------------------------------------------------------ throughput
@@ -144,9 +178,14 @@ def main():
         step(i)
     torch.cuda.synchronize()
     use_graph = (decode or skinny) and not args.eager
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     if use_graph:
-        # one rotation of (layer, batch) pairs (or 8 full stack passes), captured once and replayed
-        g_len = 8 if stack else period
+        # exactly `steps` steps: a captured rotation of g_len steps (the whole
+        # (layer, batch) period, 8 stack passes, or all the steps when fewer)
+        # replayed steps // g_len times, plus a graph of the remainder
+        g_len = min(steps, 8 if stack else period)
+        reps, rem = divmod(steps, g_len)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -158,53 +197,54 @@ def main():
         with torch.cuda.graph(graph):
             for i in range(g_len):
                 step(i)
-        reps = max(1, steps // g_len)
-        steps = reps * g_len
+        tail = None
+        if rem:
+            tail = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(tail):
+                for i in range(rem):
+                    step(i)
         graph.replay()
+        if tail is not None:
+            tail.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
             graph.replay()
+        if tail is not None:
+            tail.replay()
         e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        gpu_ms = e0.elapsed_time(e1)
     else:
         t0 = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
             step(i)
         e1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        gpu_ms = e0.elapsed_time(e1)
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
     ms_per_step = gpu_ms / steps
-    tokens_per_step = T
-    value = tokens_per_step * steps / (gpu_ms / 1e3)
-    log(f"{steps} steps in {gpu_ms:.2f} ms GPU ({wall * 1e3:.1f} ms wall): {ms_per_step * 1e3:.2f} us/step")
+    value = T * steps / (gpu_ms / 1e3)
+    log(f"{name}: {steps} steps in {gpu_ms:.2f} ms GPU ({wall * 1e3:.1f} ms wall): {ms_per_step * 1e3:.2f} us/step")
 
     # ------------------------------------------------------------ per-kernel durations (HIP events)
     if decode:                                              # (stack: layer 0 of each pass)
-        names = ["route_gemv", "topk", "gateup", "down_combine"]
+        knames = ["route_gemv", "topk", "gateup", "down_combine"]
     else:
-        names = ["router_gemm", "topk", "colscan", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
+        knames = ["router_gemm", "topk", "colscan", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
         if T <= 32:                        # one top-k chunk also scans and scatters
-            names = ["router_gemm", "topk_scan_scatter", "gateup_gemm", "down_gemm", "combine"]
+            knames = ["router_gemm", "topk_scan_scatter", "gateup_gemm", "down_gemm", "combine"]
     # each kernel's own dispatch start/end, bound to a pair of events on the
-    # launch stream (eager launches of the same steps, after the timed replay)
+    # launch stream (eager launches of the same steps, after the timed region)
     n_trace = min(steps, 256)
-    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(knames))]
                for _ in range(n_trace)]
     torch.cuda.synchronize()
     for i in range(n_trace):
         step(i, trace_events=ev_sets[i])
     torch.cuda.synchronize()
-    dur = np.array([[ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(len(names))] for ev in ev_sets])
+    dur = np.array([[ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(len(knames))] for ev in ev_sets])
     kern_us = dur.mean(axis=0) * 1e3
 
     # algorithmic work per launch
@@ -215,22 +255,21 @@ def main():
     out_bytes = T * w.hidden * 4
     router_bytes = w.n_experts * w.hidden * 4
     kernels = {}
+    counters = None
     if decode:
         ue = u_mean + w.n_shared
         alg = {"route_gemv": router_bytes + x_bytes,
                "topk": T * w.n_experts * 4,
                "gateup": ue * gu_bytes + x_bytes,
                "down_combine": ue * dn_bytes + out_bytes}
-        for j, n in enumerate(names):
+        for j, n in enumerate(knames):
             kernels[n] = {"us": round(float(kern_us[j]), 3), "alg_bytes": int(alg[n]),
                           "GBps": round(alg[n] / (kern_us[j] * 1e-6) / 1e9, 1)}
-        dom = max(names, key=lambda n: kernels[n]["us"])
+        dom = max(knames, key=lambda n: kernels[n]["us"])
         achieved = kernels[dom]["GBps"]
         # HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
         # if it was taken on the current kernel sources
-        from quantized_moe_expert_gemv_amd import prof_summary
-        measured = prof_summary.read_traffic(
-            os.path.join(ROOT, "profiles", f"decode_hbm_traffic_{args.workload}.md"))
+        measured = prof_summary.read_traffic(os.path.join(ROOT, "profiles", f"decode_hbm_traffic_{name}.md"))
         roofline = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": int(measured[dom]) if dom in measured else None,
@@ -244,20 +283,22 @@ def main():
         fl = {"router_gemm": 2.0 * T * w.hidden * w.n_experts,
               "gateup_gemm": 2.0 * (P + w.n_shared * T) * w.hidden * 2 * w.inter,
               "down_gemm": 2.0 * (P + w.n_shared * T) * w.inter * w.hidden}
-        for j, n in enumerate(names):
+        for j, n in enumerate(knames):
             kernels[n] = {"us": round(float(kern_us[j]), 3)}
             if n in fl:
                 kernels[n]["TFLOPs"] = round(fl[n] / (kern_us[j] * 1e-6) / 1e12, 1)
-        dom = max(names, key=lambda n: kernels[n]["us"])
+        dom = max(knames, key=lambda n: kernels[n]["us"])
         achieved = kernels[dom].get("TFLOPs", 0.0)
         # HBM bytes per launch of that kernel (FETCH_SIZE + WRITE_SIZE summary
         # taken on the current kernel sources), for reference next to the flops
-        from quantized_moe_expert_gemv_amd import prof_summary
-        measured = prof_summary.read_traffic(
-            os.path.join(ROOT, "profiles", f"prefill_hbm_traffic_{args.workload}.md"))
+        measured = prof_summary.read_traffic(os.path.join(ROOT, "profiles", f"prefill_hbm_traffic_{name}.md"))
         roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                     "traffic": int(measured[dom]) if dom in measured else None}
+        # matrix-core busy fraction from the committed SQ counter summary
+        counters = prof_summary.read_mfma(os.path.join(ROOT, "profiles", f"prefill_mfma_counters_{name}.md")) or None
+        if counters and dom in counters:
+            roofline["mfma_busy_frac_counter"] = counters[dom]["busy_frac"]
         layer_flops = sum(fl.values())
         layer_frac = layer_flops / (ms_per_step * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12)
         layer_bytes = None
@@ -266,9 +307,10 @@ def main():
             # against the HBM peak (algorithmic bytes: the unique experts'
             # packed gate/up or down bytes plus the tokens in / rows out)
             ue = u_mean + w.n_shared
-            alg = {"gateup_gemm": ue * gu_bytes + x_bytes, "down_gemm": ue * dn_bytes + (P + w.n_shared * T) * w.hidden * 2}
+            alg = {"gateup_gemm": ue * gu_bytes + x_bytes,
+                   "down_gemm": ue * dn_bytes + (P + w.n_shared * T) * w.hidden * 2}
             for n in alg:
-                j = names.index(n)
+                j = knames.index(n)
                 kernels[n]["alg_bytes"] = int(alg[n])
                 kernels[n]["GBps"] = round(alg[n] / (kern_us[j] * 1e-6) / 1e9, 1)
             dom = max(alg, key=lambda n: kernels[n]["us"])
@@ -279,12 +321,11 @@ def main():
             layer_bytes = router_bytes + ue * (gu_bytes + dn_bytes) + x_bytes + out_bytes
             layer_frac = layer_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
 
-    # ------------------------------------------------------------ CPU oracle baseline
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(args, w, host0, xs_h, G)
+    # the CPU oracle baseline, run by the caller once every GPU measurement is done
+    cpu_job = None if args.no_cpu else (lambda: cpu_baseline(args, w, host0, xs_h, G))
 
-    res = {
+    del layers, xs, outs, tmp
+    return {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "tokens/s",
@@ -297,7 +338,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32" if decode else "fp16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens_per_step": T, "hidden": w.hidden,
+        "config": {"workload": name, "tokens_per_step": T, "hidden": w.hidden,
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
                    "shared": w.n_shared, "format": ("MXFP4" if w.fmt == 5 else f"Q{w.fmt}"), "layers_rotated": n_inst,
                    "stack_layers": w.n_layers, "launch": "hip_graph" if use_graph else "eager",
@@ -306,9 +347,9 @@ def main():
         "layer_roofline_frac": None if layer_frac is None else round(layer_frac, 4),
         "step_alg_bytes": None if layer_bytes is None else int(layer_bytes),
         "kernels": kernels,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(res), flush=True)
+        "mfma_counters": counters,
+        "cpu_baseline": None,
+    }, cpu_job
 
 
 def copy_calibration(mib):

@@ -4,6 +4,7 @@ library's measurements.
     python -m quantized_moe_expert_gemv_amd.prof_summary stats OUT.md CMD KERNEL_STATS_CSV
     python -m quantized_moe_expert_gemv_amd.prof_summary traffic OUT.md CMD_FETCH CMD_WRITE \
         FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES
+    python -m quantized_moe_expert_gemv_amd.prof_summary mfma OUT.md CMD PMC_CSV N_CU
 
 `stats` lists every kernel of a `--kernel-trace --stats` run (calls, average
 and total time).  `traffic` takes two `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE`
@@ -11,7 +12,12 @@ runs of a workload and of a plain device copy of COPY_BYTES bytes each way;
 the copy gives the bytes each counter unit stands for, so a kernel's HBM
 bytes per dispatch = mean counter value x that factor.  The summary ends with
 one `traffic:` line per library kernel (and the hash of the kernel sources the
-counters were taken on), which the benchmark reads.
+counters were taken on), which the benchmark reads.  `mfma` takes one `--pmc`
+run of the matrix-core counters (SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA,
+SQ_INSTS_VALU, SQ_INSTS_VALU_MFMA_MOPS_F16/BF16, SQ_BUSY_CYCLES,
+GRBM_GUI_ACTIVE) and writes, per kernel, the fraction of SIMD cycles the
+matrix cores were busy, the MFMA flops the hardware counted and the VALU
+instructions issued per MFMA, ending with one `mfma:` line per kernel.
 """
 
 import csv
@@ -23,7 +29,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # library kernel name fragment -> benchmark name
-KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_gateup", "gateup"),
+KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_topk_block", "topk"), ("k_gateup", "gateup"),
            ("k_down", "down_combine"), ("k_router", "router_gemm"), ("k_topk_chunks", "topk"),
            ("k_colscan", "colscan"), ("k_scan", "scan"), ("k_scatter", "scatter"), ("k_gemm_gateup", "gateup_gemm"),
            ("k_gemm_down", "down_gemm"), ("k_combine", "combine")]
@@ -33,7 +39,7 @@ KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_gateup", "gat
 # valid while these are unchanged)
 PATH_SOURCES = {"decode": ("common.hpp", "decode.hip", "kernels.hpp"),
                 "prefill": ("common.hpp", "kernels.hpp", "prefill.hip")}
-DECODE_KERNELS = ("k_route_gemv", "k_topk", "k_permute", "k_gateup", "k_down")
+DECODE_KERNELS = ("k_route_gemv", "k_topk", "k_topk_block", "k_permute", "k_gateup", "k_down")
 
 
 def source_hash(path=None):
@@ -127,6 +133,77 @@ def traffic(out, cmd_f, cmd_w, fetch_csv, write_csv, cfetch_csv, cwrite_csv, cop
     open(out, "w").write("\n".join(lines))
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+N_XCC = 8                  # GRBM_GUI_ACTIVE is summed over the accelerator dies
+
+
+def per_kernel_counters(path):
+    """{kernel: {counter: [value per dispatch]}} of a multi-counter pmc CSV."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return acc
+
+
+def mfma(out, cmd, pmc_csv, n_cu):
+    """Matrix-core utilisation per kernel: busy = SQ_VALU_MFMA_BUSY_CYCLES
+    (summed over SIMDs) / (GRBM_GUI_ACTIVE / N_XCC cycles x 4 SIMDs x n_cu);
+    flops = (MOPS_F16 + MOPS_BF16) x 512; VALU per MFMA = SQ_INSTS_VALU /
+    SQ_INSTS_MFMA (the MFMAs are counted among the VALU instructions, so the
+    plain VALU work is SQ_INSTS_VALU - SQ_INSTS_MFMA)."""
+    n_cu = int(n_cu)
+    acc = per_kernel_counters(pmc_csv)
+    lines = ["# Matrix-core counters per dispatch (rocprofv3 --pmc)", "", "Command:", "", "    " + cmd, "",
+             f"Busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {N_XCC} x 4 SIMDs x {n_cu} CUs); "
+             "flops = (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16) x 512; VALU/MFMA = (SQ_INSTS_VALU - SQ_INSTS_MFMA) / "
+             "SQ_INSTS_MFMA.", "",
+             "| kernel | dispatches | GUI cycles / die | MFMA busy cycles | MFMA busy | MFMA insts | MFMA GFLOP "
+             "| other VALU / MFMA |", "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    tagged = {}
+    for k in sorted(acc):
+        c = {n: (sum(v) / len(v) if v else 0.0) for n, v in acc[k].items()}
+        if not c.get("SQ_INSTS_MFMA"):
+            continue
+        gui = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCC
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        frac = busy / (gui * 4 * n_cu) if gui else 0.0
+        flops = (c.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)) * 512
+        other = (c.get("SQ_INSTS_VALU", 0.0) - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"]
+        short = k if len(k) < 70 else k[:67] + "..."
+        n = len(next(iter(acc[k].values())))
+        lines.append(f"| `{short}` | {n} | {gui:.0f} | {busy:.4g} | {frac:.3f} | {c['SQ_INSTS_MFMA']:.4g} | "
+                     f"{flops / 1e9:.2f} | {other:.2f} |")
+        name = bench_name(k)
+        if name:
+            tb = tagged.setdefault((name, kernel_path(k)), [0.0, 0.0, 0.0, 0])
+            tb[0] += frac * n; tb[1] += flops * n; tb[2] += other * n; tb[3] += n
+    lines += ["", f"kernel sources: decode {source_hash('decode')}, prefill {source_hash('prefill')}", ""]
+    for (name, kp), (fr, fl, ot, n) in sorted(tagged.items()):
+        lines.append(f"mfma: kernel={name} path={kp} busy_frac={fr / n:.4f} mfma_flops={fl / n:.0f} "
+                     f"valu_per_mfma={ot / n:.3f} sources={source_hash(kp)}")
+    lines.append("")
+    open(out, "w").write("\n".join(lines))
+
+
+def read_mfma(path):
+    """{bench kernel name: {busy_frac, mfma_flops, valu_per_mfma}} from a
+    matrix-core counter summary, or {} when missing or taken on other kernel
+    sources."""
+    if not os.path.exists(path):
+        return {}
+    cur = {p: source_hash(p) for p in PATH_SOURCES}
+    res = {}
+    for line in open(path):
+        if line.startswith("mfma:"):
+            kv = dict(p.split("=", 1) for p in line.split()[1:])
+            if kv.get("path") in cur and kv.get("sources") == cur[kv["path"]]:
+                res[kv["kernel"]] = {"busy_frac": float(kv["busy_frac"]), "mfma_flops": float(kv["mfma_flops"]),
+                                     "valu_per_mfma": float(kv["valu_per_mfma"])}
+    return res
+
+
 def read_traffic(path):
     """{bench kernel name: bytes per dispatch} from a traffic summary, or {}
     when it is missing or was taken on other kernel sources."""
@@ -148,6 +225,8 @@ if __name__ == "__main__":
         stats(*sys.argv[2:5])
     elif mode == "traffic":
         traffic(*sys.argv[2:11])
+    elif mode == "mfma":
+        mfma(*sys.argv[2:6])
     elif mode == "hash":
         print(source_hash(sys.argv[2] if len(sys.argv) > 2 else None))
     else:

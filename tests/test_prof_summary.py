@@ -34,3 +34,36 @@ def test_kernel_paths_and_names():
 
 def test_missing_summary_gives_nothing(tmp_path):
     assert P.read_traffic(os.path.join(str(tmp_path), "absent.md")) == {}
+
+
+def test_read_mfma_matches_path_sources(tmp_path):
+    pf = P.source_hash("prefill")
+    p = _write(str(tmp_path), [
+        f"mfma: kernel=gateup_gemm path=prefill busy_frac=0.5 mfma_flops=1000 valu_per_mfma=1.5 sources={pf}",
+        f"mfma: kernel=down_gemm path=prefill busy_frac=0.4 mfma_flops=10 valu_per_mfma=1 sources={'0' * 16}",
+    ])
+    assert P.read_mfma(p) == {"gateup_gemm": {"busy_frac": 0.5, "mfma_flops": 1000.0, "valu_per_mfma": 1.5}}
+
+
+def test_mfma_summary_from_counter_rows(tmp_path):
+    """The busy fraction divides the summed MFMA busy cycles by the cycles of
+    every SIMD of the device (GRBM_GUI_ACTIVE is summed over the 8 dies)."""
+    import csv
+    rows = []
+    kern = "void strata::(anonymous namespace)::k_gemm_gateup<2, 4>(x)"
+    for d in range(2):
+        for name, val in (("SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1000 * 4 * 256), ("SQ_INSTS_MFMA", 100.0),
+                          ("SQ_INSTS_VALU", 250.0), ("SQ_INSTS_VALU_MFMA_MOPS_F16", 32.0),
+                          ("GRBM_GUI_ACTIVE", 8 * 1000.0)):
+            rows.append({"Kernel_Name": kern, "Counter_Name": name, "Counter_Value": val})
+    src = os.path.join(str(tmp_path), "pmc.csv")
+    with open(src, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+    out = os.path.join(str(tmp_path), "m.md")
+    P.mfma(out, "cmd", src, 256)
+    got = P.read_mfma(out)["gateup_gemm"]
+    assert abs(got["busy_frac"] - 0.5) < 1e-9
+    assert got["mfma_flops"] == 32 * 512
+    assert abs(got["valu_per_mfma"] - 1.5) < 1e-9
