@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replay")
+    ap.add_argument("--route", choices=("auto", "fused", "split"), default="auto",
+                    help="grouped-path routing: the library's choice, one launch, or the multi-launch sequence")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 4 times (reference for HBM counters)")
     return ap.parse_args()
@@ -149,6 +151,10 @@ def run_workload(args, name):
     outs = [torch.empty((T, w.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
     tmp = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
 
+    flags = {"auto": 0, "fused": B.STRATA_FUSED_ROUTE, "split": B.STRATA_SPLIT_ROUTE}[args.route]
+    one_launch_route = (not decode and T <= 64 and w.n_experts <= 512 and w.top_k <= 64 and
+                        (args.route == "fused" or (args.route == "auto" and T <= B.STRATA_FUSED_ROUTE_DEFAULT_T)))
+
     def step(i, trace_events=None):
         x = xs[i % n_batches]
         if stack:
@@ -159,7 +165,7 @@ def run_workload(args, name):
             layer = layers[i % n_inst]
             if trace_events is not None:
                 B.strata_moe_trace_next_call(layer.handle, trace_events)
-            layer.forward(x, out=outs[i % 2])
+            layer.forward(x, out=outs[i % 2], flags=flags)
 
     # ------------------------------------------------------------ routing statistics (for bytes)
     # unique experts per step, from the library's own routing of each (layer, batch) pair
@@ -233,7 +239,9 @@ def run_workload(args, name):
         knames = ["route_gemv", "topk", "gateup", "down_combine"]
     else:
         knames = ["router_gemm", "topk", "colscan", "scan", "scatter", "gateup_gemm", "down_gemm", "combine"]
-        if T <= 32:                        # one top-k chunk also scans and scatters
+        if one_launch_route:               # router, top-k and permutation in one launch
+            knames = ["route_one_launch", "gateup_gemm", "down_gemm", "combine"]
+        elif T <= 32:                      # one top-k chunk also scans and scatters
             knames = ["router_gemm", "topk_scan_scatter", "gateup_gemm", "down_gemm", "combine"]
     # each kernel's own dispatch start/end, bound to a pair of events on the
     # launch stream (eager launches of the same steps, after the timed region)
@@ -280,7 +288,7 @@ def run_workload(args, name):
         layer_frac = layer_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
     else:
         P = T * w.top_k
-        fl = {"router_gemm": 2.0 * T * w.hidden * w.n_experts,
+        fl = {"router_gemm": 2.0 * T * w.hidden * w.n_experts, "route_one_launch": 2.0 * T * w.hidden * w.n_experts,
               "gateup_gemm": 2.0 * (P + w.n_shared * T) * w.hidden * 2 * w.inter,
               "down_gemm": 2.0 * (P + w.n_shared * T) * w.inter * w.hidden}
         for j, n in enumerate(knames):
@@ -342,6 +350,7 @@ def run_workload(args, name):
                    "inter": w.inter, "experts": w.n_experts, "top_k": w.top_k,
                    "shared": w.n_shared, "format": ("MXFP4" if w.fmt == 5 else f"Q{w.fmt}"), "layers_rotated": n_inst,
                    "stack_layers": w.n_layers, "launch": "hip_graph" if use_graph else "eager",
+                   "routing": None if decode else ("one_launch" if one_launch_route else "multi_launch"),
                    "unique_experts_per_step": round(u_mean, 2)},
         "roofline": roofline,
         "layer_roofline_frac": None if layer_frac is None else round(layer_frac, 4),

@@ -75,12 +75,21 @@ enum {
     STRATA_ACCUMULATE = 1u,     /* out[t] += moe(x)[t]                          */
     STRATA_ADD_INPUT = 2u,      /* out[t]  = x[t] + moe(x)[t] (residual)        */
     STRATA_FORCE_DECODE = 4u,   /* use the GEMV path (T <= STRATA_DECODE_MAX_T) */
-    STRATA_FORCE_PREFILL = 8u   /* use the grouped-GEMM path at any T           */
+    STRATA_FORCE_PREFILL = 8u,  /* use the grouped-GEMM path at any T           */
+    /* grouped path only (calls on the decode path ignore them): route in one
+     * launch (router, top-k, permutation; T <= 64, E <= 512, k <= 64, else
+     * STRATA_E_UNSUPPORTED), or in the multi-launch sequence.  Without
+     * either the library picks the faster for the call. */
+    STRATA_FUSED_ROUTE = 16u,
+    STRATA_SPLIT_ROUTE = 32u
 };
 
 /* Calls with T <= STRATA_DECODE_MAX_T take the decode (GEMV) path unless
  * STRATA_FORCE_PREFILL is given; larger T take the grouped-GEMM path. */
 #define STRATA_DECODE_MAX_T 8
+/* Grouped-path calls of at most this many tokens (and E <= 512, k <= 64)
+ * route in one launch unless STRATA_SPLIT_ROUTE is given. */
+#define STRATA_FUSED_ROUTE_DEFAULT_T 0
 
 typedef struct {
     int32_t hidden;      /* H: multiple of 32 (whole blocks), <= 65536        */

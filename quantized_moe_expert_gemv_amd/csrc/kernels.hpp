@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include "strata_moe.h"
+
 namespace strata {
 
 // Workspace regions (device pointers), sized for max_tokens by the host.
@@ -51,6 +53,7 @@ struct Layer {
   size_t expert_stride;         // bytes per expert
   const uint16_t* router_hi;    // bf16 high part of router_w, MFMA operand order (k_router_split)
   const uint16_t* router_lo;    // bf16 remainder, same order
+  int* route_done;              // one-launch routing: completion counter (0 between calls)
 };
 
 struct Call {
@@ -110,5 +113,12 @@ hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, 
 
 constexpr int PREFILL_BM = 128;     // token rows per GEMM tile
 constexpr int PREFILL_CHUNK_T = 32; // tokens per top-k/histogram chunk
+
+// one-launch routing of the grouped path (forward/route flag bits as in the
+// public header): where it applies, and up to how many tokens it is taken
+// without being asked for
+constexpr uint32_t STRATA_FUSED_ROUTE_FLAG = 16u, STRATA_SPLIT_ROUTE_FLAG = 32u;
+constexpr int FUSED_ROUTE_DEFAULT_T = STRATA_FUSED_ROUTE_DEFAULT_T;
+inline bool fused_route_fits(int E, int k, int T) { return T <= 64 && E <= 512 && k <= 64; }
 
 }  // namespace strata

@@ -1157,6 +1157,170 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ one-launch routing
+// For calls of at most 64 tokens (E <= 512, k <= 64) the whole routing can
+// run in one launch.  Workgroup g computes the complete logits of experts
+// 16 g .. 16 g + 15 for every token (the full K, so no partial planes): its
+// 16 waves each take a range of 32-wide K blocks on the bf16 MFMA with the
+// router's hi/lo split (as the router GEMM; an fp32 token is split too,
+// three products), and their partial sums meet in LDS in wave order.  It
+// also writes its slice of the fp16 token rows for the expert GEMMs.  Then
+// it counts itself done on a counter kept in the layer's packed buffer; the
+// last workgroup to finish (it sees every other one counted, after their
+// stores) takes the top-k of every token, each expert's token mask (64-bit:
+// the expert counts and every pair's rank among the earlier tokens), the
+// offsets and tile list and the scatter, and resets the counter.
+constexpr int FR_WAVES = 16;
+constexpr int FR_MAXT = 64;
+constexpr int FR_MAXE = 512;
+constexpr int FR_MAXK = 64;
+
+struct FusedRouteArgs {
+  const void* x;            // [T][Ho] bf16 or fp32
+  int T, H, Ho, E;
+  const uint16_t* whi;      // router rows in operand order (k_router_split)
+  const uint16_t* wlo;
+  uint16_t* x16;            // [T][H] the tokens as fp16, zero past Ho
+  int* done;                // completion counter, 0 between calls
+  TopkArgs t;               // part = the logits (one plane), bias
+};
+
+// the routing of every token of the call, in one workgroup (see above)
+__device__ inline void fused_route_tail(const TopkArgs& a) {
+  __shared__ int s_sel[FR_MAXT * FR_MAXK];               // [T][k]
+  __shared__ unsigned long long s_tm[FR_MAXE];           // tokens of each expert
+  const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int T = a.T, k = a.k, E = a.E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_tm[e] = 0ull;
+  for (int t = wv; t < T; t += nw) token_topk(a, t, s_sel + t * k, a.w.topk_w + (size_t)t * k, nullptr);
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
+    const int e = s_sel[i];
+    a.w.topk_idx[i] = e;
+    atomicOr(&s_tm[e], 1ull << (i / k));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += blockDim.x)
+    a.w.pair_rank[i] = __popcll(s_tm[s_sel[i]] & ((1ull << (i / k)) - 1ull));
+  // every pair's rank is among all earlier tokens, so every chunk base is 0
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    a.w.counts[e] = __popcll(s_tm[e]);
+    for (int c = 0; c < a.nchunks; ++c) a.w.chunk_base[(size_t)c * E + e] = 0;
+  }
+  __syncthreads();
+  ScanArgs sa;
+  sa.T = T; sa.E = E; sa.k = k; sa.n_shared = a.n_shared; sa.nchunks = a.nchunks; sa.w = a.w;
+  scan_tiles(sa);
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * k; p += blockDim.x) scatter_pair(a, p);
+}
+
+template <bool XF32>
+__global__ __launch_bounds__(64 * FR_WAVES, 1) void k_route_fused(FusedRouteArgs a) {
+  constexpr int INF = XF32 ? 2 : 4;                      // K blocks of loads in flight per wave
+  constexpr int NX = XF32 ? 2 : 1;                       // 16-byte token loads per block and subtile
+  constexpr uint32_t OOBV = 0x80000000u;                 // buffer offset past the tokens: reads 0
+  __shared__ f32x4 red[FR_WAVES][4][64];
+  __shared__ int s_last;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = blockIdx.x, ng = gridDim.x;
+  const int nkb = a.H / 32;
+  const int kb0 = wv * nkb / FR_WAVES, kb1 = (wv + 1) * nkb / FR_WAVES;
+  const int esz = XF32 ? 4 : 2;
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)((size_t)a.T * a.Ho * esz));
+  // lane l: token 16 m + l % 16 of subtile m, K 32 kb + 8 (l / 16) .. + 7
+  uint32_t xrow[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = 16 * m + (lane & 15);
+    xrow[m] = t < a.T ? (uint32_t)((size_t)t * a.Ho * esz) : OOBV;
+  }
+  const int kl = 8 * (lane >> 4);
+  const size_t wbase = (size_t)g * nkb * AFRAG + 8 * lane;
+  f32x4 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = kb0; kb < kb1; kb += INF) {
+    u32x4_t A[INF][2], X[INF][4][NX];
+#pragma unroll
+    for (int j = 0; j < INF; ++j) {
+      const int kbj = min(kb + j, kb1 - 1);
+      A[j][0] = *(gu32x4_t*)(a.whi + wbase + (size_t)kbj * AFRAG);
+      A[j][1] = *(gu32x4_t*)(a.wlo + wbase + (size_t)kbj * AFRAG);
+      const int kk = 32 * kbj + kl;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t off = (kk < a.Ho && xrow[m] != OOBV) ? xrow[m] + (uint32_t)(kk * esz) : OOBV;
+#pragma unroll
+        for (int q = 0; q < NX; ++q) {
+          const uint4 v = bload4(rx, off == OOBV ? OOBV : off + 16 * q, 0);
+          X[j][m][q] = u32x4_t{v.x, v.y, v.z, v.w};
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < INF; ++j) {
+      if (kb + j >= kb1) break;
+      const bf16x8 wh = __builtin_bit_cast(bf16x8, A[j][0]), wl = __builtin_bit_cast(bf16x8, A[j][1]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if constexpr (XF32) {
+          const u32x4_t f0 = X[j][m][0], f1 = X[j][m][1];
+          uint32_t h[4], l[4];
+          split_bf16x2(__uint_as_float(f0[0]), __uint_as_float(f0[1]), &h[0], &l[0]);
+          split_bf16x2(__uint_as_float(f0[2]), __uint_as_float(f0[3]), &h[1], &l[1]);
+          split_bf16x2(__uint_as_float(f1[0]), __uint_as_float(f1[1]), &h[2], &l[2]);
+          split_bf16x2(__uint_as_float(f1[2]), __uint_as_float(f1[3]), &h[3], &l[3]);
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, u32x4_t{h[0], h[1], h[2], h[3]});
+          const bf16x8 xl = __builtin_bit_cast(bf16x8, u32x4_t{l[0], l[1], l[2], l[3]});
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, xh, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, xh, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, xl, acc[m], 0, 0, 0);
+        } else {
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, X[j][m][0]);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wh, xh, acc[m], 0, 0, 0);
+          acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wl, xh, acc[m], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) red[wv][m][lane] = acc[m];
+  // this workgroup's slice of the fp16 token rows [T][H] (zero past Ho)
+  {
+    const int n = a.T * a.H, chunk = (n + ng - 1) / ng;
+    for (int i = g * chunk + (int)threadIdx.x; i < min(n, (g + 1) * chunk); i += blockDim.x) {
+      const int t = i / a.H, h = i - t * a.H;
+      const size_t src = (size_t)t * a.Ho + min(h, a.Ho - 1);
+      float v = XF32 ? reinterpret_cast<const float*>(a.x)[src]
+                     : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[src]);
+      const _Float16 hv = (_Float16)(h < a.Ho ? v : 0.f);
+      a.x16[i] = __builtin_bit_cast(uint16_t, hv);
+    }
+  }
+  __syncthreads();
+  // D[e][t] of subtile m: lane l holds experts 4 (l / 16) .. + 3 of the group
+  // for token 16 m + l % 16; the waves' partial sums in wave order
+  {
+    const int m = threadIdx.x >> 8, l = (threadIdx.x >> 2) & 63, v = threadIdx.x & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < FR_WAVES; ++w) sum += red[w][m][l][v];
+    const int t = 16 * m + (l & 15), e = 16 * g + 4 * (l >> 4) + v;
+    if (t < a.T && e < a.E) a.t.w.logits[(size_t)t * a.E + e] = sum;   // (= a.t.part)
+  }
+  // count this workgroup done once all its stores are visible on the device;
+  // the last one routes
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(a.done, 1) == ng - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();                                       // (acquire: the other workgroups' logits)
+  fused_route_tail(a.t);
+  if (threadIdx.x == 0) *a.done = 0;                     // every other workgroup has counted
+}
+
 // The tokens widened to whole superblocks (zero columns past Ho) for the
 // router GEMM, in their own type (2 or 4 bytes per element), when the
 // layer's width is not a multiple of 256.
@@ -1308,11 +1472,21 @@ RouterPlan router_plan(const Layer& L, const Work& W, int T) {
   return r;
 }
 
+// Whether a call routes in one launch (k_route_fused): asked for with
+// STRATA_FUSED_ROUTE, refused with STRATA_SPLIT_ROUTE, else by default for
+// calls of at most FUSED_ROUTE_DEFAULT_T tokens; only where its tail holds
+// the call (T <= 64, E <= 512, k <= 64).
+bool fused_route(const Layer& L, int T, uint32_t flags) {
+  if (!fused_route_fits(L.E, L.k, T) || (flags & STRATA_SPLIT_ROUTE_FLAG)) return false;
+  return (flags & STRATA_FUSED_ROUTE_FLAG) || T <= FUSED_ROUTE_DEFAULT_T;
+}
+
 template <int FMT>
 hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   GemmArgs g;
   g.packed = L.packed; g.stride = L.expert_stride; g.H = L.H; g.I = L.I; g.E = L.E; g.k = L.k;
-  g.T = c.T; g.P = c.T * L.k; g.x16 = router_plan(L, W, c.T).x16; g.w = W;
+  g.T = c.T; g.P = c.T * L.k; g.w = W;
+  g.x16 = fused_route(L, c.T, c.flags) ? reinterpret_cast<uint16_t*>(W.ybf) : router_plan(L, W, c.T).x16;
   const int max_tiles = W.max_tiles;
   // Skinny calls (up to 64 tokens: tiles of a few rows, one or two per
   // touched expert) are bound by streaming each expert's weights through one
@@ -1336,6 +1510,20 @@ hipError_t launch_gemms_fmt(const Layer& L, const Work& W, const Call& c, hipStr
 }  // namespace
 
 hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
+  if (fused_route(L, c.T, c.flags)) {
+    FusedRouteArgs f;
+    f.x = c.x; f.T = c.T; f.H = L.H; f.Ho = L.Ho; f.E = L.E;
+    f.whi = L.router_hi; f.wlo = L.router_lo;
+    f.x16 = reinterpret_cast<uint16_t*>(W.ybf);
+    f.done = L.route_done;
+    TopkArgs& t = f.t;
+    t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.n_shared = L.n_shared; t.presel = 0;
+    t.S = 1; t.plane = (size_t)c.T * L.E; t.part = W.logits; t.bias = L.router_b; t.w = W;
+    const dim3 grid((L.E + 15) / 16), block(64 * FR_WAVES);
+    if (c.x_f32) launch(tr, k_route_fused<true>, grid, block, 0, s, f);
+    else launch(tr, k_route_fused<false>, grid, block, 0, s, f);
+    return hipGetLastError();
+  }
   const RouterPlan rp = router_plan(L, W, c.T);
   const int S = rp.S;
   const size_t plane = rp.plane;

@@ -198,8 +198,12 @@ size_t packed_experts_bytes(const strata_moe_config& c) {
                   packed_expert_bytes(c.qfmt, (int)pad256(c.hidden), (int)pad256(c.inter)));
 }
 
+// after the experts and the router split: 256 bytes of per-layer state
+// (the one-launch routing's completion counter), zeroed at create
+constexpr size_t STATE_BYTES = 256;
+
 size_t packed_total(const strata_moe_config& c) {
-  return packed_experts_bytes(c) + 2 * router_part_bytes(c);
+  return packed_experts_bytes(c) + 2 * router_part_bytes(c) + STATE_BYTES;
 }
 
 int hip_fail(hipError_t e, const char* what) {
@@ -225,8 +229,13 @@ bool use_decode(const strata_moe_config& c, int T, uint32_t flags) {
 }
 
 int check_flags(const strata_moe_config& c, int T, uint32_t flags) {
-  const uint32_t known = STRATA_ACCUMULATE | STRATA_ADD_INPUT | STRATA_FORCE_DECODE | STRATA_FORCE_PREFILL;
+  const uint32_t known = STRATA_ACCUMULATE | STRATA_ADD_INPUT | STRATA_FORCE_DECODE | STRATA_FORCE_PREFILL |
+                         STRATA_FUSED_ROUTE | STRATA_SPLIT_ROUTE;
   if (flags & ~known) return fail(STRATA_E_INVALID, "unknown flag bits 0x%x", flags & ~known);
+  if ((flags & STRATA_FUSED_ROUTE) && (flags & STRATA_SPLIT_ROUTE))
+    return fail(STRATA_E_INVALID, "FUSED_ROUTE and SPLIT_ROUTE are exclusive");
+  if ((flags & STRATA_FUSED_ROUTE) && !fused_route_fits(c.n_experts, c.top_k, T))
+    return fail(STRATA_E_UNSUPPORTED, "one-launch routing covers T <= 64, n_experts <= 512, top_k <= 64");
   if ((flags & STRATA_FORCE_DECODE) && (flags & STRATA_FORCE_PREFILL))
     return fail(STRATA_E_INVALID, "FORCE_DECODE and FORCE_PREFILL are exclusive");
   if ((flags & STRATA_FORCE_DECODE) && T > STRATA_DECODE_MAX_T)
@@ -349,11 +358,16 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   const size_t rh = packed_experts_bytes(*cfg);
   L.router_hi = reinterpret_cast<const uint16_t*>(L.packed + rh);
   L.router_lo = reinterpret_cast<const uint16_t*>(L.packed + rh + router_part_bytes(*cfg));
+  uint8_t* state = static_cast<uint8_t*>(packed) + rh + 2 * router_part_bytes(*cfg);
+  L.route_done = reinterpret_cast<int*>(state);
   h->W = layout_work(ws, p);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const char* step = "zeroing counters";
+  static_assert(STRATA_FUSED_ROUTE == STRATA_FUSED_ROUTE_FLAG && STRATA_SPLIT_ROUTE == STRATA_SPLIT_ROUTE_FLAG,
+                "flag bits");
   hipError_t e = hipMemsetAsync(ws + p.meta, 0, 16 * 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(state, 0, STATE_BYTES, s);
   if (e == hipSuccess) {
     step = "expert repack";
     e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
