@@ -461,14 +461,16 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
   const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)((B & 1) ? (sw >> 16) : (sw & 0xffffu)));
   h2_t q[4];
   if constexpr (FMT == 4) {
+    // (1 + q/16) * 16 d - 24 d in one fused multiply-add per pair: 16 d is
+    // exact, 24 d is rounded once to fp16 (an absolute error of at most
+    // 2^-11 |24 d| on top of the single rounding of the product)
     const uint32_t W = c.w[B & 3];
-    const h2_t off = {(_Float16)-1.5f, (_Float16)-1.5f};
-    const _Float16 s16 = d * (_Float16)16.0f;
-    const h2_t s2 = {s16, s16};
+    const _Float16 s16 = d * (_Float16)16.0f, c24 = (_Float16)-1.5f * s16;
+    const h2_t s2 = {s16, s16}, n2 = {c24, c24};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
-      q[k] = (__builtin_bit_cast(h2_t, (t & 0x03C003C0u) | 0x3C003C00u) + off) * s2;
+      q[k] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, (t & 0x03C003C0u) | 0x3C003C00u), s2, n2);
     }
   } else {
     const uint32_t W = ((B >> 1) & 1) ? c.w.y : c.w.x;
@@ -1346,12 +1348,14 @@ struct CombineArgs {
 };
 
 // out[t] = sum_j w[t][j] * y[slot(t, j)] (+ shared expert row) (+ x) (+ out),
-// fixed j order.  One workgroup per token; each thread 8 columns per pass;
-// the bf16 per-pair rows are read in batches of 8 unconditional loads.
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+// fixed j order.  One workgroup per token, one thread per 8 columns (a single
+// pass over the row); the bf16 per-pair rows are read KB at a time, all KB
+// loads in flight together (KB divides k where it can, so no padding rows are
+// read; otherwise the last batch reads the last row again with weight 0).
+template <int KB>
+__global__ __launch_bounds__(512) void k_combine(CombineArgs a) {
   const int t = blockIdx.x;
-  const int k = a.k, kp = (k + 7) & ~7;
-  // the token's slots and weights, padded to a multiple of 8 with weight 0
+  const int k = a.k, kp = (k + KB - 1) / KB * KB;
   extern __shared__ int s_cmb[];
   int* s_slot = s_cmb;                                   // [kp]
   float* s_w = reinterpret_cast<float*>(s_cmb + kp);     // [kp]
@@ -1363,13 +1367,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
   __syncthreads();
   for (int h = threadIdx.x * 8; h < a.Ho; h += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      uint4 y[8];
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      uint4 y[KB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < KB; ++j)
         y[j] = *reinterpret_cast<const uint4*>(a.w.ybf + (size_t)s_slot[j0 + j] * a.H + h);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < KB; ++j) {
         const float wj = s_w[j0 + j];                          // 0 past k
         const uint32_t q[4] = {y[j].x, y[j].y, y[j].z, y[j].w};
 #pragma unroll
@@ -1410,6 +1414,15 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       *reinterpret_cast<float4*>(a.out + o) = r;
     }
   }
+}
+
+// loads per batch of the combine: k itself up to 8, else its largest divisor
+// in 4..8, else 8 (with a padded last batch)
+int combine_batch(int k) {
+  if (k <= 8) return k;
+  for (int d = 8; d >= 4; --d)
+    if (k % d == 0) return d;
+  return 8;
 }
 
 // Router split-K plan and the place of the fp16 token rows.  Both live in
@@ -1575,7 +1588,17 @@ hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, 
   CombineArgs cb;
   cb.T = c.T; cb.H = L.H; cb.Ho = L.Ho; cb.k = L.k; cb.P = c.T * L.k; cb.n_shared = L.n_shared;
   cb.x = c.x; cb.x_f32 = c.x_f32; cb.flags = c.flags; cb.out = c.out; cb.w = W;
-  launch(tr, k_combine, dim3(c.T), dim3(256), (size_t)((L.k + 7) & ~7) * 8, s, cb);
+  const int kb = combine_batch(L.k);
+  const size_t lds = (size_t)((L.k + kb - 1) / kb * kb) * 8;
+  const dim3 cgrid(c.T), cblock(std::min(512, ((L.Ho / 8 + 63) / 64) * 64));
+  switch (kb) {
+#define STRATA_COMBINE(KB) \
+    case KB: launch(tr, k_combine<KB>, cgrid, cblock, lds, s, cb); break;
+    STRATA_COMBINE(1) STRATA_COMBINE(2) STRATA_COMBINE(3) STRATA_COMBINE(4)
+    STRATA_COMBINE(5) STRATA_COMBINE(6) STRATA_COMBINE(7) STRATA_COMBINE(8)
+#undef STRATA_COMBINE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
