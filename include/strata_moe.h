@@ -21,8 +21,11 @@
  * the code bytes read as one little-endian bit string.  MXFP4 (OCP
  * Microscaling Formats v1.0, a format the pages name for their DeepSeek
  * suites): 16 bytes of FP4 E2M1 codes in the same bit order, then one E8M0
- * scale byte e, w = 2^(e - 127) E2M1(q); e = 0 (2^-127) is read as 0 and
- * e = 255 (NaN) is not supported.
+ * scale byte e, w = 2^(e - 127) E2M1(q).
+ * Block scales the 16-bit weight operands cannot carry are refused at
+ * create (STRATA_E_UNSUPPORTED): an fp16 d that is NaN, infinite or above
+ * 2^15 (Q2), 2^14 (Q3) or 2^11 (Q4); an MXFP4 byte e above 140 (2^13), 255
+ * (NaN) included.
  *
  * Canonical expert record (the input of strata_moe_create): gate
  * [I rows][H/32 blocks], up [I][H/32], down [H rows][I/32 blocks], each
@@ -183,9 +186,17 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
  * x and out must not overlap.  Stream-ordered and asynchronous.
  * Precision: the decode kernels (T <= 8) multiply exact weight values by the
  * activations carried as two fp16 parts (22 significant bits) with fp32
- * accumulation; |x| and the SwiGLU outputs must stay below 65504 there.  The
- * prefill expert GEMMs round weights and activations to fp16 (same range
- * limit) with fp32 accumulation; the prefill router stays fp32-accurate.
+ * accumulation.  The prefill expert GEMMs round weights and activations to
+ * fp16 with fp32 accumulation (weights below 2^-24 in magnitude round to
+ * zero there); the prefill router stays fp32-accurate.
+ * Range: the 16-bit token operands of both paths hold x_t 2^-e_t, with e_t
+ * chosen per token from its largest magnitude m_t (0 while m_t < 16, else
+ * the power that brings it below 16, at most 60), the SwiGLU activations
+ * are kept as silu(g) u 2^-2e_t and the expert outputs are scaled back by
+ * 2^2e_t: every step is a power of two, so a token's results do not depend
+ * on e_t and tokens up to 2^64 in magnitude stay in range.  The activations
+ * still have to fit the 16-bit range at that scale (|silu(g) u| 2^-2e_t
+ * below 65504: weights of ordinary magnitude keep them far inside it).
  */
 STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
                        float* out, uint32_t flags, void* stream);

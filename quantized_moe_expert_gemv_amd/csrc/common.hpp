@@ -172,6 +172,22 @@ __device__ inline void wave_argmax(float& v, int& i) {
 
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+// ------------------------------------------------------------------ token range
+// The 16-bit token operands of both paths hold x 2^-e, where e is chosen per
+// token from its largest magnitude m (m < 2^E): e = E - 4 when m reaches 16,
+// else 0, at most 60 (so an ordinary token is not scaled at all).  The
+// expert sums then come out scaled by 2^-e; gate/up takes silu on the
+// unscaled gate and stores silu(g) u 2^-2e (the activation grows with the
+// square of the input, so it stays in range with it), and the combine
+// multiplies that expert output by 2^2e.  Every step is a power of two, exact.
+constexpr int TOKEN_SCALE_MAX_EXP = 60;
+__device__ inline int token_scale_exp(float maxabs) {
+  const int E = (int)((__float_as_uint(maxabs) >> 23) & 0xffu) - 126;
+  return min(max(E - 4, 0), TOKEN_SCALE_MAX_EXP);
+}
+// 2^n for |n| <= 126, exactly
+__device__ inline float pow2i(int n) { return __uint_as_float((uint32_t)(127 + n) << 23); }
+
 // ------------------------------------------------------------------ top-k
 // Selection order: value descending, then expert id ascending; NaN ranks
 // below every number (-inf included).  Each entry becomes one 64-bit key
@@ -209,6 +225,17 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// maximum unsigned 32-bit value over the wave; every lane receives it
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_QUAD_XOR2>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_ROW_HALF_MIRROR>((int)v));
+  v = max(v, (uint32_t)dpp_i<DPP_ROW_MIRROR>((int)v));         // row maxima
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 __device__ inline uint64_t topk_key(float v, int e) {

@@ -164,12 +164,13 @@ __device__ inline f16x8 mx_operand(const Codes<5>& c) {
 }
 
 // scale of block BB of this lane's row; Q4 folds in the factor 16; MXFP4's
-// 16-bit slot holds the E8M0 byte e: 2^(e - 127) (e = 0 reads as 0)
+// 16-bit slot holds the E8M0 byte e: 2^(e - 127) (e = 0: 2^-127, a
+// subnormal, e <= 140 checked at create)
 template <int FMT, int BB>
 __device__ inline float block_scale(const uint4& sc) {
   const uint32_t w = comp(sc, BB >> 1);
   const uint32_t h = (BB & 1) ? (w >> 16) : (w & 0xffffu);
-  if constexpr (FMT == FMT_MXFP4) return __uint_as_float(h << 23);
+  if constexpr (FMT == FMT_MXFP4) return __uint_as_float(h ? h << 23 : 0x00400000u);
   const float d = half_bits_to_f32((uint16_t)h);
   return FMT == 4 ? 16.0f * d : d;
 }
@@ -211,7 +212,7 @@ struct RouteArgs {
   int x_f32, T, H, E;        // H: the token-part rows' width (whole superblocks)
   int Ho;                    // the layer's hidden width
   float* logits;
-  _Float16* xparts;          // [2][T][H], zero past Ho
+  _Float16* xparts;          // [2][T][H], zero past Ho (x 2^-e, see k_topk)
 };
 
 constexpr int ROUTE_WAVES = 4;
@@ -285,7 +286,8 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
       if (lane == 0) part[wv][r][t] = s;
     }
   // this workgroup's slice of the token rows as fp16 parts [part][t][a.H]
-  // (columns past the layer's width are zero)
+  // (columns past the layer's width are zero); the top-k kernel rewrites the
+  // rows of a token that needs an operand scale (rare)
   const int Hp = a.H, n = TT * Hp, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
   for (int i = b * chunk + tid; i < min(n, (b + 1) * chunk); i += blockDim.x) {
     const int t = i / Hp, h = i - t * Hp;
@@ -347,8 +349,47 @@ __device__ inline void wave_select(const uint32_t (&u)[V], int k, bool (&sel)[V]
 
 struct TopkArgs {
   int T, E, k, n_shared;
+  const void* x;             // [T][Ho] the tokens (bf16, or fp32 when x_f32)
+  int x_f32, H, Ho;          // H: the token-part rows' width
   Work w;
 };
+
+// The operand scale of token t (one workgroup, any number of waves): e from
+// the token's largest magnitude (token_scale_exp) into texp[t]; a token with
+// e > 0 has its fp16 parts (written unscaled by the router kernel) rewritten
+// as parts of x 2^-e.  s_m: one LDS word per wave.  Ends with a barrier.
+__device__ inline void decode_token_scale(const TopkArgs& a, int t, uint32_t* s_m) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int per = a.x_f32 ? 4 : 8;                 // elements per 16-byte load
+  const int nch = a.Ho / per;
+  const char* row = reinterpret_cast<const char*>(a.x) + (size_t)t * a.Ho * (a.x_f32 ? 4 : 2);
+  uint32_t m = 0;                                  // largest |x| as bits (non-negative: bit order)
+  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+    const uint4 v = *reinterpret_cast<const uint4*>(row + 16 * (size_t)c);
+    const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m = a.x_f32 ? max(m, q[i] & 0x7fffffffu) : max(m, max((q[i] & 0x7fffu) << 16, q[i] & 0x7fff0000u));
+  }
+  m = wave_max_u32(m);
+  if (lane == 0) s_m[wv] = m;
+  __syncthreads();
+  for (int w = 0; w < nw; ++w) m = max(m, s_m[w]);
+  const int e = token_scale_exp(__uint_as_float(m));
+  if (threadIdx.x == 0) a.w.texp[t] = e;
+  if (e == 0) return;
+  const size_t n = (size_t)a.T * a.H;
+  const float sc = pow2i(-e);
+  for (int h = threadIdx.x; h < a.Ho; h += blockDim.x) {
+    const size_t src = (size_t)t * a.Ho + h;
+    const float v = (a.x_f32 ? reinterpret_cast<const float*>(a.x)[src]
+                             : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[src])) * sc;
+    _Float16 p[NPART];
+    split2(v, p);
+#pragma unroll
+    for (int q = 0; q < NPART; ++q) a.w.xparts[q * n + (size_t)t * a.H + h] = p[q];
+  }
+}
 
 constexpr int TOPK_WAVES = 8;
 
@@ -362,8 +403,10 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void k_topk(TopkArgs a) {
   __shared__ uint32_t c_key[TOPK_WAVES * 64];
   __shared__ float c_val[TOPK_WAVES * 64];
   __shared__ int c_id[TOPK_WAVES * 64];
+  __shared__ uint32_t s_m[TOPK_WAVES];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int E = a.E, k = a.k, t = blockIdx.x;
+  decode_token_scale(a, t, s_m);
   const float* row = a.w.logits + (size_t)t * E;
   const int e0 = wv * 64 * V1;
   uint32_t u[V1];
@@ -428,6 +471,15 @@ __global__ __launch_bounds__(1024) void k_topk_block(const float* rows, size_t s
                                                      int k, int* idx, float* w) {
   const size_t t = blockIdx.x;
   block_topk(rows + t * stride, bias, E, k, idx + t * k, w + t * k);
+}
+
+// the decode path's selection past 64 (as above) and its token scale
+__global__ __launch_bounds__(1024) void k_topk_block_decode(TopkArgs a) {
+  __shared__ uint32_t s_m[16];
+  const int t = blockIdx.x;
+  decode_token_scale(a, t, s_m);
+  block_topk(a.w.logits + (size_t)t * a.E, nullptr, a.E, a.k, a.w.topk_idx + (size_t)t * a.k,
+             a.w.topk_w + (size_t)t * a.k);
 }
 
 // The stable token->expert permutation of the routing (route() only): counts,
@@ -712,6 +764,7 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   // partial sums [GU_SLABS][64 lanes] x 4
   extern __shared__ float4 red4[];
   __shared__ uint64_t s_bits[16][64];                // per wave: the chosen-expert mask
+  __shared__ int s_texp[DECODE_MAX_T];               // the tokens' operand scale exponents
   const int u = blockIdx.y, gp = blockIdx.x;
   const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
   const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
@@ -726,6 +779,7 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   const char* rbase = region + (arow >> 1) * GU_SLOT + 512 * (arow & 1) + 16 * ks;
   const ALane al{rbase + 128 * (arow & 1), rbase - 128 * (arow & 1)};
   reinterpret_cast<uint2*>(region + T * GU_SLOT)[lane] = make_uint2(0u, 0u);   // the zero row
+  const int te = a.w.texp[min(lane, T - 1)];         // lane t < T: token t's scale exponent
   // the first superblock's activation operand does not depend on the expert:
   // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
   int e, U;
@@ -736,14 +790,16 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
     return;
   }
+  if (wv == 0 && lane < T) s_texp[lane] = te;
   if (gp == 0 && wv == 0) {
-    // routing of this active expert for the down kernel
+    // routing of this active expert for the down kernel; the weight of
+    // token t also undoes the 2^-2e of its activations (exact)
     if (lane == 0) {
       a.w.udesc[(size_t)u * DESC] = e;
       a.w.udesc[(size_t)u * DESC + 1] = (int)mask;
       if (u == 0) a.w.meta[0] = U;
     }
-    if (lane < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + lane] = wt;
+    if (lane < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + lane] = wt * pow2i(2 * te);
   }
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
   const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
@@ -781,7 +837,10 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
       g += rg[4 * l0] + rg[4 * l1];
       uu += ru[4 * l0] + ru[4 * l1];
     }
-    const float act = silu_f(g) * uu;
+    // g, uu carry the token's 2^-e: silu of the unscaled gate, and the
+    // activation kept at 2^-2e (exact powers of two)
+    const int te_t = s_texp[t];
+    const float act = silu_f(g * pow2i(te_t)) * uu * pow2i(-te_t);
     _Float16 p[NPART];
     split2(act, p);
     const int i = (GU_GROUPS * gp + gi) * 16 + row;
@@ -1097,9 +1156,10 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
   }
   TopkArgs t;
   t.T = c.T; t.E = L.E; t.k = L.k; t.n_shared = L.n_shared; t.w = W;
+  t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho;
   const int per_wave = (L.E + 64 * TOPK_WAVES - 1) / (64 * TOPK_WAVES);
-  hipError_t e;
-  if (L.k > 64) e = launch_topk_block(W.logits, L.E, nullptr, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
+  hipError_t e = hipSuccess;
+  if (L.k > 64) launch(tr, k_topk_block_decode, dim3(c.T), dim3(1024), 0, s, t);
   else if (per_wave <= 1) e = launch_topk_v1<1>(t, s, tr);
   else if (per_wave <= 2) e = launch_topk_v1<2>(t, s, tr);
   else if (per_wave <= 4) e = launch_topk_v1<4>(t, s, tr);

@@ -22,9 +22,11 @@ struct Work {
   int* slot_tok;      // [Tmax*k]   prefill: sorted slot -> token
   int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
   float* wtab;        // [E+1][8]   decode: routing weight per (active expert, token), 0 if not routed
-  int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill)
+  int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill),
+                      //            meta[2] prefill: some token of the call is scaled (e > 0)
   int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
+  int* texp;          // [Tmax]     the exponent e of each token's operand scale 2^-e
   int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}, in XCD segments,
                       //             each sorted by row class (see k_scan)
   float* act;         // prefill: fp16 SwiGLU rows [slots][I] (same region as actp)
@@ -88,6 +90,9 @@ inline void launch(Tracer* tr, K kernel, dim3 grid, dim3 block, size_t lds, hipS
 hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in, int first_expert,
                          hipStream_t s);
 hipError_t launch_router_split(const Layer& L, hipStream_t s);
+// count (into *bad, device) the canonical blocks whose scale the kernels
+// cannot carry (see k_check_scales)
+hipError_t launch_check_scales(const Layer& L, const uint8_t* canon, int n_records, int* bad, hipStream_t s);
 
 // decode path: router GEMV, top-k (+ the permutation when asked for), then
 // gate/up and down + combine; prepare_decode_kernels raises the gate/up

@@ -87,8 +87,59 @@ struct TopkArgs {
   size_t plane;           // elements between planes
   const float* part;      // [S][T][E] partial logits
   const float* bias;      // [E] or null
+  const void* x;          // [T][Ho] the tokens (bf16, or fp32 when x_f32)
+  int x_f32, H, Ho;
+  uint16_t* x16;          // [T][H] their fp16 rows
   Work w;
 };
+
+// The operand scale of token t (one wave): e from the token's largest
+// magnitude (token_scale_exp); when e > 0 the wave rewrites the token's fp16
+// row as x 2^-e (the router wrote it unscaled) and marks the call scaled
+// (meta[2], cleared by the router kernel, read by the gate/up GEMM).
+__device__ inline void token_scale(const TopkArgs& a, int t) {
+  const int lane = threadIdx.x & 63;
+  const int per = a.x_f32 ? 4 : 8;                 // elements per 16-byte load
+  const int nch = a.Ho / per;
+  const char* row = reinterpret_cast<const char*>(a.x) + (size_t)t * a.Ho * (a.x_f32 ? 4 : 2);
+  uint32_t m = 0;                                  // largest |x| as bits (non-negative: bit order)
+  for (int c0 = 0; c0 < nch; c0 += 4 * 64) {
+    uint4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<const uint4*>(row + 16 * (size_t)min(c0 + 64 * j + lane, nch - 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (a.x_f32) {
+          m = max(m, q[i] & 0x7fffffffu);
+        } else {
+          m = max(m, (q[i] & 0x7fffu) << 16);
+          m = max(m, q[i] & 0x7fff0000u);
+        }
+      }
+    }
+  }
+  const int e = token_scale_exp(__uint_as_float((uint32_t)wave_max_u64(m)));
+  if (lane == 0) a.w.texp[t] = e;
+  if (e == 0) return;
+  if (lane == 0) a.w.meta[2] = 1;
+  const float sc = pow2i(-e);
+  for (int h = 8 * lane; h < a.Ho; h += 8 * 64) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      f[i] = a.x_f32 ? reinterpret_cast<const float*>(a.x)[(size_t)t * a.Ho + h + i]
+                     : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[(size_t)t * a.Ho + h + i]);
+    uint16_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = __builtin_bit_cast(uint16_t, (_Float16)(f[i] * sc));
+    *reinterpret_cast<uint4*>(a.x16 + (size_t)t * a.H + h) =
+        make_uint4(o[0] | (uint32_t)o[1] << 16, o[2] | (uint32_t)o[3] << 16, o[4] | (uint32_t)o[5] << 16,
+                   o[6] | (uint32_t)o[7] << 16);
+  }
+}
 
 // logits of token t for ids lane + 64 i: the partial planes summed in plane
 // order, then the bias (ids past E read id E - 1 and are masked by the caller)
@@ -166,11 +217,11 @@ __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs 
   const int k = a.k, E = a.E;
   static_assert(CT <= 32, "token masks are 32-bit");
   for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
-  if (!a.presel) {
-    for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
-      const int t = tb + tl;
-      if (t < a.T) token_topk(a, t, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
-    }
+  for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
+    const int t = tb + tl;
+    if (t >= a.T) continue;
+    if (!a.presel) token_topk(a, t, sel + tl * k, a.w.topk_w + (size_t)t * k, s_sel[wv]);
+    token_scale(a, t);
   }
   __syncthreads();
   const int nt = min(CT, a.T - tb);
@@ -754,18 +805,32 @@ __device__ inline void gateup_item(const GemmArgs& a, const ItemSrc<NSL>& cur, N
 #pragma unroll
     for (int n = 0; n < NSL; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   gemm_kloop<FMT, MC, true>(cur, next, a.H, As, wv, lane, ar, bc, acc);
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
+  // SwiGLU of this lane's token row 16 m + lane % 16; in a call with scaled
+  // tokens (rare) the sums carry the row's 2^-e: silu of the unscaled gate,
+  // the activation kept at 2^-2e
+  auto swiglu = [&](int m, float sg, float su) __attribute__((always_inline)) {
     const int row = 16 * m + (lane & 15);
 #pragma unroll
     for (int n = 0; n < NSL / 2; ++n) {
       h2_t h[2];
 #pragma unroll
       for (int v = 0; v < 2; ++v)
-        h[v] = h2_t{(_Float16)(silu_fast(acc[m][n][2 * v]) * acc[m][NSL / 2 + n][2 * v]),
-                    (_Float16)(silu_fast(acc[m][n][2 * v + 1]) * acc[m][NSL / 2 + n][2 * v + 1])};
+        h[v] = h2_t{(_Float16)(silu_fast(acc[m][n][2 * v] * sg) * acc[m][NSL / 2 + n][2 * v] * su),
+                    (_Float16)(silu_fast(acc[m][n][2 * v + 1] * sg) * acc[m][NSL / 2 + n][2 * v + 1] * su)};
       stage_put<NC>(stg, row, 16 * (wv * (NSL / 2) + n) + 4 * (lane >> 4),
                     make_uint2(__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1])));
+    }
+  };
+  if (*(cint_ptr)(a.w.meta + 2) == 0) {
+#pragma unroll
+    for (int m = 0; m < MC; ++m) swiglu(m, 1.f, 1.f);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const int slot = slot0 + min(16 * m + (lane & 15), rows - 1);
+      const int tok = slot < a.P ? a.w.slot_tok[slot] : slot - a.P;
+      const int e = a.w.texp[tok];
+      swiglu(m, pow2i(e), pow2i(-e));
     }
   }
   lds_barrier();
@@ -952,6 +1017,7 @@ struct RouterArgs {
   const uint16_t* wlo;    // Wr remainders, operand order
   float* part;            // [S][T][E]
   uint16_t* x16;          // [T][H] the tokens as fp16
+  int* meta;              // meta[2] (the call's scaled-token mark) is cleared here
 };
 
 // fp32 pair -> bf16 pair (RNE) in *hi and the bf16 of the remainders in *lo
@@ -1022,6 +1088,7 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
   const int ne = (a.E + RT_E - 1) / RT_E, nt = (a.T + BM - 1) / BM, total = ne * nt * a.S;
   const int per = (total + 7) >> 3, idx = blockIdx.x >> 3, w = (blockIdx.x & 7) * per + idx;
   if (idx >= per || w >= total) return;
+  if (w == 0 && threadIdx.x == 0) a.meta[2] = 0;        // (the top-k kernel sets it)
   const int ty = w % nt, ex = (w / nt) % ne, kz = w / (nt * ne);
   const int t0 = ty * BM, e0 = ex * RT_E;
   const int kb0 = kz * a.kper, ke = min(a.H, kb0 + a.kper), ns = (ke - kb0) / XBK;
@@ -1194,7 +1261,12 @@ __device__ inline void fused_route_tail(const TopkArgs& a) {
   const int wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int T = a.T, k = a.k, E = a.E;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_tm[e] = 0ull;
-  for (int t = wv; t < T; t += nw) token_topk(a, t, s_sel + t * k, a.w.topk_w + (size_t)t * k, nullptr);
+  if (threadIdx.x == 0) a.w.meta[2] = 0;
+  __syncthreads();
+  for (int t = wv; t < T; t += nw) {
+    token_topk(a, t, s_sel + t * k, a.w.topk_w + (size_t)t * k, nullptr);
+    token_scale(a, t);
+  }
   __syncthreads();
   for (int i = threadIdx.x; i < T * k; i += blockDim.x) {
     const int e = s_sel[i];
@@ -1359,10 +1431,12 @@ __global__ __launch_bounds__(512) void k_combine(CombineArgs a) {
   extern __shared__ int s_cmb[];
   int* s_slot = s_cmb;                                   // [kp]
   float* s_w = reinterpret_cast<float*>(s_cmb + kp);     // [kp]
+  // the expert rows of a scaled token carry 2^-2e: the weights undo it
+  const float tsc = pow2i(2 * a.w.texp[t]);
   for (int j = threadIdx.x; j < kp; j += blockDim.x) {
     const int jj = min(j, k - 1);
     s_slot[j] = a.w.inv[(size_t)t * k + jj];
-    s_w[j] = j < k ? a.w.topk_w[(size_t)t * k + jj] : 0.f;
+    s_w[j] = j < k ? a.w.topk_w[(size_t)t * k + jj] * tsc : 0.f;
   }
   __syncthreads();
   for (int h = threadIdx.x * 8; h < a.Ho; h += blockDim.x * 8) {
@@ -1388,8 +1462,8 @@ __global__ __launch_bounds__(512) void k_combine(CombineArgs a) {
       const uint32_t q[4] = {ys.x, ys.y, ys.z, ys.w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        acc[2 * c] += __uint_as_float(q[c] << 16);
-        acc[2 * c + 1] += __uint_as_float(q[c] & 0xffff0000u);
+        acc[2 * c] = fmaf(tsc, __uint_as_float(q[c] << 16), acc[2 * c]);
+        acc[2 * c + 1] = fmaf(tsc, __uint_as_float(q[c] & 0xffff0000u), acc[2 * c + 1]);
       }
     }
 #pragma unroll
@@ -1531,6 +1605,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
     f.done = L.route_done;
     TopkArgs& t = f.t;
     t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.n_shared = L.n_shared; t.presel = 0;
+    t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = f.x16;
     t.S = 1; t.plane = (size_t)c.T * L.E; t.part = W.logits; t.bias = L.router_b; t.w = W;
     const dim3 grid((L.E + 15) / 16), block(64 * FR_WAVES);
     if (c.x_f32) launch(tr, k_route_fused<true>, grid, block, 0, s, f);
@@ -1552,6 +1627,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   r.whi = L.router_hi; r.wlo = L.router_lo;
   r.part = rp.part;
   r.x16 = rp.x16;
+  r.meta = W.meta;
   const int items = ((L.E + RT_E - 1) / RT_E) * ((c.T + BM - 1) / BM) * S;
   const dim3 grid(8 * ((items + 7) / 8)), block(64 * RT_WAVES);
   if (c.x_f32) launch(tr, k_router<true>, grid, block, 0, s, r);
@@ -1560,6 +1636,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b; t.n_shared = L.n_shared;
   t.presel = L.k > 64;
+  t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = rp.x16;
   if (t.presel) {
     const hipError_t e = launch_topk_block(r.part, L.E, L.router_b, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
     if (e != hipSuccess) return e;

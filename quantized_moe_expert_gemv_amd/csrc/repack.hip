@@ -150,7 +150,39 @@ __global__ void k_router_split(const float* __restrict__ w, uint16_t* __restrict
   lo[i] = f32_to_bf16_rne(v - bf16_to_f32(h));
 }
 
+// Scales the kernels cannot carry: every 16-bit weight operand (the prefill
+// path's dequantised d (q - c) in fp16, and the products the decode path
+// scales in fp32) must stay finite.  fp16 d: NaN or infinite, or above
+// 2^15 (Q2), 2^14 (Q3), 2^11 (Q4, whose 16 d and 24 d are fp16 operands
+// too); MXFP4: e = 255 (NaN) or e > 140 (2^13 and up).  One thread per
+// canonical block; bad blocks are counted in *bad.
+__global__ void k_check_scales(const uint8_t* __restrict__ canon, long long n_blocks, int fmt, int* bad) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_blocks) return;
+  const int bq = canon_block_bytes(fmt);
+  const uint8_t* b = canon + (size_t)i * bq;
+  bool ok;
+  if (fmt == FMT_MXFP4) {
+    const int e = b[bq - 1];
+    ok = e <= 140;
+  } else {
+    const uint32_t h = (uint32_t)b[bq - 2] | ((uint32_t)b[bq - 1] << 8);
+    const uint32_t mag = h & 0x7fffu;
+    const uint32_t lim = fmt == 4 ? 0x6800u : fmt == 3 ? 0x7400u : 0x7800u;   // 2^11, 2^14, 2^15
+    ok = mag <= lim;                             // (NaN and infinity encode above every limit)
+  }
+  if (!ok) atomicAdd(bad, 1);
+}
+
 }  // namespace
+
+hipError_t launch_check_scales(const Layer& L, const uint8_t* canon, int n_records, int* bad, hipStream_t s) {
+  const long long n = (long long)n_records * (canon_expert_bytes(L.fmt, L.Ho, L.Io) / canon_block_bytes(L.fmt));
+  if (n == 0) return hipSuccess;
+  const int bs = 256;
+  hipLaunchKernelGGL(k_check_scales, dim3((unsigned)((n + bs - 1) / bs)), dim3(bs), 0, s, canon, n, L.fmt, bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_repack(const Layer& L, const uint8_t* canon, int n_experts_in, int first_expert,
                          hipStream_t s) {

@@ -85,7 +85,7 @@ int check_config(const strata_moe_config* c) {
 
 struct WsPlan {
   size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, slot_tok, udesc, wtab, meta,
-      chunk_base, pair_rank, tiles, act, xparts, xpad, y, total;
+      chunk_base, pair_rank, texp, tiles, act, xparts, xpad, y, total;
   int nchunks, max_tiles;
 };
 
@@ -118,6 +118,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.meta = take(16 * 4);
   p.chunk_base = take(E * (size_t)p.nchunks * 4);
   p.pair_rank = take(P * 4);
+  p.texp = take(T * 4);
   p.tiles = take((size_t)p.max_tiles * 16);
   const size_t Td = T < STRATA_DECODE_MAX_T ? T : STRATA_DECODE_MAX_T;
   const size_t act_prefill = slots * I * 2;                                   // bf16 rows
@@ -146,6 +147,7 @@ Work layout_work(uint8_t* ws, const WsPlan& p) {
   W.meta = reinterpret_cast<int*>(ws + p.meta);
   W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
   W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
+  W.texp = reinterpret_cast<int*>(ws + p.texp);
   W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
   W.act = reinterpret_cast<float*>(ws + p.act);
   W.actp = reinterpret_cast<_Float16*>(ws + p.act);
@@ -363,11 +365,18 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
   h->W = layout_work(ws, p);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  int* bad_scales = h->W.meta + 4;
   const char* step = "zeroing counters";
   static_assert(STRATA_FUSED_ROUTE == STRATA_FUSED_ROUTE_FLAG && STRATA_SPLIT_ROUTE == STRATA_SPLIT_ROUTE_FLAG,
                 "flag bits");
   hipError_t e = hipMemsetAsync(ws + p.meta, 0, 16 * 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(state, 0, STATE_BYTES, s);
+  if (e == hipSuccess) {
+    step = "scale check";
+    e = launch_check_scales(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, bad_scales, s);
+    if (e == hipSuccess && cfg->n_shared)
+      e = launch_check_scales(L, static_cast<const uint8_t*>(shared_canon), 1, bad_scales, s);
+  }
   if (e == hipSuccess) {
     step = "expert repack";
     e = launch_repack(L, static_cast<const uint8_t*>(experts_canon), cfg->n_experts, 0, s);
@@ -396,12 +405,23 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
     step = "stream synchronize";
     e = hipStreamSynchronize(s);
   }
+  int n_bad = 0;
+  if (e == hipSuccess) {
+    step = "scale check result";
+    e = hipMemcpy(&n_bad, bad_scales, sizeof n_bad, hipMemcpyDeviceToHost);
+  }
   if (e != hipSuccess) {
     (void)hipGetLastError();
     delete h;
     char what[64];
     snprintf(what, sizeof what, "create (%s)", step);
     return hip_fail(e, what);
+  }
+  if (n_bad) {
+    delete h;
+    return fail(STRATA_E_UNSUPPORTED,
+                "%d block scale(s) outside what the 16-bit operands carry (fp16 d NaN, infinite or above "
+                "2^15 / 2^14 / 2^11 for Q2 / Q3 / Q4; MXFP4 e = 255 or above 140)", n_bad);
   }
   *out = h;
   return ok();

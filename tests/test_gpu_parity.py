@@ -292,6 +292,58 @@ def test_one_launch_route_refuses_large_calls(B):
     assert e.value.code == B.STRATA_E_UNSUPPORTED
 
 
+@pytest.mark.parametrize("fmt,n_shared", [(2, 0), (5, 1)])
+@pytest.mark.parametrize("factor", [1e3, 1e6, 2.0 ** 40])
+@pytest.mark.parametrize("T", [3, 40])
+def test_tokens_far_beyond_the_fp16_range(B, fmt, n_shared, factor, T):
+    """Tokens scaled up to 2^40 (bf16 and fp32): the 16-bit operands hold each
+    token times a power of two chosen from its largest magnitude, the
+    activations carry its square, and the weights undo both, so decode and
+    grouped outputs still match the oracle row by row (the selection of
+    such tokens is set by their router logits alone; the bias is negligible
+    beside them)."""
+    hl, layer = tiny(fmt, n_shared=n_shared)
+    bits, xf = tokens(hl, 1300 + T, T)
+    xs = xf * factor
+    xb = torch.from_numpy(G.f32_to_bf16_bits(xs.astype(np.float32)).astype(np.int16)).to(DEV).view(torch.bfloat16)
+    xsb = G.bf16_bits_to_f32(G.f32_to_bf16_bits(xs.astype(np.float32))).astype(np.float64)
+    tol = DECODE_TOL if T <= 8 else PREFILL_TOL
+    ref, _ = hl.oracle(xsb)
+    # ids exact; the grouped path's router (bf16 hi/lo products) is accurate to
+    # about 2^-16 of the logits, so near-equal logits of a few thousand move
+    # their softmax weights by ~1e-4
+    check_route(layer, hl, xb, xsb, w_atol=2e-6 if T <= 8 else 5e-5 * max(1.0, factor / 100))
+    check_rows(layer.forward(xb).cpu().numpy(), ref, tol, f"x * {factor:g} bf16 fmt {fmt} T {T}")
+    x32 = torch.from_numpy(xs.astype(np.float32)).to(DEV)
+    ref32, _ = hl.oracle(xs.astype(np.float32).astype(np.float64))
+    check_rows(layer.forward(x32).cpu().numpy(), ref32, tol, f"x * {factor:g} fp32 fmt {fmt} T {T}")
+
+
+@pytest.mark.parametrize("fmt,scale", [(2, np.inf), (2, np.nan), (2, 40000.0), (3, 20000.0), (4, 4096.0),
+                                       (5, 141), (5, 200), (5, 255)])
+def test_block_scales_the_operands_cannot_carry_are_refused(B, fmt, scale):
+    """A block scale that no 16-bit weight operand can hold (fp16 d NaN,
+    infinite or beyond the format's limit; MXFP4 scale byte 255 or above 140)
+    makes create fail with STRATA_E_UNSUPPORTED; the limit itself is
+    accepted."""
+    hl = HostLayer(51, 0, 256, 256, 8, 2, fmt, True)
+    canon = hl.canon.reshape(hl.E, -1, 17 if fmt == 5 else 2 + 4 * fmt).copy()
+    good = canon.copy()
+    if fmt == 5:
+        canon[3, 5, 16] = scale
+        good[3, 5, 16] = 140
+    else:
+        canon[3, 5, -2:] = np.array([scale], dtype="<f2").view(np.uint8)
+        good[3, 5, -2:] = np.array([{2: 32768.0, 3: 16384.0, 4: 2048.0}[fmt]], dtype="<f2").view(np.uint8)
+    cfg = B.make_config(hl.H, hl.I, hl.E, hl.k, 0, fmt, 16)
+    wr = torch.from_numpy(hl.wr).to(DEV)
+    b = torch.from_numpy(hl.b).to(DEV)
+    with pytest.raises(B.StrataError) as e:
+        B.StrataMoE(cfg, wr, b, torch.from_numpy(canon.reshape(-1)).to(DEV))
+    assert e.value.code == B.STRATA_E_UNSUPPORTED and "scale" in str(e.value)
+    B.StrataMoE(cfg, wr, b, torch.from_numpy(good.reshape(-1)).to(DEV)).close()
+
+
 @pytest.mark.parametrize("flags_name", ["STRATA_ADD_INPUT", "STRATA_ACCUMULATE"])
 @pytest.mark.parametrize("T", [2, 40])
 def test_residual_flags(B, flags_name, T):
