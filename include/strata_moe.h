@@ -89,7 +89,7 @@ enum {
 
 /* Calls with T <= STRATA_DECODE_MAX_T take the decode (GEMV) path unless
  * STRATA_FORCE_PREFILL is given; larger T take the grouped-GEMM path. */
-#define STRATA_DECODE_MAX_T 8
+#define STRATA_DECODE_MAX_T 16
 /* Grouped-path calls of at most this many tokens (and E <= 512, k <= 64)
  * route in one launch unless STRATA_SPLIT_ROUTE is given. */
 #define STRATA_FUSED_ROUTE_DEFAULT_T 0

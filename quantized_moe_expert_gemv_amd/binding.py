@@ -19,7 +19,7 @@ STRATA_Q2, STRATA_Q3, STRATA_Q4, STRATA_MXFP4 = 2, 3, 4, 5
 STRATA_BF16, STRATA_FP32 = 0, 1
 STRATA_ACCUMULATE, STRATA_ADD_INPUT, STRATA_FORCE_DECODE, STRATA_FORCE_PREFILL = 1, 2, 4, 8
 STRATA_FUSED_ROUTE, STRATA_SPLIT_ROUTE = 16, 32
-STRATA_DECODE_MAX_T = 8
+STRATA_DECODE_MAX_T = 16
 STRATA_FUSED_ROUTE_DEFAULT_T = 0
 
 EXPORTS = ("strata_moe_expert_bytes", "strata_moe_packed_bytes", "strata_moe_workspace_bytes",

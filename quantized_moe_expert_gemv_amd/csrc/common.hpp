@@ -35,7 +35,8 @@ constexpr int WAVE = 64;
 constexpr int GROUP_ROWS = 16;
 constexpr int SB_WEIGHTS = 256;        // weights per superblock (8 blocks)
 constexpr int BLOCK_W = 32;            // weights per quantised block
-constexpr int DECODE_MAX_T = 8;
+constexpr int DECODE_MAX_T = 16;      // tokens of one decode call (one pass over the weights)
+constexpr int DECODE_NARROW_T = 8;     // up to here the A operand holds 2 parts x 8 tokens
 
 template <int FMT> struct Fmt;
 template <> struct Fmt<2> {

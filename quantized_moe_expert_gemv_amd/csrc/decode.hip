@@ -1,4 +1,4 @@
-// Decode path (T <= 8 tokens): the per-token expert GEMV regime of the
+// Decode path (T <= 16 tokens): the per-token expert GEMV regime of the
 // pages (ai-coding.wiselychen.com "Strata two weeks", section 成功思路一: per
 // layer the GPU runs the router, picks 10 experts and computes them; the
 // expert step is bound by the bytes of expert weights read), including the
@@ -32,8 +32,10 @@
 // accumulation): the code q of a weight becomes the fp16 value q (2-bit codes
 // through the FP4->fp16 conversion, Q3 as a 2-bit and a 1-bit plane) or
 // (q - 8)/16 (Q4, magic-number construction), exactly; the activations enter
-// as two fp16 parts (16 A-operand rows: 2 parts x up to 8 tokens, so every
-// decode call is one pass over the weights), which carry 22 significant bits
+// as two fp16 parts (16 A-operand rows: 2 parts x up to 8 tokens; from 9 to
+// 16 tokens the rows are the tokens and each part is its own MFMA into the
+// same result, so every decode call is one pass over the weights), which
+// carry 22 significant bits
 // (bf16 inputs exactly); the per-block offset -c * sum_j x_j comes from one
 // extra MFMA against a constant operand.  Every product is exact; the fp32
 // accumulation and the 2^-22 activation split are the only roundings.  The
@@ -51,7 +53,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int DESC = 2;    // ints per active expert for the down kernel: expert id, token mask
-constexpr int WTAB = 8;    // routing weights per active expert, indexed by token
+constexpr int WTAB = 8;    // routing weights per active expert, indexed by token (T <= 8)
+constexpr int WTAB16 = 16; // the same for 9..16 tokens
 constexpr int NPART = 2;   // fp16 parts of an fp32 activation
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past every record: the load returns 0
 
@@ -189,18 +192,22 @@ __device__ inline f32x4 block_product(const f16x8& a, const Codes<FMT>& c, const
   }
 }
 
-// the block offset -c * sum_j x_j, for every output column
+// the block offset -c * sum_j x_j, for every output column, added to acc
 template <int FMT>
-__device__ inline f32x4 block_offset(const f16x8& a) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+__device__ inline f32x4 block_offset_acc(const f16x8& a, const f32x4& acc) {
   if constexpr (FMT == 4 || FMT == FMT_MXFP4) {   // no offset term (Q4 folds it into the operand)
-    return z;
+    return acc;
   } else {
     f16x8 cst;
 #pragma unroll
     for (int i = 0; i < 8; ++i) cst[i] = (_Float16)(-Fmt<FMT>::c);
-    return mfma(a, cst, z);
+    return mfma(a, cst, acc);
   }
+}
+template <int FMT>
+__device__ inline f32x4 block_offset(const f16x8& a) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return block_offset_acc<FMT>(a, z);
 }
 
 
@@ -213,6 +220,7 @@ struct RouteArgs {
   int Ho;                    // the layer's hidden width
   float* logits;
   _Float16* xparts;          // [2][T][H], zero past Ho (x 2^-e, see k_topk)
+  int* part1;                // set to 1 when some token has a nonzero second part
 };
 
 constexpr int ROUTE_WAVES = 4;
@@ -229,19 +237,24 @@ __device__ inline float4 x_quad(const void* x, int H, int t, int q) {
 // Expert rows per router workgroup: every wave reads its columns of the
 // tokens once for all of them (fewer register batches for more tokens)
 constexpr int route_rows(int T) { return T <= 4 ? 2 : 1; }
+// float4 columns per lane in flight together (the token columns of 16 tokens
+// take 64 registers per column)
+constexpr int route_batch(int T) { return T <= 8 ? ROUTE_BATCH : 2; }
 
 // route_rows(T) expert rows per workgroup; its waves split the rows into
 // float4 columns (strided, so every load instruction of a wave reads 1 KiB
 // contiguously) and meet in LDS.  Each workgroup also writes its slice of the
-// tokens as fp16 parts.  TT = T and the input type are template constants so
+// tokens as fp16 parts.  TT and the input type are template constants so
 // that every load is unconditional (clamped into bounds) and all of a batch
-// are in flight together.
+// are in flight together: TT = T up to 8, TT = 16 for 9..16 tokens (tokens
+// past T repeat the last one: loaded and computed, not stored).
 template <int TT, bool XF32>
 __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
   constexpr int RR = route_rows(TT);
+  constexpr int RB = route_batch(TT);
   __shared__ float part[ROUTE_WAVES][RR][TT];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int H = a.Ho, E = a.E, e0 = blockIdx.x * RR;
+  const int H = a.Ho, E = a.E, e0 = blockIdx.x * RR, T = a.T;
   const int nq = H >> 2;
   const float4* rows[RR];
 #pragma unroll
@@ -252,19 +265,19 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
   for (int r = 0; r < RR; ++r)
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
-  for (int q0 = tid; q0 < nq; q0 += ROUTE_BATCH * 64 * ROUTE_WAVES) {
-    float4 w[ROUTE_BATCH][RR];
-    float4 xv[ROUTE_BATCH][TT];
+  for (int q0 = tid; q0 < nq; q0 += RB * 64 * ROUTE_WAVES) {
+    float4 w[RB][RR];
+    float4 xv[RB][TT];
 #pragma unroll
-    for (int j = 0; j < ROUTE_BATCH; ++j) {
+    for (int j = 0; j < RB; ++j) {
       const int q = min(q0 + j * 64 * ROUTE_WAVES, nq - 1);
 #pragma unroll
       for (int r = 0; r < RR; ++r) w[j][r] = rows[r][q];
 #pragma unroll
-      for (int t = 0; t < TT; ++t) xv[j][t] = x_quad<XF32>(a.x, H, t, q);
+      for (int t = 0; t < TT; ++t) xv[j][t] = x_quad<XF32>(a.x, H, TT <= DECODE_NARROW_T ? t : min(t, T - 1), q);
     }
 #pragma unroll
-    for (int j = 0; j < ROUTE_BATCH; ++j) {
+    for (int j = 0; j < RB; ++j) {
       const float m = (q0 + j * 64 * ROUTE_WAVES < nq) ? 1.f : 0.f;   // clamped duplicates count 0
 #pragma unroll
       for (int r = 0; r < RR; ++r)
@@ -288,7 +301,8 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
   // this workgroup's slice of the token rows as fp16 parts [part][t][a.H]
   // (columns past the layer's width are zero); the top-k kernel rewrites the
   // rows of a token that needs an operand scale (rare)
-  const int Hp = a.H, n = TT * Hp, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
+  const int Hp = a.H, n = T * Hp, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
+  bool nz = false;
   for (int i = b * chunk + tid; i < min(n, (b + 1) * chunk); i += blockDim.x) {
     const int t = i / Hp, h = i - t * Hp;
     const int src = t * H + min(h, H - 1);
@@ -299,14 +313,16 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     split2(v, p);
 #pragma unroll
     for (int q = 0; q < NPART; ++q) a.xparts[(size_t)q * n + i] = p[q];
+    nz |= p[1] != (_Float16)0.0f;
   }
+  if (__ballot(nz) && lane == 0) *a.part1 = 1;
   __syncthreads();
   if (tid < RR * TT) {
     const int r = tid / TT, t = tid - r * TT, e = e0 + r;
     float s = 0.f;
 #pragma unroll
     for (int w = 0; w < ROUTE_WAVES; ++w) s += part[w][r][t];
-    if (e < E) a.logits[(size_t)t * E + e] = s + (a.bias ? a.bias[e] : 0.f);
+    if (e < E && t < T) a.logits[(size_t)t * E + e] = s + (a.bias ? a.bias[e] : 0.f);
   }
 }
 
@@ -378,6 +394,7 @@ __device__ inline void decode_token_scale(const TopkArgs& a, int t, uint32_t* s_
   const int e = token_scale_exp(__uint_as_float(m));
   if (threadIdx.x == 0) a.w.texp[t] = e;
   if (e == 0) return;
+  bool nz = false;
   const size_t n = (size_t)a.T * a.H;
   const float sc = pow2i(-e);
   for (int h = threadIdx.x; h < a.Ho; h += blockDim.x) {
@@ -388,7 +405,9 @@ __device__ inline void decode_token_scale(const TopkArgs& a, int t, uint32_t* s_
     split2(v, p);
 #pragma unroll
     for (int q = 0; q < NPART; ++q) a.w.xparts[q * n + (size_t)t * a.H + h] = p[q];
+    nz |= p[1] != (_Float16)0.0f;
   }
+  if (__ballot(nz) && (threadIdx.x & 63) == 0) a.w.meta[3] = 1;
 }
 
 constexpr int TOPK_WAVES = 8;
@@ -659,25 +678,45 @@ template <int FMT, int G> struct GuStage {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// an empty asm that takes and returns every register of a stage: values
+// computed from it before cannot be reused after
+__device__ inline void opaque(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+__device__ inline void opaque(uint2& v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
+__device__ inline void opaque(Codes<2>& c) { opaque(c.lo); }
+__device__ inline void opaque(Codes<3>& c) { opaque(c.lo); opaque(c.hi); }
+__device__ inline void opaque(Codes<4>& c) { opaque(c.v0); opaque(c.v1); }
+__device__ inline void opaque(Codes<5>& c) { opaque(c.v0); opaque(c.v1); }
+template <int FMT, int G>
+__device__ inline void opaque(GuStage<FMT, G>& st) {
+#pragma unroll
+  for (int s = 0; s < 2 * G; ++s) { opaque(st.cd[s]); opaque(st.sc[s]); }
+}
+
 // The token rows of superblock sb in this wave's LDS region, compact: row
-// r = q T + t (part q, token t) holds the superblock's 512 bytes of that row;
+// r = q T + t (part q, token t, T <= 16) holds the superblock's 512 bytes of that row;
 // rows 2 i and 2 i + 1 come from one buffer->LDS load (1 KiB, lane j's 16
 // bytes land at 16 j) into slot i of the region (slots 1040 bytes apart).
 // Row 2 i + h keeps its 16-byte chunk g at 512 h + 16 (g ^ 8 h) of the slot,
 // so the 16 rows one operand read touches (a 64-byte block of every row)
 // fall into distinct LDS banks for T <= 8.  Slot T holds a row of zeros for
 // the A-operand rows of tokens past T.  T loads per superblock instead of 8
-// for a 16-row operand.
+// (or 16) for a 16-row operand.
 constexpr int GU_SLOT = 1040;
+constexpr int GU_MAX_WAVES = 10;   // gate/up waves per workgroup
+// dynamic LDS ceiling of the gate/up kernels: the CU's 160 KiB less their
+// static arrays (chosen-expert masks, scale exponents)
+constexpr size_t GU_DYN_LDS = 160 * 1024 - (GU_MAX_WAVES * 64 * 8 + 16 * 4 + 64);
 
 __device__ inline int gu_region_bytes(int T) { return max(8192, (T + 1) * GU_SLOT); }
 
-__device__ inline void gu_aload_lds(rsrc_t xr, int T, int H, int sb, int lane, char* region) {
+// (n row pairs from byte base of the token parts: base 0 and n = T for the
+// rows of both parts; base = part 1's plane for its rows alone)
+__device__ inline void gu_aload_lds(rsrc_t xr, int n, int H, int sb, int lane, char* region, uint32_t base = 0) {
   const int h = lane >> 5, g = (lane & 31) ^ (8 * h);
-  for (int i = 0; i < T; ++i)
+  for (int i = 0; i < n; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(region + i * GU_SLOT), 16,
-                                             (uint32_t)((2 * i + h) * 2 * H + 16 * g), (uint32_t)sb * SB_WEIGHTS * 2,
-                                             0, 0);
+                                             base + (uint32_t)((2 * i + h) * 2 * H + 16 * g),
+                                             (uint32_t)sb * SB_WEIGHTS * 2, 0, 0);
 }
 
 // vector-memory instructions gu_load issues (codes, then the scales, per slab)
@@ -688,6 +727,11 @@ constexpr int gu_load_count() { return 2 * G * (FMT == 2 ? 2 : 3); }
 // h = arow % 2), chunk 4 BB + ks stored at 16 ((4 BB + ks) ^ 8 h); as BB ^ 2 h
 // = BB + 2 h or BB - 2 h by bit 1 of BB, two per-lane bases cover every BB
 struct ALane { const char* plus; const char* minus; };
+// the lane's A-operand bases for LDS row arow of a wave region, K-slice ks
+__device__ inline ALane a_lane(const char* region, int arow, int ks) {
+  const char* rbase = region + (arow >> 1) * GU_SLOT + 512 * (arow & 1) + 16 * ks;
+  return ALane{rbase + 128 * (arow & 1), rbase - 128 * (arow & 1)};
+}
 template <int BB>
 __device__ inline const uint4* a_operand(const ALane& al) {
   return reinterpret_cast<const uint4*>(((BB >> 1) & 1 ? al.minus : al.plus) + 64 * BB);
@@ -757,13 +801,20 @@ __device__ inline void gu_compute(const GuStage<FMT, G>& st, const ALane& al, fl
   gu_compute_pairs<FMT, G, G / 2, G / 2>(st, al, acc);
 }
 
-template <int FMT, int G>
-__global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
+// WIDE (9..16 tokens, or fewer when k_down's LDS cannot hold the call): A
+// rows = the 16 tokens, the wave region holds the part-0 rows of the
+// superblock, and a call with a nonzero second part (flag meta[3], set by
+// the router and token-scale kernels) takes a second pass over the same
+// weights with the part-1 rows: bf16 tokens rarely have one.  The
+// activations are stored [active expert][token][part][I] for k_down16.
+template <int FMT, int G, bool WIDE>
+__global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
   constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
+  constexpr int WT = WIDE ? WTAB16 : WTAB;
   // per wave gu_region_bytes(T) of LDS: its superblock's token rows, then its
   // partial sums [GU_SLABS][64 lanes] x 4
   extern __shared__ float4 red4[];
-  __shared__ uint64_t s_bits[16][64];                // per wave: the chosen-expert mask
+  __shared__ uint64_t s_bits[GU_MAX_WAVES][64];      // per wave: the chosen-expert mask
   __shared__ int s_texp[DECODE_MAX_T];               // the tokens' operand scale exponents
   const int u = blockIdx.y, gp = blockIdx.x;
   const int H = a.H, I = a.I, T = a.T, nsb = H / SB_WEIGHTS;
@@ -771,14 +822,16 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = lane >> 4;                          // K-slice
   const rsrc_t xr = make_rsrc(a.w.xparts, (uint32_t)(NPART * T * H * 2));
-  const int wreg = gu_region_bytes(T);
+  const int npr = WIDE ? (T + 1) / 2 : T;          // row-pair loads per staging
+  const int wreg = gu_region_bytes(npr);
   char* region = reinterpret_cast<char*>(red4) + wv * wreg;
   // A row (part, token) of this lane: its token row, the zero row past T
-  const int tok = arow_token(lane);
-  const int arow = tok < T ? arow_part(lane) * T + tok : 2 * T;
-  const char* rbase = region + (arow >> 1) * GU_SLOT + 512 * (arow & 1) + 16 * ks;
-  const ALane al{rbase + 128 * (arow & 1), rbase - 128 * (arow & 1)};
-  reinterpret_cast<uint2*>(region + T * GU_SLOT)[lane] = make_uint2(0u, 0u);   // the zero row
+  // (WIDE: row token lane % 16 of the staged part)
+  const int tok = WIDE ? (lane & 15) : arow_token(lane);
+  const int arow = tok < T ? (WIDE ? 0 : arow_part(lane)) * T + tok : 2 * npr;
+  const ALane al = a_lane(region, arow, ks);
+  reinterpret_cast<uint2*>(region + npr * GU_SLOT)[lane] = make_uint2(0u, 0u);   // the zero row
+  const int part1 = WIDE ? __builtin_amdgcn_readfirstlane(a.w.meta[3]) : 0;
   const int te = a.w.texp[min(lane, T - 1)];         // lane t < T: token t's scale exponent
   // the first superblock's activation operand does not depend on the expert:
   // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
@@ -786,7 +839,7 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   uint32_t mask;
   float wt;
   if (!wave_route(a, u, s_bits[wv], e, mask, U, wt,
-                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, T, H, wv, lane, region); })) {
+                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, npr, H, wv, lane, region); })) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
     return;
   }
@@ -799,7 +852,7 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
       a.w.udesc[(size_t)u * DESC + 1] = (int)mask;
       if (u == 0) a.w.meta[0] = U;
     }
-    if (lane < DECODE_MAX_T) a.w.wtab[(size_t)u * WTAB + lane] = wt * pow2i(2 * te);
+    if (lane < WT) a.w.wtab[(size_t)u * WT + lane] = wt * pow2i(2 * te);
   }
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
   const uint32_t up_base = (uint32_t)up_off(FMT, H, I);
@@ -812,11 +865,21 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   for (int sb = wv; sb < nsb; sb += nw) {
     // the activation operand first (the first one is already requested),
     // then the weights; the compute waits for each part as it needs it
-    if (sb > wv) gu_aload_lds(xr, T, H, sb, lane, region);
+    if (sb > wv) gu_aload_lds(xr, npr, H, sb, lane, region);
     __builtin_amdgcn_sched_barrier(0);
     GuStage<FMT, G> st;
     gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
     gu_compute<FMT, G>(st, al, acc);
+    if (WIDE && part1) {
+      // the part-1 rows into the region once the part-0 operand reads are
+      // done, then the same weights again (converted afresh: opaque() keeps
+      // the compiler from holding every converted operand of the first pass)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      gu_aload_lds(xr, npr, H, sb, lane, region, (uint32_t)(T * H * 2));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      opaque(st);
+      gu_compute<FMT, G>(st, al, acc);
+    }
   }
   // raw 16x16 results to this wave's LDS region (its operand is consumed)
   float4* dst = reinterpret_cast<float4*>(region) + lane;
@@ -827,15 +890,21 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
   for (int idx = threadIdx.x; idx < 16 * GU_GROUPS * T; idx += blockDim.x) {
     const int row = idx & 15, gi = (idx >> 4) % GU_GROUPS, t = idx / (16 * GU_GROUPS);
     if (!((mask >> t) & 1u)) continue;
-    // D row (part q, token t) sits in lane 16 (2q + t / 4) + row, element t % 4
+    // D row (part q, token t) sits in lane 16 (2q + t / 4) + row, element
+    // t % 4; WIDE: D row t (both parts) in lane 16 (t / 4) + row
     const int l0 = 16 * (t >> 2) + row, l1 = l0 + 32, v = t & 3;
     float g = 0.f, uu = 0.f;
     for (int w = 0; w < nw; ++w) {
       const float* rw = reinterpret_cast<const float*>(reinterpret_cast<const char*>(red4) + w * wreg);
       const float* rg = rw + (size_t)gi * 256 + v;
       const float* ru = rw + (size_t)(GU_GROUPS + gi) * 256 + v;
-      g += rg[4 * l0] + rg[4 * l1];
-      uu += ru[4 * l0] + ru[4 * l1];
+      if constexpr (WIDE) {
+        g += rg[4 * l0];
+        uu += ru[4 * l0];
+      } else {
+        g += rg[4 * l0] + rg[4 * l1];
+        uu += ru[4 * l0] + ru[4 * l1];
+      }
     }
     // g, uu carry the token's 2^-e: silu of the unscaled gate, and the
     // activation kept at 2^-2e (exact powers of two)
@@ -845,7 +914,11 @@ __global__ __launch_bounds__(640) void k_gateup(ExpertArgs a) {
     split2(act, p);
     const int i = (GU_GROUPS * gp + gi) * 16 + row;
 #pragma unroll
-    for (int q = 0; q < NPART; ++q) a.w.actp[(((size_t)u * NPART + q) * T + t) * I + i] = p[q];
+    for (int q = 0; q < NPART; ++q) {
+      // [active expert][part][token][I], WIDE: [active expert][token][part][I]
+      const size_t row = WIDE ? ((size_t)u * T + t) * NPART + q : ((size_t)u * NPART + q) * T + t;
+      a.w.actp[row * I + i] = p[q];
+    }
   }
 }
 
@@ -1014,6 +1087,224 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
   }
 }
 
+// down + weighted combine for 9..16 tokens (and for fewer when k_down's LDS
+// cannot hold the call): the work split of k_down (one 16-row group of H
+// per workgroup, waves taking (active expert, superblock) units two at a
+// time).  A row = token lane % 16, one operand per fp16 part.  Only the rows
+// of tokens routed to the unit's expert are staged: one buffer->LDS load of
+// 1 KiB per token (its two parts are adjacent in the activation buffer,
+// [active expert][token][part][I]) into the next free slot; lanes of other
+// tokens read the wave's zero row.  A unit stages its first DN16_SLOTS
+// routed tokens with its own loads (always DN16_SLOTS of them, the unused
+// ones past the end of the buffer: a fixed count keeps the waits static);
+// an expert with more routed tokens takes further passes over the same
+// weights, each staging the next DN16_SLOTS (the rows of each token are
+// fixed, so the passes add up in one accumulator).
+constexpr int DN16_DEPTH = 2;
+constexpr int DN16_SLOTS = 4;
+constexpr int dn16_wave_bytes() { return (DN16_DEPTH * DN16_SLOTS + 1) * GU_SLOT; }
+
+template <int FMT> struct DownUnit16 {
+  Codes<FMT> cd;
+  uint4 sc;
+};
+
+// vector-memory instructions of one unit: the token rows, then codes and scales
+template <int FMT>
+constexpr int dn16_load_count() { return DN16_SLOTS + (FMT == 2 ? 2 : 3); }
+
+// Token rows of ranks first .. first + DN16_SLOTS - 1 among the tokens of
+// mask (expert u, superblock sb) into the slots at slot; ranks past the
+// last routed token load from past the end of the buffer.
+__device__ inline void down16_rows(const ExpertArgs& a, int u, int sb, uint32_t mask, int first, char* slot) {
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, gch = (lane & 31) ^ (8 * h);
+  const rsrc_t ar = make_rsrc(a.w.actp, a.actp_bytes);
+  uint32_t m = mask;
+  for (int r = 0; r < first; ++r) m &= m - 1u;
+#pragma unroll
+  for (int j = 0; j < DN16_SLOTS; ++j) {
+    const int t = m ? __builtin_ctz(m) : 0;
+    // rows (u, t, part 0) and (u, t, part 1): 512 bytes of superblock sb each
+    const uint32_t off = m ? (uint32_t)((((size_t)u * a.T + t) * NPART * a.I + (size_t)sb * SB_WEIGHTS) * 2 +
+                                        (size_t)h * a.I * 2 + 16 * gch)
+                           : OOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(slot + j * GU_SLOT), 16, off, 0, 0, 0);
+    m &= m - 1u;
+  }
+}
+
+template <int FMT>
+__device__ inline void down16_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, char* slot,
+                                   DownUnit16<FMT>& du) {
+  const int lane = threadIdx.x & 63, r = lane & 15;
+  const int u = unit / nsb, sb = unit - u * nsb;
+  const int e = __builtin_amdgcn_readfirstlane(ldesc[DESC * u]);
+  const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[DESC * u + 1]);
+  down16_rows(a, u, sb, mask, 0, slot);
+  const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
+  const uint32_t soff = (uint32_t)(down_off(FMT, a.H, a.I) + ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256));
+  bload_codes<FMT>(wr, soff, lane, du.cd);
+  du.sc = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
+}
+
+// acc += this unit's 16x16 product for the tokens staged in the slots (A
+// row = token lane % 16, its two parts from al0 / al1)
+template <int FMT>
+__device__ inline void down16_product(const DownUnit16<FMT>& du, const ALane& al0, const ALane& al1, float* acc) {
+  f32x4 dd[2];
+  f16x8 a0[8], a1[8];
+  a0[0] = as_f16x8(*a_operand<0>(al0)); a0[1] = as_f16x8(*a_operand<1>(al0));
+  a0[2] = as_f16x8(*a_operand<2>(al0)); a0[3] = as_f16x8(*a_operand<3>(al0));
+  a0[4] = as_f16x8(*a_operand<4>(al0)); a0[5] = as_f16x8(*a_operand<5>(al0));
+  a0[6] = as_f16x8(*a_operand<6>(al0)); a0[7] = as_f16x8(*a_operand<7>(al0));
+  a1[0] = as_f16x8(*a_operand<0>(al1)); a1[1] = as_f16x8(*a_operand<1>(al1));
+  a1[2] = as_f16x8(*a_operand<2>(al1)); a1[3] = as_f16x8(*a_operand<3>(al1));
+  a1[4] = as_f16x8(*a_operand<4>(al1)); a1[5] = as_f16x8(*a_operand<5>(al1));
+  a1[6] = as_f16x8(*a_operand<6>(al1)); a1[7] = as_f16x8(*a_operand<7>(al1));
+  __builtin_amdgcn_sched_barrier(0);
+#define STRATA_BLOCK(BB)                                                          \
+  {                                                                               \
+    f32x4 d = block_offset_acc<FMT>(a1[BB], block_offset<FMT>(a0[BB]));           \
+    d = block_product<FMT, BB>(a0[BB], du.cd, d);                                 \
+    dd[BB & 1] = block_product<FMT, BB>(a1[BB], du.cd, d);                        \
+    if (BB > 0) {                                                                 \
+      const float ds = block_scale<FMT, (BB > 0 ? BB - 1 : 0)>(du.sc);            \
+      _Pragma("unroll") for (int v = 0; v < 4; ++v)                               \
+        acc[v] = fmaf(ds, dd[(BB - 1) & 1][v], acc[v]);                           \
+    }                                                                             \
+  }
+  STRATA_BLOCK(0) STRATA_BLOCK(1) STRATA_BLOCK(2) STRATA_BLOCK(3)
+  STRATA_BLOCK(4) STRATA_BLOCK(5) STRATA_BLOCK(6) STRATA_BLOCK(7)
+#undef STRATA_BLOCK
+  const float ds = block_scale<FMT, 7>(du.sc);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(ds, dd[1][v], acc[v]);
+}
+
+// dynamic LDS of k_down16: the routing table, partial sums, staged rows
+inline size_t down16_lds(int umax) {
+  return (((size_t)umax * (DESC + WTAB16) * 4 + 15) & ~(size_t)15) + (size_t)DN_WAVES * 1024 +
+         (size_t)DN_WAVES * dn16_wave_bytes();
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
+  extern __shared__ float4 lds_dn4[];
+  char* lds = reinterpret_cast<char*>(lds_dn4);
+  const int U = a.w.meta[0];
+  const int nsb = a.I / SB_WEIGHTS, T = a.T;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6, ks = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.x;
+  int* ldesc = reinterpret_cast<int*>(lds);                        // [umax][2]: expert, token mask
+  float* lwt = reinterpret_cast<float*>(ldesc + DESC * a.umax);    // [umax][WTAB16]
+  const size_t tb = ((size_t)a.umax * (DESC + WTAB16) * 4 + 15) & ~(size_t)15;
+  float* red = reinterpret_cast<float*>(lds + tb);                 // [nw][64 lanes][4]
+  char* stage = lds + tb + (size_t)DN_WAVES * 1024 + (size_t)wv * dn16_wave_bytes();
+  char* zrow = stage + DN16_DEPTH * DN16_SLOTS * GU_SLOT;
+  reinterpret_cast<uint2*>(zrow)[lane] = make_uint2(0u, 0u);
+  if (g == 0 && threadIdx.x == 0) a.w.meta[3] = 0;                 // the part-1 flag is consumed
+  for (int i = threadIdx.x; i < DESC * a.umax; i += blockDim.x) ldesc[i] = a.w.udesc[i];
+  for (int i = threadIdx.x; i < a.umax * WTAB16; i += blockDim.x) lwt[i] = a.w.wtab[i];
+  __syncthreads();
+
+  const int units = U * nsb;
+  const int tok = lane & 15;                                       // this lane's A row
+  const int wt_off = 4 * (lane >> 4);                              // token of this lane's D element 0
+  const ALane zl = a_lane(zrow, 0, ks);
+  float out[4] = {0.f, 0.f, 0.f, 0.f};
+  DownUnit16<FMT> b[DN16_DEPTH];
+  // every load unconditional (unit index clamped; a repeated unit is loaded
+  // but not computed)
+#pragma unroll
+  for (int q = 0; q < DN16_DEPTH; ++q)
+    down16_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, stage + q * DN16_SLOTS * GU_SLOT, b[q]);
+  for (int unit = wv; unit < units; unit += DN16_DEPTH * nw) {
+#pragma unroll
+    for (int q = 0; q < DN16_DEPTH; ++q) {
+      const int cu = unit + q * nw;
+      char* slots = stage + q * DN16_SLOTS * GU_SLOT;
+      // this unit's token rows have landed once no more than the loads
+      // issued after them are outstanding (its weights and the other unit's
+      // loads); the memory clobber keeps the LDS reads below
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(dn16_load_count<FMT>() - DN16_SLOTS +
+                                               (DN16_DEPTH - 1) * dn16_load_count<FMT>())
+                   : "memory");
+      if (cu < units) {
+        const int uu = cu / nsb, sb = cu - uu * nsb;
+        const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[DESC * uu + 1]);
+        const int n = __popc(mask);
+        const bool routed = tok < T && ((mask >> tok) & 1u);
+        const int rank = __popc(mask & ((1u << tok) - 1u));     // among the unit's tokens
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int first = 0;;) {
+          const bool here = routed && rank >= first && rank < first + DN16_SLOTS;
+          const ALane l0 = here ? a_lane(slots, 2 * (rank - first), ks) : zl;
+          const ALane l1 = here ? a_lane(slots, 2 * (rank - first) + 1, ks) : zl;
+          down16_product<FMT>(b[q], l0, l1, acc);
+          first += DN16_SLOTS;
+          if (first >= n) break;
+          // an expert with more routed tokens: stage the next ones (after
+          // this pass's reads) and wait for them
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          down16_rows(a, uu, sb, mask, first, slots);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const float* wt = lwt + uu * WTAB16 + wt_off;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) out[v] = fmaf(wt[v], acc[v], out[v]);
+      }
+      // the slots are refilled only once their operand reads have completed
+      // (see k_down)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      down16_load<FMT>(a, ldesc, min(cu + DN16_DEPTH * nw, units - 1), nsb, g, slots, b[q]);
+    }
+  }
+  reinterpret_cast<float4*>(red)[(size_t)wv * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
+  __syncthreads();                                   // (also drains the last, unused loads)
+  for (int idx = threadIdx.x; idx < 16 * T; idx += blockDim.x) {
+    const int row = idx & 15, t = idx >> 4;
+    // D row t sits in lane 16 (t / 4) + row, element t % 4
+    const int l0 = 16 * (t >> 2) + row, v = t & 3;
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += red[(size_t)w * 256 + 4 * l0 + v];
+    const int h = g * 16 + row;
+    const size_t o = (size_t)t * a.Ho + h;
+    if (a.flags & 2u) {
+      s += a.x_f32 ? reinterpret_cast<const float*>(a.x)[o]
+                   : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[o]);
+    }
+    if (a.flags & 1u) s += a.out[o];
+    a.out[o] = s;
+  }
+}
+
+// Whether a call's down kernel keeps what it needs in LDS: up to 8 tokens
+// the staged kernel (routing table, partial sums, staged activation rows),
+// else the register-operand kernel (routing table, partial sums; its
+// activation rows must also lie within the 2 GiB a buffer offset
+// addresses).  A call of up to 8 tokens that the staged kernel cannot hold
+// takes the register-operand kernels.
+bool narrow_fits(int T, int umax) {
+  size_t need = 0;
+  switch (T) {
+    case 1: need = down_lds<1>(umax); break;
+    case 2: need = down_lds<2>(umax); break;
+    case 3: need = down_lds<3>(umax); break;
+    case 4: need = down_lds<4>(umax); break;
+    case 5: need = down_lds<5>(umax); break;
+    case 6: need = down_lds<6>(umax); break;
+    case 7: need = down_lds<7>(umax); break;
+    default: need = down_lds<8>(umax); break;
+  }
+  return need <= DECODE_LDS_MAX;
+}
+
+bool wide_fits(int T, int umax, int I) {
+  return down16_lds(umax) <= DECODE_LDS_MAX && (size_t)umax * T * NPART * I * 2 < ((size_t)1 << 31);
+}
+
 template <int FMT>
 hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr) {
   ExpertArgs a;
@@ -1029,20 +1320,32 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   // so every wave takes the same number of superblocks.  Row groups per
   // workgroup: 4 when 2 would give more workgroups than CUs (one 10-wave
   // workgroup fits a CU at this register count); Q3/Q4 keep 2 (4 would spill).
+  // (and whose wave regions fit in LDS: always 10 here, as a wave stages
+  // at most 8 row pairs)
   const int nsbH = L.H / SB_WEIGHTS;
+  const bool wide_t = c.T > DECODE_NARROW_T || !narrow_fits(c.T, umax);
+  const int npr = wide_t ? (c.T + 1) / 2 : c.T;     // row pairs one staging loads
+  const size_t wave_lds = (size_t)std::max(8192, (npr + 1) * GU_SLOT);
   int nwg = 1;
-  for (int d = 1; d <= 10; ++d)
-    if (nsbH % d == 0) nwg = d;
+  for (int d = 1; d <= GU_MAX_WAVES; ++d)
+    if (nsbH % d == 0 && d * wave_lds <= GU_DYN_LDS) nwg = d;
   const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
-  const size_t lds_gu = (size_t)nwg * std::max(8192, (c.T + 1) * 1040);   // <= 94 KiB: ceiling raised at create
+  const size_t lds_gu = (size_t)nwg * wave_lds;   // ceiling raised at create
 
   const dim3 ggu(L.I / (16 * G), umax);
+#define STRATA_GATEUP(GG)                                                                 \
+  if (wide_t) launch(tr, k_gateup<FMT, GG, true>, ggu, dim3(64 * nwg), lds_gu, s, a);      \
+  else launch(tr, k_gateup<FMT, GG, false>, ggu, dim3(64 * nwg), lds_gu, s, a);
   if constexpr (FMT == 2) {
-    if (wide) launch(tr, k_gateup<FMT, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
-    else launch(tr, k_gateup<FMT, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    if (wide) { STRATA_GATEUP(4) } else { STRATA_GATEUP(2) }
   } else {
-    launch(tr, k_gateup<FMT, 2>, ggu, dim3(64 * nwg), lds_gu, s, a);
+    STRATA_GATEUP(2)
+  }
+#undef STRATA_GATEUP
+  if (wide_t) {
+    launch(tr, k_down16<FMT>, dim3(L.Ho / 16), dim3(64 * DN_WAVES), down16_lds(umax), s, a);
+    return hipGetLastError();
   }
   switch (c.T) {
 #define STRATA_DOWN(TT)                                                                            \
@@ -1065,7 +1368,9 @@ hipError_t raise_down_lds() {
 
 template <int FMT>
 hipError_t raise_down_lds_all() {
-  hipError_t e = raise_down_lds<FMT, 1>();
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_down16<FMT>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)DECODE_LDS_MAX);
+  if (e == hipSuccess) e = raise_down_lds<FMT, 1>();
   if (e == hipSuccess) e = raise_down_lds<FMT, 2>();
   if (e == hipSuccess) e = raise_down_lds<FMT, 3>();
   if (e == hipSuccess) e = raise_down_lds<FMT, 4>();
@@ -1076,15 +1381,19 @@ hipError_t raise_down_lds_all() {
   return e;
 }
 
+template <int FMT, int G, bool WIDE>
+hipError_t raise_gateup_lds1() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, G, WIDE>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GU_DYN_LDS);
+}
+
 template <int FMT>
 hipError_t raise_gateup_lds() {
-  const int want = 96 * 1024;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, 2>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  hipError_t e = raise_gateup_lds1<FMT, 2, false>();
+  if (e == hipSuccess) e = raise_gateup_lds1<FMT, 2, true>();
   if constexpr (FMT == 2) {
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, 4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, want);
+    if (e == hipSuccess) e = raise_gateup_lds1<FMT, 4, false>();
+    if (e == hipSuccess) e = raise_gateup_lds1<FMT, 4, true>();
   }
   return e;
 }
@@ -1098,22 +1407,11 @@ hipError_t launch_topk_v1(const TopkArgs& t, hipStream_t s, Tracer* tr) {
 
 }  // namespace
 
-// The gate/up kernels keep up to 80 KiB of dynamic LDS (8 KiB per wave).
-bool decode_fits(int T, int k, int E, int n_shared) {
+// The gate/up kernels always fit (one wave region at the least).
+bool decode_fits(int T, int k, int E, int n_shared, int I) {
   if (T < 1 || T > DECODE_MAX_T) return false;
   const int umax = (T * k < E ? T * k : E) + n_shared;
-  size_t need = 0;
-  switch (T) {
-    case 1: need = down_lds<1>(umax); break;
-    case 2: need = down_lds<2>(umax); break;
-    case 3: need = down_lds<3>(umax); break;
-    case 4: need = down_lds<4>(umax); break;
-    case 5: need = down_lds<5>(umax); break;
-    case 6: need = down_lds<6>(umax); break;
-    case 7: need = down_lds<7>(umax); break;
-    default: need = down_lds<8>(umax); break;
-  }
-  return need <= DECODE_LDS_MAX;
+  return (T <= DECODE_NARROW_T && narrow_fits(T, umax)) || wide_fits(T, umax, I);
 }
 
 hipError_t prepare_decode_kernels() {
@@ -1138,7 +1436,7 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
                                bool permutation) {
   RouteArgs a;
   a.Wr = L.router_w; a.bias = L.router_b; a.x = c.x; a.x_f32 = c.x_f32; a.T = c.T;
-  a.H = L.H; a.Ho = L.Ho; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts;
+  a.H = L.H; a.Ho = L.Ho; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts; a.part1 = W.meta + 3;
   switch (c.T) {
 #define STRATA_ROUTE(TT)                                                                 \
     case TT:                                                                               \
@@ -1151,6 +1449,8 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
       break;
     STRATA_ROUTE(1) STRATA_ROUTE(2) STRATA_ROUTE(3) STRATA_ROUTE(4)
     STRATA_ROUTE(5) STRATA_ROUTE(6) STRATA_ROUTE(7) STRATA_ROUTE(8)
+    case 9: case 10: case 11: case 12: case 13: case 14: case 15:
+    STRATA_ROUTE(16)
 #undef STRATA_ROUTE
     default: return hipErrorInvalidValue;
   }

@@ -21,7 +21,7 @@ struct Work {
   int* inv;           // [Tmax*k]   pair -> sorted slot
   int* slot_tok;      // [Tmax*k]   prefill: sorted slot -> token
   int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
-  float* wtab;        // [E+1][8]   decode: routing weight per (active expert, token), 0 if not routed
+  float* wtab;        // [E+1][8 or 16] decode: routing weight per (active expert, token), 0 if not routed
   int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill),
                       //            meta[2] prefill: some token of the call is scaled (e > 0)
   int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
@@ -102,7 +102,7 @@ hipError_t prepare_decode_kernels();
 // tokens of a layer with top-k k over E experts (+ n_shared): its down kernel
 // keeps the routing table and the staged activation rows in LDS
 constexpr size_t DECODE_LDS_MAX = 160 * 1024;
-bool decode_fits(int T, int k, int E, int n_shared);
+bool decode_fits(int T, int k, int E, int n_shared, int I);
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);

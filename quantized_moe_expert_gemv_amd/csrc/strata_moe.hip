@@ -114,7 +114,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.inv = take(P * 4);
   p.slot_tok = take(P * 4);
   p.udesc = take((E + 1) * 2 * 4);
-  p.wtab = take((E + 1) * 8 * 4);
+  p.wtab = take((E + 1) * 16 * 4);
   p.meta = take(16 * 4);
   p.chunk_base = take(E * (size_t)p.nchunks * 4);
   p.pair_rank = take(P * 4);
@@ -223,7 +223,9 @@ int check_call(strata_moe* h, const void* x, int32_t x_dtype, int32_t T) {
   return STRATA_OK;
 }
 
-bool fits(const strata_moe_config& c, int T) { return decode_fits(T, c.top_k, c.n_experts, c.n_shared); }
+bool fits(const strata_moe_config& c, int T) {
+  return decode_fits(T, c.top_k, c.n_experts, c.n_shared, (int)pad256(c.inter));
+}
 
 bool use_decode(const strata_moe_config& c, int T, uint32_t flags) {
   if (flags & STRATA_FORCE_PREFILL) return false;

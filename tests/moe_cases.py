@@ -35,6 +35,22 @@ class HostLayer:
     def logits(self, x):
         return O.router_logits(np.asarray(x, np.float64), self.wr, self.b)
 
+    def mixture(self, x, idx, w):
+        """The layer's output for given ids and routing weights (the oracle's
+        expert FFNs, weighted as the layer defines), e.g. the weights a device
+        router computed: separates the expert path's precision from the
+        router's rounding."""
+        x = np.asarray(x, np.float64)
+        out = np.zeros((x.shape[0], self.H), dtype=np.float64)
+        for e in np.unique(idx):
+            rows, cols = np.nonzero(idx == e)
+            wg, wu, wd = O.dequant_expert(self.record(int(e)), self.H, self.I, self.fmt)
+            out[rows] += np.asarray(w, np.float64)[rows, cols][:, None] * O.expert_ffn(x[rows], wg, wu, wd)
+        if self.shared is not None:
+            wg, wu, wd = O.dequant_expert(self.shared, self.H, self.I, self.fmt)
+            out += O.expert_ffn(x, wg, wu, wd)
+        return out
+
 
 def tokens(hl, stream, T, min_gap=MIN_GAP, max_attempts=200):
     """Gap-filtered bf16 tokens for layer hl: returns (bits uint16 [T,H], fp64 values)."""
