@@ -88,7 +88,9 @@ enum {
 };
 
 /* Calls with T <= STRATA_DECODE_MAX_T take the decode (GEMV) path unless
- * STRATA_FORCE_PREFILL is given; larger T take the grouped-GEMM path. */
+ * STRATA_FORCE_PREFILL is given or its down kernel's LDS cannot hold the
+ * call's routing table (thousands of active experts); larger T take the
+ * grouped-GEMM path. */
 #define STRATA_DECODE_MAX_T 16
 /* Grouped-path calls of at most this many tokens (and E <= 512, k <= 64)
  * route in one launch unless STRATA_SPLIT_ROUTE is given. */
@@ -184,7 +186,7 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
  * section 一: the always-on shared expert): out[T][H] fp32 (device) = moe(x), or with
  * STRATA_ACCUMULATE out += moe(x), or with STRATA_ADD_INPUT out = x + moe(x).
  * x and out must not overlap.  Stream-ordered and asynchronous.
- * Precision: the decode kernels (T <= 8) multiply exact weight values by the
+ * Precision: the decode kernels (T <= 16) multiply exact weight values by the
  * activations carried as two fp16 parts (22 significant bits) with fp32
  * accumulation.  The prefill expert GEMMs round weights and activations to
  * fp16 with fp32 accumulation (weights below 2^-24 in magnitude round to
@@ -212,7 +214,7 @@ STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype,
  * the device current at strata_moe_create and kept until the process ends.
  * Calls whose regions exceed the array (more tokens than fit; a 2560-wide,
  * 512-expert, top-10 layer fits up to about 256 tokens, every decode call of
- * 8 tokens or fewer fits) return STRATA_E_UNSUPPORTED before anything is
+ * 16 tokens or fewer of it fits) return STRATA_E_UNSUPPORTED before anything is
  * enqueued.  Every handle on a device shares that device's one array:
  * static calls that overlap in time on one device (different streams, or
  * different threads) race and give wrong results; order them on one stream.

@@ -13,7 +13,9 @@
 //                 its waves; each workgroup also writes a slice of the tokens as
 //                 two fp16 parts (x = p0 + p1 to 22 significant bits);
 //   k_topk        one workgroup per token: two-level radix selection of the k
-//                 largest logits and the renormalised softmax weights;
+//                 largest logits and the renormalised softmax weights; it
+//                 also finds the token's operand scale (and rescales its
+//                 parts when the token needs one);
 //   k_gateup      one workgroup per (active expert, 32 rows of I): it finds
 //                 its expert from the top-k ids (experts chosen by any token,
 //                 ascending, then the shared one), its waves split the H
@@ -24,7 +26,8 @@
 //                 scale each expert's rows by its routing weights and the
 //                 workgroup reduces them in a fixed order: the weighted
 //                 combine happens here, with no cross-workgroup
-//                 synchronisation.
+//                 synchronisation (k_down16 from 9 tokens: the token rows of
+//                 each unit's routed tokens only).
 // A route() call runs k_route_gemv, k_topk and k_permute (the stable
 // token->expert permutation that the expert kernels do not need).
 //
@@ -504,7 +507,7 @@ __global__ __launch_bounds__(1024) void k_topk_block_decode(TopkArgs a) {
 // The stable token->expert permutation of the routing (route() only): counts,
 // offsets (exclusive scan over experts), and for every pair p = t * k + j its
 // slot, earlier tokens of the same expert first: its rank is the number of
-// earlier tokens in the expert's token bitmask (T <= 8).  One workgroup.
+// earlier tokens in the expert's token bitmask (T <= 16).  One workgroup.
 __global__ __launch_bounds__(512) void k_permute(TopkArgs a) {
   extern __shared__ int lds_i[];
   __shared__ int2 tmp[16];
