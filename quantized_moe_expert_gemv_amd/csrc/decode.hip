@@ -1329,10 +1329,14 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   const bool wide_t = c.T > DECODE_NARROW_T || !narrow_fits(c.T, umax);
   const int npr = wide_t ? (c.T + 1) / 2 : c.T;     // row pairs one staging loads
   const size_t wave_lds = (size_t)std::max(8192, (npr + 1) * GU_SLOT);
+  // The wide kernels take 2 row groups and at most 5 waves: three such
+  // workgroups share a CU, so a call's many active experts spread evenly
+  // instead of a second round of 10-wave workgroups on some CUs.
+  const int max_waves = wide_t ? GU_MAX_WAVES / 2 : GU_MAX_WAVES;
   int nwg = 1;
-  for (int d = 1; d <= GU_MAX_WAVES; ++d)
+  for (int d = 1; d <= max_waves; ++d)
     if (nsbH % d == 0 && d * wave_lds <= GU_DYN_LDS) nwg = d;
-  const bool wide = FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
+  const bool wide = !wide_t && FMT == 2 && (L.I % 64 == 0) && (size_t)(L.I / 32) * umax > 256;
   const int G = wide ? 4 : 2;
   const size_t lds_gu = (size_t)nwg * wave_lds;   // ceiling raised at create
 
