@@ -1097,15 +1097,18 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
 // of tokens routed to the unit's expert are staged: one buffer->LDS load of
 // 1 KiB per token (its two parts are adjacent in the activation buffer,
 // [active expert][token][part][I]) into the next free slot; lanes of other
-// tokens read the wave's zero row.  A unit stages its first DN16_SLOTS
-// routed tokens with its own loads (always DN16_SLOTS of them, the unused
+// tokens read the wave's zero row.  A unit stages its first S routed
+// tokens with its own loads (always S of them, the unused
 // ones past the end of the buffer: a fixed count keeps the waits static);
 // an expert with more routed tokens takes further passes over the same
-// weights, each staging the next DN16_SLOTS (the rows of each token are
+// weights, each staging the next S (the rows of each token are
 // fixed, so the passes add up in one accumulator).
 constexpr int DN16_DEPTH = 2;
-constexpr int DN16_SLOTS = 4;
-constexpr int dn16_wave_bytes() { return (DN16_DEPTH * DN16_SLOTS + 1) * GU_SLOT; }
+// S = staged token slots per unit: 7 (an expert's routed tokens at 16 tokens
+// per call rarely exceed it) where the call's routing table leaves room in
+// LDS, else 4
+constexpr int DN16_SLOTS_WIDE = 7, DN16_SLOTS_NARROW = 4;
+template <int S> constexpr int dn16_wave_bytes() { return (DN16_DEPTH * S + 1) * GU_SLOT; }
 
 template <int FMT> struct DownUnit16 {
   Codes<FMT> cd;
@@ -1114,11 +1117,12 @@ template <int FMT> struct DownUnit16 {
 
 // vector-memory instructions of one unit: the token rows, then codes and scales
 template <int FMT>
-constexpr int dn16_load_count() { return DN16_SLOTS + (FMT == 2 ? 2 : 3); }
+constexpr int dn16_load_count(int S) { return S + (FMT == 2 ? 2 : 3); }
 
-// Token rows of ranks first .. first + DN16_SLOTS - 1 among the tokens of
+// Token rows of ranks first .. first + S - 1 among the tokens of
 // mask (expert u, superblock sb) into the slots at slot; ranks past the
 // last routed token load from past the end of the buffer.
+template <int S>
 __device__ inline void down16_rows(const ExpertArgs& a, int u, int sb, uint32_t mask, int first, char* slot) {
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, gch = (lane & 31) ^ (8 * h);
@@ -1126,7 +1130,7 @@ __device__ inline void down16_rows(const ExpertArgs& a, int u, int sb, uint32_t 
   uint32_t m = mask;
   for (int r = 0; r < first; ++r) m &= m - 1u;
 #pragma unroll
-  for (int j = 0; j < DN16_SLOTS; ++j) {
+  for (int j = 0; j < S; ++j) {
     const int t = m ? __builtin_ctz(m) : 0;
     // rows (u, t, part 0) and (u, t, part 1): 512 bytes of superblock sb each
     const uint32_t off = m ? (uint32_t)((((size_t)u * a.T + t) * NPART * a.I + (size_t)sb * SB_WEIGHTS) * 2 +
@@ -1137,14 +1141,14 @@ __device__ inline void down16_rows(const ExpertArgs& a, int u, int sb, uint32_t 
   }
 }
 
-template <int FMT>
+template <int FMT, int S>
 __device__ inline void down16_load(const ExpertArgs& a, const int* ldesc, int unit, int nsb, int g, char* slot,
                                    DownUnit16<FMT>& du) {
   const int lane = threadIdx.x & 63, r = lane & 15;
   const int u = unit / nsb, sb = unit - u * nsb;
   const int e = __builtin_amdgcn_readfirstlane(ldesc[DESC * u]);
   const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane(ldesc[DESC * u + 1]);
-  down16_rows(a, u, sb, mask, 0, slot);
+  down16_rows<S>(a, u, sb, mask, 0, slot);
   const rsrc_t wr = make_rsrc(a.packed + (size_t)e * a.stride, (uint32_t)a.stride);
   const uint32_t soff = (uint32_t)(down_off(FMT, a.H, a.I) + ((size_t)g * nsb + sb) * (Fmt<FMT>::slab_codes + 256));
   bload_codes<FMT>(wr, soff, lane, du.cd);
@@ -1186,12 +1190,13 @@ __device__ inline void down16_product(const DownUnit16<FMT>& du, const ALane& al
 }
 
 // dynamic LDS of k_down16: the routing table, partial sums, staged rows
+template <int S>
 inline size_t down16_lds(int umax) {
   return (((size_t)umax * (DESC + WTAB16) * 4 + 15) & ~(size_t)15) + (size_t)DN_WAVES * 1024 +
-         (size_t)DN_WAVES * dn16_wave_bytes();
+         (size_t)DN_WAVES * dn16_wave_bytes<S>();
 }
 
-template <int FMT>
+template <int FMT, int S>
 __global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
   extern __shared__ float4 lds_dn4[];
   char* lds = reinterpret_cast<char*>(lds_dn4);
@@ -1204,8 +1209,8 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
   float* lwt = reinterpret_cast<float*>(ldesc + DESC * a.umax);    // [umax][WTAB16]
   const size_t tb = ((size_t)a.umax * (DESC + WTAB16) * 4 + 15) & ~(size_t)15;
   float* red = reinterpret_cast<float*>(lds + tb);                 // [nw][64 lanes][4]
-  char* stage = lds + tb + (size_t)DN_WAVES * 1024 + (size_t)wv * dn16_wave_bytes();
-  char* zrow = stage + DN16_DEPTH * DN16_SLOTS * GU_SLOT;
+  char* stage = lds + tb + (size_t)DN_WAVES * 1024 + (size_t)wv * dn16_wave_bytes<S>();
+  char* zrow = stage + DN16_DEPTH * S * GU_SLOT;
   reinterpret_cast<uint2*>(zrow)[lane] = make_uint2(0u, 0u);
   if (g == 0 && threadIdx.x == 0) a.w.meta[3] = 0;                 // the part-1 flag is consumed
   for (int i = threadIdx.x; i < DESC * a.umax; i += blockDim.x) ldesc[i] = a.w.udesc[i];
@@ -1222,17 +1227,17 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
   // but not computed)
 #pragma unroll
   for (int q = 0; q < DN16_DEPTH; ++q)
-    down16_load<FMT>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, stage + q * DN16_SLOTS * GU_SLOT, b[q]);
+    down16_load<FMT, S>(a, ldesc, min(wv + q * nw, units - 1), nsb, g, stage + q * S * GU_SLOT, b[q]);
   for (int unit = wv; unit < units; unit += DN16_DEPTH * nw) {
 #pragma unroll
     for (int q = 0; q < DN16_DEPTH; ++q) {
       const int cu = unit + q * nw;
-      char* slots = stage + q * DN16_SLOTS * GU_SLOT;
+      char* slots = stage + q * S * GU_SLOT;
       // this unit's token rows have landed once no more than the loads
       // issued after them are outstanding (its weights and the other unit's
       // loads); the memory clobber keeps the LDS reads below
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(dn16_load_count<FMT>() - DN16_SLOTS +
-                                               (DN16_DEPTH - 1) * dn16_load_count<FMT>())
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(dn16_load_count<FMT>(S) - S +
+                                               (DN16_DEPTH - 1) * dn16_load_count<FMT>(S))
                    : "memory");
       if (cu < units) {
         const int uu = cu / nsb, sb = cu - uu * nsb;
@@ -1242,16 +1247,16 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
         const int rank = __popc(mask & ((1u << tok) - 1u));     // among the unit's tokens
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
         for (int first = 0;;) {
-          const bool here = routed && rank >= first && rank < first + DN16_SLOTS;
+          const bool here = routed && rank >= first && rank < first + S;
           const ALane l0 = here ? a_lane(slots, 2 * (rank - first), ks) : zl;
           const ALane l1 = here ? a_lane(slots, 2 * (rank - first) + 1, ks) : zl;
           down16_product<FMT>(b[q], l0, l1, acc);
-          first += DN16_SLOTS;
+          first += S;
           if (first >= n) break;
           // an expert with more routed tokens: stage the next ones (after
           // this pass's reads) and wait for them
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          down16_rows(a, uu, sb, mask, first, slots);
+          down16_rows<S>(a, uu, sb, mask, first, slots);
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         const float* wt = lwt + uu * WTAB16 + wt_off;
@@ -1261,7 +1266,7 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down16(ExpertArgs a) {
       // the slots are refilled only once their operand reads have completed
       // (see k_down)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      down16_load<FMT>(a, ldesc, min(cu + DN16_DEPTH * nw, units - 1), nsb, g, slots, b[q]);
+      down16_load<FMT, S>(a, ldesc, min(cu + DN16_DEPTH * nw, units - 1), nsb, g, slots, b[q]);
     }
   }
   reinterpret_cast<float4*>(red)[(size_t)wv * 64 + lane] = make_float4(out[0], out[1], out[2], out[3]);
@@ -1305,7 +1310,8 @@ bool narrow_fits(int T, int umax) {
 }
 
 bool wide_fits(int T, int umax, int I) {
-  return down16_lds(umax) <= DECODE_LDS_MAX && (size_t)umax * T * NPART * I * 2 < ((size_t)1 << 31);
+  return down16_lds<DN16_SLOTS_NARROW>(umax) <= DECODE_LDS_MAX &&
+         (size_t)umax * T * NPART * I * 2 < ((size_t)1 << 31);
 }
 
 template <int FMT>
@@ -1351,7 +1357,12 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   }
 #undef STRATA_GATEUP
   if (wide_t) {
-    launch(tr, k_down16<FMT>, dim3(L.Ho / 16), dim3(64 * DN_WAVES), down16_lds(umax), s, a);
+    if (down16_lds<DN16_SLOTS_WIDE>(umax) <= DECODE_LDS_MAX)
+      launch(tr, k_down16<FMT, DN16_SLOTS_WIDE>, dim3(L.Ho / 16), dim3(64 * DN_WAVES),
+             down16_lds<DN16_SLOTS_WIDE>(umax), s, a);
+    else
+      launch(tr, k_down16<FMT, DN16_SLOTS_NARROW>, dim3(L.Ho / 16), dim3(64 * DN_WAVES),
+             down16_lds<DN16_SLOTS_NARROW>(umax), s, a);
     return hipGetLastError();
   }
   switch (c.T) {
@@ -1375,8 +1386,11 @@ hipError_t raise_down_lds() {
 
 template <int FMT>
 hipError_t raise_down_lds_all() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_down16<FMT>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_down16<FMT, DN16_SLOTS_WIDE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)DECODE_LDS_MAX);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_down16<FMT, DN16_SLOTS_NARROW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)DECODE_LDS_MAX);
   if (e == hipSuccess) e = raise_down_lds<FMT, 1>();
   if (e == hipSuccess) e = raise_down_lds<FMT, 2>();
   if (e == hipSuccess) e = raise_down_lds<FMT, 3>();
