@@ -428,17 +428,17 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void k_topk(TopkArgs a) {
   __shared__ uint32_t s_m[TOPK_WAVES];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int E = a.E, k = a.k, t = blockIdx.x;
-  decode_token_scale(a, t, s_m);
   const float* row = a.w.logits + (size_t)t * E;
   const int e0 = wv * 64 * V1;
-  uint32_t u[V1];
+  // the logits are requested first, so that they and the token row of the
+  // operand scale are in flight together
   float val[V1];
 #pragma unroll
-  for (int i = 0; i < V1; ++i) {
-    const int e = e0 + lane + 64 * i;
-    val[i] = row[min(e, E - 1)];
-    u[i] = e < E ? sortable_bits(val[i]) : 0u;
-  }
+  for (int i = 0; i < V1; ++i) val[i] = row[min(e0 + lane + 64 * i, E - 1)];
+  decode_token_scale(a, t, s_m);
+  uint32_t u[V1];
+#pragma unroll
+  for (int i = 0; i < V1; ++i) u[i] = e0 + lane + 64 * i < E ? sortable_bits(val[i]) : 0u;
   bool sel[V1];
   int pos[V1];
   wave_select<V1>(u, k, sel, pos);
