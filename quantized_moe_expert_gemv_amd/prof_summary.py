@@ -29,8 +29,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # library kernel name fragment -> benchmark name
-KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_topk_block", "topk"), ("k_gateup", "gateup"),
-           ("k_down", "down_combine"), ("k_router", "router_gemm"), ("k_topk_chunks", "topk"),
+KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_topk_block", "topk"),
+           ("k_topk_block_decode", "topk"), ("k_gateup", "gateup"), ("k_down", "down_combine"),
+           ("k_down16", "down_combine"), ("k_router", "router_gemm"), ("k_topk_chunks", "topk"),
            ("k_colscan", "colscan"), ("k_scan", "scan"), ("k_scatter", "scatter"), ("k_gemm_gateup", "gateup_gemm"),
            ("k_gemm_down", "down_gemm"), ("k_combine", "combine")]
 
@@ -39,7 +40,8 @@ KERNELS = [("k_route_gemv", "route_gemv"), ("k_topk", "topk"), ("k_topk_block", 
 # valid while these are unchanged)
 PATH_SOURCES = {"decode": ("common.hpp", "decode.hip", "kernels.hpp"),
                 "prefill": ("common.hpp", "kernels.hpp", "prefill.hip")}
-DECODE_KERNELS = ("k_route_gemv", "k_topk", "k_topk_block", "k_permute", "k_gateup", "k_down")
+DECODE_KERNELS = ("k_route_gemv", "k_topk", "k_topk_block", "k_topk_block_decode", "k_permute", "k_gateup", "k_down",
+                  "k_down16")
 
 
 def source_hash(path=None):
