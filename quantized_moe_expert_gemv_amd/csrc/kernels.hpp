@@ -27,6 +27,7 @@ struct Work {
   int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
   int* texp;          // [Tmax]     the exponent e of each token's operand scale 2^-e
+  uint32_t* tmax;     // [32][Tmax] prefill: each token's largest |x| (float bits) per router K split
   int4* tiles;        // [max_tiles] prefill: {expert, first slot, rows, 0}, in XCD segments,
                       //             each sorted by row class (see k_scan)
   float* act;         // prefill: fp16 SwiGLU rows [slots][I] (same region as actp)

@@ -90,19 +90,23 @@ struct TopkArgs {
   const void* x;          // [T][Ho] the tokens (bf16, or fp32 when x_f32)
   int x_f32, H, Ho;
   uint16_t* x16;          // [T][H] their fp16 rows
+  const uint32_t* tmax;   // [S][T] each token's largest |x| per router split, or null (read the rows)
   Work w;
 };
 
 // The operand scale of token t (one wave): e from the token's largest
-// magnitude (token_scale_exp); when e > 0 the wave rewrites the token's fp16
-// row as x 2^-e (the router wrote it unscaled) and marks the call scaled
-// (meta[2], cleared by the router kernel, read by the gate/up GEMM).
+// magnitude (token_scale_exp), taken from the router's per-split maxima when
+// it wrote them, else from the token row; when e > 0 the wave rewrites the
+// token's fp16 row as x 2^-e (the router wrote it unscaled) and marks the
+// call scaled (meta[2], cleared by the router kernel, read by the gate/up
+// GEMM).
 __device__ inline void token_scale(const TopkArgs& a, int t) {
   const int lane = threadIdx.x & 63;
   const int per = a.x_f32 ? 4 : 8;                 // elements per 16-byte load
-  const int nch = a.Ho / per;
+  const int nch = a.tmax ? 0 : a.Ho / per;
   const char* row = reinterpret_cast<const char*>(a.x) + (size_t)t * a.Ho * (a.x_f32 ? 4 : 2);
   uint32_t m = 0;                                  // largest |x| as bits (non-negative: bit order)
+  if (a.tmax && lane < a.S) m = a.tmax[(size_t)lane * a.T + t];
   for (int c0 = 0; c0 < nch; c0 += 4 * 64) {
     uint4 v[4];
 #pragma unroll
@@ -1017,6 +1021,7 @@ struct RouterArgs {
   const uint16_t* wlo;    // Wr remainders, operand order
   float* part;            // [S][T][E]
   uint16_t* x16;          // [T][H] the tokens as fp16
+  uint32_t* tmax;         // [S][T] each token's largest |x| (float bits) over the split's K range
   int* meta;              // meta[2] (the call's scaled-token mark) is cleared here
 };
 
@@ -1157,6 +1162,7 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
     }
   };
   const bool write_x16 = ex == 0 && t0 + 16 * wv + r4 < a.T;
+  uint32_t xm = 0;          // largest |x| (bits) of this lane's token values, for the operand scale
   auto put_x16 = [&](const XSt& st, int s) __attribute__((always_inline)) {
     if (write_x16) {
       uint16_t* d = a.x16 + xoff + kb0 + s * XBK;
@@ -1170,6 +1176,17 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
         }
         *reinterpret_cast<u32x4_t*>(d + 32 * q) = h;
       }
+#pragma unroll
+      for (int i = 0; i < NX; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = st.v[i][j];
+          if constexpr (XF32) {
+            xm = max(xm, w & 0x7fffffffu);
+          } else {
+            xm = max(xm, max((w & 0x7fffu) << 16, w & 0x7fff0000u));
+          }
+        }
     }
   };
   f32x4 acc[8][2];
@@ -1205,6 +1222,13 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
     }
     STRATA_RSTAGE(0) STRATA_RSTAGE(1) STRATA_RSTAGE(2) STRATA_RSTAGE(3)
 #undef STRATA_RSTAGE
+  }
+  // the token's largest magnitude over this K range: its 4 lanes (l / 4 = row)
+  if (ex == 0) {
+    xm = max(xm, (uint32_t)dpp_i<DPP_QUAD_XOR1>((int)xm));
+    xm = max(xm, (uint32_t)dpp_i<DPP_QUAD_XOR2>((int)xm));
+    const int t = t0 + 16 * wv + r4;
+    if ((lane & 3) == 0 && t < a.T) a.tmax[(size_t)kz * a.T + t] = xm;
   }
   // D[e][t]: lane l holds experts 4 (l / 16) .. + 3 of group n for token 16 m + l % 16
   float* out = a.part + (size_t)kz * a.plane;
@@ -1605,7 +1629,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
     f.done = L.route_done;
     TopkArgs& t = f.t;
     t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.n_shared = L.n_shared; t.presel = 0;
-    t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = f.x16;
+    t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = f.x16; t.tmax = nullptr;
     t.S = 1; t.plane = (size_t)c.T * L.E; t.part = W.logits; t.bias = L.router_b; t.w = W;
     const dim3 grid((L.E + 15) / 16), block(64 * FR_WAVES);
     if (c.x_f32) launch(tr, k_route_fused<true>, grid, block, 0, s, f);
@@ -1627,6 +1651,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   r.whi = L.router_hi; r.wlo = L.router_lo;
   r.part = rp.part;
   r.x16 = rp.x16;
+  r.tmax = W.tmax;
   r.meta = W.meta;
   const int items = ((L.E + RT_E - 1) / RT_E) * ((c.T + BM - 1) / BM) * S;
   const dim3 grid(8 * ((items + 7) / 8)), block(64 * RT_WAVES);
@@ -1636,7 +1661,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b; t.n_shared = L.n_shared;
   t.presel = L.k > 64;
-  t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = rp.x16;
+  t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = rp.x16; t.tmax = W.tmax;
   if (t.presel) {
     const hipError_t e = launch_topk_block(r.part, L.E, L.router_b, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
     if (e != hipSuccess) return e;

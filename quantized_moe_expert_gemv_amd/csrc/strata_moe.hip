@@ -85,7 +85,7 @@ int check_config(const strata_moe_config* c) {
 
 struct WsPlan {
   size_t logits, topk_idx, topk_w, counts, offsets, perm, inv, slot_tok, udesc, wtab, meta,
-      chunk_base, pair_rank, texp, tiles, act, xparts, xpad, y, total;
+      chunk_base, pair_rank, texp, tmax, tiles, act, xparts, xpad, y, total;
   int nchunks, max_tiles;
 };
 
@@ -119,6 +119,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   p.chunk_base = take(E * (size_t)p.nchunks * 4);
   p.pair_rank = take(P * 4);
   p.texp = take(T * 4);
+  p.tmax = take(32 * T * 4);
   p.tiles = take((size_t)p.max_tiles * 16);
   const size_t Td = T < STRATA_DECODE_MAX_T ? T : STRATA_DECODE_MAX_T;
   const size_t act_prefill = slots * I * 2;                                   // bf16 rows
@@ -148,6 +149,7 @@ Work layout_work(uint8_t* ws, const WsPlan& p) {
   W.chunk_base = reinterpret_cast<int*>(ws + p.chunk_base);
   W.pair_rank = reinterpret_cast<int*>(ws + p.pair_rank);
   W.texp = reinterpret_cast<int*>(ws + p.texp);
+  W.tmax = reinterpret_cast<uint32_t*>(ws + p.tmax);
   W.tiles = reinterpret_cast<int4*>(ws + p.tiles);
   W.act = reinterpret_cast<float*>(ws + p.act);
   W.actp = reinterpret_cast<_Float16*>(ws + p.act);
