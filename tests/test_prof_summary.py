@@ -28,6 +28,11 @@ def test_kernel_paths_and_names():
     assert P.kernel_path("void strata::(anonymous namespace)::k_gateup<2, 4>(x)") == "decode"
     assert P.kernel_path("strata::(anonymous namespace)::k_gemm_gateup<2, false>(x)") == "prefill"
     assert P.bench_name("strata::(anonymous namespace)::k_down<2>(x)") == "down_combine"
+    # the decode kernels of 9..16 tokens and the decode block top-k
+    assert P.bench_name("void strata::(anonymous namespace)::k_down16<2, 7>(x)") == "down_combine"
+    assert P.kernel_path("void strata::(anonymous namespace)::k_down16<2, 7>(x)") == "decode"
+    assert P.bench_name("strata::(anonymous namespace)::k_topk_block_decode(x)") == "topk"
+    assert P.kernel_path("strata::(anonymous namespace)::k_topk_block(x)") == "decode"   # built from decode.hip
     assert P.bench_name("__amd_rocclr_copyBuffer") is None
     assert P.source_hash("decode") != P.source_hash("prefill")
 
