@@ -173,6 +173,14 @@ __device__ inline void wave_argmax(float& v, int& i) {
 
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
+// the bits of a where m is set, the bits of b elsewhere: one v_bfi_b32 (for
+// the masked form with constants the compiler writes an and and an or)
+__device__ inline uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
 // ------------------------------------------------------------------ token range
 // The 16-bit token operands of both paths hold x 2^-e, where e is chosen per
 // token from its largest magnitude m (m < 2^E): e = E - 4 when m reaches 16,

@@ -152,7 +152,7 @@ __device__ inline f16x8 q4_operand(const Codes<4>& c) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
-    const uint32_t bits = (t & 0x03C003C0u) | 0x3C003C00u;
+    const uint32_t bits = bit_select(0x03C003C0u, t, 0x3C003C00u);   // (disjoint masks)
     p[k] = __builtin_bit_cast(half2_t, bits) + off;
   }
   return join(p[0], p[1], p[2], p[3]);

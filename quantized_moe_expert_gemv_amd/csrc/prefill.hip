@@ -525,7 +525,8 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
-      q[k] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, (t & 0x03C003C0u) | 0x3C003C00u), s2, n2);
+      // nibbles at bits 6..9 and 22..25 of 0x3C00 0x3C00 (the masks are disjoint)
+      q[k] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, bit_select(0x03C003C0u, t, 0x3C003C00u)), s2, n2);
     }
   } else {
     const uint32_t W = ((B >> 1) & 1) ? c.w.y : c.w.x;
