@@ -24,7 +24,7 @@
  * scale byte e, w = 2^(e - 127) E2M1(q).
  * Block scales the 16-bit weight operands cannot carry are refused at
  * create (STRATA_E_UNSUPPORTED): an fp16 d that is NaN, infinite or above
- * 2^15 (Q2), 2^14 (Q3) or 2^11 (Q4); an MXFP4 byte e above 140 (2^13), 255
+ * 2^15 (Q2), 2^14 (Q3) or 2^12 (Q4); an MXFP4 byte e above 140 (2^13), 255
  * (NaN) included.
  *
  * Canonical expert record (the input of strata_moe_create): gate

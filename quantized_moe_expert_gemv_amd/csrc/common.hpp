@@ -23,8 +23,11 @@
 //         whose byte-wise conversion returns the 8 codes in offset order.
 //     Q3: the low two bits as Q2; the third bit of offset e of block 4h + b at
 //         bit 4e + b of hi dword h.
-//     Q4: 32 bits per block (vector h, dword i holds block 4h + i); the code of
-//         offset e sits at nibble NIB4[e] = {0,4,1,5,2,6,3,7}[e].
+//     Q4: 32 bits per block (vector h, dword i holds block 4h + i); byte j
+//         holds the codes of offsets j (low nibble) and j + 4 (high nibble),
+//         so the dword masked with 0x0F0F0F0F (and after >> 4) is four bytes
+//         0000qqqq, each the E4M3 value q 2^-9, whose conversion in byte
+//         order returns the codes of offsets 0..3 (4..7).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -172,14 +175,6 @@ __device__ inline void wave_argmax(float& v, int& i) {
 }
 
 __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
-
-// the bits of a where m is set, the bits of b elsewhere: one v_bfi_b32 (for
-// the masked form with constants the compiler writes an and and an or)
-__device__ inline uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b) {
-  uint32_t r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
-  return r;
-}
 
 // ------------------------------------------------------------------ token range
 // The 16-bit token operands of both paths hold x 2^-e, where e is chosen per

@@ -33,8 +33,8 @@
 //
 // The multiply-accumulate runs on the matrix cores (16x16x32 fp16 MFMA, fp32
 // accumulation): the code q of a weight becomes the fp16 value q (2-bit codes
-// through the FP4->fp16 conversion, Q3 as a 2-bit and a 1-bit plane) or
-// (q - 8)/16 (Q4, magic-number construction), exactly; the activations enter
+// through the FP4->fp16 conversion, Q3 as a 2-bit and a 1-bit plane, Q4
+// through the E4M3->fp16 conversion), exactly; the activations enter
 // as two fp16 parts (16 A-operand rows: 2 parts x up to 8 tokens; from 9 to
 // 16 tokens the rows are the tokens and each part is its own MFMA into the
 // same result, so every decode call is one pass over the weights), which
@@ -142,20 +142,16 @@ __device__ inline f16x8 hi3_operand(const uint2& hi) {
               __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(X, 8.0f, 3));
 }
 
-// Q4 codes of block BB as fp16 values (q - 8) / 16: 1 + q/16 from the bit
-// pattern 0x3C00 | q << 6, minus 1.5 (both steps exact).
+// Q4 codes of block BB as fp16 values q: each byte 0000qqqq of the masked
+// word is the E4M3 value q 2^-9, converted at scale 2^9 (exact)
 template <int BB>
 __device__ inline f16x8 q4_operand(const Codes<4>& c) {
   const uint32_t W = comp((BB >> 2) ? c.v1 : c.v0, BB & 3);
-  const half2_t off = {(_Float16)-1.5f, (_Float16)-1.5f};
-  half2_t p[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
-    const uint32_t bits = bit_select(0x03C003C0u, t, 0x3C003C00u);   // (disjoint masks)
-    p[k] = __builtin_bit_cast(half2_t, bits) + off;
-  }
-  return join(p[0], p[1], p[2], p[3]);
+  const uint32_t E = W & 0x0F0F0F0Fu, O = (W >> 4) & 0x0F0F0F0Fu;
+  return join(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(E, 512.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(E, 512.0f, true),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(O, 512.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(O, 512.0f, true));
 }
 
 // MXFP4 codes of block BB as their E2M1 values (exact in fp16): byte j of
@@ -169,8 +165,7 @@ __device__ inline f16x8 mx_operand(const Codes<5>& c) {
               __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(W, 1.0f, 3));
 }
 
-// scale of block BB of this lane's row; Q4 folds in the factor 16; MXFP4's
-// 16-bit slot holds the E8M0 byte e: 2^(e - 127) (e = 0: 2^-127, a
+// scale of block BB of this lane's row; MXFP4's 16-bit slot holds the E8M0 byte e: 2^(e - 127) (e = 0: 2^-127, a
 // subnormal, e <= 140 checked at create)
 template <int FMT, int BB>
 __device__ inline float block_scale(const uint4& sc) {
@@ -178,7 +173,7 @@ __device__ inline float block_scale(const uint4& sc) {
   const uint32_t h = (BB & 1) ? (w >> 16) : (w & 0xffffu);
   if constexpr (FMT == FMT_MXFP4) return __uint_as_float(h ? h << 23 : 0x00400000u);
   const float d = half_bits_to_f32((uint16_t)h);
-  return FMT == 4 ? 16.0f * d : d;
+  return d;
 }
 
 // D = A * B(codes of block BB) + Doff, in fp32
@@ -198,7 +193,7 @@ __device__ inline f32x4 block_product(const f16x8& a, const Codes<FMT>& c, const
 // the block offset -c * sum_j x_j, for every output column, added to acc
 template <int FMT>
 __device__ inline f32x4 block_offset_acc(const f16x8& a, const f32x4& acc) {
-  if constexpr (FMT == 4 || FMT == FMT_MXFP4) {   // no offset term (Q4 folds it into the operand)
+  if constexpr (FMT == FMT_MXFP4) {               // no offset term
     return acc;
   } else {
     f16x8 cst;
@@ -761,8 +756,9 @@ __device__ inline void gu_load(rsrc_t wr, uint32_t up_base, int gp, int nsb, int
 
 // Slab pairs J0 .. J0 + NJ - 1 of one superblock: per block, the activation
 // operand from LDS, the offset MFMA, the 2 NJ product MFMAs (independent, so
-// their latency overlaps), then their scale FMAs.
-template <int FMT, int G, int J0, int NJ>
+// their latency overlaps), then their scale FMAs on the first NV of each
+// lane's 4 D rows (the rows past the call's tokens hold zeros).
+template <int FMT, int G, int J0, int NJ, int NV>
 __device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const ALane& al, float (&acc)[2 * G][4]) {
 #define STRATA_BLOCK(BB)                                                          \
   {                                                                               \
@@ -776,7 +772,7 @@ __device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const ALane& 
     _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                              \
       const float sg = block_scale<FMT, BB>(st.sc[J0 + j]);                       \
       const float su = block_scale<FMT, BB>(st.sc[G + J0 + j]);                   \
-      _Pragma("unroll") for (int v = 0; v < 4; ++v) {                             \
+      _Pragma("unroll") for (int v = 0; v < NV; ++v) {                            \
         acc[J0 + j][v] = fmaf(sg, d[2 * j][v], acc[J0 + j][v]);                   \
         acc[G + J0 + j][v] = fmaf(su, d[2 * j + 1][v], acc[G + J0 + j][v]);       \
       }                                                                           \
@@ -790,18 +786,18 @@ __device__ inline void gu_compute_pairs(const GuStage<FMT, G>& st, const ALane& 
 // One superblock in halves of G/2 slab pairs, each as soon as its weights
 // have arrived (the compiler waits on the half's registers; the other half
 // stays in flight).
-template <int FMT, int G>
+template <int FMT, int G, int NV>
 __device__ inline void gu_compute(const GuStage<FMT, G>& st, const ALane& al, float (&acc)[2 * G][4]) {
   // the activation operand was requested by buffer->LDS loads before the
   // gu_load_count() weight loads: once no more than those are outstanding it
   // has landed (the compiler does not track these loads; the memory clobber
   // keeps every LDS read below this point)
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(gu_load_count<FMT, G>()) : "memory");
-  gu_compute_pairs<FMT, G, 0, G / 2>(st, al, acc);
+  gu_compute_pairs<FMT, G, 0, G / 2, NV>(st, al, acc);
   // (the empty memory clobber makes the second half re-read the operands
   // from LDS instead of keeping every block's operand in registers)
   asm volatile("" ::: "memory");
-  gu_compute_pairs<FMT, G, G / 2, G / 2>(st, al, acc);
+  gu_compute_pairs<FMT, G, G / 2, G / 2, NV>(st, al, acc);
 }
 
 // WIDE (9..16 tokens, or fewer when k_down's LDS cannot hold the call): A
@@ -810,7 +806,8 @@ __device__ inline void gu_compute(const GuStage<FMT, G>& st, const ALane& al, fl
 // the router and token-scale kernels) takes a second pass over the same
 // weights with the part-1 rows: bf16 tokens rarely have one.  The
 // activations are stored [active expert][token][part][I] for k_down16.
-template <int FMT, int G, bool WIDE>
+// NV: live D rows per lane, min(T, 4) (4 when WIDE).
+template <int FMT, int G, bool WIDE, int NV>
 __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
   constexpr int GU_GROUPS = G, GU_SLABS = 2 * G;
   constexpr int WT = WIDE ? WTAB16 : WTAB;
@@ -872,7 +869,7 @@ __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     GuStage<FMT, G> st;
     gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
-    gu_compute<FMT, G>(st, al, acc);
+    gu_compute<FMT, G, NV>(st, al, acc);
     if (WIDE && part1) {
       // the part-1 rows into the region once the part-0 operand reads are
       // done, then the same weights again (converted afresh: opaque() keeps
@@ -881,7 +878,7 @@ __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
       gu_aload_lds(xr, npr, H, sb, lane, region, (uint32_t)(T * H * 2));
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       opaque(st);
-      gu_compute<FMT, G>(st, al, acc);
+      gu_compute<FMT, G, NV>(st, al, acc);
     }
   }
   // raw 16x16 results to this wave's LDS region (its operand is consumed)
@@ -966,8 +963,9 @@ __device__ inline void down_load(const ExpertArgs& a, const int* ldesc, int unit
   du.sc = bload4(wr, Fmt<FMT>::slab_codes + r * 16, soff);
 }
 
-// out[v] += routing weight of this lane's D-row token v * (this unit's 16x16 product)
-template <int FMT>
+// out[v] += routing weight of this lane's D-row token v * (this unit's 16x16
+// product), for the first NV of the lane's 4 D rows (the others are zero rows)
+template <int FMT, int NV>
 __device__ inline void down_compute(const DownUnit<FMT>& du, const ALane& al, const float* wt, float* out) {
   f32x4 dd[2];
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -984,7 +982,7 @@ __device__ inline void down_compute(const DownUnit<FMT>& du, const ALane& al, co
     dd[BB & 1] = block_product<FMT, BB>(af, du.cd, block_offset<FMT>(af));        \
     if (BB > 0) {                                                                 \
       const float ds = block_scale<FMT, (BB > 0 ? BB - 1 : 0)>(du.sc);            \
-      _Pragma("unroll") for (int v = 0; v < 4; ++v)                               \
+      _Pragma("unroll") for (int v = 0; v < NV; ++v)                              \
         acc[v] = fmaf(ds, dd[(BB - 1) & 1][v], acc[v]);                           \
     }                                                                             \
   }
@@ -993,7 +991,7 @@ __device__ inline void down_compute(const DownUnit<FMT>& du, const ALane& al, co
 #undef STRATA_BLOCK
   const float ds = block_scale<FMT, 7>(du.sc);
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
+  for (int v = 0; v < NV; ++v) {
     acc[v] = fmaf(ds, dd[1][v], acc[v]);
     out[v] = fmaf(wt[v], acc[v], out[v]);
   }
@@ -1057,7 +1055,7 @@ __global__ __launch_bounds__(64 * DN_WAVES) void k_down(ExpertArgs a) {
         const char* base = routed ? stage + q * TT * GU_SLOT + (arow >> 1) * GU_SLOT + 512 * (arow & 1) : zrow;
         const int hh = routed ? (arow & 1) : 0;
         const ALane al{base + 16 * ks + 128 * hh, base + 16 * ks - 128 * hh};
-        down_compute<FMT>(b[q], al, lwt + uu * WTAB + wt_off, out);
+        down_compute<FMT, (TT < 4 ? TT : 4)>(b[q], al, lwt + uu * WTAB + wt_off, out);
       }
       // the slot is refilled only once its operand reads have completed: a
       // buffer->LDS load issued while a read of the same bytes is still
@@ -1347,9 +1345,12 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   const size_t lds_gu = (size_t)nwg * wave_lds;   // ceiling raised at create
 
   const dim3 ggu(L.I / (16 * G), umax);
-#define STRATA_GATEUP(GG)                                                                 \
-  if (wide_t) launch(tr, k_gateup<FMT, GG, true>, ggu, dim3(64 * nwg), lds_gu, s, a);      \
-  else launch(tr, k_gateup<FMT, GG, false>, ggu, dim3(64 * nwg), lds_gu, s, a);
+#define STRATA_GATEUP(GG)                                                                  \
+  if (wide_t) launch(tr, k_gateup<FMT, GG, true, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);    \
+  else if (c.T == 1) launch(tr, k_gateup<FMT, GG, false, 1>, ggu, dim3(64 * nwg), lds_gu, s, a); \
+  else if (c.T == 2) launch(tr, k_gateup<FMT, GG, false, 2>, ggu, dim3(64 * nwg), lds_gu, s, a); \
+  else if (c.T == 3) launch(tr, k_gateup<FMT, GG, false, 3>, ggu, dim3(64 * nwg), lds_gu, s, a); \
+  else launch(tr, k_gateup<FMT, GG, false, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);
   if constexpr (FMT == 2) {
     if (wide) { STRATA_GATEUP(4) } else { STRATA_GATEUP(2) }
   } else {
@@ -1402,19 +1403,27 @@ hipError_t raise_down_lds_all() {
   return e;
 }
 
-template <int FMT, int G, bool WIDE>
+template <int FMT, int G, bool WIDE, int NV>
 hipError_t raise_gateup_lds1() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, G, WIDE>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gateup<FMT, G, WIDE, NV>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GU_DYN_LDS);
+}
+
+template <int FMT, int G>
+hipError_t raise_gateup_lds_g() {
+  hipError_t e = raise_gateup_lds1<FMT, G, true, 4>();
+  if (e == hipSuccess) e = raise_gateup_lds1<FMT, G, false, 1>();
+  if (e == hipSuccess) e = raise_gateup_lds1<FMT, G, false, 2>();
+  if (e == hipSuccess) e = raise_gateup_lds1<FMT, G, false, 3>();
+  if (e == hipSuccess) e = raise_gateup_lds1<FMT, G, false, 4>();
+  return e;
 }
 
 template <int FMT>
 hipError_t raise_gateup_lds() {
-  hipError_t e = raise_gateup_lds1<FMT, 2, false>();
-  if (e == hipSuccess) e = raise_gateup_lds1<FMT, 2, true>();
+  hipError_t e = raise_gateup_lds_g<FMT, 2>();
   if constexpr (FMT == 2) {
-    if (e == hipSuccess) e = raise_gateup_lds1<FMT, 4, false>();
-    if (e == hipSuccess) e = raise_gateup_lds1<FMT, 4, true>();
+    if (e == hipSuccess) e = raise_gateup_lds_g<FMT, 4>();
   }
   return e;
 }

@@ -494,10 +494,10 @@ __device__ inline h2_t fp4x2_f16(uint32_t src, float scale) {
 
 // The B operand of block B (of its superblock) for this lane: its 8 weights
 // d (q - c) in K order, as fp16 (one rounding: q d - c d by fused
-// multiply-add with c d rounded to fp16 first; Q4 as ((q - 8) / 16) (16 d),
-// both factors exact).  Codes become fp16 q exactly through the FP4
-// conversions (nibble 0b00qq at scale 2, Q3's third bit 0b000h at scale 8),
-// Q4 through the bit pattern 0x3C00 | q << 6.
+// multiply-add with c d rounded to fp16 first, exact for Q4's c = 8).
+// Codes become fp16 q exactly through the FP4 conversions (nibble 0b00qq at
+// scale 2, Q3's third bit 0b000h at scale 8), Q4's through the E4M3
+// conversion (byte 0000qqqq is q 2^-9, at scale 2^9).
 template <int FMT, int B>
 __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
   const uint32_t sw = ((B >> 1) & 1) ? c.sc.y : c.sc.x;
@@ -516,18 +516,12 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
   const _Float16 d = __builtin_bit_cast(_Float16, (uint16_t)((B & 1) ? (sw >> 16) : (sw & 0xffffu)));
   h2_t q[4];
   if constexpr (FMT == 4) {
-    // (1 + q/16) * 16 d - 24 d in one fused multiply-add per pair: 16 d is
-    // exact, 24 d is rounded once to fp16 (an absolute error of at most
-    // 2^-11 |24 d| on top of the single rounding of the product)
     const uint32_t W = c.w[B & 3];
-    const _Float16 s16 = d * (_Float16)16.0f, c24 = (_Float16)-1.5f * s16;
-    const h2_t s2 = {s16, s16}, n2 = {c24, c24};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t t = (k == 0) ? (W << 6) : (k == 1) ? (W << 2) : (k == 2) ? (W >> 2) : (W >> 6);
-      // nibbles at bits 6..9 and 22..25 of 0x3C00 0x3C00 (the masks are disjoint)
-      q[k] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, bit_select(0x03C003C0u, t, 0x3C003C00u)), s2, n2);
-    }
+    const uint32_t E = W & 0x0F0F0F0Fu, O = (W >> 4) & 0x0F0F0F0Fu;
+    q[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(E, 512.0f, false);
+    q[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(E, 512.0f, true);
+    q[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(O, 512.0f, false);
+    q[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(O, 512.0f, true);
   } else {
     const uint32_t W = ((B >> 1) & 1) ? c.w.y : c.w.x;
     const uint32_t E = W & 0x33333333u, O = (W >> 2) & 0x33333333u;
@@ -543,11 +537,11 @@ __device__ inline f16x8 dequant_b(const PairCodes<FMT>& c) {
       q[2] += fp4x2_f16<2>(X, 8.0f);
       q[3] += fp4x2_f16<3>(X, 8.0f);
     }
-    const _Float16 ncd = -((_Float16)Fmt<FMT>::c * d);
-    const h2_t d2 = {d, d}, n2 = {ncd, ncd};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = __builtin_elementwise_fma(q[k], d2, n2);
   }
+  const _Float16 ncd = -((_Float16)Fmt<FMT>::c * d);
+  const h2_t d2 = {d, d}, n2 = {ncd, ncd};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) q[k] = __builtin_elementwise_fma(q[k], d2, n2);
   f16x8 r;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

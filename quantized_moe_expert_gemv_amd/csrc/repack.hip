@@ -20,7 +20,7 @@ namespace strata {
 namespace {
 
 __constant__ int POS2[8] = {0, 4, 2, 6, 8, 12, 10, 14};   // Q2/Q3 low-plane bit of offset e
-__constant__ int NIB4[8] = {0, 4, 1, 5, 2, 6, 3, 7};      // Q4 nibble of offset e
+__constant__ int NIB4[8] = {0, 2, 4, 6, 1, 3, 5, 7};      // Q4 nibble of offset e
 
 // code j (0..31) of a canonical block: bits [b*j, b*j + b) of the code bytes
 // read as one little-endian bit string
@@ -82,9 +82,10 @@ __global__ void k_repack(const uint8_t* __restrict__ canon, uint8_t* __restrict_
   for (int q = 0; q < 4; ++q) {                 // K-slice -> lane q*16 + r
     const int lane = q * 16 + r;
     if (fmt == 4 || fmt == FMT_MXFP4) {
-      // Q4: nibbles in the order of its magic-number conversion; MXFP4: in K
-      // order (byte j = elements 2j, 2j + 1, low nibble first), the order of
-      // the FP4 -> fp16 conversion
+      // Q4: byte j = elements j and j + 4 (low nibble first), so that the
+      // masked bytes convert as E4M3 in K order; MXFP4: in K order (byte j =
+      // elements 2j, 2j + 1, low nibble first), the order of the FP4 -> fp16
+      // conversion
       uint32_t w[8];
       for (int bb = 0; bb < 8; ++bb) {
         uint32_t d = 0;
@@ -153,8 +154,8 @@ __global__ void k_router_split(const float* __restrict__ w, uint16_t* __restrict
 // Scales the kernels cannot carry: every 16-bit weight operand (the prefill
 // path's dequantised d (q - c) in fp16, and the products the decode path
 // scales in fp32) must stay finite.  fp16 d: NaN or infinite, or above
-// 2^15 (Q2), 2^14 (Q3), 2^11 (Q4, whose 16 d and 24 d are fp16 operands
-// too); MXFP4: e = 255 (NaN) or e > 140 (2^13 and up).  One thread per
+// 2^15 (Q2), 2^14 (Q3), 2^12 (Q4, whose 8 d is an fp16 operand too);
+// MXFP4: e = 255 (NaN) or e > 140 (2^13 and up).  One thread per
 // canonical block; bad blocks are counted in *bad.
 __global__ void k_check_scales(const uint8_t* __restrict__ canon, long long n_blocks, int fmt, int* bad) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -168,7 +169,7 @@ __global__ void k_check_scales(const uint8_t* __restrict__ canon, long long n_bl
   } else {
     const uint32_t h = (uint32_t)b[bq - 2] | ((uint32_t)b[bq - 1] << 8);
     const uint32_t mag = h & 0x7fffu;
-    const uint32_t lim = fmt == 4 ? 0x6800u : fmt == 3 ? 0x7400u : 0x7800u;   // 2^11, 2^14, 2^15
+    const uint32_t lim = fmt == 4 ? 0x6C00u : fmt == 3 ? 0x7400u : 0x7800u;   // 2^12, 2^14, 2^15
     ok = mag <= lim;                             // (NaN and infinity encode above every limit)
   }
   if (!ok) atomicAdd(bad, 1);

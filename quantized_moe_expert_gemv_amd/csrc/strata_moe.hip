@@ -425,7 +425,7 @@ int strata_moe_create(const strata_moe_config* cfg, const float* router_w, const
     delete h;
     return fail(STRATA_E_UNSUPPORTED,
                 "%d block scale(s) outside what the 16-bit operands carry (fp16 d NaN, infinite or above "
-                "2^15 / 2^14 / 2^11 for Q2 / Q3 / Q4; MXFP4 e = 255 or above 140)", n_bad);
+                "2^15 / 2^14 / 2^12 for Q2 / Q3 / Q4; MXFP4 e = 255 or above 140)", n_bad);
   }
   *out = h;
   return ok();

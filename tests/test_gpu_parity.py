@@ -343,7 +343,7 @@ def test_tokens_far_beyond_the_fp16_range(B, fmt, n_shared, factor, T):
                f"x * {factor:g} fp32 fmt {fmt} T {T}, device weights")
 
 
-@pytest.mark.parametrize("fmt,scale", [(2, np.inf), (2, np.nan), (2, 40000.0), (3, 20000.0), (4, 4096.0),
+@pytest.mark.parametrize("fmt,scale", [(2, np.inf), (2, np.nan), (2, 40000.0), (3, 20000.0), (4, 8192.0),
                                        (5, 141), (5, 200), (5, 255)])
 def test_block_scales_the_operands_cannot_carry_are_refused(B, fmt, scale):
     """A block scale that no 16-bit weight operand can hold (fp16 d NaN,
@@ -358,7 +358,7 @@ def test_block_scales_the_operands_cannot_carry_are_refused(B, fmt, scale):
         good[3, 5, 16] = 140
     else:
         canon[3, 5, -2:] = np.array([scale], dtype="<f2").view(np.uint8)
-        good[3, 5, -2:] = np.array([{2: 32768.0, 3: 16384.0, 4: 2048.0}[fmt]], dtype="<f2").view(np.uint8)
+        good[3, 5, -2:] = np.array([{2: 32768.0, 3: 16384.0, 4: 4096.0}[fmt]], dtype="<f2").view(np.uint8)
     cfg = B.make_config(hl.H, hl.I, hl.E, hl.k, 0, fmt, 16)
     wr = torch.from_numpy(hl.wr).to(DEV)
     b = torch.from_numpy(hl.b).to(DEV)
