@@ -224,20 +224,28 @@ struct RouteArgs {
 constexpr int ROUTE_WAVES = 4;
 constexpr int ROUTE_BATCH = 4;   // float4 columns per lane issued together
 
-// token t, columns 4q..4q+3 of x as fp32
+// token t, columns 4q..4q+3 of x as loaded (fp32 or bf16), and as fp32
+template <bool XF32> struct XQuad;
+template <> struct XQuad<true> { float4 v; };
+template <> struct XQuad<false> { uint2 v; };
 template <bool XF32>
-__device__ inline float4 x_quad(const void* x, int H, int t, int q) {
-  if constexpr (XF32) return reinterpret_cast<const float4*>(x)[((size_t)t * H >> 2) + q];
-  const uint2 v = reinterpret_cast<const uint2*>(x)[((size_t)t * H >> 2) + q];
-  return bf16x4(v.x, v.y);
+__device__ inline XQuad<XF32> x_quad_load(const void* x, int H, int t, int q) {
+  if constexpr (XF32) return {reinterpret_cast<const float4*>(x)[((size_t)t * H >> 2) + q]};
+  else return {reinterpret_cast<const uint2*>(x)[((size_t)t * H >> 2) + q]};
+}
+template <bool XF32>
+__device__ inline float4 x_quad_f32(const XQuad<XF32>& r) {
+  if constexpr (XF32) return r.v;
+  else return bf16x4(r.v.x, r.v.y);
 }
 
 // Expert rows per router workgroup: every wave reads its columns of the
 // tokens once for all of them (fewer register batches for more tokens)
 constexpr int route_rows(int T) { return T <= 4 ? 2 : 1; }
-// float4 columns per lane in flight together (the token columns of 16 tokens
-// take 64 registers per column)
-constexpr int route_batch(int T) { return T <= 8 ? ROUTE_BATCH : 2; }
+// float4 columns per lane in flight together: every load of a batch is
+// issued before the first is used, so a batch costs one memory round trip;
+// 3 columns of 16 tokens cover a 3072-wide row in one batch
+constexpr int route_batch(int T) { return T <= 8 ? ROUTE_BATCH : 3; }
 
 // route_rows(T) expert rows per workgroup; its waves split the rows into
 // float4 columns (strided, so every load instruction of a wave reads 1 KiB
@@ -265,28 +273,33 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     for (int t = 0; t < TT; ++t) acc[r][t] = 0.f;
   for (int q0 = tid; q0 < nq; q0 += RB * 64 * ROUTE_WAVES) {
     float4 w[RB][RR];
-    float4 xv[RB][TT];
+    XQuad<XF32> xr[RB][TT];
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const int q = min(q0 + j * 64 * ROUTE_WAVES, nq - 1);
 #pragma unroll
       for (int r = 0; r < RR; ++r) w[j][r] = rows[r][q];
 #pragma unroll
-      for (int t = 0; t < TT; ++t) xv[j][t] = x_quad<XF32>(a.x, H, TT <= DECODE_NARROW_T ? t : min(t, T - 1), q);
+      for (int t = 0; t < TT; ++t) xr[j][t] = x_quad_load<XF32>(a.x, H, TT <= DECODE_NARROW_T ? t : min(t, T - 1), q);
     }
+    // (without this the scheduler interleaves the loads with their uses and
+    // pays several round trips per batch at 4 and 16 tokens)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < RB; ++j) {
       const float m = (q0 + j * 64 * ROUTE_WAVES < nq) ? 1.f : 0.f;   // clamped duplicates count 0
 #pragma unroll
-      for (int r = 0; r < RR; ++r)
+      for (int t = 0; t < TT; ++t) {
+        const float4 xv = x_quad_f32<XF32>(xr[j][t]);
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-          float d = w[j][r].x * xv[j][t].x;
-          d = fmaf(w[j][r].y, xv[j][t].y, d);
-          d = fmaf(w[j][r].z, xv[j][t].z, d);
-          d = fmaf(w[j][r].w, xv[j][t].w, d);
+        for (int r = 0; r < RR; ++r) {
+          float d = w[j][r].x * xv.x;
+          d = fmaf(w[j][r].y, xv.y, d);
+          d = fmaf(w[j][r].z, xv.z, d);
+          d = fmaf(w[j][r].w, xv.w, d);
           acc[r][t] = fmaf(m, d, acc[r][t]);
         }
+      }
     }
   }
 #pragma unroll
