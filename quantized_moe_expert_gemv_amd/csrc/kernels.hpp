@@ -118,7 +118,21 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
 hipError_t launch_prefill_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);
 
 constexpr int PREFILL_BM = 128;     // token rows per GEMM tile
-constexpr int PREFILL_CHUNK_T = 32; // tokens per top-k/histogram chunk
+constexpr int PREFILL_CHUNK_T = 32; // most tokens per top-k/histogram chunk (32-bit token masks)
+// Tokens per chunk for a call of T tokens.  A chunk is one workgroup whose
+// waves select one or two tokens each, a chain of dependent memory round
+// trips and a radix descent: small chunks spread a short call's selections
+// over more workgroups, large ones keep the column scan of the chunk
+// histograms short for long calls.
+inline int prefill_chunk_t(int T) { return T <= 256 ? 8 : T <= 4096 ? 16 : PREFILL_CHUNK_T; }
+inline int prefill_chunks(int T) { return (T + prefill_chunk_t(T) - 1) / prefill_chunk_t(T); }
+// most chunks of any call of up to Tmax tokens (the chunk count grows with T
+// inside each range of prefill_chunk_t)
+inline int prefill_max_chunks(int Tmax) {
+  const int a = prefill_chunks(Tmax < 256 ? Tmax : 256), b = prefill_chunks(Tmax < 4096 ? Tmax : 4096);
+  const int c = prefill_chunks(Tmax);
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
+}
 
 // one-launch routing of the grouped path (forward/route flag bits as in the
 // public header): where it applies, and up to how many tokens it is taken

@@ -42,9 +42,6 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 
 constexpr int BM = PREFILL_BM;      // 128 token rows
-constexpr int CT = PREFILL_CHUNK_T;
-
-
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -83,6 +80,7 @@ __device__ inline u32x4_t f32x8_to_f16(f32x4_t lo, f32x4_t hi) {
 struct TopkArgs {
   int T, E, k, nchunks, n_shared;
   int presel;             // 1: the selection is already in topk_idx / topk_w (k > 64)
+  int ct;                 // tokens per chunk (prefill_chunk_t)
   int S;                  // router partial planes
   size_t plane;           // elements between planes
   const float* part;      // [S][T][E] partial logits
@@ -196,7 +194,7 @@ __device__ inline void token_topk(const TopkArgs& a, int t, int* sel, float* w, 
   }
 }
 
-// One chunk of CT tokens per workgroup, one wave per token: top-k ids
+// One chunk of a.ct tokens per workgroup, one wave per token: top-k ids
 // (ascending) and renormalised weights; then per expert the bitmask of the
 // chunk's tokens that chose it, which gives the chunk's expert histogram and
 // each pair's rank among the chunk's earlier tokens with the same expert.
@@ -212,14 +210,15 @@ __device__ inline void scatter_pair(const TopkArgs& a, int p);
 __global__ __launch_bounds__(64 * TOPK_CHUNK_WAVES) void k_topk_chunks(TopkArgs a) {
   extern __shared__ int lds_i[];
   uint32_t* tmask = reinterpret_cast<uint32_t*>(lds_i);         // [E]
-  // the chunk's selections: [CT][k] in LDS after tmask, or (preselected, any
+  // the chunk's selections: [ct][k] in LDS after tmask, or (preselected, any
   // k) the chunk's rows of topk_idx
+  const int CT = a.ct;
   int* sel = a.presel ? a.w.topk_idx + (size_t)blockIdx.x * CT * a.k : reinterpret_cast<int*>(tmask + a.E);
   __shared__ int s_sel[TOPK_CHUNK_WAVES][64];
   const int wv = threadIdx.x >> 6;
   const int chunk = blockIdx.x, tb = chunk * CT;
   const int k = a.k, E = a.E;
-  static_assert(CT <= 32, "token masks are 32-bit");
+  static_assert(PREFILL_CHUNK_T <= 32, "token masks are 32-bit");
   for (int e = threadIdx.x; e < E; e += blockDim.x) tmask[e] = 0u;
   for (int tl = wv; tl < CT; tl += TOPK_CHUNK_WAVES) {
     const int t = tb + tl;
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(1024) void k_scan(ScanArgs a) { scan_tiles(a); }
 // chunks + its rank in its own chunk
 __device__ inline void scatter_pair(const TopkArgs& a, int p) {
   const int e = a.w.topk_idx[p];
-  const int chunk = (p / a.k) / CT;
+  const int chunk = (p / a.k) / a.ct;
   const int slot = a.w.offsets[e] + a.w.chunk_base[(size_t)chunk * a.E + e] + a.w.pair_rank[p];
   a.w.perm[slot] = p;
   a.w.inv[p] = slot;
@@ -1623,7 +1622,8 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
     f.x16 = reinterpret_cast<uint16_t*>(W.ybf);
     f.done = L.route_done;
     TopkArgs& t = f.t;
-    t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.n_shared = L.n_shared; t.presel = 0;
+    t.T = c.T; t.E = L.E; t.k = L.k; t.ct = prefill_chunk_t(c.T); t.nchunks = prefill_chunks(c.T);
+    t.n_shared = L.n_shared; t.presel = 0;
     t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = f.x16; t.tmax = nullptr;
     t.S = 1; t.plane = (size_t)c.T * L.E; t.part = W.logits; t.bias = L.router_b; t.w = W;
     const dim3 grid((L.E + 15) / 16), block(64 * FR_WAVES);
@@ -1653,7 +1653,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
   if (c.x_f32) launch(tr, k_router<true>, grid, block, 0, s, r);
   else launch(tr, k_router<false>, grid, block, 0, s, r);
   TopkArgs t;
-  t.T = c.T; t.E = L.E; t.k = L.k; t.nchunks = (c.T + CT - 1) / CT; t.w = W;
+  t.T = c.T; t.E = L.E; t.k = L.k; t.ct = prefill_chunk_t(c.T); t.nchunks = prefill_chunks(c.T); t.w = W;
   t.S = S; t.plane = plane; t.part = r.part; t.bias = L.router_b; t.n_shared = L.n_shared;
   t.presel = L.k > 64;
   t.x = c.x; t.x_f32 = c.x_f32; t.H = L.H; t.Ho = L.Ho; t.x16 = rp.x16; t.tmax = W.tmax;
@@ -1661,7 +1661,7 @@ hipError_t launch_prefill_route(const Layer& L, const Work& W, const Call& c, hi
     const hipError_t e = launch_topk_block(r.part, L.E, L.router_b, c.T, L.E, L.k, W.topk_idx, W.topk_w, s, tr);
     if (e != hipSuccess) return e;
   }
-  const size_t lds = ((t.presel ? 0 : (size_t)CT * L.k) + L.E) * 4;
+  const size_t lds = ((t.presel ? 0 : (size_t)t.ct * L.k) + L.E) * 4;
   launch(tr, k_topk_chunks, dim3(t.nchunks), dim3(64 * TOPK_CHUNK_WAVES), lds, s, t);
   if (t.nchunks == 1) return hipGetLastError();   // the one chunk did the scan and the scatter
   ScanArgs sa;

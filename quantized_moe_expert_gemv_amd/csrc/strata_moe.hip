@@ -101,7 +101,7 @@ WsPlan plan_workspace(const strata_moe_config& c) {
   // H, I: the kernels' widths (whole superblocks)
   const size_t T = c.max_tokens, E = c.n_experts, k = c.top_k, H = pad256(c.hidden), I = pad256(c.inter);
   const size_t P = T * k, slots = P + (size_t)c.n_shared * T;
-  p.nchunks = (int)((T + PREFILL_CHUNK_T - 1) / PREFILL_CHUNK_T);
+  p.nchunks = prefill_max_chunks((int)T);
   p.max_tiles = max_tiles_for(c, (int)T);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
