@@ -1091,6 +1091,13 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
   const int ty = w % nt, ex = (w / nt) % ne, kz = w / (nt * ne);
   const int t0 = ty * BM, e0 = ex * RT_E;
   const int kb0 = kz * a.kper, ke = min(a.H, kb0 + a.kper), ns = (ke - kb0) / XBK;
+  // The XCD's workgroups share this item's router-weight slice; each starts
+  // its K loop at its own stage (wrapping around), so a stage's weights are
+  // fetched once by the first workgroup to reach them and found in the L2 by
+  // the others, instead of all of them waiting on the same lines at once.
+  // (Each workgroup's sum order is fixed, so results are run-to-run exact.)
+  const int rot = (int)((long long)idx * ns / per);
+  auto rs = [&](int st) { const int r = st + rot; return r >= ns ? r - ns : r; };
   // token loads of this lane: row l/4 of subtile w, 8 elements at column
   // 8 (l % 4) of each 32-wide block (operand lane l / 4 + 16 (l % 4))
   const int r4 = lane >> 2, c4 = 8 * (lane & 3);
@@ -1193,24 +1200,24 @@ __global__ __launch_bounds__(64 * RT_WAVES, 1) void k_router(RouterArgs a) {
   constexpr int BD = XF32 ? 1 : 2, RB = 2 * BD;
   XSt ar[4];
   BSt br[RB];
-  bload(0, br[0]);
-  if constexpr (BD == 2) bload(min(1, ns - 1), br[1]);
-  xload(0, ar[0]);
-  xload(min(1, ns - 1), ar[1]);
+  bload(rs(0), br[0]);
+  if constexpr (BD == 2) bload(rs(min(1, ns - 1)), br[1]);
+  xload(rs(0), ar[0]);
+  xload(rs(min(1, ns - 1)), ar[1]);
   xstore(ar[0], Ls[0]);
-  put_x16(ar[0], 0);
+  put_x16(ar[0], rs(0));
   __syncthreads();
   for (int s4 = 0; s4 < ns; s4 += 4) {
 #define STRATA_RSTAGE(ST)                                                                    \
     if (s4 + ST < ns) {                                                                      \
       const int s = s4 + ST;                                                                 \
-      bload(min(s + BD, ns - 1), br[(ST + BD) & (RB - 1)]);                                  \
-      xload(min(s + 2, ns - 1), ar[(ST + 2) & 3]);                                           \
+      bload(rs(min(s + BD, ns - 1)), br[(ST + BD) & (RB - 1)]);                              \
+      xload(rs(min(s + 2, ns - 1)), ar[(ST + 2) & 3]);                                       \
       __builtin_amdgcn_sched_barrier(0);                                                     \
       router_stage<XF32>(Ls[ST & 1], br[ST & (RB - 1)].v, lane, acc);                        \
       if (s + 1 < ns) {                                                                      \
         xstore(ar[(ST + 1) & 3], Ls[(ST + 1) & 1]);                                          \
-        put_x16(ar[(ST + 1) & 3], s + 1);                                                    \
+        put_x16(ar[(ST + 1) & 3], rs(s + 1));                                                \
       }                                                                                      \
       __syncthreads();                                                                       \
     }
