@@ -390,25 +390,37 @@ __device__ inline void scan_tiles(const ScanArgs& a) {
     a.w.meta[1] = n;
   }
   __syncthreads();
-  // full tiles (class 0) of a segment are placed consecutively from
-  // x tp + (class-0 tiles of the segment before them); only an entry's
-  // remainder tile needs the lower classes' counts
+  // Full tiles (class 0) of a segment are placed consecutively from
+  // x tp + (class-0 tiles of the segment before them): full tile q of an
+  // entry whose tiles start at expert-order index j0, after r0 class-0 tiles,
+  // goes to x tp + r0 + q - bnd[x].x with x = (j0 + q) / tp.  A heavy expert
+  // has hundreds of them, so each wave writes its lanes' entries' full tiles
+  // one entry at a time with all its lanes.  Only an entry's remainder tile
+  // needs the lower classes' counts; its own thread places it.
   int4 run = cpre;
-  int x = base.y / tp;
-  int4 b0 = bnd[x];
-  for (int e = e0; e < e1; ++e) {
-    const int c = cnt_of(e), full = c / BM, rem = c - full * BM;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    const bool has = e < e1;
+    const int cv = cnt_of(min(e, n_ent - 1));          // (an in-bounds read for every lane)
+    const int c = has ? cv : 0, full = c / BM, rem = c - full * BM;
     const int first = (e < E) ? base.x : P;
-    if (e < E) a.w.offsets[e] = base.x;
-    for (int q = 0; q < full; ++q, ++base.y) {
-      if (base.y >= (x + 1) * tp) b0 = bnd[++x];
-      a.w.tiles[x * tp + run.x - b0.x] = make_int4(e, first + q * BM, BM, 0);
-      ++run.x;
+    if (has && e < E) a.w.offsets[e] = base.x;
+    for (uint64_t m = __ballot(full > 0); m; m &= m - 1) {       // the lanes with full tiles
+      const int L = __builtin_ctzll(m);
+      const int fL = __builtin_amdgcn_readlane(full, L);
+      const int eL = __builtin_amdgcn_readlane(e, L), firstL = __builtin_amdgcn_readlane(first, L);
+      const int j0 = __builtin_amdgcn_readlane(base.y, L), r0 = __builtin_amdgcn_readlane(run.x, L);
+      for (int q = (int)(threadIdx.x & 63); q < fL; q += 64) {
+        const int xq = (j0 + q) / tp;
+        a.w.tiles[xq * tp + r0 + q - bnd[xq].x] = make_int4(eL, firstL + q * BM, BM, 0);
+      }
     }
-    if (rem > 0) {
-      if (base.y >= (x + 1) * tp) b0 = bnd[++x];
+    base.y += full;
+    run.x += full;
+    if (has && rem > 0) {
+      const int x = base.y / tp;
+      const int4 b0 = bnd[x], b1 = bnd[x + 1];
       const int k = row_class(rem);
-      const int4 b1 = bnd[x + 1];
       int pos = x * tp + class_of(run, k) - class_of(b0, k);
       for (int kk = 0; kk < k; ++kk) pos += class_of(b1, kk) - class_of(b0, kk);
       a.w.tiles[pos] = make_int4(e, first + full * BM, rem, 0);
@@ -416,7 +428,7 @@ __device__ inline void scan_tiles(const ScanArgs& a) {
       run.x += u.x; run.y += u.y; run.z += u.z; run.w += u.w;
       ++base.y;
     }
-    if (e < E) base.x += c;
+    if (has && e < E) base.x += c;
   }
 }
 
