@@ -44,6 +44,7 @@
 // accumulation and the 2^-22 activation split are the only roundings.  The
 // fp16 block scale d multiplies each block's 16x16 result in fp32.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -567,6 +568,13 @@ struct ExpertArgs {
   uint32_t flags;
   float* out;
   Work w;
+  // prefetch by the gate/up waves (pf_issue): the next stack layer's router
+  // rows (pf_next_chunks = 0: none) and this call's down slabs
+  const void* pf_next;
+  uint32_t pf_next_bytes, pf_next_chunk;
+  int pf_next_chunks;
+  int pf_down;
+  uint32_t pf_key;
 };
 
 // Active expert u of this call: the experts chosen by any token in ascending
@@ -671,6 +679,42 @@ __device__ inline bool wave_route(const ExpertArgs& a, int u, uint64_t* bits, in
   e_out = __builtin_amdgcn_readfirstlane(e);
   mask_out = (uint32_t)__builtin_amdgcn_readfirstlane((int)m);
   return true;
+}
+
+// Prefetch.  While a gate/up wave waits for its routing lookup and its
+// weights, it also requests bytes that a later kernel will read, so that
+// they come from the caches then instead of HBM: the next stack layer's
+// router rows, and the down slabs of its own expert.  A launch's workgroup w
+// runs on XCD w % 8 and each XCD has its own L2, so the later kernel's bytes
+// are taken as the chunks its workgroups read (chunk c read by its workgroup
+// c), and the nwx waves on XCD x (this one: jw) request the chunks x, x + 8,
+// ... in 1 KiB pieces, N per lane at most (a hint: what is left over is not
+// requested).  Pieces outside the chunks read past the buffer record, which
+// fetches nothing.  No result depends on the loaded values: they are folded
+// by pf_fold into one word that is stored only if it equals a key
+// (a spare meta word, never read), so that the loads are kept.
+constexpr int PF_LOADS = 3;
+template <int N>
+__device__ inline void pf_issue(const void* base, uint32_t bytes, uint32_t chunk, int nchunks, int x, int jw,
+                                int nwx, uint4 (&v)[N]) {
+  const int lane = threadIdx.x & 63;
+  const rsrc_t r = make_rsrc(base, bytes);
+  const uint32_t P = (chunk + 1023u) >> 10;                        // pieces per chunk
+  const uint32_t mine = nchunks > x ? (uint32_t)(nchunks - x + 7) >> 3 : 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t q = (uint32_t)(jw + i * nwx);
+    const uint32_t m = q / P, in = (q - m * P) * 1024u + 16u * (uint32_t)lane;
+    const bool ok = q < mine * P && in < chunk;
+    v[i] = bload4(r, ok ? ((uint32_t)x + 8u * m) * chunk + in : bytes, 0u);
+  }
+}
+template <int N>
+__device__ inline uint32_t pf_fold(const uint4 (&v)[N]) {
+  uint32_t h = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) h ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  return h;
 }
 
 // gate/up: a workgroup covers G row groups (16G rows i) of one active
@@ -846,14 +890,32 @@ __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
   reinterpret_cast<uint2*>(region + npr * GU_SLOT)[lane] = make_uint2(0u, 0u);   // the zero row
   const int part1 = WIDE ? __builtin_amdgcn_readfirstlane(a.w.meta[3]) : 0;
   const int te = a.w.texp[min(lane, T - 1)];         // lane t < T: token t's scale exponent
-  // the first superblock's activation operand does not depend on the expert:
-  // it is requested right behind the routing lookup's loads (wv < nw <= nsb)
+  // The prefetch costs ~20-35 registers per lane.  It is taken where it was
+  // measured to gain: single-token calls of 2- and 3-bit experts with two row
+  // groups per workgroup (1 token 20.3 -> 19.9 us, 48-layer Q3 stack 1083 ->
+  // 1066 us per step); at 4 tokens it gained nothing and for 4-bit experts
+  // the lower occupancy cost a second round of workgroups.
+  constexpr bool PF = !WIDE && NV == 1 && FMT <= 3 && G == 2;
+  constexpr int NPF = PF ? PF_LOADS : 1;
+  // this wave among the waves of its XCD (the next layer's router prefetch)
+  const int lw = u * gridDim.x + gp, nwg = gridDim.x * gridDim.y;
+  const int xcd = lw & 7;
+  uint4 pfr[NPF], pfd[NPF];
+  // the first superblock's activation operand and the router prefetch do not
+  // depend on the expert: they are requested right behind the routing
+  // lookup's loads (wv < nw <= nsb)
   int e, U;
   uint32_t mask;
   float wt;
-  if (!wave_route(a, u, s_bits[wv], e, mask, U, wt,
-                  [&]() __attribute__((always_inline)) { gu_aload_lds(xr, npr, H, wv, lane, region); })) {
+  if (!wave_route(a, u, s_bits[wv], e, mask, U, wt, [&]() __attribute__((always_inline)) {
+        gu_aload_lds(xr, npr, H, wv, lane, region);
+        if constexpr (PF)
+          pf_issue(a.pf_next, a.pf_next_bytes, a.pf_next_chunk, a.pf_next_chunks, xcd, (lw >> 3) * nw + wv,
+                   ((nwg - xcd + 7) >> 3) * nw, pfr);
+      })) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS write may land after the exit
+    if constexpr (PF)
+      if (pf_fold(pfr) == a.pf_key) a.w.meta[8] = 1;
     return;
   }
   if (wv == 0 && lane < T) s_texp[lane] = te;
@@ -875,13 +937,25 @@ __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
   for (int s = 0; s < GU_SLABS; ++s)
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[s][v] = 0.f;
-  for (int sb = wv; sb < nsb; sb += nw) {
-    // the activation operand first (the first one is already requested),
-    // then the weights; the compute waits for each part as it needs it
-    if (sb > wv) gu_aload_lds(xr, npr, H, sb, lane, region);
+  // the down slabs of this expert that the down kernel's workgroups on this
+  // XCD read (group g of 16 rows of H: nsbI slabs, read by workgroup g)
+  const int nsbI = I / SB_WEIGHTS;
+  const uint32_t dchunk = (uint32_t)nsbI * (Fmt<FMT>::slab_codes + 256);
+  const int gdx = gridDim.x, gp0 = (xcd - u * gdx) & 7;             // this XCD's first row group of u
+  const int dgroups = a.pf_down ? a.Ho / 16 : 0;
+  // One superblock: its activation operand (unless already requested), then
+  // the weights, and the compute waits for each part as it needs it; the
+  // first superblock with the prefetch also requests the down slabs behind
+  // its weights.
+  auto superblock = [&](int sb, bool stage_a, auto issue_down) __attribute__((always_inline)) {
+    if (stage_a) gu_aload_lds(xr, npr, H, sb, lane, region);
     __builtin_amdgcn_sched_barrier(0);
     GuStage<FMT, G> st;
     gu_load<FMT, G>(wr, up_base, gp, nsb, sb, lane, st);
+    if constexpr (decltype(issue_down)::value)
+      pf_issue(a.packed + (size_t)e * a.stride + down_off(FMT, H, I), dchunk * (uint32_t)dgroups, dchunk, dgroups,
+               xcd, ((gp - gp0) >> 3) * nw + wv, ((gdx - gp0 + 7) >> 3) * nw, pfd);
+    __builtin_amdgcn_sched_barrier(0);
     gu_compute<FMT, G, NV>(st, al, acc);
     if (WIDE && part1) {
       // the part-1 rows into the region once the part-0 operand reads are
@@ -893,7 +967,15 @@ __global__ __launch_bounds__(64 * GU_MAX_WAVES) void k_gateup(ExpertArgs a) {
       opaque(st);
       gu_compute<FMT, G, NV>(st, al, acc);
     }
+  };
+  if constexpr (PF) {
+    superblock(wv, false, std::true_type{});
+    for (int sb = wv + nw; sb < nsb; sb += nw) superblock(sb, true, std::false_type{});
+  } else {
+    for (int sb = wv; sb < nsb; sb += nw) superblock(sb, sb > wv, std::false_type{});
   }
+  if constexpr (PF)
+    if ((pf_fold(pfr) ^ pf_fold(pfd)) == a.pf_key) a.w.meta[8] = 1;
   // raw 16x16 results to this wave's LDS region (its operand is consumed)
   float4* dst = reinterpret_cast<float4*>(region) + lane;
 #pragma unroll
@@ -1357,6 +1439,14 @@ hipError_t launch_experts_fmt(const Layer& L, const Work& W, const Call& c, hipS
   const int G = wide ? 4 : 2;
   const size_t lds_gu = (size_t)nwg * wave_lds;   // ceiling raised at create
 
+  // prefetch: the next stack layer's router rows (as its router kernel's
+  // workgroups read them) and the down slabs
+  a.pf_key = 0x9E3779B9u;
+  a.pf_down = 1;
+  a.pf_next = c.next_router ? (const void*)c.next_router : (const void*)L.packed;
+  a.pf_next_bytes = c.next_router ? (uint32_t)((size_t)c.next_E * c.next_Ho * 4) : 0u;
+  a.pf_next_chunk = c.next_router ? decode_route_chunk_bytes(c.T, c.next_Ho) : 1024u;
+  a.pf_next_chunks = c.next_router ? (int)((a.pf_next_bytes + a.pf_next_chunk - 1) / a.pf_next_chunk) : 0;
   const dim3 ggu(L.I / (16 * G), umax);
 #define STRATA_GATEUP(GG)                                                                  \
   if (wide_t) launch(tr, k_gateup<FMT, GG, true, 4>, ggu, dim3(64 * nwg), lds_gu, s, a);    \
@@ -1473,6 +1563,10 @@ hipError_t launch_topk_block(const float* rows, size_t stride, const float* bias
                              float* w, hipStream_t s, Tracer* tr) {
   launch(tr, k_topk_block, dim3(T), dim3(1024), 0, s, rows, stride, bias, E, k, idx, w);
   return hipGetLastError();
+}
+
+uint32_t decode_route_chunk_bytes(int T, int Ho) {
+  return (uint32_t)(route_rows(T <= DECODE_NARROW_T ? T : 16) * Ho * 4);
 }
 
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,

@@ -65,6 +65,10 @@ struct Call {
   int T;
   float* out;
   uint32_t flags;
+  // decode gate/up prefetch of what a later kernel reads (a hint: no result
+  // depends on it): the router rows of the next layer of a stack (null: none)
+  const float* next_router = nullptr;
+  int next_E = 0, next_Ho = 0;
 };
 
 // Optional per-kernel timing: with a tracer armed, each kernel is launched
@@ -107,6 +111,9 @@ bool decode_fits(int T, int k, int E, int n_shared, int I);
 hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr,
                                bool permutation);
 hipError_t launch_decode_experts(const Layer& L, const Work& W, const Call& c, hipStream_t s, Tracer* tr);
+// bytes of the router rows one decode router workgroup reads for a call of T
+// tokens (the unit the gate/up kernel prefetches them in)
+uint32_t decode_route_chunk_bytes(int T, int Ho);
 
 // top-k of T logit rows (row t at rows + t * stride, + bias[e] when bias is
 // not null) for any k <= E <= 4096: one workgroup per token

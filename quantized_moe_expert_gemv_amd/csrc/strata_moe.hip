@@ -507,9 +507,16 @@ int strata_moe_stack_forward(strata_moe* const* layers, int32_t n_layers, const 
   for (int l = 0; l < n_layers; ++l) {
     // the last layer writes `out`; earlier layers alternate so that happens
     float* dst = ((n_layers - 1 - l) % 2 == 0) ? out : tmp;
-    const Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
+    Call c = make_call(cur, cur_dtype, T, dst, STRATA_ADD_INPUT);
+    const bool decode = use_decode(layers[l]->cfg, T, 0);
+    if (decode && l + 1 < n_layers && use_decode(layers[l + 1]->cfg, T, 0)) {
+      // this layer's gate/up kernel prefetches the next layer's router rows
+      c.next_router = layers[l + 1]->L.router_w;
+      c.next_E = layers[l + 1]->L.E;
+      c.next_Ho = layers[l + 1]->L.Ho;
+    }
     TraceScope ts(layers[l]);
-    int rc = run_forward(layers[l], layers[l]->W, c, use_decode(layers[l]->cfg, T, 0), s, ts.ptr);
+    int rc = run_forward(layers[l], layers[l]->W, c, decode, s, ts.ptr);
     if (rc) return rc;
     cur = dst;
     cur_dtype = STRATA_FP32;
