@@ -183,13 +183,15 @@ def run_workload(args, name):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    use_graph = (decode or skinny) and not args.eager
+    use_graph = not args.eager
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     if use_graph:
         # exactly `steps` steps: a captured rotation of g_len steps (the whole
         # (layer, batch) period, 8 stack passes, or all the steps when fewer)
-        # replayed steps // g_len times, plus a graph of the remainder
+        # replayed steps // g_len times, plus a graph of the remainder (the
+        # prefill chunks too: a graph replay is how a serving loop launches
+        # the layer, and its kernels then start without host launch gaps)
         g_len = min(steps, 8 if stack else period)
         reps, rem = divmod(steps, g_len)
         s = torch.cuda.Stream()

@@ -678,6 +678,31 @@ def test_trace_events_bracket_each_kernel(B, T, n_kernels):
         B.strata_moe_trace_next_call(layer.handle, evs[:3])
 
 
+# ------------------------------------------------------------------ stack driver vs chained layer calls
+@pytest.mark.parametrize("fmt", [2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2])
+def test_stack_matches_chained_layer_calls(B, fmt, T):
+    """The stack driver (whose single-token 2/3-bit layers also prefetch the
+    next layer's router rows and their down slabs) gives exactly what the
+    same layers give one call at a time, each adding its input; the first
+    layer's own output is also checked against the oracle."""
+    hls = [HostLayer(211, l, 256, 512, 16, 4, fmt, True) for l in range(4)]
+    layers = [device_layer(hl, 16, DEV) for hl in hls]
+    bits, xf = tokens(hls[0], 7, T)
+    x = to_device_bf16(bits, DEV)
+    h = B.stack_forward(layers, x)
+    cur = x
+    for layer in layers:
+        cur = layer.forward(cur, flags=B.STRATA_ADD_INPUT)
+    torch.cuda.synchronize()
+    assert torch.equal(h, cur), (h - cur).abs().max().item()
+    y1 = layers[0].forward(x).cpu().numpy().astype(np.float64)
+    ref, _ = hls[0].oracle(xf)
+    assert rel_l2(y1, ref) <= DECODE_TOL
+    for layer in layers:
+        layer.close()
+
+
 # ------------------------------------------------------------------ 48-layer Q3 stack (full size)
 @pytest.mark.timeout(900)
 def test_workload_stack48_q3(B):
