@@ -52,6 +52,21 @@ def test_decode_route_and_forward_tiny(B, fmt, T):
 
 
 @pytest.mark.parametrize("fmt", [2, 3, 4, 5])
+def test_decode_two_superblocks_per_wave(B, fmt):
+    """H = 3072 (12 superblocks): six gate/up waves of two superblocks each,
+    the case whose second superblock's slabs are requested while the first
+    computes (1-3 tokens), with the shared expert."""
+    hl, layer = tiny(fmt, n_shared=1, H=3072, I=256, E=16, k=4, max_tokens=16)
+    for T in (1, 2, 3, 5):
+        bits, xf = tokens(hl, 50 + T, T)
+        x = to_device_bf16(bits, DEV)
+        check_route(layer, hl, x, xf)
+        out = layer.forward(x).cpu().numpy()
+        ref, _ = hl.oracle(xf)
+        check_rows(out, ref, DECODE_TOL, f"decode H 3072 fmt {fmt} T {T}")
+
+
+@pytest.mark.parametrize("fmt", [2, 3, 4, 5])
 def test_decode_shared_expert_tiny(B, fmt):
     hl, layer = tiny(fmt, n_shared=1)
     for T in (1, 4, 16):
