@@ -10,12 +10,14 @@
 // kernel this small is the longest chain of dependent memory round trips and
 // instructions of one wave, not the bytes):
 //   k_route_gemv  router GEMV, one workgroup per 1 or 2 expert rows split over
-//                 its waves; each workgroup also writes a slice of the tokens as
-//                 two fp16 parts (x = p0 + p1 to 22 significant bits);
+//                 its waves; each workgroup reads the whole token rows, so it
+//                 also finds each token's operand scale 2^-e (up to 4
+//                 tokens) and writes a slice of the tokens as two fp16 parts
+//                 of x 2^-e (x 2^-e = p0 + p1 to 22 significant bits);
 //   k_topk        one workgroup per token: two-level radix selection of the k
-//                 largest logits and the renormalised softmax weights; it
-//                 also finds the token's operand scale (and rescales its
-//                 parts when the token needs one);
+//                 largest logits and the renormalised softmax weights (more
+//                 than 4 tokens: also the operand scale, rescaling the parts
+//                 of a token that needs one);
 //   k_gateup      one workgroup per (active expert, 32 rows of I): it finds
 //                 its expert from the top-k ids (experts chosen by any token,
 //                 ascending, then the shared one), its waves split the H
@@ -218,11 +220,14 @@ struct RouteArgs {
   int x_f32, T, H, E;        // H: the token-part rows' width (whole superblocks)
   int Ho;                    // the layer's hidden width
   float* logits;
-  _Float16* xparts;          // [2][T][H], zero past Ho (x 2^-e, see k_topk)
+  _Float16* xparts;          // [2][T][H], zero past Ho, of x 2^-e (e: the token's operand scale)
   int* part1;                // set to 1 when some token has a nonzero second part
+  int* texp;                 // [T] the exponent e of each token's operand scale 2^-e
 };
 
 constexpr int ROUTE_WAVES = 4;
+// up to this many tokens the router kernel finds the tokens' operand scales
+constexpr int TOKEN_SCALE_IN_ROUTE_T = 4;
 constexpr int ROUTE_BATCH = 4;   // float4 columns per lane issued together
 
 // token t, columns 4q..4q+3 of x as loaded (fp32 or bf16), and as fp32
@@ -250,8 +255,14 @@ constexpr int route_batch(int T) { return T <= 8 ? ROUTE_BATCH : 3; }
 
 // route_rows(T) expert rows per workgroup; its waves split the rows into
 // float4 columns (strided, so every load instruction of a wave reads 1 KiB
-// contiguously) and meet in LDS.  Each workgroup also writes its slice of the
-// tokens as fp16 parts.  TT and the input type are template constants so
+// contiguously) and meet in LDS.  Each workgroup reads every token's whole
+// row, so up to 4 tokens (SCALE) each also finds the tokens' operand scales
+// 2^-e (e from the largest magnitude: token_scale_exp) and writes its slice
+// of the tokens as fp16 parts of x 2^-e; workgroup 0 writes the exponents.
+// For more tokens the per-column maxima lengthen this kernel by more than
+// the top-k kernel's pass over the tokens costs (measured at 6 and 16
+// tokens): the parts are written unscaled and the top-k kernel rescales
+// (decode_token_scale).  TT and the input type are template constants so
 // that every load is unconditional (clamped into bounds) and all of a batch
 // are in flight together: TT = T up to 8, TT = 16 for 9..16 tokens (tokens
 // past T repeat the last one: loaded and computed, not stored).
@@ -259,9 +270,14 @@ template <int TT, bool XF32>
 __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
   constexpr int RR = route_rows(TT);
   constexpr int RB = route_batch(TT);
+  constexpr bool SCALE = TT <= TOKEN_SCALE_IN_ROUTE_T;
   __shared__ float part[ROUTE_WAVES][RR][TT];
+  __shared__ uint32_t s_max[ROUTE_WAVES][TT];         // per wave: each token's largest |x| (bits)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.Ho, E = a.E, e0 = blockIdx.x * RR, T = a.T;
+  uint32_t mx[TT];                                    // each token's largest |x| seen (bits)
+#pragma unroll
+  for (int t = 0; t < TT; ++t) mx[t] = 0u;
   const int nq = H >> 2;
   const float4* rows[RR];
 #pragma unroll
@@ -292,6 +308,9 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
         const float4 xv = x_quad_f32<XF32>(xr[j][t]);
+        if constexpr (SCALE)       // (clamped duplicate columns do not change a maximum)
+          mx[t] = max(mx[t], max(max(__float_as_uint(xv.x) & 0x7fffffffu, __float_as_uint(xv.y) & 0x7fffffffu),
+                                 max(__float_as_uint(xv.z) & 0x7fffffffu, __float_as_uint(xv.w) & 0x7fffffffu)));
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
           float d = w[j][r].x * xv.x;
@@ -310,9 +329,24 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
       const float s = wave_sum(acc[r][t]);
       if (lane == 0) part[wv][r][t] = s;
     }
-  // this workgroup's slice of the token rows as fp16 parts [part][t][a.H]
-  // (columns past the layer's width are zero); the top-k kernel rewrites the
-  // rows of a token that needs an operand scale (rare)
+  if constexpr (SCALE) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const uint32_t m = wave_max_u32(mx[t]);
+      if (lane == 0) s_max[wv][t] = m;
+    }
+  }
+  __syncthreads();
+  // token t's operand scale exponent
+  auto texp_of = [&](int t) __attribute__((always_inline)) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int w = 0; w < ROUTE_WAVES; ++w) m = max(m, s_max[w][t]);
+    return token_scale_exp(__uint_as_float(m));
+  };
+  if (SCALE && blockIdx.x == 0 && tid < T) a.texp[tid] = texp_of(tid);
+  // this workgroup's slice of the token rows as fp16 parts of x 2^-e (SCALE;
+  // else of x), [part][t][a.H] (columns past the layer's width are zero)
   const int Hp = a.H, n = T * Hp, chunk = (n + gridDim.x - 1) / gridDim.x, b = blockIdx.x;
   bool nz = false;
   for (int i = b * chunk + tid; i < min(n, (b + 1) * chunk); i += blockDim.x) {
@@ -320,7 +354,7 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     const int src = t * H + min(h, H - 1);
     float v = XF32 ? reinterpret_cast<const float*>(a.x)[src]
                    : bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[src]);
-    v = h < H ? v : 0.f;
+    v = h < H ? (SCALE ? v * pow2i(-texp_of(t)) : v) : 0.f;
     _Float16 p[NPART];
     split2(v, p);
 #pragma unroll
@@ -328,7 +362,6 @@ __global__ __launch_bounds__(64 * ROUTE_WAVES) void k_route_gemv(RouteArgs a) {
     nz |= p[1] != (_Float16)0.0f;
   }
   if (__ballot(nz) && lane == 0) *a.part1 = 1;
-  __syncthreads();
   if (tid < RR * TT) {
     const int r = tid / TT, t = tid - r * TT, e = e0 + r;
     float s = 0.f;
@@ -382,10 +415,12 @@ struct TopkArgs {
   Work w;
 };
 
-// The operand scale of token t (one workgroup, any number of waves): e from
-// the token's largest magnitude (token_scale_exp) into texp[t]; a token with
-// e > 0 has its fp16 parts (written unscaled by the router kernel) rewritten
-// as parts of x 2^-e.  s_m: one LDS word per wave.  Ends with a barrier.
+// The operand scale of token t for calls of more than 4 tokens (one
+// workgroup, any number of waves; up to 4 tokens the router kernel finds it):
+// e from the token's largest magnitude (token_scale_exp) into texp[t]; a
+// token with e > 0 has its fp16 parts (written unscaled by the router
+// kernel) rewritten as parts of x 2^-e.  s_m: one LDS word per wave.  Ends
+// with a barrier.
 __device__ inline void decode_token_scale(const TopkArgs& a, int t, uint32_t* s_m) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int per = a.x_f32 ? 4 : 8;                 // elements per 16-byte load
@@ -440,11 +475,11 @@ __global__ __launch_bounds__(64 * TOPK_WAVES) void k_topk(TopkArgs a) {
   const float* row = a.w.logits + (size_t)t * E;
   const int e0 = wv * 64 * V1;
   // the logits are requested first, so that they and the token row of the
-  // operand scale are in flight together
+  // operand scale (more than 4 tokens) are in flight together
   float val[V1];
 #pragma unroll
   for (int i = 0; i < V1; ++i) val[i] = row[min(e0 + lane + 64 * i, E - 1)];
-  decode_token_scale(a, t, s_m);
+  if (a.T > TOKEN_SCALE_IN_ROUTE_T) decode_token_scale(a, t, s_m);
   uint32_t u[V1];
 #pragma unroll
   for (int i = 0; i < V1; ++i) u[i] = e0 + lane + 64 * i < E ? sortable_bits(val[i]) : 0u;
@@ -504,11 +539,12 @@ __global__ __launch_bounds__(1024) void k_topk_block(const float* rows, size_t s
   block_topk(rows + t * stride, bias, E, k, idx + t * k, w + t * k);
 }
 
-// the decode path's selection past 64 (as above) and its token scale
+// the decode path's selection past 64 (as above), and its token scale for
+// more than 4 tokens
 __global__ __launch_bounds__(1024) void k_topk_block_decode(TopkArgs a) {
   __shared__ uint32_t s_m[16];
   const int t = blockIdx.x;
-  decode_token_scale(a, t, s_m);
+  if (a.T > TOKEN_SCALE_IN_ROUTE_T) decode_token_scale(a, t, s_m);
   block_topk(a.w.logits + (size_t)t * a.E, nullptr, a.E, a.k, a.w.topk_idx + (size_t)t * a.k,
              a.w.topk_w + (size_t)t * a.k);
 }
@@ -1574,6 +1610,7 @@ hipError_t launch_decode_route(const Layer& L, const Work& W, const Call& c, hip
   RouteArgs a;
   a.Wr = L.router_w; a.bias = L.router_b; a.x = c.x; a.x_f32 = c.x_f32; a.T = c.T;
   a.H = L.H; a.Ho = L.Ho; a.E = L.E; a.logits = W.logits; a.xparts = W.xparts; a.part1 = W.meta + 3;
+  a.texp = W.texp;
   switch (c.T) {
 #define STRATA_ROUTE(TT)                                                                 \
     case TT:                                                                               \
