@@ -256,7 +256,10 @@ def run_workload(args, name):
         step(i, trace_events=ev_sets[i])
     torch.cuda.synchronize()
     dur = np.array([[ev[2 * j].elapsed_time(ev[2 * j + 1]) for j in range(len(knames))] for ev in ev_sets])
-    kern_us = dur.mean(axis=0) * 1e3
+    # the median over the traced steps: single dispatches launched one at a
+    # time with their own events now and then run several microseconds long
+    # (the mean of a decode kernel moved by up to 3 us from run to run)
+    kern_us = np.median(dur, axis=0) * 1e3
 
     # algorithmic work per launch
     bq = canonical_block_bytes(w.fmt)
