@@ -192,13 +192,14 @@ STRATA_API int strata_moe_route(strata_moe* h, const void* x, int32_t x_dtype, i
  * fp16 with fp32 accumulation (weights below 2^-24 in magnitude round to
  * zero there); the prefill router stays fp32-accurate.
  * Range: the 16-bit token operands of both paths hold x_t 2^-e_t, with e_t
- * chosen per token from its largest magnitude m_t (0 while m_t < 16, else
- * the power that brings it below 16, at most 60), the SwiGLU activations
- * are kept as silu(g) u 2^-2e_t and the expert outputs are scaled back by
- * 2^2e_t: every step is a power of two, so a token's results do not depend
- * on e_t and tokens up to 2^64 in magnitude stay in range.  The activations
- * still have to fit the 16-bit range at that scale (|silu(g) u| 2^-2e_t
- * below 65504: weights of ordinary magnitude keep them far inside it).
+ * chosen per token from its largest magnitude m_t (0 while 2^-4 <= m_t < 16,
+ * else the power that brings m_t into [8, 16), |e_t| <= 60; 0 for an
+ * all-zero token), the SwiGLU activations are kept as silu(g) u 2^-2e_t and
+ * the expert outputs are scaled back by 2^2e_t: every step is a power of
+ * two, so a token's results do not depend on e_t, and tokens from about
+ * 2^-64 to 2^64 in magnitude keep their precision.  The activations still
+ * have to fit the 16-bit range at that scale (|silu(g) u| 2^-2e_t below
+ * 65504: weights of ordinary magnitude keep them far inside it).
  */
 STRATA_API int strata_moe_forward(strata_moe* h, const void* x, int32_t x_dtype, int32_t T,
                        float* out, uint32_t flags, void* stream);

@@ -178,16 +178,21 @@ __device__ inline float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------ token range
 // The 16-bit token operands of both paths hold x 2^-e, where e is chosen per
-// token from its largest magnitude m (m < 2^E): e = E - 4 when m reaches 16,
-// else 0, at most 60 (so an ordinary token is not scaled at all).  The
-// expert sums then come out scaled by 2^-e; gate/up takes silu on the
-// unscaled gate and stores silu(g) u 2^-2e (the activation grows with the
-// square of the input, so it stays in range with it), and the combine
-// multiplies that expert output by 2^2e.  Every step is a power of two, exact.
+// token from its largest magnitude m (2^(E-1) <= m < 2^E): e = E - 4 when m
+// reaches 16 or stays below 2^-4 (either way the scaled token's largest
+// magnitude lands in [8, 16)), else 0, and |e| <= 60 (an ordinary token, and
+// an all-zero one, is not scaled at all).  The expert sums then come out
+// scaled by 2^-e; gate/up takes silu on the unscaled gate and stores
+// silu(g) u 2^-2e (the activation goes with the square of the input: a large
+// token's would overflow fp16, a tiny token's would sink below fp16's normal
+// range and lose its bits), and the combine multiplies that expert output by
+// 2^2e.  Every step is a power of two, exact.
 constexpr int TOKEN_SCALE_MAX_EXP = 60;
 __device__ inline int token_scale_exp(float maxabs) {
-  const int E = (int)((__float_as_uint(maxabs) >> 23) & 0xffu) - 126;
-  return min(max(E - 4, 0), TOKEN_SCALE_MAX_EXP);
+  const uint32_t b = __float_as_uint(maxabs);
+  const int E = (int)((b >> 23) & 0xffu) - 126;
+  const int e = (E > 4 || E < -3) ? E - 4 : 0;
+  return b == 0u ? 0 : min(max(e, -TOKEN_SCALE_MAX_EXP), TOKEN_SCALE_MAX_EXP);
 }
 // 2^n for |n| <= 126, exactly
 __device__ inline float pow2i(int n) { return __uint_as_float((uint32_t)(127 + n) << 23); }

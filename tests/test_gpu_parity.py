@@ -320,7 +320,7 @@ def test_one_launch_route_refuses_large_calls(B):
 
 @pytest.mark.parametrize("fmt,n_shared", [(2, 0), (5, 1)])
 @pytest.mark.parametrize("factor", [1e3, 1e6, 2.0 ** 40])
-@pytest.mark.parametrize("T", [3, 12, 40])
+@pytest.mark.parametrize("T", [1, 3, 6, 12, 40])
 def test_tokens_far_beyond_the_fp16_range(B, fmt, n_shared, factor, T):
     """Tokens scaled up to 2^40 (bf16 and fp32): the 16-bit operands hold each
     token times a power of two chosen from its largest magnitude, the
@@ -356,6 +356,26 @@ def test_tokens_far_beyond_the_fp16_range(B, fmt, n_shared, factor, T):
     idx, w, _, _ = layer.route(x32)
     check_rows(out32, hl.mixture(x32f, idx.cpu().numpy(), w.cpu().numpy()), tol,
                f"x * {factor:g} fp32 fmt {fmt} T {T}, device weights")
+
+
+@pytest.mark.parametrize("fmt", [2, 4])
+@pytest.mark.parametrize("T", [2, 4, 6, 12])
+def test_mixed_token_scales_in_one_call(B, fmt, T):
+    """Tokens of one call at different magnitudes (x1, x1e3, x2^40, x1e-3
+    in turn): each takes its own operand scale (found by the router kernel up
+    to 4 tokens, by the top-k kernel above), so every row matches the
+    oracle's experts weighted by the device router's weights."""
+    hl, layer = tiny(fmt)
+    bits, xf = tokens(hl, 1700 + T, T)
+    f = np.array([1.0, 1e3, 2.0 ** 40, 1e-3])[np.arange(T) % 4][:, None]
+    xs = (xf * f).astype(np.float32)
+    for x, xd in ((xs.astype(np.float64), torch.from_numpy(xs).to(DEV)),
+                  (G.bf16_bits_to_f32(G.f32_to_bf16_bits(xs)).astype(np.float64),
+                   torch.from_numpy(G.f32_to_bf16_bits(xs).astype(np.int16)).to(DEV).view(torch.bfloat16))):
+        out = layer.forward(xd).cpu().numpy()
+        idx, w, _, _ = layer.route(xd)
+        check_rows(out, hl.mixture(x, idx.cpu().numpy(), w.cpu().numpy()), DECODE_TOL,
+                   f"mixed scales fmt {fmt} T {T} {xd.dtype}")
 
 
 @pytest.mark.parametrize("fmt,scale", [(2, np.inf), (2, np.nan), (2, 40000.0), (3, 20000.0), (4, 8192.0),
