@@ -418,7 +418,7 @@ struct TopkArgs {
 // The operand scale of token t for calls of more than 4 tokens (one
 // workgroup, any number of waves; up to 4 tokens the router kernel finds it):
 // e from the token's largest magnitude (token_scale_exp) into texp[t]; a
-// token with e > 0 has its fp16 parts (written unscaled by the router
+// token with e != 0 has its fp16 parts (written unscaled by the router
 // kernel) rewritten as parts of x 2^-e.  s_m: one LDS word per wave.  Ends
 // with a barrier.
 __device__ inline void decode_token_scale(const TopkArgs& a, int t, uint32_t* s_m) {

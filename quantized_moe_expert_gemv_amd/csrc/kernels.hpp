@@ -23,7 +23,10 @@ struct Work {
   int* udesc;         // [E+1][2]   decode: per active expert {expert id, token mask}
   float* wtab;        // [E+1][8 or 16] decode: routing weight per (active expert, token), 0 if not routed
   int* meta;          // [16]       meta[0] active experts (decode), meta[1] GEMM tiles (prefill),
-                      //            meta[2] prefill: some token of the call is scaled (e > 0)
+                      //            meta[2] prefill: some token of the call is scaled (e != 0),
+                      //            meta[3] decode: some token has a nonzero second fp16 part,
+                      //            meta[4] create: block scales the operands cannot carry,
+                      //            meta[8] decode: the prefetch's discarded word
   int* chunk_base;    // [nchunks][E] prefill: per-chunk counts, then bases
   int* pair_rank;     // [Tmax*k]   prefill: rank of a pair inside its chunk
   int* texp;          // [Tmax]     the exponent e of each token's operand scale 2^-e

@@ -94,7 +94,7 @@ struct TopkArgs {
 
 // The operand scale of token t (one wave): e from the token's largest
 // magnitude (token_scale_exp), taken from the router's per-split maxima when
-// it wrote them, else from the token row; when e > 0 the wave rewrites the
+// it wrote them, else from the token row; when e != 0 the wave rewrites the
 // token's fp16 row as x 2^-e (the router wrote it unscaled) and marks the
 // call scaled (meta[2], cleared by the router kernel, read by the gate/up
 // GEMM).
